@@ -1,0 +1,167 @@
+/*
+ * hc.h — C ABI of the sparse-KV hot-cache decode step for one MI355X (gfx950).
+ *
+ * Source of the method: the page "From 1M Total to 15+ × 1M Contexts: GLM-5.3
+ * KV Cache Offloading" (zhuai.tech).  Each decode step the DSA indexer picks
+ * the top-2,048 history positions (section "Separate historical capacity from
+ * the current working set"); the GPU itself checks its hot slots, hits are read
+ * from VRAM, misses are read from registered host RAM, and the gather emits a
+ * compact selection for attention (section "Decision three: let the GPU manage
+ * the hot cache directly", and its data-flow figure).  Slots used by the
+ * current round may not be replaced, and a slot filled in a round is not read
+ * by another block of the same gather (section "GPU cache management has
+ * hazards too").  Replacement here is a deterministic LRU: the victim is the
+ * slot with the oldest last-use step, ties to the lowest slot index.
+ *
+ * One call of hc_step performs, for every session s and selection group g:
+ *   1. exact top-K of the fp32 scores over positions [0, hist_len[s]),
+ *      ranked by IEEE-754 totalOrder, ties to the lower position, emitted in
+ *      ascending position order;
+ *   2. a lookup of each selected position in the group's slot map; hits get
+ *      last_use = t;
+ *   3. the i-th miss (ascending position) takes the i-th victim in ascending
+ *      (last_use, slot) order among slots with last_use != t; the evicted
+ *      position leaves the map;
+ *   4. for every layer of the group, the missing rows are copied from pinned
+ *      host RAM into the victim slots;
+ *   5. every selected row is read from its hot slot and dequantised:
+ *      out[j] = bf16_rne((float)int8 latent[j] * (float)fp16 scale[j / 64])
+ *      for j < 512, out[512 + k] = RoPE bf16 k for k < 64.
+ * t is the number of earlier hc_step calls on the context (0-based).
+ *
+ * Row format (Q8G64 MLA row, 656 B; the page's payload description): bytes
+ * [0,512) int8 latent, [512,528) 8 little-endian fp16 scales (scale g covers
+ * latent bytes [64g, 64g+64)), [528,656) 64 little-endian bf16 RoPE values.
+ *
+ * Layout conventions used below:  S sessions, L layers per session, R layers
+ * per selection, G = ceil(L / R) selection groups (layer l is in group l / R),
+ * K = top_k, C = cache_slots, Hcap = max_positions.
+ *
+ * Threading: a context is not thread-safe.  Steps of one context must be issued
+ * in order; they may use different streams only if the caller orders them.
+ * All entry points return HC_OK or a negative hc_status; none throws.
+ */
+#ifndef HC_H
+#define HC_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define HC_ROW_BYTES     656   /* bytes of one Q8G64 MLA row                */
+#define HC_LATENT_BYTES  512   /* int8 latent bytes, offset 0               */
+#define HC_SCALE_OFFSET  512   /* 8 x fp16 group scales                     */
+#define HC_ROPE_OFFSET   528   /* 64 x bf16 RoPE                            */
+#define HC_OUT_ELEMS     576   /* bf16 values per gathered row (512 + 64)   */
+#define HC_MAX_TOPK      4096  /* largest supported top_k                   */
+#define HC_MAX_SLOTS     262144 /* largest supported cache_slots            */
+
+/* Per-unit trace record: HC_TRACE_INTS(K) int32 values per (session, group),
+ * units ordered u = s * G + g.  Layout:
+ *   [0] n_hit   [1] n_miss   [2] n_evict (victims whose slot held a position)
+ *   [3] reserved (0)
+ *   [4 + 0K .. 4 + 1K)  slot of selected row i after the step (sel order)
+ *   [4 + 1K .. 4 + 2K)  miss_pos: missing positions, ascending; -1 past n_miss
+ *   [4 + 2K .. 4 + 3K)  victim slot paired with miss i; -1 past n_miss
+ *   [4 + 3K .. 4 + 4K)  position evicted from that slot, -1 if it was empty   */
+#define HC_TRACE_HEADER  4
+#define HC_TRACE_INTS(k) (HC_TRACE_HEADER + 4 * (k))
+
+/* Kernel stages timed by hc_profile_read, in launch order. */
+#define HC_STAGE_TOPK_HIST   0  /* score scan: top-12-bit key histogram     */
+#define HC_STAGE_TOPK_FILTER 1  /* score scan: bin filter and compaction    */
+#define HC_STAGE_SELECT      2  /* exact cut, lookup, miss compaction, LRU  */
+#define HC_STAGE_FETCH       3  /* host RAM -> HBM miss rows (PCIe)          */
+#define HC_STAGE_GATHER      4  /* hot slots -> bf16 attention buffer        */
+#define HC_NUM_STAGES        5
+
+typedef enum {
+  HC_OK      = 0,
+  HC_E_INVAL = -1,  /* bad argument or configuration; nothing was changed   */
+  HC_E_NOMEM = -2,  /* workspace too small or host allocation failed        */
+  HC_E_HIP   = -3,  /* a HIP call failed; the context is now poisoned       */
+  HC_E_STATE = -4   /* the context is poisoned; only hc_destroy is allowed  */
+} hc_status;
+
+typedef struct hc_config {
+  uint32_t struct_size;       /* sizeof(hc_config)                              */
+  uint32_t n_sessions;        /* S >= 1                                         */
+  uint32_t n_layers;          /* L >= 1 layers per session                      */
+  uint32_t layers_per_select; /* R >= 1                                         */
+  uint32_t cache_slots;       /* C, top_k <= C <= HC_MAX_SLOTS                  */
+  uint32_t top_k;             /* K, 1 <= K <= HC_MAX_TOPK                       */
+  uint64_t max_positions;     /* Hcap: host rows per (session, layer),
+                                 K <= Hcap < 2^31                               */
+  int32_t  device;            /* HIP device ordinal                             */
+  uint32_t flags;             /* must be 0                                      */
+} hc_config;
+
+typedef struct hc_ctx hc_ctx;
+
+/* Exact device-workspace size in bytes for cfg (slot maps, LRU order, score
+ * scan scratch, and the S*L*C hot rows).  HC_E_INVAL for an invalid cfg. */
+hc_status hc_workspace_bytes(const hc_config* cfg, uint64_t* bytes);
+
+/* Creates a context on cfg->device.  dev_workspace: caller-owned device memory
+ * of at least hc_workspace_bytes bytes, 256-B aligned, that the caller keeps
+ * alive and untouched until hc_destroy returns.  The library allocates the
+ * pinned host row store itself: S*L buffers of Hcap*656 B (hipHostMalloc,
+ * mapped), and initialises the workspace (all caches empty) before returning.
+ * All-or-nothing: on failure nothing stays allocated and *out is NULL. */
+hc_status hc_create(const hc_config* cfg, void* dev_workspace, uint64_t ws_bytes,
+                    hc_ctx** out);
+
+/* Host pointer to the pinned row store of (session, layer): Hcap rows of
+ * HC_ROW_BYTES, row p at offset p * 656.  Owned by the library, valid until
+ * hc_destroy.  The caller writes row p before the first hc_step whose
+ * hist_len exceeds p and never changes it afterwards.  NULL on a bad index. */
+uint8_t* hc_host_rows(hc_ctx* ctx, uint32_t session, uint32_t layer);
+
+/* One decode step, enqueued on `stream` (a hipStream_t; NULL = default stream).
+ *   d_scores     device fp32 [S][G][score_stride]; unit (s,g) uses entries
+ *                [0, hist_len[s]).
+ *   score_stride elements between units, >= max_s hist_len[s].
+ *   hist_len     host uint64 [S]: positions in each session's history this
+ *                step; K <= hist_len[s] <= Hcap, never smaller than at the
+ *                previous step.
+ *   d_out        device bf16 bits [S][L][K][576], rows in selection order.
+ *   d_sel        device int32 [S][G][K]: selected positions, ascending.
+ *   d_trace      NULL, or device int32 [S*G][HC_TRACE_INTS(K)] (see above).
+ * Asynchronous: results are valid once the stream has completed the step.
+ * All arguments are checked before anything is enqueued; a rejected call
+ * (HC_E_INVAL) changes nothing.  A HIP launch failure returns HC_E_HIP and
+ * poisons the context. */
+hc_status hc_step(hc_ctx* ctx, void* stream, const float* d_scores,
+                  uint64_t score_stride, const uint64_t* hist_len,
+                  uint16_t* d_out, int32_t* d_sel, int32_t* d_trace);
+
+/* Synchronous snapshot for tests: waits for all enqueued steps, then copies
+ * the state that layer `layer` of `session` sees into host buffers:
+ * slot2pos[C] and last_use[C] (-1 = empty / never used), pos2slot[Hcap] if
+ * non-NULL, and the layer's hot rows [C][656] if hot_rows is non-NULL. */
+hc_status hc_export_state(hc_ctx* ctx, uint32_t session, uint32_t layer,
+                          int32_t* slot2pos, int32_t* last_use,
+                          int32_t* pos2slot, uint8_t* hot_rows);
+
+/* Per-stage kernel timing with HIP events recorded around each launch on the
+ * step's stream.  hc_profile_enable(ctx, n) arms timing for the next n steps
+ * (n = 0 disarms); hc_profile_read waits for them and returns the summed
+ * milliseconds per stage (HC_NUM_STAGES values) and the number of steps. */
+hc_status hc_profile_enable(hc_ctx* ctx, uint32_t max_steps);
+hc_status hc_profile_read(hc_ctx* ctx, double* stage_ms, uint64_t* n_steps);
+
+/* Number of steps issued so far (the t the next hc_step will use). */
+hc_status hc_steps_done(const hc_ctx* ctx, uint64_t* n);
+
+/* Waits for every step the context enqueued, then frees the pinned host store
+ * and the context.  The caller's workspace is not freed.  NULL-safe. */
+hc_status hc_destroy(hc_ctx* ctx);
+
+const char* hc_status_str(hc_status s);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* HC_H */

@@ -1,0 +1,220 @@
+"""ctypes binding of the plain-C CPU oracle (oracle/oracle.c).
+
+TEST INFRASTRUCTURE ONLY.  Only tests/, __graft_entry__.smoke() and the
+CPU-baseline leg of bench.py may import this package; the HIP product path
+never does.  The oracle shares no code with the HIP library.
+"""
+import ctypes
+import os
+
+import numpy as np
+
+from . import build as _build
+
+_LIB = None
+
+_i32p = ctypes.POINTER(ctypes.c_int32)
+_u16p = ctypes.POINTER(ctypes.c_uint16)
+_u8p = ctypes.POINTER(ctypes.c_uint8)
+_f32p = ctypes.POINTER(ctypes.c_float)
+
+ROW_BYTES = 656
+OUT_ELEMS = 576
+
+
+class StepInfo(ctypes.Structure):
+    _fields_ = [("n_hit", ctypes.c_int32), ("n_miss", ctypes.c_int32),
+                ("n_evict", ctypes.c_int32),
+                ("slot", _i32p), ("miss_pos", _i32p),
+                ("victim", _i32p), ("evicted", _i32p)]
+
+
+def lib():
+    global _LIB
+    if _LIB is None:
+        path = _build.LIB
+        if not os.path.exists(path):
+            _build.build()
+        L = ctypes.CDLL(path)
+        L.orc_topk.argtypes = [_f32p, ctypes.c_int64, ctypes.c_int32, _i32p]
+        L.orc_topk.restype = ctypes.c_int
+        L.orc_dequant_elem.argtypes = [ctypes.c_int8, ctypes.c_uint16]
+        L.orc_dequant_elem.restype = ctypes.c_uint16
+        L.orc_dequant_row.argtypes = [_u8p, _u16p]
+        L.orc_dequant_row.restype = None
+        L.orc_dequant_table.argtypes = [_u16p]
+        L.orc_dequant_table.restype = None
+        L.orc_cache_new.argtypes = [ctypes.c_int32, ctypes.c_int64]
+        L.orc_cache_new.restype = ctypes.c_void_p
+        L.orc_cache_free.argtypes = [ctypes.c_void_p]
+        L.orc_cache_free.restype = None
+        L.orc_cache_step.argtypes = [ctypes.c_void_p, ctypes.c_int32, _i32p, ctypes.c_int32,
+                                     _u8p, ctypes.POINTER(StepInfo)]
+        L.orc_cache_step.restype = ctypes.c_int
+        L.orc_gather.argtypes = [ctypes.c_void_p, _i32p, ctypes.c_int32, _u16p]
+        L.orc_gather.restype = ctypes.c_int
+        for name in ("orc_cache_slot_of", "orc_cache_pos_of", "orc_cache_last"):
+            getattr(L, name).argtypes = [ctypes.c_void_p]
+            getattr(L, name).restype = _i32p
+        L.orc_cache_hot.argtypes = [ctypes.c_void_p]
+        L.orc_cache_hot.restype = _u8p
+        L.orc_model_step.argtypes = [
+            ctypes.POINTER(ctypes.c_void_p), ctypes.POINTER(_u8p),
+            ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+            ctypes.POINTER(_f32p), ctypes.POINTER(ctypes.c_int64),
+            _i32p, _u16p, ctypes.POINTER(StepInfo), ctypes.c_int32]
+        L.orc_model_step.restype = ctypes.c_int
+        _LIB = L
+    return _LIB
+
+
+def _ptr(a, typ):
+    return a.ctypes.data_as(typ)
+
+
+def topk(scores, k):
+    """Exact top-k positions of fp32 scores (totalOrder, ties to lower
+    position), ascending."""
+    s = np.ascontiguousarray(scores, dtype=np.float32)
+    sel = np.empty(k, dtype=np.int32)
+    if lib().orc_topk(_ptr(s, _f32p), s.size, k, _ptr(sel, _i32p)) != 0:
+        raise ValueError("orc_topk: need 1 <= k <= len(scores)")
+    return sel
+
+
+def dequant_elem(q, scale_bits):
+    return lib().orc_dequant_elem(int(q), int(scale_bits))
+
+
+def dequant_row(row):
+    r = np.ascontiguousarray(row, dtype=np.uint8)
+    assert r.size == ROW_BYTES
+    out = np.empty(OUT_ELEMS, dtype=np.uint16)
+    lib().orc_dequant_row(_ptr(r, _u8p), _ptr(out, _u16p))
+    return out
+
+
+def dequant_table():
+    """table[q + 128, scale_bits] for every int8 q and every fp16 bit pattern."""
+    t = np.empty((256, 65536), dtype=np.uint16)
+    lib().orc_dequant_table(_ptr(t, _u16p))
+    return t
+
+
+class _InfoBufs:
+    def __init__(self, k):
+        self.slot = np.empty(k, np.int32)
+        self.miss_pos = np.empty(k, np.int32)
+        self.victim = np.empty(k, np.int32)
+        self.evicted = np.empty(k, np.int32)
+        self.info = StepInfo(0, 0, 0, _ptr(self.slot, _i32p), _ptr(self.miss_pos, _i32p),
+                             _ptr(self.victim, _i32p), _ptr(self.evicted, _i32p))
+
+    def result(self):
+        n = self.info.n_miss
+        return {"n_hit": self.info.n_hit, "n_miss": n, "n_evict": self.info.n_evict,
+                "slot": self.slot.copy(), "miss_pos": self.miss_pos.copy(),
+                "victim": self.victim.copy(), "evicted": self.evicted.copy()}
+
+
+class Cache:
+    """LRU hot cache of one (session, layer)."""
+
+    def __init__(self, slots, hcap):
+        self.C, self.hcap = int(slots), int(hcap)
+        self._p = lib().orc_cache_new(self.C, self.hcap)
+        if not self._p:
+            raise MemoryError("orc_cache_new failed")
+
+    def close(self):
+        if self._p:
+            lib().orc_cache_free(self._p)
+            self._p = None
+
+    def __del__(self):
+        self.close()
+
+    def step(self, t, sel, host_rows):
+        sel = np.ascontiguousarray(sel, dtype=np.int32)
+        rows = np.ascontiguousarray(host_rows, dtype=np.uint8)
+        assert rows.size >= self.hcap * ROW_BYTES
+        bufs = _InfoBufs(sel.size)
+        rc = lib().orc_cache_step(self._p, int(t), _ptr(sel, _i32p), sel.size,
+                                  _ptr(rows, _u8p), ctypes.byref(bufs.info))
+        if rc != 0:
+            raise ValueError("orc_cache_step rejected its input")
+        return bufs.result()
+
+    def gather(self, sel):
+        sel = np.ascontiguousarray(sel, dtype=np.int32)
+        out = np.empty((sel.size, OUT_ELEMS), dtype=np.uint16)
+        if lib().orc_gather(self._p, _ptr(sel, _i32p), sel.size, _ptr(out, _u16p)) != 0:
+            raise ValueError("orc_gather: a selected position is not resident")
+        return out
+
+    def slot_of(self):
+        return np.ctypeslib.as_array(lib().orc_cache_slot_of(self._p), (self.hcap,)).copy()
+
+    def pos_of(self):
+        return np.ctypeslib.as_array(lib().orc_cache_pos_of(self._p), (self.C,)).copy()
+
+    def last(self):
+        return np.ctypeslib.as_array(lib().orc_cache_last(self._p), (self.C,)).copy()
+
+    def hot(self):
+        return np.ctypeslib.as_array(lib().orc_cache_hot(self._p),
+                                     (self.C, ROW_BYTES)).copy()
+
+
+class Model:
+    """S sessions x L layers, one selection per group of R layers; each layer
+    keeps its own LRU cache.  host_rows[s][l] is a uint8 [hcap, 656] array."""
+
+    def __init__(self, n_sessions, n_layers, layers_per_select, top_k, slots, hcap, host_rows):
+        self.S, self.L, self.R = int(n_sessions), int(n_layers), int(layers_per_select)
+        self.G = -(-self.L // self.R)
+        self.K, self.C, self.hcap = int(top_k), int(slots), int(hcap)
+        self.caches = [Cache(slots, hcap) for _ in range(self.S * self.L)]
+        self.rows = [np.ascontiguousarray(host_rows[s][l], dtype=np.uint8)
+                     for s in range(self.S) for l in range(self.L)]
+        for r in self.rows:
+            assert r.size >= self.hcap * ROW_BYTES
+        n = self.S * self.L
+        self._cache_arr = (ctypes.c_void_p * n)(*[c._p for c in self.caches])
+        self._rows_arr = (_u8p * n)(*[_ptr(r, _u8p) for r in self.rows])
+
+    def cache(self, s, l):
+        return self.caches[s * self.L + l]
+
+    def step(self, t, scores, hist_len, gather=True, info=True, nthreads=1):
+        """scores[s*G + g]: fp32 array of at least hist_len[s] entries.
+        Returns (sel [S,G,K], out [S,L,K,576] or None, infos list or None)."""
+        units = self.S * self.G
+        sc = [np.ascontiguousarray(x, dtype=np.float32) for x in scores]
+        assert len(sc) == units
+        for u, x in enumerate(sc):
+            assert x.size >= hist_len[u // self.G]
+        sc_arr = (_f32p * units)(*[_ptr(x, _f32p) for x in sc])
+        hl = np.ascontiguousarray(hist_len, dtype=np.int64)
+        sel = np.empty((self.S, self.G, self.K), np.int32)
+        out = np.empty((self.S, self.L, self.K, OUT_ELEMS), np.uint16) if gather else None
+        bufs = [_InfoBufs(self.K) for _ in range(self.S * self.L)] if info else None
+        info_arr = (StepInfo * (self.S * self.L))(*[b.info for b in bufs]) if info else None
+        rc = lib().orc_model_step(
+            self._cache_arr, self._rows_arr, self.S, self.L, self.R, self.K, int(t),
+            sc_arr, _ptr(hl, ctypes.POINTER(ctypes.c_int64)), _ptr(sel, _i32p),
+            _ptr(out, _u16p) if gather else None, info_arr, int(nthreads))
+        if rc != 0:
+            raise ValueError("orc_model_step failed")
+        infos = None
+        if info:
+            # the structs were copied into info_arr; read counts back from there
+            infos = []
+            for i, b in enumerate(bufs):
+                b.info = info_arr[i]
+                infos.append(b.result())
+        return sel, out, infos
+
+    def close(self):
+        for c in self.caches:
+            c.close()

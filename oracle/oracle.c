@@ -1,0 +1,325 @@
+/*
+ * oracle.c — plain CPU oracle of the sparse-KV hot-cache decode step.
+ *
+ * TEST INFRASTRUCTURE ONLY: used by the tests, the smoke check and the
+ * CPU-baseline leg of the benchmark; never by the product path.  Written from
+ * the page "From 1M Total to 15+ × 1M Contexts: GLM-5.3 KV Cache Offloading"
+ * (zhuai.tech), sections "Separate historical capacity from the current
+ * working set", "Decision three: let the GPU manage the hot cache directly"
+ * and "GPU cache management has hazards too".  Each function is the plain
+ * definition of its step, in the order the step is defined; no blocking,
+ * fusion or reordering.  Parity pins: tests/test_oracle_*.py.
+ */
+#include "oracle.h"
+
+#include <math.h>
+#include <pthread.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* ---------------------------------------------------------------- top-K -- */
+
+/* IEEE-754 totalOrder as an unsigned integer: negative numbers reverse their
+ * bit order below all positive ones, so -0 < +0 and NaNs sort by their bits. */
+static uint32_t total_order_key(float f) {
+  uint32_t b;
+  memcpy(&b, &f, sizeof b);
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+
+typedef struct { uint32_t key; int32_t pos; } ranked;
+
+/* Rank order: larger key first; equal keys by ascending position. */
+static int cmp_rank(const void* a, const void* b) {
+  const ranked* x = (const ranked*)a;
+  const ranked* y = (const ranked*)b;
+  if (x->key != y->key) return x->key > y->key ? -1 : 1;
+  return (x->pos > y->pos) - (x->pos < y->pos);
+}
+
+static int cmp_int32(const void* a, const void* b) {
+  int32_t x = *(const int32_t*)a, y = *(const int32_t*)b;
+  return (x > y) - (x < y);
+}
+
+int orc_topk(const float* scores, int64_t H, int32_t K, int32_t* sel) {
+  if (K < 1 || (int64_t)K > H) return -1;
+  ranked* all = (ranked*)malloc((size_t)H * sizeof(ranked));
+  if (!all) return -1;
+  for (int64_t p = 0; p < H; ++p) {
+    all[p].key = total_order_key(scores[p]);
+    all[p].pos = (int32_t)p;
+  }
+  /* Full sort of every position by rank, then the first K by position. */
+  qsort(all, (size_t)H, sizeof(ranked), cmp_rank);
+  for (int32_t i = 0; i < K; ++i) sel[i] = all[i].pos;
+  qsort(sel, (size_t)K, sizeof(int32_t), cmp_int32);
+  free(all);
+  return 0;
+}
+
+/* -------------------------------------------------------------- dequant -- */
+
+/* Value of an IEEE binary16 bit pattern (sign, 5-bit exponent, 10-bit
+ * fraction; exponent 0 = subnormal, 31 = Inf/NaN). */
+static double fp16_value(uint16_t h) {
+  int sign = h >> 15, e = (h >> 10) & 31, m = h & 1023;
+  double v;
+  if (e == 0)
+    v = ldexp((double)m, -24);            /* 0.m x 2^-14 = m x 2^-24        */
+  else if (e == 31)
+    v = m ? NAN : INFINITY;
+  else
+    v = ldexp((double)(1024 + m), e - 25); /* 1.m x 2^(e-15)                */
+  return sign ? -v : v;
+}
+
+/* Round a double to the nearest bfloat16 (1 sign, 8 exponent, 7 fraction
+ * bits), ties to even, and return its bit pattern. */
+static uint16_t bf16_round_double(double x) {
+  uint16_t sign = signbit(x) ? 0x8000 : 0;
+  if (isnan(x)) return 0x7FC0;
+  double a = fabs(x);
+  if (a == 0.0) return sign;
+  if (isinf(a)) return sign | 0x7F80;
+  int e;
+  double m = frexp(a, &e);            /* a = m x 2^e, m in [0.5, 1)        */
+  int E = e - 1;                      /* a = (2m) x 2^E, 2m in [1, 2)      */
+  double units, ulp_exp;
+  if (E >= -126) {
+    units = ldexp(m, 8);              /* significand in units of its ulp   */
+    ulp_exp = E - 7;
+  } else {                            /* subnormal: fixed ulp 2^-133       */
+    units = ldexp(a, 133);
+    ulp_exp = -133;
+  }
+  double fl = floor(units), frac = units - fl;
+  if (frac > 0.5 || (frac == 0.5 && fmod(fl, 2.0) != 0.0)) fl += 1.0;
+  double r = ldexp(fl, (int)ulp_exp); /* rounded magnitude, exact          */
+  if (r >= 0x1.0p128) return sign | 0x7F80;  /* beyond the bf16 range     */
+  /* Encode r: normal if r >= 2^-126, else subnormal with ulp 2^-133. */
+  if (r < 0x1.0p-126) return sign | (uint16_t)ldexp(r, 133);
+  int re;
+  double rm = frexp(r, &re);          /* r = rm x 2^re, rm in [0.5, 1)     */
+  uint16_t exp_field = (uint16_t)(re - 1 + 127);
+  uint16_t frac_field = (uint16_t)(ldexp(rm, 8) - 128.0);
+  return sign | (uint16_t)(exp_field << 7) | frac_field;
+}
+
+uint16_t orc_dequant_elem(int8_t q, uint16_t scale_bits) {
+  /* |q| <= 2^7 and an fp16 significand has 11 bits: the product is exact in
+   * double (and in fp32), so the only rounding is the one to bf16. */
+  return bf16_round_double((double)q * fp16_value(scale_bits));
+}
+
+void orc_dequant_row(const uint8_t* row, uint16_t* out) {
+  for (int j = 0; j < 512; ++j) {
+    int g = j / 64;
+    uint16_t scale = (uint16_t)(row[512 + 2 * g] | (row[512 + 2 * g + 1] << 8));
+    out[j] = orc_dequant_elem((int8_t)row[j], scale);
+  }
+  for (int k = 0; k < 64; ++k)
+    out[512 + k] = (uint16_t)(row[528 + 2 * k] | (row[528 + 2 * k + 1] << 8));
+}
+
+void orc_dequant_table(uint16_t* table) {
+  for (int q = -128; q < 128; ++q)
+    for (int s = 0; s < 65536; ++s)
+      table[(size_t)(q + 128) * 65536 + s] = orc_dequant_elem((int8_t)q, (uint16_t)s);
+}
+
+/* ------------------------------------------------------------ LRU cache -- */
+
+struct orc_cache {
+  int32_t C;
+  int64_t hcap;
+  int32_t* slot_of;  /* position -> slot, -1 if not resident */
+  int32_t* pos_of;   /* slot -> position, -1 if empty        */
+  int32_t* last;     /* slot -> last-use step, -1 if unused  */
+  uint8_t* hot;      /* slot contents                        */
+};
+
+orc_cache* orc_cache_new(int32_t C, int64_t hcap) {
+  if (C < 1 || hcap < 1) return NULL;
+  orc_cache* c = (orc_cache*)calloc(1, sizeof *c);
+  if (!c) return NULL;
+  c->C = C;
+  c->hcap = hcap;
+  c->slot_of = (int32_t*)malloc((size_t)hcap * sizeof(int32_t));
+  c->pos_of = (int32_t*)malloc((size_t)C * sizeof(int32_t));
+  c->last = (int32_t*)malloc((size_t)C * sizeof(int32_t));
+  c->hot = (uint8_t*)calloc((size_t)C, ORC_ROW_BYTES);
+  if (!c->slot_of || !c->pos_of || !c->last || !c->hot) {
+    orc_cache_free(c);
+    return NULL;
+  }
+  for (int64_t p = 0; p < hcap; ++p) c->slot_of[p] = -1;
+  for (int32_t v = 0; v < C; ++v) c->pos_of[v] = -1, c->last[v] = -1;
+  return c;
+}
+
+void orc_cache_free(orc_cache* c) {
+  if (!c) return;
+  free(c->slot_of);
+  free(c->pos_of);
+  free(c->last);
+  free(c->hot);
+  free(c);
+}
+
+/* The slot minimising (last, slot) over slots not used in step t. */
+static int32_t lru_victim(const orc_cache* c, int32_t t) {
+  int32_t best = -1;
+  for (int32_t v = 0; v < c->C; ++v) {
+    if (c->last[v] == t) continue;
+    if (best < 0 || c->last[v] < c->last[best]) best = v;
+  }
+  return best;
+}
+
+int orc_cache_step(orc_cache* c, int32_t t, const int32_t* sel, int32_t K,
+                   const uint8_t* host_rows, orc_step_info* info) {
+  if (K < 1 || K > c->C) return -1;
+  for (int32_t i = 0; i < K; ++i)
+    if (sel[i] < 0 || sel[i] >= c->hcap) return -1;
+  int32_t n_hit = 0, n_miss = 0, n_evict = 0;
+  /* Hits: a selected position already resident is used in step t. */
+  for (int32_t i = 0; i < K; ++i) {
+    int32_t s = c->slot_of[sel[i]];
+    if (s >= 0) {
+      c->last[s] = t;
+      ++n_hit;
+    }
+  }
+  /* Misses, one at a time in selection order. */
+  for (int32_t i = 0; i < K; ++i) {
+    int32_t p = sel[i];
+    if (c->slot_of[p] >= 0) continue;
+    int32_t v = lru_victim(c, t);
+    if (v < 0) return -1;
+    int32_t old = c->pos_of[v];
+    if (old >= 0) {
+      c->slot_of[old] = -1;
+      ++n_evict;
+    }
+    c->pos_of[v] = p;
+    c->slot_of[p] = v;
+    c->last[v] = t;
+    memcpy(c->hot + (size_t)v * ORC_ROW_BYTES, host_rows + (size_t)p * ORC_ROW_BYTES,
+           ORC_ROW_BYTES);
+    if (info) {
+      info->miss_pos[n_miss] = p;
+      info->victim[n_miss] = v;
+      info->evicted[n_miss] = old;
+    }
+    ++n_miss;
+  }
+  if (info) {
+    for (int32_t i = 0; i < K; ++i) info->slot[i] = c->slot_of[sel[i]];
+    for (int32_t j = n_miss; j < K; ++j)
+      info->miss_pos[j] = info->victim[j] = info->evicted[j] = -1;
+    info->n_hit = n_hit;
+    info->n_miss = n_miss;
+    info->n_evict = n_evict;
+  }
+  return 0;
+}
+
+int orc_gather(const orc_cache* c, const int32_t* sel, int32_t K, uint16_t* out) {
+  for (int32_t i = 0; i < K; ++i) {
+    if (sel[i] < 0 || sel[i] >= c->hcap) return -1;
+    int32_t s = c->slot_of[sel[i]];
+    if (s < 0) return -1;
+    orc_dequant_row(c->hot + (size_t)s * ORC_ROW_BYTES, out + (size_t)i * ORC_OUT_ELEMS);
+  }
+  return 0;
+}
+
+const int32_t* orc_cache_slot_of(const orc_cache* c) { return c->slot_of; }
+const int32_t* orc_cache_pos_of(const orc_cache* c) { return c->pos_of; }
+const int32_t* orc_cache_last(const orc_cache* c) { return c->last; }
+const uint8_t* orc_cache_hot(const orc_cache* c) { return c->hot; }
+
+/* --------------------------------------------------- whole-model driver -- */
+
+typedef struct {
+  orc_cache* const* caches;
+  const uint8_t* const* host_rows;
+  int32_t S, L, R, K, G, t;
+  const float* const* scores;
+  const int64_t* hist_len;
+  int32_t* sel_out;
+  uint16_t* out;
+  orc_step_info* infos;
+  pthread_mutex_t lock;
+  int32_t next_unit;
+  int status;
+} model_job;
+
+static int run_unit(model_job* j, int32_t u) {
+  int32_t s = u / j->G, g = u % j->G;
+  int32_t* sel = j->sel_out + (size_t)u * j->K;
+  if (orc_topk(j->scores[u], j->hist_len[s], j->K, sel)) return -1;
+  int32_t l_end = (g + 1) * j->R < j->L ? (g + 1) * j->R : j->L;
+  for (int32_t l = g * j->R; l < l_end; ++l) {
+    size_t sl = (size_t)s * j->L + l;
+    orc_step_info* info = j->infos ? &j->infos[sl] : NULL;
+    if (orc_cache_step(j->caches[sl], j->t, sel, j->K, j->host_rows[sl], info)) return -1;
+    if (j->out &&
+        orc_gather(j->caches[sl], sel, j->K, j->out + sl * (size_t)j->K * ORC_OUT_ELEMS))
+      return -1;
+  }
+  return 0;
+}
+
+static void* model_worker(void* arg) {
+  model_job* j = (model_job*)arg;
+  for (;;) {
+    pthread_mutex_lock(&j->lock);
+    int32_t u = j->next_unit++;
+    pthread_mutex_unlock(&j->lock);
+    if (u >= j->S * j->G) break;
+    if (run_unit(j, u)) {
+      pthread_mutex_lock(&j->lock);
+      j->status = -1;
+      pthread_mutex_unlock(&j->lock);
+    }
+  }
+  return NULL;
+}
+
+int orc_model_step(orc_cache* const* caches, const uint8_t* const* host_rows,
+                   int32_t S, int32_t L, int32_t R, int32_t K, int32_t t,
+                   const float* const* scores, const int64_t* hist_len,
+                   int32_t* sel_out, uint16_t* out, orc_step_info* infos,
+                   int32_t nthreads) {
+  if (S < 1 || L < 1 || R < 1 || K < 1) return -1;
+  model_job j;
+  j.caches = caches;
+  j.host_rows = host_rows;
+  j.S = S, j.L = L, j.R = R, j.K = K, j.G = (L + R - 1) / R, j.t = t;
+  j.scores = scores;
+  j.hist_len = hist_len;
+  j.sel_out = sel_out;
+  j.out = out;
+  j.infos = infos;
+  j.next_unit = 0;
+  j.status = 0;
+  pthread_mutex_init(&j.lock, NULL);
+  int32_t units = S * j.G;
+  if (nthreads < 1) nthreads = 1;
+  if (nthreads > units) nthreads = units;
+  if (nthreads == 1) {
+    model_worker(&j);
+  } else {
+    pthread_t* th = (pthread_t*)malloc((size_t)nthreads * sizeof(pthread_t));
+    int32_t started = 0;
+    for (; th && started < nthreads; ++started)
+      if (pthread_create(&th[started], NULL, model_worker, &j)) break;
+    if (started == 0) model_worker(&j);
+    for (int32_t i = 0; i < started; ++i) pthread_join(th[i], NULL);
+    free(th);
+  }
+  pthread_mutex_destroy(&j.lock);
+  return j.status;
+}
