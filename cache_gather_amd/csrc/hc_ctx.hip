@@ -1,0 +1,385 @@
+// hc_ctx.hip — host side of the C ABI declared in include/hc.h.
+//
+// The CPU only manages resources and lifetimes; every per-selection decision
+// (ranking, lookup, replacement, transfer) is made by the kernels (page "From
+// 1M Total to 15+ × 1M Contexts: GLM-5.3 KV Cache Offloading", section
+// "Decision three: let the GPU manage the hot cache directly").  Long-lived
+// buffers are sized exactly (section "Ten sessions exposed a
+// physical-allocation problem"): the device workspace is one caller-owned
+// block whose exact size hc_workspace_bytes reports, and the host row store
+// is one exact-size pinned allocation per (session, layer).  Creation is
+// all-or-nothing and destruction first waits for every enqueued step (the
+// page "Making KV offload correct", sections "A grouped allocation is a
+// transaction" and "Response completion is not copy completion").
+#include <algorithm>
+#include <new>
+#include <vector>
+
+#include "hc_internal.h"
+
+using namespace hc;
+
+namespace {
+
+constexpr uint64_t kAlign = 256;
+
+struct Layout {
+  uint64_t pos2slot, slot2pos, last_use, order, hist, cnt, above, cand, sel_slot, miss_pos,
+      victim, host_tab, hot, total;
+};
+
+uint64_t align_up(uint64_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+bool valid_config(const hc_config* c) {
+  if (!c || c->struct_size != sizeof(hc_config)) return false;
+  if (c->n_sessions < 1 || c->n_sessions > (uint32_t)kMaxSessions) return false;
+  if (c->n_layers < 1 || c->layers_per_select < 1) return false;
+  if (c->top_k < 1 || c->top_k > HC_MAX_TOPK) return false;
+  if (c->cache_slots < c->top_k || c->cache_slots > HC_MAX_SLOTS) return false;
+  if (c->max_positions < c->top_k || c->max_positions >= (1ull << 31)) return false;
+  if (c->flags != 0) return false;
+  const uint64_t layers = (uint64_t)c->n_sessions * c->n_layers;
+  if (layers > 65535) return false;  // one grid row per layer in the fetch launch
+  return true;
+}
+
+Layout layout_of(const hc_config* c) {
+  const uint64_t S = c->n_sessions, L = c->n_layers;
+  const uint64_t G = (L + c->layers_per_select - 1) / c->layers_per_select;
+  const uint64_t U = S * G, C = c->cache_slots, K = c->top_k, hcap = c->max_positions;
+  Layout lo{};
+  uint64_t off = 0;
+  auto take = [&](uint64_t bytes) {
+    const uint64_t o = align_up(off);
+    off = o + bytes;
+    return o;
+  };
+  lo.pos2slot = take(U * hcap * 4);
+  lo.slot2pos = take(U * C * 4);
+  lo.last_use = take(U * C * 4);
+  lo.order = take(U * 2 * C * 4);
+  lo.hist = take(U * kBins1 * 4);
+  lo.cnt = take(U * kCnt * 4);
+  lo.above = take(U * K * 4);
+  lo.cand = take(U * hcap * 8);
+  lo.sel_slot = take(U * K * 4);
+  lo.miss_pos = take(U * K * 4);
+  lo.victim = take(U * K * 4);
+  lo.host_tab = take(S * L * 8);
+  lo.hot = take(S * L * C * kRow);
+  lo.total = align_up(off);
+  return lo;
+}
+
+// Restores the calling thread's current device on scope exit.
+struct DeviceGuard {
+  int prev = -1;
+  bool ok = false;
+  explicit DeviceGuard(int dev) {
+    if (hipGetDevice(&prev) != hipSuccess) prev = -1;
+    ok = hipSetDevice(dev) == hipSuccess;
+  }
+  ~DeviceGuard() {
+    if (prev >= 0) (void)hipSetDevice(prev);
+  }
+};
+
+__global__ void k_init(DevState d, int64_t n_pos, int64_t n_slots) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  const int64_t i0 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  for (int64_t i = i0; i < n_pos; i += stride) d.pos2slot[i] = -1;
+  for (int64_t i = i0; i < n_slots; i += stride) {
+    d.slot2pos[i] = -1;
+    d.last_use[i] = -1;
+    const int64_t u = i / d.C, v = i - u * d.C;
+    d.order[(u * 2) * d.C + v] = (int32_t)v;      // step 0 reads parity 0
+    d.order[(u * 2 + 1) * d.C + v] = (int32_t)v;
+  }
+  const int64_t units = (int64_t)d.S * d.G;
+  for (int64_t i = i0; i < units * d.K; i += stride) d.sel_slot[i] = 0;
+  for (int64_t i = i0; i < units * kBins1; i += stride) d.hist[i] = 0;
+  for (int64_t i = i0; i < units * kCnt; i += stride) d.cnt[i] = 0;
+}
+
+}  // namespace
+
+namespace hc {
+hipError_t launch_init(const DevState& d, hipStream_t st) {
+  const int64_t units = (int64_t)d.S * d.G;
+  hipLaunchKernelGGL(k_init, dim3(1024), dim3(256), 0, st, d, units * d.hcap, units * d.C);
+  return hipGetLastError();
+}
+}  // namespace hc
+
+struct hc_ctx {
+  hc_config cfg;
+  DevState dev;
+  Layout lo;
+  uint8_t* ws = nullptr;
+  std::vector<uint8_t*> host_rows;   // S*L pinned buffers
+  uint64_t t = 0;                    // steps issued
+  std::vector<uint64_t> last_len;    // previous hist_len per session
+  bool poisoned = false;
+  bool enqueued = false;
+  hipEvent_t done = nullptr;         // recorded after every step
+  // profiling: 6 events per step, bracketing the 5 kernels
+  std::vector<hipEvent_t> prof;
+  uint32_t prof_cap = 0, prof_used = 0;
+};
+
+namespace {
+
+void free_host(hc_ctx* c) {
+  for (uint8_t* p : c->host_rows)
+    if (p) (void)hipHostFree(p);
+  c->host_rows.clear();
+}
+
+void free_prof(hc_ctx* c) {
+  for (hipEvent_t e : c->prof)
+    if (e) (void)hipEventDestroy(e);
+  c->prof.clear();
+  c->prof_cap = c->prof_used = 0;
+}
+
+hc_status fail_hip(hc_ctx* c) {
+  c->poisoned = true;
+  return HC_E_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+hc_status hc_workspace_bytes(const hc_config* cfg, uint64_t* bytes) {
+  if (!valid_config(cfg) || !bytes) return HC_E_INVAL;
+  *bytes = layout_of(cfg).total;
+  return HC_OK;
+}
+
+hc_status hc_create(const hc_config* cfg, void* dev_workspace, uint64_t ws_bytes, hc_ctx** out) {
+  if (out) *out = nullptr;
+  if (!valid_config(cfg) || !out || !dev_workspace) return HC_E_INVAL;
+  if (reinterpret_cast<uintptr_t>(dev_workspace) % kAlign) return HC_E_INVAL;
+  const Layout lo = layout_of(cfg);
+  if (ws_bytes < lo.total) return HC_E_NOMEM;
+  DeviceGuard dg(cfg->device);
+  if (!dg.ok) return HC_E_INVAL;
+
+  hc_ctx* c = new (std::nothrow) hc_ctx();
+  if (!c) return HC_E_NOMEM;
+  c->cfg = *cfg;
+  c->lo = lo;
+  c->ws = static_cast<uint8_t*>(dev_workspace);
+  const uint32_t S = cfg->n_sessions, L = cfg->n_layers, R = cfg->layers_per_select;
+  const uint32_t G = (L + R - 1) / R;
+  c->last_len.assign(S, 0);
+
+  // pinned, mapped host rows: one exact-size buffer per (session, layer)
+  const uint64_t row_bytes = cfg->max_positions * (uint64_t)kRow;
+  std::vector<const uint8_t*> dev_ptrs(S * (size_t)L);
+  c->host_rows.assign(S * (size_t)L, nullptr);
+  hc_status st = HC_OK;
+  for (size_t i = 0; i < c->host_rows.size() && st == HC_OK; ++i) {
+    void* p = nullptr;
+    if (hipHostMalloc(&p, row_bytes, hipHostMallocMapped) != hipSuccess || !p) {
+      st = HC_E_NOMEM;
+      break;
+    }
+    c->host_rows[i] = static_cast<uint8_t*>(p);
+    void* dp = nullptr;
+    if (hipHostGetDevicePointer(&dp, p, 0) != hipSuccess || !dp) st = HC_E_HIP;
+    dev_ptrs[i] = static_cast<const uint8_t*>(dp);
+  }
+  if (st == HC_OK && hipEventCreateWithFlags(&c->done, hipEventDisableTiming) != hipSuccess)
+    st = HC_E_HIP;
+
+  DevState& d = c->dev;
+  d.S = (int32_t)S;
+  d.L = (int32_t)L;
+  d.R = (int32_t)R;
+  d.G = (int32_t)G;
+  d.K = (int32_t)cfg->top_k;
+  d.C = (int32_t)cfg->cache_slots;
+  d.hcap = (int64_t)cfg->max_positions;
+  uint8_t* w = c->ws;
+  d.pos2slot = reinterpret_cast<int32_t*>(w + lo.pos2slot);
+  d.slot2pos = reinterpret_cast<int32_t*>(w + lo.slot2pos);
+  d.last_use = reinterpret_cast<int32_t*>(w + lo.last_use);
+  d.order = reinterpret_cast<int32_t*>(w + lo.order);
+  d.hist = reinterpret_cast<uint32_t*>(w + lo.hist);
+  d.cnt = reinterpret_cast<int32_t*>(w + lo.cnt);
+  d.above = reinterpret_cast<int32_t*>(w + lo.above);
+  d.cand = reinterpret_cast<uint2*>(w + lo.cand);
+  d.sel_slot = reinterpret_cast<int32_t*>(w + lo.sel_slot);
+  d.miss_pos = reinterpret_cast<int32_t*>(w + lo.miss_pos);
+  d.victim = reinterpret_cast<int32_t*>(w + lo.victim);
+  d.host = reinterpret_cast<const uint8_t* const*>(w + lo.host_tab);
+  d.hot = w + lo.hot;
+
+  if (st == HC_OK &&
+      hipMemcpy(w + lo.host_tab, dev_ptrs.data(), dev_ptrs.size() * sizeof(void*),
+                hipMemcpyHostToDevice) != hipSuccess)
+    st = HC_E_HIP;
+  if (st == HC_OK && launch_init(d, nullptr) != hipSuccess) st = HC_E_HIP;
+  if (st == HC_OK && hipDeviceSynchronize() != hipSuccess) st = HC_E_HIP;
+  if (st != HC_OK) {
+    free_host(c);
+    if (c->done) (void)hipEventDestroy(c->done);
+    delete c;
+    return st;
+  }
+  *out = c;
+  return HC_OK;
+}
+
+uint8_t* hc_host_rows(hc_ctx* c, uint32_t session, uint32_t layer) {
+  if (!c || session >= c->cfg.n_sessions || layer >= c->cfg.n_layers) return nullptr;
+  return c->host_rows[(size_t)session * c->cfg.n_layers + layer];
+}
+
+hc_status hc_step(hc_ctx* c, void* stream, const float* d_scores, uint64_t score_stride,
+                  const uint64_t* hist_len, uint16_t* d_out, int32_t* d_sel, int32_t* d_trace) {
+  if (!c) return HC_E_INVAL;
+  if (c->poisoned) return HC_E_STATE;
+  if (!d_scores || !hist_len || !d_out || !d_sel) return HC_E_INVAL;
+  const uint32_t S = c->cfg.n_sessions;
+  uint64_t max_len = 0;
+  for (uint32_t s = 0; s < S; ++s) {
+    const uint64_t h = hist_len[s];
+    if (h < c->cfg.top_k || h > c->cfg.max_positions || h < c->last_len[s]) return HC_E_INVAL;
+    max_len = std::max(max_len, h);
+  }
+  if (score_stride < max_len) return HC_E_INVAL;
+  if (reinterpret_cast<uintptr_t>(d_out) % 16) return HC_E_INVAL;
+  if (c->t >= 0x7FFFFFFFull) return HC_E_INVAL;  // last-use stamps are int32
+
+  DeviceGuard dg(c->cfg.device);
+  if (!dg.ok) return HC_E_INVAL;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  StepArgs a;
+  a.t = (int32_t)c->t;
+  for (uint32_t s = 0; s < (uint32_t)kMaxSessions; ++s)
+    a.hist_len[s] = s < S ? (uint32_t)hist_len[s] : 0u;
+  const int n_chunks = (int)((max_len + kScanChunk - 1) / kScanChunk);
+  const bool vec4 =
+      (reinterpret_cast<uintptr_t>(d_scores) % 16 == 0) && (score_stride % 4 == 0);
+
+  const bool prof = c->prof_used < c->prof_cap;
+  hipEvent_t* ev = prof ? &c->prof[(size_t)c->prof_used * 6] : nullptr;
+  auto mark = [&](int i) { return prof ? hipEventRecord(ev[i], st) : hipSuccess; };
+
+  hipError_t e = mark(0);
+  if (e == hipSuccess) e = launch_topk_hist(c->dev, a, d_scores, score_stride, n_chunks, vec4, st);
+  if (e == hipSuccess) e = mark(1);
+  if (e == hipSuccess)
+    e = launch_topk_filter(c->dev, a, d_scores, score_stride, n_chunks, vec4, st);
+  if (e == hipSuccess) e = mark(2);
+  if (e == hipSuccess) e = launch_select(c->dev, a.t, d_sel, d_trace, st);
+  if (e == hipSuccess) e = mark(3);
+  if (e == hipSuccess) e = launch_fetch(c->dev, st);
+  if (e == hipSuccess) e = mark(4);
+  if (e == hipSuccess) e = launch_gather(c->dev, d_out, st);
+  if (e == hipSuccess) e = mark(5);
+  if (e == hipSuccess) e = hipEventRecord(c->done, st);
+  c->enqueued = true;
+  if (e != hipSuccess) return fail_hip(c);
+  if (prof) ++c->prof_used;
+  for (uint32_t s = 0; s < S; ++s) c->last_len[s] = hist_len[s];
+  ++c->t;
+  return HC_OK;
+}
+
+hc_status hc_export_state(hc_ctx* c, uint32_t session, uint32_t layer, int32_t* slot2pos,
+                          int32_t* last_use, int32_t* pos2slot, uint8_t* hot_rows) {
+  if (!c || !slot2pos || !last_use) return HC_E_INVAL;
+  if (c->poisoned) return HC_E_STATE;
+  if (session >= c->cfg.n_sessions || layer >= c->cfg.n_layers) return HC_E_INVAL;
+  DeviceGuard dg(c->cfg.device);
+  if (!dg.ok) return HC_E_INVAL;
+  if (c->enqueued && hipEventSynchronize(c->done) != hipSuccess) return fail_hip(c);
+  const DevState& d = c->dev;
+  const size_t u = (size_t)session * d.G + layer / d.R;
+  const size_t sl = (size_t)session * d.L + layer;
+  const size_t C = (size_t)d.C;
+  bool ok = hipMemcpy(slot2pos, d.slot2pos + u * C, C * 4, hipMemcpyDeviceToHost) == hipSuccess &&
+            hipMemcpy(last_use, d.last_use + u * C, C * 4, hipMemcpyDeviceToHost) == hipSuccess;
+  if (ok && pos2slot)
+    ok = hipMemcpy(pos2slot, d.pos2slot + u * (size_t)d.hcap, (size_t)d.hcap * 4,
+                   hipMemcpyDeviceToHost) == hipSuccess;
+  if (ok && hot_rows)
+    ok = hipMemcpy(hot_rows, d.hot + sl * C * kRow, C * kRow, hipMemcpyDeviceToHost) ==
+         hipSuccess;
+  return ok ? HC_OK : fail_hip(c);
+}
+
+hc_status hc_profile_enable(hc_ctx* c, uint32_t max_steps) {
+  if (!c) return HC_E_INVAL;
+  if (c->poisoned) return HC_E_STATE;
+  DeviceGuard dg(c->cfg.device);
+  if (!dg.ok) return HC_E_INVAL;
+  if (c->enqueued && hipEventSynchronize(c->done) != hipSuccess) return fail_hip(c);
+  free_prof(c);
+  if (max_steps == 0) return HC_OK;
+  c->prof.assign((size_t)max_steps * 6, nullptr);
+  for (hipEvent_t& e : c->prof) {
+    if (hipEventCreate(&e) != hipSuccess) {
+      free_prof(c);
+      return HC_E_NOMEM;
+    }
+  }
+  c->prof_cap = max_steps;
+  return HC_OK;
+}
+
+hc_status hc_profile_read(hc_ctx* c, double* stage_ms, uint64_t* n_steps) {
+  if (!c || !stage_ms || !n_steps) return HC_E_INVAL;
+  if (c->poisoned) return HC_E_STATE;
+  DeviceGuard dg(c->cfg.device);
+  if (!dg.ok) return HC_E_INVAL;
+  for (int i = 0; i < HC_NUM_STAGES; ++i) stage_ms[i] = 0.0;
+  for (uint32_t k = 0; k < c->prof_used; ++k) {
+    hipEvent_t* ev = &c->prof[(size_t)k * 6];
+    if (hipEventSynchronize(ev[5]) != hipSuccess) return fail_hip(c);
+    for (int i = 0; i < HC_NUM_STAGES; ++i) {
+      float ms = 0.f;
+      if (hipEventElapsedTime(&ms, ev[i], ev[i + 1]) != hipSuccess) return fail_hip(c);
+      stage_ms[i] += ms;
+    }
+  }
+  *n_steps = c->prof_used;
+  return HC_OK;
+}
+
+hc_status hc_steps_done(const hc_ctx* c, uint64_t* n) {
+  if (!c || !n) return HC_E_INVAL;
+  *n = c->t;
+  return HC_OK;
+}
+
+hc_status hc_destroy(hc_ctx* c) {
+  if (!c) return HC_OK;
+  hc_status st = HC_OK;
+  {
+    DeviceGuard dg(c->cfg.device);
+    if (c->enqueued && c->done && hipEventSynchronize(c->done) != hipSuccess) st = HC_E_HIP;
+    free_prof(c);
+    if (c->done) (void)hipEventDestroy(c->done);
+    free_host(c);
+  }
+  delete c;
+  return st;
+}
+
+const char* hc_status_str(hc_status s) {
+  switch (s) {
+    case HC_OK: return "ok";
+    case HC_E_INVAL: return "invalid argument";
+    case HC_E_NOMEM: return "out of memory or workspace too small";
+    case HC_E_HIP: return "HIP error (context poisoned)";
+    case HC_E_STATE: return "context poisoned by an earlier HIP error";
+  }
+  return "unknown status";
+}
+
+}  // extern "C"

@@ -1,0 +1,67 @@
+// hc_internal.h — device-side layout shared by the host orchestration and the
+// gfx950 kernels of the hot-cache decode step.  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "hc.h"
+
+namespace hc {
+
+constexpr int kRow = HC_ROW_BYTES;        // 656 B per Q8G64 row
+constexpr int kOut = HC_OUT_ELEMS;        // 576 bf16 per gathered row
+constexpr int kBin1Bits = 12;             // first radix digit: key bits [20, 32)
+constexpr int kBins1 = 1 << kBin1Bits;    // 4096 histogram bins per unit
+constexpr int kMaxSessions = HC_MAX_SESSIONS;  // session lengths travel as kernel args
+constexpr int kScanChunk = 8192;          // scores per workgroup in the scan kernels
+
+// Per-unit counters (int32 each): unit u owns cnt[u * kCnt .. +kCnt).
+enum { kCntAbove = 0, kCntCand = 1, kCntMiss = 2, kCntBin1 = 3, kCnt = 4 };
+
+// Device view of the caller's workspace.  Unit u = s * G + g; layer index
+// sl = s * L + l.  All arrays are carved from one allocation (see hc_ctx.hip).
+struct DevState {
+  int32_t S, L, R, G, K, C;
+  int64_t hcap;
+  int32_t* pos2slot;   // [U][hcap]  slot holding a position, -1 if none
+  int32_t* slot2pos;   // [U][C]     position held by a slot, -1 if empty
+  int32_t* last_use;   // [U][C]     step of the slot's last use, -1 if never
+  int32_t* order;      // [U][2][C]  slots in ascending (last_use, slot); ping-pong by step parity
+  uint32_t* hist;      // [U][kBins1] top-digit histogram of the current step (zero between steps)
+  int32_t* cnt;        // [U][kCnt]
+  int32_t* above;      // [U][K]     positions whose top digit beats the cut bin
+  uint2* cand;         // [U][hcap]  (key, position) of scores in the cut bin
+  int32_t* sel_slot;   // [U][K]     slot of selected row i after this step
+  int32_t* miss_pos;   // [U][K]     missing positions, ascending
+  int32_t* victim;     // [U][K]     slot assigned to miss k
+  const uint8_t* const* host;  // [S*L] device-visible pointers of the pinned host rows
+  uint8_t* hot;        // [S*L][C][kRow]
+};
+
+struct StepArgs {
+  int32_t t;                          // step number (last-use stamp)
+  uint32_t hist_len[kMaxSessions];    // positions per session this step
+};
+
+// 16-byte vector usable with the nontemporal load/store builtins.
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// IEEE-754 totalOrder of a float as an unsigned integer key.
+__device__ __forceinline__ uint32_t order_key(float f) {
+  uint32_t b = __float_as_uint(f);
+  return b ^ ((uint32_t)((int32_t)b >> 31) | 0x80000000u);
+}
+
+// Launchers (each defined next to its kernel).  All return hipGetLastError().
+hipError_t launch_init(const DevState& d, hipStream_t st);
+hipError_t launch_topk_hist(const DevState& d, const StepArgs& a, const float* scores,
+                            uint64_t stride, int n_chunks, bool vec4, hipStream_t st);
+hipError_t launch_topk_filter(const DevState& d, const StepArgs& a, const float* scores,
+                              uint64_t stride, int n_chunks, bool vec4, hipStream_t st);
+hipError_t launch_select(const DevState& d, int32_t t, int32_t* d_sel, int32_t* d_trace,
+                         hipStream_t st);
+hipError_t launch_fetch(const DevState& d, hipStream_t st);
+hipError_t launch_gather(const DevState& d, uint16_t* d_out, hipStream_t st);
+
+}  // namespace hc

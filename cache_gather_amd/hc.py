@@ -1,0 +1,237 @@
+"""ctypes binding of libhc.so (include/hc.h), with the same entry-point names.
+
+Argument marshalling only: every step of the decode path runs in the HIP
+kernels of libhc.so.  There is no fallback: if the library is missing or
+cannot be loaded, every call raises.  torch is imported before the library
+is loaded so that the process uses the one HIP runtime torch ships with;
+torch only provides device memory and streams.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+LIB_PATH = os.path.join(HERE, "libhc.so")
+HEADER = os.path.join(ROOT, "include", "hc.h")
+
+ROW_BYTES = 656
+OUT_ELEMS = 576
+TRACE_HEADER = 4
+NUM_STAGES = 5
+STAGES = ("topk_hist", "topk_filter", "select", "fetch", "gather")
+STATUS = {0: "HC_OK", -1: "HC_E_INVAL", -2: "HC_E_NOMEM", -3: "HC_E_HIP", -4: "HC_E_STATE"}
+
+
+def trace_ints(k: int) -> int:
+    return TRACE_HEADER + 4 * k
+
+
+class HcError(RuntimeError):
+    def __init__(self, fn, status):
+        self.status = status
+        super().__init__("%s failed: %s (%d)" % (fn, STATUS.get(status, "?"), status))
+
+
+class hc_config(ctypes.Structure):
+    _fields_ = [("struct_size", ctypes.c_uint32), ("n_sessions", ctypes.c_uint32),
+                ("n_layers", ctypes.c_uint32), ("layers_per_select", ctypes.c_uint32),
+                ("cache_slots", ctypes.c_uint32), ("top_k", ctypes.c_uint32),
+                ("max_positions", ctypes.c_uint64), ("device", ctypes.c_int32),
+                ("flags", ctypes.c_uint32)]
+
+
+def make_config(n_sessions, n_layers, layers_per_select, cache_slots, top_k, max_positions,
+                device=0, flags=0) -> hc_config:
+    return hc_config(ctypes.sizeof(hc_config), n_sessions, n_layers, layers_per_select,
+                     cache_slots, top_k, max_positions, device, flags)
+
+
+_LIB = None
+_vp = ctypes.c_void_p
+
+
+def lib():
+    """The loaded libhc.so; raises if it was not built."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    import torch  # noqa: F401  (its HIP runtime must be the one in the process)
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError("libhc.so is not built (%s); run __graft_entry__.build()" % LIB_PATH)
+    L = ctypes.CDLL(LIB_PATH)
+    st = ctypes.c_int
+    L.hc_workspace_bytes.argtypes = [ctypes.POINTER(hc_config), ctypes.POINTER(ctypes.c_uint64)]
+    L.hc_workspace_bytes.restype = st
+    L.hc_create.argtypes = [ctypes.POINTER(hc_config), _vp, ctypes.c_uint64, ctypes.POINTER(_vp)]
+    L.hc_create.restype = st
+    L.hc_host_rows.argtypes = [_vp, ctypes.c_uint32, ctypes.c_uint32]
+    L.hc_host_rows.restype = _vp
+    L.hc_step.argtypes = [_vp, _vp, _vp, ctypes.c_uint64, ctypes.POINTER(ctypes.c_uint64),
+                          _vp, _vp, _vp]
+    L.hc_step.restype = st
+    L.hc_export_state.argtypes = [_vp, ctypes.c_uint32, ctypes.c_uint32, _vp, _vp, _vp, _vp]
+    L.hc_export_state.restype = st
+    L.hc_profile_enable.argtypes = [_vp, ctypes.c_uint32]
+    L.hc_profile_enable.restype = st
+    L.hc_profile_read.argtypes = [_vp, ctypes.POINTER(ctypes.c_double),
+                                  ctypes.POINTER(ctypes.c_uint64)]
+    L.hc_profile_read.restype = st
+    L.hc_steps_done.argtypes = [_vp, ctypes.POINTER(ctypes.c_uint64)]
+    L.hc_steps_done.restype = st
+    L.hc_destroy.argtypes = [_vp]
+    L.hc_destroy.restype = st
+    L.hc_status_str.argtypes = [ctypes.c_int]
+    L.hc_status_str.restype = ctypes.c_char_p
+    _LIB = L
+    return L
+
+
+def declared_functions() -> list[str]:
+    """Names of the functions include/hc.h declares."""
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^[A-Za-z_][\w\s\*]*?\b(hc_\w+)\s*\(", text, re.M)))
+
+
+def _check(fn, status):
+    if status != 0:
+        raise HcError(fn, status)
+
+
+def _ptr(x):
+    """Raw address of a torch tensor, numpy array, int, or None."""
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    if hasattr(x, "data_ptr"):
+        return x.data_ptr()
+    if isinstance(x, np.ndarray):
+        return x.ctypes.data
+    raise TypeError(type(x))
+
+
+# ---------------------------------------------------------- entry points ---
+
+def hc_workspace_bytes(cfg: hc_config) -> int:
+    n = ctypes.c_uint64()
+    _check("hc_workspace_bytes", lib().hc_workspace_bytes(ctypes.byref(cfg), ctypes.byref(n)))
+    return n.value
+
+
+def hc_create(cfg: hc_config, dev_workspace, ws_bytes: int) -> int:
+    out = _vp()
+    _check("hc_create", lib().hc_create(ctypes.byref(cfg), _ptr(dev_workspace), ws_bytes,
+                                        ctypes.byref(out)))
+    return out.value
+
+
+def hc_host_rows(ctx: int, session: int, layer: int, max_positions: int) -> np.ndarray:
+    """The pinned host rows of (session, layer) as a writable uint8 [Hcap, 656] view."""
+    p = lib().hc_host_rows(ctx, session, layer)
+    if not p:
+        raise HcError("hc_host_rows", -1)
+    buf = (ctypes.c_uint8 * (max_positions * ROW_BYTES)).from_address(p)
+    return np.frombuffer(buf, dtype=np.uint8).reshape(max_positions, ROW_BYTES)
+
+
+def hc_step(ctx: int, stream, d_scores, score_stride: int, hist_len, d_out, d_sel,
+            d_trace=None) -> None:
+    hl = np.ascontiguousarray(hist_len, dtype=np.uint64)
+    _check("hc_step", lib().hc_step(ctx, _ptr(stream), _ptr(d_scores), score_stride,
+                                    hl.ctypes.data_as(ctypes.POINTER(ctypes.c_uint64)),
+                                    _ptr(d_out), _ptr(d_sel), _ptr(d_trace)))
+
+
+def hc_export_state(ctx: int, session: int, layer: int, slots: int, max_positions: int,
+                    pos2slot=False, hot_rows=False):
+    slot2pos = np.empty(slots, np.int32)
+    last_use = np.empty(slots, np.int32)
+    p2s = np.empty(max_positions, np.int32) if pos2slot else None
+    hot = np.empty((slots, ROW_BYTES), np.uint8) if hot_rows else None
+    _check("hc_export_state", lib().hc_export_state(ctx, session, layer, _ptr(slot2pos),
+                                                    _ptr(last_use), _ptr(p2s), _ptr(hot)))
+    return {"slot2pos": slot2pos, "last_use": last_use, "pos2slot": p2s, "hot": hot}
+
+
+def hc_profile_enable(ctx: int, max_steps: int) -> None:
+    _check("hc_profile_enable", lib().hc_profile_enable(ctx, max_steps))
+
+
+def hc_profile_read(ctx: int):
+    ms = (ctypes.c_double * NUM_STAGES)()
+    n = ctypes.c_uint64()
+    _check("hc_profile_read", lib().hc_profile_read(ctx, ms, ctypes.byref(n)))
+    return dict(zip(STAGES, list(ms))), n.value
+
+
+def hc_steps_done(ctx: int) -> int:
+    n = ctypes.c_uint64()
+    _check("hc_steps_done", lib().hc_steps_done(ctx, ctypes.byref(n)))
+    return n.value
+
+
+def hc_destroy(ctx: int) -> None:
+    _check("hc_destroy", lib().hc_destroy(ctx))
+
+
+def hc_status_str(status: int) -> str:
+    return lib().hc_status_str(status).decode()
+
+
+# ------------------------------------------------- torch-owned resources ---
+
+class HotCache:
+    """One context plus its torch-allocated device workspace.
+
+    torch supplies only device memory and the stream; the library does the rest.
+    """
+
+    def __init__(self, n_sessions, n_layers, layers_per_select, cache_slots, top_k,
+                 max_positions, device=0):
+        import torch
+        self.cfg = make_config(n_sessions, n_layers, layers_per_select, cache_slots, top_k,
+                               max_positions, device)
+        self.S, self.L, self.R = n_sessions, n_layers, layers_per_select
+        self.G = -(-n_layers // layers_per_select)
+        self.C, self.K, self.hcap = cache_slots, top_k, max_positions
+        self.device = torch.device("cuda", device)
+        self.ws_bytes = hc_workspace_bytes(self.cfg)
+        self.workspace = torch.empty(self.ws_bytes, dtype=torch.uint8, device=self.device)
+        assert self.workspace.data_ptr() % 256 == 0
+        self.ctx = hc_create(self.cfg, self.workspace, self.ws_bytes)
+
+    def host_rows(self, s, l) -> np.ndarray:
+        return hc_host_rows(self.ctx, s, l, self.hcap)
+
+    def step(self, scores, score_stride, hist_len, out, sel, trace=None, stream=None):
+        import torch
+        st = stream if stream is not None else torch.cuda.current_stream(self.device)
+        hc_step(self.ctx, st.cuda_stream, scores, score_stride, hist_len, out, sel, trace)
+
+    def export_state(self, s, l, pos2slot=False, hot_rows=False):
+        return hc_export_state(self.ctx, s, l, self.C, self.hcap, pos2slot, hot_rows)
+
+    def alloc_outputs(self, trace=False):
+        import torch
+        out = torch.empty((self.S, self.L, self.K, OUT_ELEMS), dtype=torch.int16,
+                          device=self.device)
+        sel = torch.empty((self.S, self.G, self.K), dtype=torch.int32, device=self.device)
+        tr = (torch.empty((self.S * self.G, trace_ints(self.K)), dtype=torch.int32,
+                          device=self.device) if trace else None)
+        return out, sel, tr
+
+    def close(self):
+        if self.ctx:
+            hc_destroy(self.ctx)
+            self.ctx = 0
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

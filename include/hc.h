@@ -57,6 +57,7 @@ extern "C" {
 #define HC_OUT_ELEMS     576   /* bf16 values per gathered row (512 + 64)   */
 #define HC_MAX_TOPK      4096  /* largest supported top_k                   */
 #define HC_MAX_SLOTS     262144 /* largest supported cache_slots            */
+#define HC_MAX_SESSIONS  256   /* largest supported n_sessions              */
 
 /* Per-unit trace record: HC_TRACE_INTS(K) int32 values per (session, group),
  * units ordered u = s * G + g.  Layout:
@@ -87,7 +88,7 @@ typedef enum {
 
 typedef struct hc_config {
   uint32_t struct_size;       /* sizeof(hc_config)                              */
-  uint32_t n_sessions;        /* S >= 1                                         */
+  uint32_t n_sessions;        /* S, 1 <= S <= HC_MAX_SESSIONS                   */
   uint32_t n_layers;          /* L >= 1 layers per session                      */
   uint32_t layers_per_select; /* R >= 1                                         */
   uint32_t cache_slots;       /* C, top_k <= C <= HC_MAX_SLOTS                  */

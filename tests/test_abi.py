@@ -1,0 +1,69 @@
+"""The C-ABI library loads, exports every function include/hc.h declares, and
+rejects invalid configurations — all without touching a GPU."""
+import ctypes
+
+import pytest
+
+from cache_gather_amd import hc
+
+
+def test_library_exports_every_declared_function():
+    names = hc.declared_functions()
+    assert set(names) >= {"hc_workspace_bytes", "hc_create", "hc_host_rows", "hc_step",
+                          "hc_export_state", "hc_profile_enable", "hc_profile_read",
+                          "hc_steps_done", "hc_destroy", "hc_status_str"}
+    L = hc.lib()
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_status_strings():
+    for code in (0, -1, -2, -3, -4):
+        assert hc.hc_status_str(code)
+    assert hc.hc_status_str(-99) == "unknown status"
+
+
+def test_workspace_grows_with_the_configuration_and_holds_the_hot_rows():
+    base = hc.hc_workspace_bytes(hc.make_config(1, 1, 1, 32768, 2048, 51047))
+    assert base >= 32768 * 656 + 51047 * 12 + 2 * 32768 * 4
+    assert base % 256 == 0
+    more_layers = hc.hc_workspace_bytes(hc.make_config(1, 78, 4, 32768, 2048, 51047))
+    assert more_layers >= 78 * 32768 * 656
+    more_pos = hc.hc_workspace_bytes(hc.make_config(1, 1, 1, 32768, 2048, 1048832))
+    assert more_pos >= base + (1048832 - 51047) * 12 - 1024   # alignment slack
+
+
+@pytest.mark.parametrize("bad", [
+    dict(top_k=0), dict(top_k=4097, cache_slots=5000), dict(cache_slots=100, top_k=200),
+    dict(n_sessions=0), dict(n_sessions=257), dict(n_layers=0), dict(layers_per_select=0),
+    dict(max_positions=100, top_k=200, cache_slots=300), dict(max_positions=1 << 31),
+    dict(flags=1), dict(cache_slots=262145),
+])
+def test_invalid_configurations_are_rejected(bad):
+    kw = dict(n_sessions=1, n_layers=2, layers_per_select=1, cache_slots=1024, top_k=256,
+              max_positions=5000)
+    kw.update(bad)
+    cfg = hc.make_config(**kw)
+    with pytest.raises(hc.HcError) as e:
+        hc.hc_workspace_bytes(cfg)
+    assert e.value.status == -1
+
+
+def test_bad_struct_size_is_rejected():
+    cfg = hc.make_config(1, 1, 1, 1024, 256, 5000)
+    cfg.struct_size = 12
+    with pytest.raises(hc.HcError):
+        hc.hc_workspace_bytes(cfg)
+
+
+def test_null_handles():
+    L = hc.lib()
+    assert L.hc_destroy(None) == 0
+    assert L.hc_host_rows(None, 0, 0) is None
+    assert L.hc_step(None, None, None, 0, None, None, None, None) == -1
+    n = ctypes.c_uint64()
+    assert L.hc_steps_done(None, ctypes.byref(n)) == -1
+    cfg = hc.make_config(1, 1, 1, 1024, 256, 5000)
+    out = ctypes.c_void_p(1)
+    assert L.hc_create(ctypes.byref(cfg), None, 0, ctypes.byref(out)) == -1
+    assert out.value is None

@@ -1,0 +1,138 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Everything must be bit-exact: selections, hit/miss/victim/eviction traces,
+slot maps, hot-row bytes and the bf16 output buffer.
+"""
+import numpy as np
+import pytest
+
+from cache_gather_amd import workload as W
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need an MI355X"
+    from cache_gather_amd import hc
+    hc.lib()
+    maps = open("/proc/self/maps").read()
+    assert "libhc.so" in maps, "the HIP library is not loaded"
+    yield
+
+
+def _pair(wl, **kw):
+    from gpu_harness import Pair
+    return Pair(wl, **kw)
+
+
+def test_tiny_workload_every_step():
+    p = _pair(W.TINY)
+    p.run()
+    p.close()
+
+
+SMALL_CASES = [
+    # name, S, L, R, H0, steps, C, K, sigma_b, sigma_n
+    ("groups_ragged", 2, 5, 2, 700, 10, 96, 48, 0.5, 1.0),
+    ("multi_chunk_tail", 1, 3, 3, 20011, 8, 700, 333, 0.3, 1.0),   # 3 scan chunks + ragged tail
+    ("c_equals_k", 2, 2, 1, 3000, 12, 257, 257, 0.2, 1.0),
+    ("k_one", 1, 2, 1, 500, 20, 4, 1, 0.2, 1.0),
+    ("k_max", 1, 1, 1, 40000, 6, 5000, 4096, 1.0, 0.5),
+    ("h_equals_k", 1, 1, 1, 2048, 1, 2048, 2048, 1.0, 1.0),
+    ("many_sessions", 9, 1, 1, 9000, 6, 1100, 1000, 0.5, 1.0),
+    ("wide_slots", 1, 1, 1, 90000, 6, 65536, 2048, 0.2, 1.0),
+]
+
+
+@pytest.mark.parametrize("case", SMALL_CASES, ids=[c[0] for c in SMALL_CASES])
+def test_small_configurations(case):
+    name, S, L, R, H0, steps, C, K, sb, sn = case
+    wl = W.Workload(name, S, L, R, H0, steps, C, K, (sb,) * S, (sn,) * S, 4242)
+    p = _pair(wl)
+    p.run()
+    p.close()
+
+
+def test_unaligned_score_stride_uses_scalar_loads():
+    wl = W.Workload("odd_stride", 2, 2, 2, 9001, 5, 600, 300, (0.5, 0.5), (1.0, 1.0), 99)
+    p = _pair(wl, score_stride=wl.hcap + 3)
+    p.run()
+    p.close()
+
+
+def _run_custom_scores(wl, make_scores):
+    p = _pair(wl)
+    for t in range(wl.steps):
+        sc = np.zeros((wl.n_units, p.stride), np.float32)
+        for u in range(wl.n_units):
+            sc[u, :wl.hist0 + t] = make_scores(t, u, wl.hist0 + t)
+        g, o = p.step(t, scores_np=sc)
+        p.compare(t, g, o)
+    p.compare_state()
+    p.close()
+
+
+def test_all_equal_scores_take_the_lowest_positions():
+    wl = W.Workload("all_equal", 1, 2, 1, 5000, 4, 600, 512, (1.0,), (1.0,), 5)
+    _run_custom_scores(wl, lambda t, u, h: np.full(h, 0.25, np.float32))
+
+
+def test_heavy_ties_at_the_cut():
+    wl = W.Workload("ties", 2, 1, 1, 30000, 6, 3000, 1500, (1.0, 1.0), (1.0, 1.0), 6)
+
+    def mk(t, u, h):
+        rng = np.random.default_rng((t, u))
+        return (np.round(rng.standard_normal(h) * 4) / 4).astype(np.float32)
+    _run_custom_scores(wl, mk)
+
+
+def test_signed_zeros_infinities_and_nans():
+    wl = W.Workload("ieee", 1, 1, 1, 3000, 4, 400, 300, (1.0,), (1.0,), 7)
+    pnan = np.array([0x7FC00000, 0x7F800001, 0xFFC00000, 0xFFFFFFFF],
+                    np.uint32).view(np.float32)
+
+    def mk(t, u, h):
+        rng = np.random.default_rng((t, 9))
+        x = rng.choice(np.array([0.0, -0.0, 1.0, -1.0, np.inf, -np.inf], np.float32), h)
+        x[rng.integers(0, h, 40)] = rng.choice(pnan, 40)
+        return x.astype(np.float32)
+    _run_custom_scores(wl, mk)
+
+
+def test_dequant_every_int8_with_every_finite_fp16_scale():
+    """Rows covering all 256 int8 values against all 63,488 finite fp16 scales,
+    gathered 2,048 rows per step through hc_step."""
+    import oracle
+    finite = np.arange(65536, dtype=np.int64)
+    finite = finite[((finite >> 10) & 31) != 31]
+    groups = np.repeat(finite, 4)                  # each scale for 4 x 64 int8 values
+    quarter = np.tile(np.arange(4), finite.size)
+    n_rows = -(-groups.size // 8)
+    K = 2048
+    steps = -(-n_rows // K)
+    hcap = steps * K
+    n_all = hcap + steps                            # the workload's Hcap is hist0 + steps
+    latent = np.zeros((n_all, 8, 64), np.int8)
+    scales = np.zeros((n_all, 8), np.uint16)
+    q = (np.arange(64)[None, :] + 64 * quarter[:, None] - 128).astype(np.int8)   # [groups, 64]
+    gi = np.arange(groups.size)
+    latent[gi // 8, gi % 8, :] = q
+    scales[gi // 8, gi % 8] = groups.astype(np.uint16)
+    rows = np.zeros((n_all, 656), np.uint8)
+    rows[:, :512] = latent.reshape(n_all, 512).view(np.uint8)
+    rows[:, 512:528] = scales.astype("<u2").view(np.uint8).reshape(n_all, 16)
+    rows[:, 528:] = np.random.default_rng(3).integers(0, 256, (n_all, 128), dtype=np.uint8)
+    wl = W.Workload("dequant_all", 1, 1, 1, hcap, steps, K, K, (1.0,), (1.0,), 8)
+    from gpu_harness import Pair
+    p = Pair(wl, rows_fn=lambda s, l: rows)
+    for t in range(steps):
+        sc_t = np.zeros((1, p.stride), np.float32)
+        sc_t[0, t * K:(t + 1) * K] = 1.0
+        g, o = p.step(t, scores_np=sc_t, hist_len=np.array([hcap], np.uint64))
+        p.compare(t, g, o)
+        np.testing.assert_array_equal(g["sel"][0, 0], np.arange(t * K, (t + 1) * K))
+        want = np.stack([oracle.dequant_row(rows[x]) for x in range(t * K, (t + 1) * K)])
+        np.testing.assert_array_equal(g["out"][0, 0], want)
+    p.close()
