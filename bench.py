@@ -1,0 +1,251 @@
+#!/usr/bin/env python3
+"""Benchmark of the sparse-KV hot-cache decode step on one MI355X.
+
+Metric: selected rows per second of decode steps — S*L*K rows gathered per
+step — plus the gather's HBM bandwidth and the miss fetch's PCIe bandwidth.
+Default workload: the full-model shape of the page "From 1M Total to 15+ ×
+1M Contexts: GLM-5.3 KV Cache Offloading" — 78 layers, a selection every 4th
+layer reused by the next 3, history 50,023 positions growing by one per step,
+32,768 hot slots per layer, top-2,048 (sections "Separate historical capacity
+from the current working set" and "Six interleaved pairs establish the
+nearly lossless result").  Inputs are seeded synthetic data
+(cache_gather_amd.workload), resident in HBM / pinned host RAM before timing.
+
+One step = one hc_step call = the whole path: top-K scan and cut, lookup, LRU,
+host->HBM miss fetch, gather + dequant.  W warmup steps (the first is the cold
+step that fills the caches) are followed by exactly K timed steps.
+
+Prints one JSON line on stdout.  `roofline` is for the kernel that takes the
+most time per step; `cpu_baseline` times the CPU oracle on a short prefix of
+the same workload (the oracle is test infrastructure, used here only for
+that baseline).
+"""
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "selected rows/s per decode step (50K hist, K=2048); gather HBM + fetch PCIe GB/s"
+HBM_PEAK_GBS = 8000.0
+PCIE_PEAK_GBS = 63.0      # PCIe Gen5 x16, 32 GT/s x 16 lanes x 128/130, one direction
+ROW, OUT_ROW = 656, 1152
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash(name):
+    path = os.path.join(ROOT, "cache_gather_amd", "csrc", name)
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+
+
+def traffic_from_profile(kernel_file, workload):
+    """Per-launch HBM bytes measured by rocprofv3 FETCH_SIZE / WRITE_SIZE,
+    from profiles/traffic_<kernel>_<workload>.md, or None if absent or taken
+    on a different version of the kernel source."""
+    stem = kernel_file.replace(".hip", "")
+    path = os.path.join(ROOT, "profiles", "traffic_%s_%s.md" % (stem, workload))
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m = re.search(r"source_sha256_16:\s*([0-9a-f]{16})", text)
+    b = re.search(r"bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not m or not b or m.group(1) != kernel_source_hash(kernel_file):
+        return None
+    return float(b.group(1))
+
+
+def run_cpu_baseline(wl, rows, n_steps):
+    """The oracle as it stands, on the first n_steps of the workload; the rate
+    is taken over steps 1..n_steps-1 (step 0 is the cold fill)."""
+    import numpy as np
+    import oracle
+    from cache_gather_amd import workload as W
+    threads = max(1, min(16, os.cpu_count() or 1, wl.n_units))
+    model = oracle.Model(wl.n_sessions, wl.n_layers, wl.layers_per_select, wl.top_k,
+                         wl.cache_slots, wl.hcap, rows)
+    sc = W.Scores(wl)
+    times = []
+    for t in range(n_steps):
+        s = sc.step(t)
+        t0 = time.perf_counter()
+        model.step(t, list(s), wl.hist_len(t).astype(np.int64), gather=True, info=False,
+                   nthreads=threads)
+        times.append(time.perf_counter() - t0)
+    model.close()
+    rows_per_step = wl.n_sessions * wl.n_layers * wl.top_k
+    warm = times[1:] if len(times) > 1 else times
+    return {
+        "value": rows_per_step * len(warm) / sum(warm),
+        "unit": "rows/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": "first %d decode steps of %s on %d threads (one per selection group); "
+                  "rate over steps 1-%d, cold step 0 took %.2f s" % (
+                      n_steps, wl.name, threads, n_steps - 1, times[0]),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=60)
+    ap.add_argument("--warmup", type=int, default=4)
+    ap.add_argument("--workload", default="model78_50k")
+    ap.add_argument("--cpu-steps", type=int, default=8)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py runs on one GPU only: the decode step has no multi-GPU path "
+              "in this build (asked for --gpus %d, WORLD_SIZE=%d)" % (args.gpus, world),
+              file=sys.stderr)
+        sys.exit(2)
+    if args.warmup < 1 or args.steps < 1:
+        sys.exit("need --warmup >= 1 (the cold step) and --steps >= 1")
+
+    import numpy as np
+    import torch
+    from cache_gather_amd import hc
+    from cache_gather_amd import workload as W
+
+    base = W.ALL[args.workload]
+    total = args.warmup + args.steps
+    wl = base.with_(steps=max(base.steps, total))
+    dev = torch.device("cuda", 0)
+    S, L, K, U = wl.n_sessions, wl.n_layers, wl.top_k, wl.n_units
+    log("workload %s: S=%d L=%d R=%d K=%d C=%d H0=%d, %d warmup + %d timed steps" % (
+        wl.name, S, L, wl.layers_per_select, K, wl.cache_slots, wl.hist0, args.warmup,
+        args.steps))
+
+    cache = hc.HotCache(S, L, wl.layers_per_select, wl.cache_slots, K, wl.hcap, 0)
+    t0 = time.time()
+    rows = W.fill_all_rows(wl)
+    for s in range(S):
+        for l in range(L):
+            np.copyto(cache.host_rows(s, l), rows[s][l])
+    log("host rows ready (%.1f GiB pinned) in %.1fs" % (
+        S * L * wl.hcap * ROW / 2 ** 30, time.time() - t0))
+
+    stride = (wl.hcap + 3) // 4 * 4
+    t0 = time.time()
+    scores = W.Scores(wl)
+    d_scores = torch.empty((total, U, stride), dtype=torch.float32, device=dev)
+    for t in range(total):
+        d_scores[t].copy_(torch.from_numpy(scores.step(t, stride)))
+    torch.cuda.synchronize()
+    log("scores for %d steps resident in HBM (%.2f GiB) in %.1fs" % (
+        total, d_scores.numel() * 4 / 2 ** 30, time.time() - t0))
+    out, sel, _ = cache.alloc_outputs()
+    trace = torch.empty((total, U, hc.trace_ints(K)), dtype=torch.int32, device=dev)
+
+    def step(t):
+        cache.step(d_scores[t], stride, wl.hist_len(t), out, sel, trace[t])
+
+    # cold step, then the rest of the warmup
+    torch.cuda.synchronize()
+    c0 = time.perf_counter()
+    step(0)
+    torch.cuda.synchronize()
+    cold_ms = (time.perf_counter() - c0) * 1e3
+    for t in range(1, args.warmup):
+        step(t)
+
+    # timed region: exactly --steps steps; per-kernel HIP events on the step's stream
+    hc.hc_profile_enable(cache.ctx, args.steps)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for t in range(args.warmup, total):
+        step(t)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    stage_ms, n_prof = hc.hc_profile_read(cache.ctx)
+    assert n_prof == args.steps
+    stage_avg = {k: v / n_prof for k, v in stage_ms.items()}
+
+    ms_per_step = elapsed * 1e3 / args.steps
+    rows_per_step = S * L * K
+    value = rows_per_step / (ms_per_step / 1e3)
+
+    # misses per step from the trace (n_miss of each unit x layers of its group)
+    tr = trace.cpu().numpy()
+    layers_of_group = np.array([min(wl.layers_per_select, L - g * wl.layers_per_select)
+                                for g in range(wl.n_groups)] * S)
+    miss_rows = (tr[:, :, 1] * layers_of_group[None, :]).sum(axis=1)   # per step
+    timed_miss_rows = miss_rows[args.warmup:]
+    fetch_bytes = float(timed_miss_rows.mean()) * ROW
+    gather_bytes = float(rows_per_step) * (ROW + OUT_ROW)
+    hist_len_mean = float(np.mean([wl.hist0 + t for t in range(args.warmup, total)]))
+    scan_bytes = U * hist_len_mean * 4   # one fp32 read per position per pass
+
+    # The gather kernel also performs the miss fetch: its HBM bytes are the hit
+    # reads + miss slot writes (656 B per row either way) + 1,152 B output per
+    # row; its PCIe bytes are 656 B per missing row.  Both rates use its time.
+    kernels = {
+        "gather": ("k_gather.hip", "hbm", gather_bytes, HBM_PEAK_GBS, "gather"),
+        "fetch": ("k_gather.hip", "pcie", fetch_bytes, PCIE_PEAK_GBS, "gather"),
+        "topk_hist": ("k_topk.hip", "hbm", scan_bytes, HBM_PEAK_GBS, "topk_hist"),
+        "topk_filter": ("k_topk.hip", "hbm", scan_bytes, HBM_PEAK_GBS, "topk_filter"),
+        "select": ("k_select.hip", "hbm", U * (wl.cache_slots * 8 + K * 16), HBM_PEAK_GBS,
+                   "select"),
+    }
+
+    def roofline(stage):
+        src, bound, nbytes, peak, timed_as = kernels[stage]
+        ms = stage_avg[timed_as]
+        achieved = nbytes / (ms * 1e-3) / 1e9 if ms > 0 else 0.0
+        traffic = traffic_from_profile(src, wl.name) if stage == "gather" else None
+        return {"kernel": stage, "bound": bound, "achieved": round(achieved, 2),
+                "peak": peak, "unit": "GB/s", "frac": round(achieved / peak, 4),
+                "traffic": traffic, "algorithmic_bytes": nbytes,
+                "avg_launch_us": round(ms * 1e3, 2)}
+
+    dominant = max(stage_avg, key=stage_avg.get)
+    result = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "rows/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "sessions": S, "layers": L,
+                   "layers_per_select": wl.layers_per_select, "history0": wl.hist0,
+                   "cache_slots": wl.cache_slots, "top_k": K,
+                   "rows_per_step": rows_per_step, "output": "bf16 [S][L][K][576]"},
+        "roofline": roofline(dominant),
+        "roofline_gather": roofline("gather"),
+        "roofline_fetch": roofline("fetch"),
+        "dominant_kernel": dominant,
+        "stage_us": {k: round(v * 1e3, 2) for k, v in stage_avg.items()},
+        "kernel_sum_us": round(sum(stage_avg.values()) * 1e3, 2),
+        "gather_hbm_gbs": roofline("gather")["achieved"],
+        "fetch_pcie_gbs": roofline("fetch")["achieved"],
+        "miss_rows_per_step": round(float(timed_miss_rows.mean()), 1),
+        "cold_step_ms": round(cold_ms, 3),
+        "cold_step_miss_rows": int(miss_rows[0]),
+        "cpu_baseline": None,
+    }
+    cache.close()
+    del d_scores, trace, out, sel
+    if not args.no_cpu_baseline:
+        log("cpu baseline: oracle on the first %d steps ..." % args.cpu_steps)
+        result["cpu_baseline"] = run_cpu_baseline(wl, rows, args.cpu_steps)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

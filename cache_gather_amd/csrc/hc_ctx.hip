@@ -25,7 +25,7 @@ constexpr uint64_t kAlign = 256;
 
 struct Layout {
   uint64_t pos2slot, slot2pos, last_use, order, hist, cnt, above, cand, sel_slot, miss_pos,
-      victim, host_tab, hot, total;
+      victim, miss_idx, host_tab, hot, total;
 };
 
 uint64_t align_up(uint64_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
@@ -39,7 +39,9 @@ bool valid_config(const hc_config* c) {
   if (c->max_positions < c->top_k || c->max_positions >= (1ull << 31)) return false;
   if (c->flags != 0) return false;
   const uint64_t layers = (uint64_t)c->n_sessions * c->n_layers;
-  if (layers > 65535) return false;  // one grid row per layer in the fetch launch
+  if (layers > 65535) return false;
+  const uint64_t G = (c->n_layers + c->layers_per_select - 1) / c->layers_per_select;
+  if ((uint64_t)c->n_sessions * G > (uint64_t)kMaxUnits) return false;
   return true;
 }
 
@@ -65,6 +67,7 @@ Layout layout_of(const hc_config* c) {
   lo.sel_slot = take(U * K * 4);
   lo.miss_pos = take(U * K * 4);
   lo.victim = take(U * K * 4);
+  lo.miss_idx = take(U * K * 4);
   lo.host_tab = take(S * L * 8);
   lo.hot = take(S * L * C * kRow);
   lo.total = align_up(off);
@@ -122,7 +125,7 @@ struct hc_ctx {
   bool poisoned = false;
   bool enqueued = false;
   hipEvent_t done = nullptr;         // recorded after every step
-  // profiling: 6 events per step, bracketing the 5 kernels
+  // profiling: HC_NUM_STAGES + 1 events per step, bracketing the kernels
   std::vector<hipEvent_t> prof;
   uint32_t prof_cap = 0, prof_used = 0;
 };
@@ -214,6 +217,7 @@ hc_status hc_create(const hc_config* cfg, void* dev_workspace, uint64_t ws_bytes
   d.sel_slot = reinterpret_cast<int32_t*>(w + lo.sel_slot);
   d.miss_pos = reinterpret_cast<int32_t*>(w + lo.miss_pos);
   d.victim = reinterpret_cast<int32_t*>(w + lo.victim);
+  d.miss_idx = reinterpret_cast<int32_t*>(w + lo.miss_idx);
   d.host = reinterpret_cast<const uint8_t* const*>(w + lo.host_tab);
   d.hot = w + lo.hot;
 
@@ -266,7 +270,7 @@ hc_status hc_step(hc_ctx* c, void* stream, const float* d_scores, uint64_t score
       (reinterpret_cast<uintptr_t>(d_scores) % 16 == 0) && (score_stride % 4 == 0);
 
   const bool prof = c->prof_used < c->prof_cap;
-  hipEvent_t* ev = prof ? &c->prof[(size_t)c->prof_used * 6] : nullptr;
+  hipEvent_t* ev = prof ? &c->prof[(size_t)c->prof_used * (HC_NUM_STAGES + 1)] : nullptr;
   auto mark = [&](int i) { return prof ? hipEventRecord(ev[i], st) : hipSuccess; };
 
   hipError_t e = mark(0);
@@ -277,10 +281,8 @@ hc_status hc_step(hc_ctx* c, void* stream, const float* d_scores, uint64_t score
   if (e == hipSuccess) e = mark(2);
   if (e == hipSuccess) e = launch_select(c->dev, a.t, d_sel, d_trace, st);
   if (e == hipSuccess) e = mark(3);
-  if (e == hipSuccess) e = launch_fetch(c->dev, st);
-  if (e == hipSuccess) e = mark(4);
   if (e == hipSuccess) e = launch_gather(c->dev, d_out, st);
-  if (e == hipSuccess) e = mark(5);
+  if (e == hipSuccess) e = mark(4);
   if (e == hipSuccess) e = hipEventRecord(c->done, st);
   c->enqueued = true;
   if (e != hipSuccess) return fail_hip(c);
@@ -321,7 +323,7 @@ hc_status hc_profile_enable(hc_ctx* c, uint32_t max_steps) {
   if (c->enqueued && hipEventSynchronize(c->done) != hipSuccess) return fail_hip(c);
   free_prof(c);
   if (max_steps == 0) return HC_OK;
-  c->prof.assign((size_t)max_steps * 6, nullptr);
+  c->prof.assign((size_t)max_steps * (HC_NUM_STAGES + 1), nullptr);
   for (hipEvent_t& e : c->prof) {
     if (hipEventCreate(&e) != hipSuccess) {
       free_prof(c);
@@ -339,8 +341,8 @@ hc_status hc_profile_read(hc_ctx* c, double* stage_ms, uint64_t* n_steps) {
   if (!dg.ok) return HC_E_INVAL;
   for (int i = 0; i < HC_NUM_STAGES; ++i) stage_ms[i] = 0.0;
   for (uint32_t k = 0; k < c->prof_used; ++k) {
-    hipEvent_t* ev = &c->prof[(size_t)k * 6];
-    if (hipEventSynchronize(ev[5]) != hipSuccess) return fail_hip(c);
+    hipEvent_t* ev = &c->prof[(size_t)k * (HC_NUM_STAGES + 1)];
+    if (hipEventSynchronize(ev[HC_NUM_STAGES]) != hipSuccess) return fail_hip(c);
     for (int i = 0; i < HC_NUM_STAGES; ++i) {
       float ms = 0.f;
       if (hipEventElapsedTime(&ms, ev[i], ev[i + 1]) != hipSuccess) return fail_hip(c);

@@ -15,6 +15,7 @@ constexpr int kBin1Bits = 12;             // first radix digit: key bits [20, 32
 constexpr int kBins1 = 1 << kBin1Bits;    // 4096 histogram bins per unit
 constexpr int kMaxSessions = HC_MAX_SESSIONS;  // session lengths travel as kernel args
 constexpr int kScanChunk = 8192;          // scores per workgroup in the scan kernels
+constexpr int kMaxUnits = HC_MAX_UNITS;   // S * G: the per-unit miss prefix lives in LDS
 
 // Per-unit counters (int32 each): unit u owns cnt[u * kCnt .. +kCnt).
 enum { kCntAbove = 0, kCntCand = 1, kCntMiss = 2, kCntBin1 = 3, kCnt = 4 };
@@ -32,9 +33,10 @@ struct DevState {
   int32_t* cnt;        // [U][kCnt]
   int32_t* above;      // [U][K]     positions whose top digit beats the cut bin
   uint2* cand;         // [U][hcap]  (key, position) of scores in the cut bin
-  int32_t* sel_slot;   // [U][K]     slot of selected row i after this step
-  int32_t* miss_pos;   // [U][K]     missing positions, ascending
-  int32_t* victim;     // [U][K]     slot assigned to miss k
+  int32_t* sel_slot;   // [U][K]     slot of selected row i; -(slot + 1) if it missed this step
+  int32_t* miss_pos;   // [U][K]     position of miss k (ascending), k < cnt[u][kCntMiss]
+  int32_t* victim;     // [U][K]     slot that miss k fills
+  int32_t* miss_idx;   // [U][K]     index in the selection of miss k
   const uint8_t* const* host;  // [S*L] device-visible pointers of the pinned host rows
   uint8_t* hot;        // [S*L][C][kRow]
 };
@@ -61,7 +63,6 @@ hipError_t launch_topk_filter(const DevState& d, const StepArgs& a, const float*
                               uint64_t stride, int n_chunks, bool vec4, hipStream_t st);
 hipError_t launch_select(const DevState& d, int32_t t, int32_t* d_sel, int32_t* d_trace,
                          hipStream_t st);
-hipError_t launch_fetch(const DevState& d, hipStream_t st);
 hipError_t launch_gather(const DevState& d, uint16_t* d_out, hipStream_t st);
 
 }  // namespace hc

@@ -1,29 +1,47 @@
-// k_gather.hip — reads every selected row from its hot slot and writes the
-// contiguous bf16 attention buffer [S][L][K][576].
+// k_gather.hip — the hot gather: every selected row, hit or miss, dequantised
+// into the contiguous bf16 attention buffer [S][L][K][576].
 //
-// The hot gather emits a compact selection that attention consumes (page "From
-// 1M Total to 15+ × 1M Contexts: GLM-5.3 KV Cache Offloading", section
-// "Decision three: let the GPU manage the hot cache directly", data-flow
-// figure).  Row format (section "Separate historical capacity from the current
-// working set"): 512 int8 latent values, 8 fp16 scales (one per 64 values),
-// 64 bf16 RoPE values.  Output element j < 512 is the fp32 product
-// int8 * scale, exact, rounded to bf16 (nearest, ties to even); the RoPE part
-// is copied.  Rows filled by k_fetch are visible here through the kernel
-// boundary, so no workgroup reads a slot another workgroup of the same launch
-// writes (section "GPU cache management has hazards too").
+// Page "From 1M Total to 15+ × 1M Contexts: GLM-5.3 KV Cache Offloading",
+// section "Decision three: let the GPU manage the hot cache directly" and its
+// data-flow figure: a hit reads the hot slot in VRAM, a miss reads the
+// registered host-memory copy, and the gather emits a compact selection for
+// attention.  Section "GPU cache management has hazards too": a slot filled
+// in a round is not read by another block of that round, and repeated misses
+// read host RAM.
+//
+// One launch, two kinds of workgroup:
+//   * the first kMissBlocks workgroups walk the dense miss list (every layer
+//     of every unit): each missing row is read from pinned host RAM over PCIe
+//     (zero-copy), written into its victim slot, and dequantised from the same
+//     registers — so its slot is only ever read in later steps, and all PCIe
+//     reads are issued as soon as the launch starts;
+//   * the remaining workgroups stream the hit rows out of the HBM slots (rows
+//     that missed are skipped; the miss workgroups write them).
+// The PCIe transfer of the few missing rows thus overlaps the HBM stream of
+// the many hits.
+//
+// Row format (section "Separate historical capacity from the current working
+// set"): 512 int8 latent, 8 fp16 scales (one per 64 values), 64 bf16 RoPE.
+// Output j < 512 is bf16_rne(int8 * scale) — the fp32 product is exact — and
+// the RoPE values are copied.
 //
 // gfx950 mapping: a row is 40 work items — 32 latent chunks (16 B in, 32 B
-// out) and 8 RoPE chunks (16 B in, 16 B out) — so 320 threads (5 wave64) do 8
-// rows with every lane busy; lanes of a row read 656 contiguous bytes and
-// write 1,152 contiguous bytes.  HBM-bound: 656 B read + 1,152 B written per
-// selected row.  bf16 rounding uses v_cvt_pk_bf16_f32 (two values per op).
+// out) and 8 RoPE chunks (16 B in, 16 B out) — so 320 threads (5 wave64) hold
+// 8 rows with every lane busy.  A workgroup covers kPasses x 8 rows per round
+// and issues all of their loads before converting anything, to keep enough
+// reads in flight.  HBM-bound: 656 B read (hit) or written (miss) + 1,152 B
+// written per selected row; PCIe: 656 B per missing row.  bf16 rounding by
+// v_cvt_pk_bf16_f32.
 #include "hc_internal.h"
 
 namespace hc {
 
-constexpr int kRowsPerGatherBlock = 8;
+constexpr int kRowsPerPass = 8;
 constexpr int kItemsPerRow = 40;
-constexpr int kGatherThreads = kRowsPerGatherBlock * kItemsPerRow;  // 320
+constexpr int kGatherThreads = kRowsPerPass * kItemsPerRow;  // 320
+constexpr int kPasses = 2;
+constexpr int kRowsPerRound = kRowsPerPass * kPasses;         // 32
+constexpr int kMissBlocks = 64;  // few CUs wait on PCIe; the rest stream HBM
 
 __device__ __forceinline__ uint32_t bf16x2(float lo, float hi) {
   const __bf16 a = (__bf16)lo, b = (__bf16)hi;
@@ -36,46 +54,155 @@ __device__ __forceinline__ float i8f(uint32_t w, int k) {
   return (float)((int32_t)(w << (24 - 8 * k)) >> 24);
 }
 
-__global__ __launch_bounds__(kGatherThreads) void k_gather(DevState d, uint16_t* __restrict__ out,
-                                                           int64_t total_rows) {
-  const int item = threadIdx.x % kItemsPerRow;
-  const int64_t row = (int64_t)blockIdx.x * kRowsPerGatherBlock + threadIdx.x / kItemsPerRow;
-  if (row >= total_rows) return;
-  const int64_t sl = row / d.K;
-  const int i = (int)(row - sl * d.K);
-  const int s = (int)(sl / d.L), l = (int)(sl - (int64_t)s * d.L);
-  const int u = s * d.G + l / d.R;
-  const int32_t slot = d.sel_slot[(size_t)u * d.K + i];
-  const uint8_t* src = d.hot + ((size_t)sl * d.C + slot) * kRow;
-  uint8_t* dst = reinterpret_cast<uint8_t*>(out) + (size_t)row * (kOut * 2);
+// Where pass p of this thread reads its row, where it writes the output row,
+// and (misses only) which slot it fills.
+struct RowJob {
+  const uint8_t* src[kPasses];
+  uint8_t* dst[kPasses];
+  uint8_t* fill[kPasses];
+};
 
-  if (item < 32) {
-    const u32x4 q = *reinterpret_cast<const u32x4*>(src + 16 * item);
-    const uint16_t sb = *reinterpret_cast<const uint16_t*>(src + HC_SCALE_OFFSET + 2 * (item >> 2));
-    const float sc = (float)__builtin_bit_cast(_Float16, sb);
-    u32x4 a, b;
-    a.x = bf16x2(i8f(q.x, 0) * sc, i8f(q.x, 1) * sc);
-    a.y = bf16x2(i8f(q.x, 2) * sc, i8f(q.x, 3) * sc);
-    a.z = bf16x2(i8f(q.y, 0) * sc, i8f(q.y, 1) * sc);
-    a.w = bf16x2(i8f(q.y, 2) * sc, i8f(q.y, 3) * sc);
-    b.x = bf16x2(i8f(q.z, 0) * sc, i8f(q.z, 1) * sc);
-    b.y = bf16x2(i8f(q.z, 2) * sc, i8f(q.z, 3) * sc);
-    b.z = bf16x2(i8f(q.w, 0) * sc, i8f(q.w, 1) * sc);
-    b.w = bf16x2(i8f(q.w, 2) * sc, i8f(q.w, 3) * sc);
-    u32x4* o = reinterpret_cast<u32x4*>(dst + 32 * item);
-    __builtin_nontemporal_store(a, o);
-    __builtin_nontemporal_store(b, o + 1);
-  } else {
-    const int r = item - 32;
-    const u32x4 v = *reinterpret_cast<const u32x4*>(src + HC_ROPE_OFFSET + 16 * r);
-    __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(dst + 2 * HC_LATENT_BYTES + 16 * r));
+// Copies / dequantises this thread's item of up to kPasses rows; all loads are
+// issued before the first store.
+__device__ __forceinline__ void run_rows(const RowJob& j, int item) {
+  u32x4 v[kPasses], scale_blk[kPasses];
+  uint16_t sb[kPasses];
+  const int off = item < 32 ? 16 * item : HC_ROPE_OFFSET + 16 * (item - 32);
+#pragma unroll
+  for (int p = 0; p < kPasses; ++p) {
+    if (!j.dst[p]) continue;
+    v[p] = *reinterpret_cast<const u32x4*>(j.src[p] + off);
+    if (item < 32)
+      sb[p] = *reinterpret_cast<const uint16_t*>(j.src[p] + HC_SCALE_OFFSET + 2 * (item >> 2));
+    else if (item == 32 && j.fill[p])
+      scale_blk[p] = *reinterpret_cast<const u32x4*>(j.src[p] + HC_SCALE_OFFSET);
   }
+#pragma unroll
+  for (int p = 0; p < kPasses; ++p) {
+    if (!j.dst[p]) continue;
+    if (j.fill[p]) {
+      *reinterpret_cast<u32x4*>(j.fill[p] + off) = v[p];
+      if (item == 32) *reinterpret_cast<u32x4*>(j.fill[p] + HC_SCALE_OFFSET) = scale_blk[p];
+    }
+    if (item < 32) {
+      const float sc = (float)__builtin_bit_cast(_Float16, sb[p]);
+      const u32x4 q = v[p];
+      u32x4 a, b;
+      a.x = bf16x2(i8f(q.x, 0) * sc, i8f(q.x, 1) * sc);
+      a.y = bf16x2(i8f(q.x, 2) * sc, i8f(q.x, 3) * sc);
+      a.z = bf16x2(i8f(q.y, 0) * sc, i8f(q.y, 1) * sc);
+      a.w = bf16x2(i8f(q.y, 2) * sc, i8f(q.y, 3) * sc);
+      b.x = bf16x2(i8f(q.z, 0) * sc, i8f(q.z, 1) * sc);
+      b.y = bf16x2(i8f(q.z, 2) * sc, i8f(q.z, 3) * sc);
+      b.z = bf16x2(i8f(q.w, 0) * sc, i8f(q.w, 1) * sc);
+      b.w = bf16x2(i8f(q.w, 2) * sc, i8f(q.w, 3) * sc);
+      u32x4* o = reinterpret_cast<u32x4*>(j.dst[p] + 32 * item);
+      __builtin_nontemporal_store(a, o);
+      __builtin_nontemporal_store(b, o + 1);
+    } else {
+      __builtin_nontemporal_store(
+          v[p], reinterpret_cast<u32x4*>(j.dst[p] + 2 * HC_LATENT_BYTES + 16 * (item - 32)));
+    }
+  }
+}
+
+__device__ __forceinline__ int layers_in_group(const DevState& d, int g) {
+  const int n = d.L - g * d.R;
+  return n < d.R ? n : d.R;
+}
+
+__global__ __launch_bounds__(kGatherThreads) void k_gather(DevState d,
+                                                           uint16_t* __restrict__ out,
+                                                           int64_t total_rows) {
+  extern __shared__ int32_t pref[];          // [S*G + 1]: miss rows (all layers) before unit u
+  __shared__ int32_t wsum[kGatherThreads / 64];
+  const int item = threadIdx.x % kItemsPerRow;
+  const int lrow = threadIdx.x / kItemsPerRow;
+  uint8_t* const out_b = reinterpret_cast<uint8_t*>(out);
+  const size_t out_row_bytes = (size_t)kOut * 2;
+  RowJob j;
+
+  if (blockIdx.x < kMissBlocks) {
+    // ---- dense miss list: prefix of (misses x layers) over units --------
+    const int U = d.S * d.G;
+    int running = 0;
+    for (int u0 = 0; u0 < U; u0 += kGatherThreads) {
+      const int u = u0 + threadIdx.x;
+      const int c = u < U ? d.cnt[u * kCnt + kCntMiss] * layers_in_group(d, u % d.G) : 0;
+      // block inclusive scan of c
+      int x = c;
+      const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int y = __shfl_up(x, o, 64);
+        if (lane >= o) x += y;
+      }
+      if (lane == 63) wsum[w] = x;
+      __syncthreads();
+      int off = running, tot = 0;
+#pragma unroll
+      for (int i = 0; i < kGatherThreads / 64; ++i) {
+        off += i < w ? wsum[i] : 0;
+        tot += wsum[i];
+      }
+      if (u < U) pref[u + 1] = off + x;
+      running += tot;
+      __syncthreads();
+    }
+    if (threadIdx.x == 0) pref[0] = 0;
+    __syncthreads();
+    const int M = pref[U];
+    for (int base = blockIdx.x * kRowsPerRound; base < M; base += kMissBlocks * kRowsPerRound) {
+#pragma unroll
+      for (int p = 0; p < kPasses; ++p) {
+        const int q = base + p * kRowsPerPass + lrow;
+        j.dst[p] = nullptr;
+        if (q >= M) continue;
+        int lo = 0, hi = U;  // largest u with pref[u] <= q
+        while (hi - lo > 1) {
+          const int mid = (lo + hi) >> 1;
+          if (pref[mid] <= q) lo = mid;
+          else hi = mid;
+        }
+        const int u = lo, g = u % d.G, s = u / d.G;
+        const int nl = layers_in_group(d, g);
+        const int r = q - pref[u], m = (pref[u + 1] - pref[u]) / nl;
+        const int lig = r / m, k = r - lig * m;
+        const int64_t sl = (int64_t)s * d.L + g * d.R + lig;
+        const size_t uk = (size_t)u * d.K + k;
+        j.src[p] = d.host[sl] + (size_t)d.miss_pos[uk] * kRow;
+        j.fill[p] = d.hot + ((size_t)sl * d.C + d.victim[uk]) * kRow;
+        j.dst[p] = out_b + ((size_t)sl * d.K + d.miss_idx[uk]) * out_row_bytes;
+      }
+      run_rows(j, item);
+    }
+    return;
+  }
+
+  // ---- hit rows, in output order ------------------------------------------
+  const int64_t row0 = (int64_t)(blockIdx.x - kMissBlocks) * kRowsPerRound + lrow;
+#pragma unroll
+  for (int p = 0; p < kPasses; ++p) {
+    const int64_t row = row0 + p * kRowsPerPass;
+    j.dst[p] = nullptr;
+    j.fill[p] = nullptr;
+    if (row >= total_rows) continue;
+    const int64_t sl = row / d.K;
+    const int i = (int)(row - sl * d.K);
+    const int s = (int)(sl / d.L), l = (int)(sl - (int64_t)s * d.L);
+    const int32_t enc = d.sel_slot[(size_t)(s * d.G + l / d.R) * d.K + i];
+    if (enc < 0) continue;  // missed this step: written by a miss workgroup
+    j.src[p] = d.hot + ((size_t)sl * d.C + enc) * kRow;
+    j.dst[p] = out_b + (size_t)row * out_row_bytes;
+  }
+  run_rows(j, item);
 }
 
 hipError_t launch_gather(const DevState& d, uint16_t* d_out, hipStream_t st) {
   const int64_t total = (int64_t)d.S * d.L * d.K;
-  const int64_t blocks = (total + kRowsPerGatherBlock - 1) / kRowsPerGatherBlock;
-  hipLaunchKernelGGL(k_gather, dim3((uint32_t)blocks), dim3(kGatherThreads), 0, st, d, d_out,
+  const int64_t blocks = kMissBlocks + (total + kRowsPerRound - 1) / kRowsPerRound;
+  const size_t lds = ((size_t)d.S * d.G + 1) * sizeof(int32_t);
+  hipLaunchKernelGGL(k_gather, dim3((uint32_t)blocks), dim3(kGatherThreads), lds, st, d, d_out,
                      total);
   return hipGetLastError();
 }

@@ -124,7 +124,61 @@ __device__ __forceinline__ void clear_hist(SelShared& sh, int nb) {
   __syncthreads();
 }
 
-// Miss count for the fetch, and a clean histogram and list counters for the
+// Bitonic sort (ascending) of the kSelThreads * E values in buf.  Value i
+// lives in register i % E of thread i / E: compare-exchange partners closer
+// than E are in the same thread, closer than 64 E in the same wave (cross-lane
+// shuffle, no barrier); only strides of 64 E and more go through LDS.
+__device__ __forceinline__ int32_t bitonic_pick(int32_t a, int32_t b, int i, int j, int k) {
+  const bool lower = (i & j) == 0, asc = (i & k) == 0;
+  return (lower == asc) ? min(a, b) : max(a, b);
+}
+
+template <int E>
+__device__ void sort_positions(int32_t* buf) {
+  constexpr int n = kSelThreads * E;
+  const int tid = threadIdx.x;
+  int32_t x[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) x[e] = buf[tid * E + e];
+  for (int k = 2; k <= n; k <<= 1) {
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      if (j >= 64 * E) {
+        __syncthreads();
+#pragma unroll
+        for (int e = 0; e < E; ++e) buf[tid * E + e] = x[e];
+        __syncthreads();
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          const int i = tid * E + e;
+          x[e] = bitonic_pick(x[e], buf[i ^ j], i, j, k);
+        }
+      } else if (j >= E) {
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          const int i = tid * E + e;
+          x[e] = bitonic_pick(x[e], __shfl_xor(x[e], j / E, 64), i, j, k);
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          const int p = e ^ j;
+          if (p > e) {
+            const bool asc = ((tid * E + e) & k) == 0;
+            const int32_t lo = min(x[e], x[p]), hi = max(x[e], x[p]);
+            x[e] = asc ? lo : hi;
+            x[p] = asc ? hi : lo;
+          }
+        }
+      }
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int e = 0; e < E; ++e) buf[tid * E + e] = x[e];
+  __syncthreads();
+}
+
+// Miss count of the step, and a clean histogram and list counters for the
 // next step's scan.
 __device__ __forceinline__ void reset_scan_state(const DevState& d, int u, int m) {
   uint32_t* gh = d.hist + (size_t)u * kBins1;
@@ -214,83 +268,103 @@ __global__ __launch_bounds__(kSelThreads) void k_select(DevState d, int32_t t,
   if (sh.bcast[2] != K - n_above) {
     // Inconsistent scan state (cannot happen when the histogram was clean):
     // report an empty selection and touch nothing.
-    for (int i = tid; i < K; i += kSelThreads) d_sel[(size_t)u * K + i] = -1;
+    for (int i = tid; i < K; i += kSelThreads) {
+      d_sel[(size_t)u * K + i] = -1;
+      d.sel_slot[(size_t)u * K + i] = 0;  // the gather then only reads slot 0
+    }
     reset_scan_state(d, u, 0);
     return;
   }
-  int kp = 1;
-  while (kp < K) kp <<= 1;
-  for (int i = K + tid; i < kp; i += kSelThreads) sh.sel[i] = 0x7FFFFFFF;
+  for (int i = K + tid; i < HC_MAX_TOPK; i += kSelThreads) sh.sel[i] = 0x7FFFFFFF;
   __syncthreads();
-  for (int k = 2; k <= kp; k <<= 1) {
-    for (int j = k >> 1; j > 0; j >>= 1) {
-      for (int i = tid; i < kp; i += kSelThreads) {
-        const int ixj = i ^ j;
-        if (ixj > i) {
-          const int32_t x = sh.sel[i], y = sh.sel[ixj];
-          if ((x > y) == ((i & k) == 0)) {
-            sh.sel[i] = y;
-            sh.sel[ixj] = x;
-          }
-        }
-      }
-      __syncthreads();
-    }
-  }
+  if (K <= kSelThreads) sort_positions<1>(sh.sel);
+  else if (K <= 2 * kSelThreads) sort_positions<2>(sh.sel);
+  else sort_positions<4>(sh.sel);
   for (int i = tid; i < K; i += kSelThreads) d_sel[(size_t)u * K + i] = sh.sel[i];
 
   // ---- 3. lookup, hits, ascending miss compaction ------------------------
   const int nwords = (C + 31) >> 5;
   for (int w = tid; w < nwords; w += kSelThreads) sh.touched[w] = 0;
-  __syncthreads();
   int32_t* pos2slot = d.pos2slot + (size_t)u * d.hcap;
   int32_t* slot2pos = d.slot2pos + (size_t)u * C;
   int32_t* last_use = d.last_use + (size_t)u * C;
+  constexpr int kLookRounds = HC_MAX_TOPK / kSelThreads;
+  int32_t lp[kLookRounds], ls[kLookRounds];
+#pragma unroll
+  for (int r = 0; r < kLookRounds; ++r) {   // all map reads in flight together
+    const int i = r * kSelThreads + tid;
+    lp[r] = i < K ? sh.sel[i] : 0;
+    ls[r] = i < K ? pos2slot[lp[r]] : 0;
+  }
+  __syncthreads();
   int m = 0;
-  for (int i0 = 0; i0 < K; i0 += kSelThreads) {
-    const int i = i0 + tid;
-    bool miss = false;
-    int32_t p = 0;
-    if (i < K) {
-      p = sh.sel[i];
-      const int32_t slot = pos2slot[p];
-      if (slot >= 0) {
-        last_use[slot] = t;
-        atomicOr(&sh.touched[slot >> 5], 1u << (slot & 31));
-      } else {
-        miss = true;
-      }
-      sh.sel[i] = slot;  // from here on sel[] holds slots (-1 = miss, filled below)
+#pragma unroll
+  for (int r = 0; r < kLookRounds; ++r) {
+    if (r * kSelThreads >= K) break;
+    const int i = r * kSelThreads + tid;
+    const bool valid = i < K;
+    const bool miss = valid && ls[r] < 0;
+    if (valid && !miss) {
+      last_use[ls[r]] = t;
+      atomicOr(&sh.touched[ls[r] >> 5], 1u << (ls[r] & 31));
     }
+    if (valid) sh.sel[i] = ls[r];  // from here on sel[] holds slots (-1 = miss, filled below)
     int total;
     const int k = m + block_flag_rank(miss, sh.wtot, total);
     if (miss) {
-      sh.mpos[k] = p;
+      sh.mpos[k] = lp[r];
       sh.midx[k] = i;
     }
     m += total;
   }
 
   // ---- 4. LRU victims: first m untouched entries of the order list --------
+  // Wave w of a round owns 2,048 consecutive entries, lane-interleaved so every
+  // load is coalesced; ranks inside the wave come from ballots, and one block
+  // scan of the 16 wave totals orders the waves.
   const int32_t* ocur = d.order + ((size_t)u * 2 + (t & 1)) * C;
   int32_t* onxt = d.order + ((size_t)u * 2 + ((t + 1) & 1)) * C;
+  const int lane = lane_id(), wv = tid >> 6;
+  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  constexpr int kOrdPer = 32;
   int kept = 0;
-  for (int j0 = 0; j0 < C; j0 += kSelThreads) {
-    const int j = j0 + tid;
-    bool keep = false;
-    int32_t v = 0;
-    if (j < C) {
-      v = ocur[j];
-      keep = !((sh.touched[v >> 5] >> (v & 31)) & 1u);
+  for (int j0 = 0; j0 < C; j0 += kSelThreads * kOrdPer) {
+    const int wb = j0 + wv * 64 * kOrdPer;
+    int32_t v[kOrdPer];
+#pragma unroll
+    for (int e = 0; e < kOrdPer; ++e) {
+      const int j = wb + e * 64 + lane;
+      v[e] = j < C ? ocur[j] : -1;
     }
-    int total;
-    const int k = kept + block_flag_rank(keep, sh.wtot, total);
-    if (keep) {
-      if (k < m) sh.vic[k] = v;
-      else onxt[k - m] = v;
+    int wave_total = 0;
+#pragma unroll
+    for (int e = 0; e < kOrdPer; ++e) {
+      const bool keep = v[e] >= 0 && !((sh.touched[v[e] >> 5] >> (v[e] & 31)) & 1u);
+      if (!keep) v[e] = -1;
+      wave_total += __popcll(__ballot(keep));
+    }
+    if (lane == 0) sh.wtot[wv] = wave_total;
+    __syncthreads();
+    int run = kept, total = 0;
+#pragma unroll
+    for (int i = 0; i < kWaves; ++i) {
+      run += i < wv ? sh.wtot[i] : 0;
+      total += sh.wtot[i];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int e = 0; e < kOrdPer; ++e) {
+      const uint64_t bal = __ballot(v[e] >= 0);
+      if (v[e] >= 0) {
+        const int k = run + __popcll(bal & lt_mask);
+        if (k < m) sh.vic[k] = v[e];
+        else onxt[k - m] = v[e];
+      }
+      run += __popcll(bal);
     }
     kept += total;
   }
+  __syncthreads();
   for (int k = tid; k < m; k += kSelThreads) atomicOr(&sh.touched[sh.vic[k] >> 5], 1u << (sh.vic[k] & 31));
   __syncthreads();
   // this step's K slots, ascending, close the order list
@@ -310,11 +384,14 @@ __global__ __launch_bounds__(kSelThreads) void k_select(DevState d, int32_t t,
   }
 
   // ---- 5. apply (miss, victim) pairs --------------------------------------
+  // A miss row is marked in sel_slot as -(slot + 1): the gather then reads it
+  // from host RAM and writes it into that slot itself.
   if (tid == 0) sh.bcast[3] = 0;
   __syncthreads();
   int32_t* tr = d_trace ? d_trace + (size_t)u * HC_TRACE_INTS(K) : nullptr;
-  int32_t* g_miss = d.miss_pos + (size_t)u * K;
+  int32_t* g_miss = d.miss_pos + (size_t)u * K;   // the gather's dense miss list
   int32_t* g_vic = d.victim + (size_t)u * K;
+  int32_t* g_midx = d.miss_idx + (size_t)u * K;
   for (int k = tid; k < m; k += kSelThreads) {
     const int32_t v = sh.vic[k], p = sh.mpos[k];
     const int32_t old = slot2pos[v];
@@ -325,9 +402,10 @@ __global__ __launch_bounds__(kSelThreads) void k_select(DevState d, int32_t t,
     pos2slot[p] = v;
     slot2pos[v] = p;
     last_use[v] = t;
-    sh.sel[sh.midx[k]] = v;
+    sh.sel[sh.midx[k]] = -(v + 1);
     g_miss[k] = p;
     g_vic[k] = v;
+    g_midx[k] = sh.midx[k];
     if (tr) {
       tr[HC_TRACE_HEADER + K + k] = p;
       tr[HC_TRACE_HEADER + 2 * K + k] = v;
@@ -337,9 +415,10 @@ __global__ __launch_bounds__(kSelThreads) void k_select(DevState d, int32_t t,
   __syncthreads();
   int32_t* g_slot = d.sel_slot + (size_t)u * K;
   for (int i = tid; i < K; i += kSelThreads) {
-    g_slot[i] = sh.sel[i];
+    const int32_t enc = sh.sel[i];
+    g_slot[i] = enc;
     if (tr) {
-      tr[HC_TRACE_HEADER + i] = sh.sel[i];
+      tr[HC_TRACE_HEADER + i] = enc < 0 ? -enc - 1 : enc;
       if (i >= m) {
         tr[HC_TRACE_HEADER + K + i] = -1;
         tr[HC_TRACE_HEADER + 2 * K + i] = -1;

@@ -143,6 +143,26 @@ def fill_rows(wl: Workload, s: int, l: int, out: np.ndarray | None = None,
     return out
 
 
+def fill_all_rows(wl: Workload, dest=None) -> list:
+    """Rows of every (session, layer), generated in parallel over (s, l, block).
+    dest(s, l) may return a uint8 [>= Hcap, 656] array to fill (e.g. pinned
+    host memory); otherwise new arrays are made.  Returns rows[s][l]."""
+    n = wl.hcap
+    rows = [[dest(s, l) if dest else np.empty((n, ROW_BYTES), np.uint8)
+             for l in range(wl.n_layers)] for s in range(wl.n_sessions)]
+    jobs = [(s, l, b) for s in range(wl.n_sessions) for l in range(wl.n_layers)
+            for b in range(-(-n // BLOCK_ROWS))]
+
+    def one(job):
+        s, l, b = job
+        lo, hi = b * BLOCK_ROWS, min(n, (b + 1) * BLOCK_ROWS)
+        _fill_block(rows[s][l][lo:hi], wl.seed, s, l, b)
+
+    with ThreadPoolExecutor(_workers()) as ex:
+        list(ex.map(one, jobs))
+    return rows
+
+
 # ---------------------------------------------------------------- scores ---
 
 class Scores:

@@ -58,6 +58,7 @@ extern "C" {
 #define HC_MAX_TOPK      4096  /* largest supported top_k                   */
 #define HC_MAX_SLOTS     262144 /* largest supported cache_slots            */
 #define HC_MAX_SESSIONS  256   /* largest supported n_sessions              */
+#define HC_MAX_UNITS     4096  /* largest S * ceil(L / R) (selection units) */
 
 /* Per-unit trace record: HC_TRACE_INTS(K) int32 values per (session, group),
  * units ordered u = s * G + g.  Layout:
@@ -74,9 +75,10 @@ extern "C" {
 #define HC_STAGE_TOPK_HIST   0  /* score scan: top-12-bit key histogram     */
 #define HC_STAGE_TOPK_FILTER 1  /* score scan: bin filter and compaction    */
 #define HC_STAGE_SELECT      2  /* exact cut, lookup, miss compaction, LRU  */
-#define HC_STAGE_FETCH       3  /* host RAM -> HBM miss rows (PCIe)          */
-#define HC_STAGE_GATHER      4  /* hot slots -> bf16 attention buffer        */
-#define HC_NUM_STAGES        5
+#define HC_STAGE_GATHER      3  /* hits from HBM slots, misses from host RAM
+                                   (also written into their victim slots),
+                                   dequantised into the bf16 buffer          */
+#define HC_NUM_STAGES        4
 
 typedef enum {
   HC_OK      = 0,
@@ -90,7 +92,7 @@ typedef struct hc_config {
   uint32_t struct_size;       /* sizeof(hc_config)                              */
   uint32_t n_sessions;        /* S, 1 <= S <= HC_MAX_SESSIONS                   */
   uint32_t n_layers;          /* L >= 1 layers per session                      */
-  uint32_t layers_per_select; /* R >= 1                                         */
+  uint32_t layers_per_select; /* R >= 1; S * ceil(L / R) <= HC_MAX_UNITS        */
   uint32_t cache_slots;       /* C, top_k <= C <= HC_MAX_SLOTS                  */
   uint32_t top_k;             /* K, 1 <= K <= HC_MAX_TOPK                       */
   uint64_t max_positions;     /* Hcap: host rows per (session, layer),
