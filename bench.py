@@ -93,6 +93,17 @@ def run_cpu_baseline(wl, rows, n_steps):
     }
 
 
+def preload_kernels(hc, torch):
+    """One step on a tiny throwaway context, so that loading the kernels'
+    code objects is not counted in the cold step."""
+    c = hc.HotCache(1, 1, 1, 64, 8, 64, 0)
+    out, sel, _ = c.alloc_outputs()
+    sc = torch.zeros(64, dtype=torch.float32, device="cuda")
+    c.step(sc, 64, [64], out, sel)
+    torch.cuda.synchronize()
+    c.close()
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -126,6 +137,7 @@ def main():
         wl.name, S, L, wl.layers_per_select, K, wl.cache_slots, wl.hist0, args.warmup,
         args.steps))
 
+    preload_kernels(hc, torch)
     cache = hc.HotCache(S, L, wl.layers_per_select, wl.cache_slots, K, wl.hcap, 0)
     t0 = time.time()
     rows = W.fill_all_rows(wl)
@@ -150,12 +162,14 @@ def main():
     def step(t):
         cache.step(d_scores[t], stride, wl.hist_len(t), out, sel, trace[t])
 
-    # cold step, then the rest of the warmup
+    # cold step (every row misses), then the rest of the warmup
+    hc.hc_profile_enable(cache.ctx, 1)
     torch.cuda.synchronize()
     c0 = time.perf_counter()
     step(0)
     torch.cuda.synchronize()
     cold_ms = (time.perf_counter() - c0) * 1e3
+    cold_stage_ms, _, _ = hc.hc_profile_read(cache.ctx)
     for t in range(1, args.warmup):
         step(t)
 
@@ -167,9 +181,10 @@ def main():
         step(t)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
-    stage_ms, n_prof = hc.hc_profile_read(cache.ctx)
+    stage_ms, n_prof, per_step = hc.hc_profile_read(cache.ctx, args.steps)
     assert n_prof == args.steps
     stage_avg = {k: v / n_prof for k, v in stage_ms.items()}
+    step_kernel_us = per_step.sum(axis=1) * 1e3
 
     ms_per_step = elapsed * 1e3 / args.steps
     rows_per_step = S * L * K
@@ -235,8 +250,15 @@ def main():
         "gather_hbm_gbs": roofline("gather")["achieved"],
         "fetch_pcie_gbs": roofline("fetch")["achieved"],
         "miss_rows_per_step": round(float(timed_miss_rows.mean()), 1),
+        "step_kernel_us": {"median": round(float(np.median(step_kernel_us)), 2),
+                           "p99": round(float(np.percentile(step_kernel_us, 99)), 2),
+                           "max": round(float(step_kernel_us.max()), 2),
+                           "mean": round(float(step_kernel_us.mean()), 2)},
         "cold_step_ms": round(cold_ms, 3),
+        "cold_step_kernel_us": {k: round(v * 1e3, 2) for k, v in cold_stage_ms.items()},
         "cold_step_miss_rows": int(miss_rows[0]),
+        "cold_step_fetch_pcie_gbs": round(int(miss_rows[0]) * ROW / (
+            cold_stage_ms["gather"] * 1e-3) / 1e9, 2),
         "cpu_baseline": None,
     }
     cache.close()

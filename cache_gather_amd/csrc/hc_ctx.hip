@@ -334,7 +334,8 @@ hc_status hc_profile_enable(hc_ctx* c, uint32_t max_steps) {
   return HC_OK;
 }
 
-hc_status hc_profile_read(hc_ctx* c, double* stage_ms, uint64_t* n_steps) {
+hc_status hc_profile_read(hc_ctx* c, double* stage_ms, double* per_step, uint64_t per_step_cap,
+                          uint64_t* n_steps) {
   if (!c || !stage_ms || !n_steps) return HC_E_INVAL;
   if (c->poisoned) return HC_E_STATE;
   DeviceGuard dg(c->cfg.device);
@@ -347,6 +348,7 @@ hc_status hc_profile_read(hc_ctx* c, double* stage_ms, uint64_t* n_steps) {
       float ms = 0.f;
       if (hipEventElapsedTime(&ms, ev[i], ev[i + 1]) != hipSuccess) return fail_hip(c);
       stage_ms[i] += ms;
+      if (per_step && k < per_step_cap) per_step[(size_t)k * HC_NUM_STAGES + i] = ms;
     }
   }
   *n_steps = c->prof_used;

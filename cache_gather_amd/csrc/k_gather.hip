@@ -10,7 +10,7 @@
 // read host RAM.
 //
 // One launch, two kinds of workgroup:
-//   * the first kMissBlocks workgroups walk the dense miss list (every layer
+//   * the first workgroups walk the dense miss list (every layer
 //     of every unit): each missing row is read from pinned host RAM over PCIe
 //     (zero-copy), written into its victim slot, and dequantised from the same
 //     registers — so its slot is only ever read in later steps, and all PCIe
@@ -41,7 +41,12 @@ constexpr int kItemsPerRow = 40;
 constexpr int kGatherThreads = kRowsPerPass * kItemsPerRow;  // 320
 constexpr int kPasses = 2;
 constexpr int kRowsPerRound = kRowsPerPass * kPasses;         // 32
-constexpr int kMissBlocks = 64;  // few CUs wait on PCIe; the rest stream HBM
+// Workgroups reserved for the miss list.  Only about one per kMissRowsPerBlock
+// missing rows is active (at least kMissBlocksMin): few CUs then wait on PCIe
+// while the rest stream HBM, and a cold step still has enough reads in flight.
+constexpr int kMissBlocks = 256;
+constexpr int kMissBlocksMin = 32;
+constexpr int kMissRowsPerBlock = 64;
 
 __device__ __forceinline__ uint32_t bf16x2(float lo, float hi) {
   const __bf16 a = (__bf16)lo, b = (__bf16)hi;
@@ -62,30 +67,35 @@ struct RowJob {
   uint8_t* fill[kPasses];
 };
 
+// fp16 scale g (0..7) of a row's 16-B scale block, as float.
+__device__ __forceinline__ float scale_of(const u32x4& blk, int g) {
+  const uint32_t w = (g >> 1) == 0 ? blk.x : (g >> 1) == 1 ? blk.y : (g >> 1) == 2 ? blk.z : blk.w;
+  const uint16_t h = (uint16_t)((g & 1) ? (w >> 16) : (w & 0xFFFF));
+  return (float)__builtin_bit_cast(_Float16, h);
+}
+
 // Copies / dequantises this thread's item of up to kPasses rows; all loads are
-// issued before the first store.
+// issued before the first store.  Latent lanes read their 16 latent bytes and
+// the row's whole 16-B scale block (one address for all 32 lanes of a row, so
+// it costs one request); RoPE lanes read 16 bytes each.
 __device__ __forceinline__ void run_rows(const RowJob& j, int item) {
-  u32x4 v[kPasses], scale_blk[kPasses];
-  uint16_t sb[kPasses];
+  u32x4 v[kPasses], sblk[kPasses];
   const int off = item < 32 ? 16 * item : HC_ROPE_OFFSET + 16 * (item - 32);
 #pragma unroll
   for (int p = 0; p < kPasses; ++p) {
     if (!j.dst[p]) continue;
     v[p] = *reinterpret_cast<const u32x4*>(j.src[p] + off);
-    if (item < 32)
-      sb[p] = *reinterpret_cast<const uint16_t*>(j.src[p] + HC_SCALE_OFFSET + 2 * (item >> 2));
-    else if (item == 32 && j.fill[p])
-      scale_blk[p] = *reinterpret_cast<const u32x4*>(j.src[p] + HC_SCALE_OFFSET);
+    if (item < 32) sblk[p] = *reinterpret_cast<const u32x4*>(j.src[p] + HC_SCALE_OFFSET);
   }
 #pragma unroll
   for (int p = 0; p < kPasses; ++p) {
     if (!j.dst[p]) continue;
     if (j.fill[p]) {
       *reinterpret_cast<u32x4*>(j.fill[p] + off) = v[p];
-      if (item == 32) *reinterpret_cast<u32x4*>(j.fill[p] + HC_SCALE_OFFSET) = scale_blk[p];
+      if (item == 0) *reinterpret_cast<u32x4*>(j.fill[p] + HC_SCALE_OFFSET) = sblk[p];
     }
     if (item < 32) {
-      const float sc = (float)__builtin_bit_cast(_Float16, sb[p]);
+      const float sc = scale_of(sblk[p], item >> 2);
       const u32x4 q = v[p];
       u32x4 a, b;
       a.x = bf16x2(i8f(q.x, 0) * sc, i8f(q.x, 1) * sc);
@@ -152,7 +162,10 @@ __global__ __launch_bounds__(kGatherThreads) void k_gather(DevState d,
     if (threadIdx.x == 0) pref[0] = 0;
     __syncthreads();
     const int M = pref[U];
-    for (int base = blockIdx.x * kRowsPerRound; base < M; base += kMissBlocks * kRowsPerRound) {
+    int active = (M + kMissRowsPerBlock - 1) / kMissRowsPerBlock;
+    active = active < kMissBlocksMin ? kMissBlocksMin : (active > kMissBlocks ? kMissBlocks : active);
+    if ((int)blockIdx.x >= active) return;
+    for (int base = blockIdx.x * kRowsPerRound; base < M; base += active * kRowsPerRound) {
 #pragma unroll
       for (int p = 0; p < kPasses; ++p) {
         const int q = base + p * kRowsPerPass + lrow;

@@ -78,7 +78,7 @@ def lib():
     L.hc_export_state.restype = st
     L.hc_profile_enable.argtypes = [_vp, ctypes.c_uint32]
     L.hc_profile_enable.restype = st
-    L.hc_profile_read.argtypes = [_vp, ctypes.POINTER(ctypes.c_double),
+    L.hc_profile_read.argtypes = [_vp, ctypes.POINTER(ctypes.c_double), _vp, ctypes.c_uint64,
                                   ctypes.POINTER(ctypes.c_uint64)]
     L.hc_profile_read.restype = st
     L.hc_steps_done.argtypes = [_vp, ctypes.POINTER(ctypes.c_uint64)]
@@ -162,11 +162,16 @@ def hc_profile_enable(ctx: int, max_steps: int) -> None:
     _check("hc_profile_enable", lib().hc_profile_enable(ctx, max_steps))
 
 
-def hc_profile_read(ctx: int):
+def hc_profile_read(ctx: int, max_steps: int = 0):
+    """(summed ms per stage, n timed steps, per-step ms [n, stages] or None)."""
     ms = (ctypes.c_double * NUM_STAGES)()
     n = ctypes.c_uint64()
-    _check("hc_profile_read", lib().hc_profile_read(ctx, ms, ctypes.byref(n)))
-    return dict(zip(STAGES, list(ms))), n.value
+    per = np.zeros((max_steps, NUM_STAGES), np.float64) if max_steps else None
+    _check("hc_profile_read", lib().hc_profile_read(ctx, ms, _ptr(per), max_steps,
+                                                    ctypes.byref(n)))
+    if per is not None:
+        per = per[:min(n.value, max_steps)]
+    return dict(zip(STAGES, list(ms))), n.value, per
 
 
 def hc_steps_done(ctx: int) -> int:

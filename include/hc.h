@@ -150,10 +150,14 @@ hc_status hc_export_state(hc_ctx* ctx, uint32_t session, uint32_t layer,
 
 /* Per-stage kernel timing with HIP events recorded around each launch on the
  * step's stream.  hc_profile_enable(ctx, n) arms timing for the next n steps
- * (n = 0 disarms); hc_profile_read waits for them and returns the summed
- * milliseconds per stage (HC_NUM_STAGES values) and the number of steps. */
+ * (n = 0 disarms; any earlier timing is dropped).  hc_profile_read waits for
+ * the timed steps and returns the summed milliseconds per stage
+ * (stage_ms[HC_NUM_STAGES]), the number of timed steps, and, if per_step is
+ * non-NULL, the milliseconds of each stage of each step, row-major
+ * [step][HC_NUM_STAGES], for at most per_step_cap steps. */
 hc_status hc_profile_enable(hc_ctx* ctx, uint32_t max_steps);
-hc_status hc_profile_read(hc_ctx* ctx, double* stage_ms, uint64_t* n_steps);
+hc_status hc_profile_read(hc_ctx* ctx, double* stage_ms, double* per_step,
+                          uint64_t per_step_cap, uint64_t* n_steps);
 
 /* Number of steps issued so far (the t the next hc_step will use). */
 hc_status hc_steps_done(const hc_ctx* ctx, uint64_t* n);
