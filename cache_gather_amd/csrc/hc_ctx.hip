@@ -39,7 +39,7 @@ bool valid_config(const hc_config* c) {
   if (c->max_positions < c->top_k || c->max_positions >= (1ull << 31)) return false;
   if (c->flags != 0) return false;
   const uint64_t layers = (uint64_t)c->n_sessions * c->n_layers;
-  if (layers > 65535) return false;
+  if (layers > 60000) return false;  // one gather grid row per layer
   const uint64_t G = (c->n_layers + c->layers_per_select - 1) / c->layers_per_select;
   if ((uint64_t)c->n_sessions * G > (uint64_t)kMaxUnits) return false;
   return true;
@@ -69,7 +69,7 @@ Layout layout_of(const hc_config* c) {
   lo.victim = take(U * K * 4);
   lo.miss_idx = take(U * K * 4);
   lo.host_tab = take(S * L * 8);
-  lo.hot = take(S * L * C * kRow);
+  lo.hot = take(S * L * C * kSlotStride);
   lo.total = align_up(off);
   return lo;
 }
@@ -310,8 +310,8 @@ hc_status hc_export_state(hc_ctx* c, uint32_t session, uint32_t layer, int32_t* 
     ok = hipMemcpy(pos2slot, d.pos2slot + u * (size_t)d.hcap, (size_t)d.hcap * 4,
                    hipMemcpyDeviceToHost) == hipSuccess;
   if (ok && hot_rows)
-    ok = hipMemcpy(hot_rows, d.hot + sl * C * kRow, C * kRow, hipMemcpyDeviceToHost) ==
-         hipSuccess;
+    ok = hipMemcpy2D(hot_rows, kRow, d.hot + sl * C * kSlotStride, kSlotStride, kRow, C,
+                     hipMemcpyDeviceToHost) == hipSuccess;
   return ok ? HC_OK : fail_hip(c);
 }
 

@@ -10,6 +10,7 @@
 namespace hc {
 
 constexpr int kRow = HC_ROW_BYTES;        // 656 B per Q8G64 row
+constexpr int kSlotStride = kRow;         // bytes between hot slots in HBM (padding measured: no gain)
 constexpr int kOut = HC_OUT_ELEMS;        // 576 bf16 per gathered row
 constexpr int kBin1Bits = 12;             // first radix digit: key bits [20, 32)
 constexpr int kBins1 = 1 << kBin1Bits;    // 4096 histogram bins per unit
@@ -38,7 +39,7 @@ struct DevState {
   int32_t* victim;     // [U][K]     slot that miss k fills
   int32_t* miss_idx;   // [U][K]     index in the selection of miss k
   const uint8_t* const* host;  // [S*L] device-visible pointers of the pinned host rows
-  uint8_t* hot;        // [S*L][C][kRow]
+  uint8_t* hot;        // [S*L][C][kSlotStride], a row in the first 656 B of its slot
 };
 
 struct StepArgs {

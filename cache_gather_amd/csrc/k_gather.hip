@@ -27,10 +27,12 @@
 //
 // gfx950 mapping: a row is 40 work items — 32 latent chunks (16 B in, 32 B
 // out) and 8 RoPE chunks (16 B in, 16 B out) — so 320 threads (5 wave64) hold
-// 8 rows with every lane busy.  A workgroup covers kPasses x 8 rows per round
-// and issues all of their loads before converting anything, to keep enough
-// reads in flight.  HBM-bound: 656 B read (hit) or written (miss) + 1,152 B
-// written per selected row; PCIe: 656 B per missing row.  bf16 rounding by
+// 8 rows with every lane busy, one row item per thread (measured on MI355X:
+// keeping several rows per thread in flight streams slower).  Grid rows
+// [0, miss_rows) are the miss workgroups, dispatched first; grid row
+// miss_rows + sl holds layer sl's hit rows, so no per-row index division is
+// needed.  HBM-bound: 656 B read (hit) or written (miss) + 1,152 B written per
+// selected row; PCIe: 656 B per missing row.  bf16 rounding by
 // v_cvt_pk_bf16_f32.
 #include "hc_internal.h"
 
@@ -39,7 +41,7 @@ namespace hc {
 constexpr int kRowsPerPass = 8;
 constexpr int kItemsPerRow = 40;
 constexpr int kGatherThreads = kRowsPerPass * kItemsPerRow;  // 320
-constexpr int kPasses = 2;
+constexpr int kPasses = 1;
 constexpr int kRowsPerRound = kRowsPerPass * kPasses;         // 32
 // Workgroups reserved for the miss list.  Only about one per kMissRowsPerBlock
 // missing rows is active (at least kMissBlocksMin): few CUs then wait on PCIe
@@ -123,7 +125,7 @@ __device__ __forceinline__ int layers_in_group(const DevState& d, int g) {
 
 __global__ __launch_bounds__(kGatherThreads) void k_gather(DevState d,
                                                            uint16_t* __restrict__ out,
-                                                           int64_t total_rows) {
+                                                           int miss_rows) {
   extern __shared__ int32_t pref[];          // [S*G + 1]: miss rows (all layers) before unit u
   __shared__ int32_t wsum[kGatherThreads / 64];
   const int item = threadIdx.x % kItemsPerRow;
@@ -132,7 +134,8 @@ __global__ __launch_bounds__(kGatherThreads) void k_gather(DevState d,
   const size_t out_row_bytes = (size_t)kOut * 2;
   RowJob j;
 
-  if (blockIdx.x < kMissBlocks) {
+  if ((int)blockIdx.y < miss_rows) {
+    const int mb = blockIdx.y * gridDim.x + blockIdx.x;  // miss workgroup number
     // ---- dense miss list: prefix of (misses x layers) over units --------
     const int U = d.S * d.G;
     int running = 0;
@@ -164,8 +167,8 @@ __global__ __launch_bounds__(kGatherThreads) void k_gather(DevState d,
     const int M = pref[U];
     int active = (M + kMissRowsPerBlock - 1) / kMissRowsPerBlock;
     active = active < kMissBlocksMin ? kMissBlocksMin : (active > kMissBlocks ? kMissBlocks : active);
-    if ((int)blockIdx.x >= active) return;
-    for (int base = blockIdx.x * kRowsPerRound; base < M; base += active * kRowsPerRound) {
+    if (mb >= active) return;
+    for (int base = mb * kRowsPerRound; base < M; base += active * kRowsPerRound) {
 #pragma unroll
       for (int p = 0; p < kPasses; ++p) {
         const int q = base + p * kRowsPerPass + lrow;
@@ -184,7 +187,7 @@ __global__ __launch_bounds__(kGatherThreads) void k_gather(DevState d,
         const int64_t sl = (int64_t)s * d.L + g * d.R + lig;
         const size_t uk = (size_t)u * d.K + k;
         j.src[p] = d.host[sl] + (size_t)d.miss_pos[uk] * kRow;
-        j.fill[p] = d.hot + ((size_t)sl * d.C + d.victim[uk]) * kRow;
+        j.fill[p] = d.hot + ((size_t)sl * d.C + d.victim[uk]) * kSlotStride;
         j.dst[p] = out_b + ((size_t)sl * d.K + d.miss_idx[uk]) * out_row_bytes;
       }
       run_rows(j, item);
@@ -192,31 +195,35 @@ __global__ __launch_bounds__(kGatherThreads) void k_gather(DevState d,
     return;
   }
 
-  // ---- hit rows, in output order ------------------------------------------
-  const int64_t row0 = (int64_t)(blockIdx.x - kMissBlocks) * kRowsPerRound + lrow;
+  // ---- hit rows of layer sl = blockIdx.y - miss_rows, in output order -----
+  const int sl = blockIdx.y - miss_rows;
+  const int s = sl / d.L, l = sl - s * d.L;           // uniform per workgroup
+  const int32_t* slot = d.sel_slot + (size_t)(s * d.G + l / d.R) * d.K;
+  const uint8_t* hot = d.hot + (size_t)sl * d.C * kSlotStride;
+  uint8_t* orow = out_b + (size_t)sl * d.K * out_row_bytes;
+  const int i0 = blockIdx.x * kRowsPerRound + lrow;
 #pragma unroll
   for (int p = 0; p < kPasses; ++p) {
-    const int64_t row = row0 + p * kRowsPerPass;
+    const int i = i0 + p * kRowsPerPass;
     j.dst[p] = nullptr;
     j.fill[p] = nullptr;
-    if (row >= total_rows) continue;
-    const int64_t sl = row / d.K;
-    const int i = (int)(row - sl * d.K);
-    const int s = (int)(sl / d.L), l = (int)(sl - (int64_t)s * d.L);
-    const int32_t enc = d.sel_slot[(size_t)(s * d.G + l / d.R) * d.K + i];
+    if (i >= d.K) continue;
+    const int32_t enc = slot[i];
     if (enc < 0) continue;  // missed this step: written by a miss workgroup
-    j.src[p] = d.hot + ((size_t)sl * d.C + enc) * kRow;
-    j.dst[p] = out_b + (size_t)row * out_row_bytes;
+    j.src[p] = hot + (size_t)enc * kSlotStride;
+    j.dst[p] = orow + (size_t)i * out_row_bytes;
   }
   run_rows(j, item);
 }
 
 hipError_t launch_gather(const DevState& d, uint16_t* d_out, hipStream_t st) {
-  const int64_t total = (int64_t)d.S * d.L * d.K;
-  const int64_t blocks = kMissBlocks + (total + kRowsPerRound - 1) / kRowsPerRound;
+  // grid rows [0, miss_rows): the miss workgroups (dispatched first);
+  // row miss_rows + sl: the hit rows of layer sl
+  const int gx = (d.K + kRowsPerRound - 1) / kRowsPerRound;
+  const int miss_rows = (kMissBlocks + gx - 1) / gx;
   const size_t lds = ((size_t)d.S * d.G + 1) * sizeof(int32_t);
-  hipLaunchKernelGGL(k_gather, dim3((uint32_t)blocks), dim3(kGatherThreads), lds, st, d, d_out,
-                     total);
+  hipLaunchKernelGGL(k_gather, dim3(gx, d.S * d.L + miss_rows), dim3(kGatherThreads), lds, st, d,
+                     d_out, miss_rows);
   return hipGetLastError();
 }
 

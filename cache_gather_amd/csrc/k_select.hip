@@ -11,9 +11,12 @@
 //
 // Design on gfx950 (1,024 threads = 16 wave64, ~104 KB LDS, one unit each):
 //  1. Radix-select the remaining 20 key bits (2 x 10-bit digits) over the
-//     candidates of the cut bin; if more keys equal the cut key than are
-//     needed, radix-select the position cut among them (lower positions win).
-//  2. Gather the K winners into LDS and bitonic-sort them by position.
+//     candidates of the cut bin (kept in LDS when they fit); if more keys
+//     equal the cut key than are needed, radix-select the position cut among
+//     them (lower positions win).
+//  2. Emit the K winners in ascending position order: per window of 262,144
+//     positions, set one bit per winner in an LDS bitmap and read the set bits
+//     back in order with one block-wide prefix sum.
 //  3. Lookup pos2slot; hits get last_use = t and are marked in an LDS bitmap of
 //     touched slots; misses are compacted in ascending order by wave ballot +
 //     mbcnt prefix.
@@ -31,15 +34,26 @@ namespace hc {
 constexpr int kSelThreads = 1024;
 constexpr int kWaves = kSelThreads / 64;
 
+constexpr int kCandCache = 8192;               // cut-bin candidates kept in LDS (64 KB)
+constexpr int kWinWords = HC_MAX_SLOTS / 32;   // bitmap words per position window
+constexpr int kWinPositions = kWinWords * 32;  // 262,144 positions per window
+
 struct SelShared {
   uint32_t hist[2048];
-  int32_t sel[HC_MAX_TOPK];       // positions, then the slot of each selected row
-  int32_t mpos[HC_MAX_TOPK];      // missing positions (ascending)
-  int32_t midx[HC_MAX_TOPK];      // index in sel of miss k
-  int32_t vic[HC_MAX_TOPK];       // victim slot of miss k
-  uint32_t touched[HC_MAX_SLOTS / 32];
+  int32_t sel[HC_MAX_TOPK];     // winners by ascending position, then the slot of each
+  int32_t mpos[HC_MAX_TOPK];    // winners unordered (phase 2), then missing positions
+  union {
+    uint2 cand[kCandCache];       // phase 1: (key, position) of the cut bin
+    uint32_t posbits[kWinWords];  // phase 2: winners of one position window
+    struct {
+      int32_t midx[HC_MAX_TOPK];  // index in sel of miss k
+      int32_t vic[HC_MAX_TOPK];   // victim slot of miss k
+      uint32_t touched[HC_MAX_SLOTS / 32];
+    } lru;                        // phases 3-5
+  } u;
   int32_t wtot[kWaves];
   int32_t bcast[4];
+  int32_t wmax;
 };
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
@@ -124,60 +138,6 @@ __device__ __forceinline__ void clear_hist(SelShared& sh, int nb) {
   __syncthreads();
 }
 
-// Bitonic sort (ascending) of the kSelThreads * E values in buf.  Value i
-// lives in register i % E of thread i / E: compare-exchange partners closer
-// than E are in the same thread, closer than 64 E in the same wave (cross-lane
-// shuffle, no barrier); only strides of 64 E and more go through LDS.
-__device__ __forceinline__ int32_t bitonic_pick(int32_t a, int32_t b, int i, int j, int k) {
-  const bool lower = (i & j) == 0, asc = (i & k) == 0;
-  return (lower == asc) ? min(a, b) : max(a, b);
-}
-
-template <int E>
-__device__ void sort_positions(int32_t* buf) {
-  constexpr int n = kSelThreads * E;
-  const int tid = threadIdx.x;
-  int32_t x[E];
-#pragma unroll
-  for (int e = 0; e < E; ++e) x[e] = buf[tid * E + e];
-  for (int k = 2; k <= n; k <<= 1) {
-    for (int j = k >> 1; j > 0; j >>= 1) {
-      if (j >= 64 * E) {
-        __syncthreads();
-#pragma unroll
-        for (int e = 0; e < E; ++e) buf[tid * E + e] = x[e];
-        __syncthreads();
-#pragma unroll
-        for (int e = 0; e < E; ++e) {
-          const int i = tid * E + e;
-          x[e] = bitonic_pick(x[e], buf[i ^ j], i, j, k);
-        }
-      } else if (j >= E) {
-#pragma unroll
-        for (int e = 0; e < E; ++e) {
-          const int i = tid * E + e;
-          x[e] = bitonic_pick(x[e], __shfl_xor(x[e], j / E, 64), i, j, k);
-        }
-      } else {
-#pragma unroll
-        for (int e = 0; e < E; ++e) {
-          const int p = e ^ j;
-          if (p > e) {
-            const bool asc = ((tid * E + e) & k) == 0;
-            const int32_t lo = min(x[e], x[p]), hi = max(x[e], x[p]);
-            x[e] = asc ? lo : hi;
-            x[p] = asc ? hi : lo;
-          }
-        }
-      }
-    }
-  }
-  __syncthreads();
-#pragma unroll
-  for (int e = 0; e < E; ++e) buf[tid * E + e] = x[e];
-  __syncthreads();
-}
-
 // Miss count of the step, and a clean histogram and list counters for the
 // next step's scan.
 __device__ __forceinline__ void reset_scan_state(const DevState& d, int u, int m) {
@@ -200,13 +160,20 @@ __global__ __launch_bounds__(kSelThreads) void k_select(DevState d, int32_t t,
   const int n_above = min(cnt[kCntAbove], K - 1);          // < K by construction
   const int n_cand = (int)min((int64_t)cnt[kCntCand], d.hcap);
   const uint32_t b1 = (uint32_t)cnt[kCntBin1];
-  const uint2* cand = d.cand + (size_t)u * d.hcap;
+  const uint2* gcand = d.cand + (size_t)u * d.hcap;
   int r = K - n_above;  // winners still to take from the cut bin, >= 1
 
   // ---- 1. exact cut key T and position cut among keys equal to T ----------
+  // The first pass also copies the candidates into LDS when they fit.
+  const bool cached = n_cand <= kCandCache;
+  const uint2* cand = cached ? sh.u.cand : gcand;
   int d2, d3, skip;
   clear_hist(sh, 1024);
-  for (int i = tid; i < n_cand; i += kSelThreads) atomicAdd(&sh.hist[(cand[i].x >> 10) & 1023], 1u);
+  for (int i = tid; i < n_cand; i += kSelThreads) {
+    const uint2 c = gcand[i];
+    if (cached) sh.u.cand[i] = c;
+    atomicAdd(&sh.hist[(c.x >> 10) & 1023], 1u);
+  }
   __syncthreads();
   find_digit(sh.hist, 1024, r, true, sh, d2, skip);
   r -= skip;
@@ -252,18 +219,43 @@ __global__ __launch_bounds__(kSelThreads) void k_select(DevState d, int32_t t,
     pcut = (int32_t)((hi << 10) | (uint32_t)e3);
   }
 
-  // ---- 2. the K winners, sorted by position ------------------------------
-  if (tid == 0) sh.bcast[2] = 0;
+  // ---- 2. the K winners, in ascending position order ---------------------
+  if (tid == 0) {
+    sh.bcast[2] = 0;
+    sh.wmax = 0;
+  }
   __syncthreads();
   const int32_t* above = d.above + (size_t)u * K;
-  for (int i = tid; i < n_above; i += kSelThreads) sh.sel[i] = above[i];
-  for (int i = tid; i < n_cand; i += kSelThreads) {
-    const uint2 c = cand[i];
-    if (c.x > T || (c.x == T && (int32_t)c.y <= pcut)) {
-      const int o = n_above + atomicAdd(&sh.bcast[2], 1);
-      if (o < K) sh.sel[o] = (int32_t)c.y;  // exactly K - n_above winners by construction
+  int32_t pmax = 0;
+  for (int i = tid; i < n_above; i += kSelThreads) {
+    const int32_t p = above[i];
+    sh.mpos[i] = p;
+    pmax = max(pmax, p);
+  }
+  // candidates that win, compacted per wave: one LDS atomic per wave
+  const uint64_t lt_mask = (lane_id() == 0) ? 0ull : (~0ull >> (64 - lane_id()));
+  for (int i0 = 0; i0 < n_cand; i0 += kSelThreads) {
+    const int i = i0 + tid;
+    bool win = false;
+    int32_t p = 0;
+    if (i < n_cand) {
+      const uint2 c = cand[i];
+      p = (int32_t)c.y;
+      win = c.x > T || (c.x == T && p <= pcut);
+    }
+    const uint64_t bal = __ballot(win);
+    int base = 0;
+    if (lane_id() == 0 && bal) base = atomicAdd(&sh.bcast[2], __popcll(bal));
+    base = __shfl(base, 0, 64);
+    if (win) {
+      const int o = n_above + base + __popcll(bal & lt_mask);
+      if (o < K) sh.mpos[o] = p;  // exactly K - n_above winners by construction
+      pmax = max(pmax, p);
     }
   }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) pmax = max(pmax, __shfl_xor(pmax, o, 64));
+  if (lane_id() == 0) atomicMax(&sh.wmax, pmax);
   __syncthreads();
   if (sh.bcast[2] != K - n_above) {
     // Inconsistent scan state (cannot happen when the histogram was clean):
@@ -275,16 +267,46 @@ __global__ __launch_bounds__(kSelThreads) void k_select(DevState d, int32_t t,
     reset_scan_state(d, u, 0);
     return;
   }
-  for (int i = K + tid; i < HC_MAX_TOPK; i += kSelThreads) sh.sel[i] = 0x7FFFFFFF;
+  {
+    constexpr int kWordsPerThread = kWinWords / kSelThreads;  // 8
+    const int wmax = sh.wmax;
+    int emitted = 0;
+    for (int64_t w0 = 0; w0 <= wmax; w0 += kWinPositions) {
+      for (int i = tid; i < kWinWords; i += kSelThreads) sh.u.posbits[i] = 0;
+      __syncthreads();
+      for (int i = tid; i < K; i += kSelThreads) {
+        const int p = sh.mpos[i];
+        if (p >= w0 && p - w0 < kWinPositions)
+          atomicOr(&sh.u.posbits[(int)(p - w0) >> 5], 1u << (p & 31));
+      }
+      __syncthreads();
+      uint32_t wd[kWordsPerThread];
+      int n = 0;
+#pragma unroll
+      for (int e = 0; e < kWordsPerThread; ++e) {
+        wd[e] = sh.u.posbits[kWordsPerThread * tid + e];
+        n += __popc(wd[e]);
+      }
+      int total;
+      int o = emitted + block_incl_scan(n, sh.wtot, total) - n;
+#pragma unroll
+      for (int e = 0; e < kWordsPerThread; ++e) {
+        uint32_t bits = wd[e];
+        while (bits) {
+          const int b = __ffs(bits) - 1;
+          bits &= bits - 1;
+          sh.sel[o++] = (int32_t)(w0 + (kWordsPerThread * tid + e) * 32 + b);
+        }
+      }
+      emitted += total;
+    }
+  }
   __syncthreads();
-  if (K <= kSelThreads) sort_positions<1>(sh.sel);
-  else if (K <= 2 * kSelThreads) sort_positions<2>(sh.sel);
-  else sort_positions<4>(sh.sel);
   for (int i = tid; i < K; i += kSelThreads) d_sel[(size_t)u * K + i] = sh.sel[i];
 
   // ---- 3. lookup, hits, ascending miss compaction ------------------------
   const int nwords = (C + 31) >> 5;
-  for (int w = tid; w < nwords; w += kSelThreads) sh.touched[w] = 0;
+  for (int w = tid; w < nwords; w += kSelThreads) sh.u.lru.touched[w] = 0;
   int32_t* pos2slot = d.pos2slot + (size_t)u * d.hcap;
   int32_t* slot2pos = d.slot2pos + (size_t)u * C;
   int32_t* last_use = d.last_use + (size_t)u * C;
@@ -306,14 +328,14 @@ __global__ __launch_bounds__(kSelThreads) void k_select(DevState d, int32_t t,
     const bool miss = valid && ls[r] < 0;
     if (valid && !miss) {
       last_use[ls[r]] = t;
-      atomicOr(&sh.touched[ls[r] >> 5], 1u << (ls[r] & 31));
+      atomicOr(&sh.u.lru.touched[ls[r] >> 5], 1u << (ls[r] & 31));
     }
     if (valid) sh.sel[i] = ls[r];  // from here on sel[] holds slots (-1 = miss, filled below)
     int total;
     const int k = m + block_flag_rank(miss, sh.wtot, total);
     if (miss) {
       sh.mpos[k] = lp[r];
-      sh.midx[k] = i;
+      sh.u.lru.midx[k] = i;
     }
     m += total;
   }
@@ -325,7 +347,6 @@ __global__ __launch_bounds__(kSelThreads) void k_select(DevState d, int32_t t,
   const int32_t* ocur = d.order + ((size_t)u * 2 + (t & 1)) * C;
   int32_t* onxt = d.order + ((size_t)u * 2 + ((t + 1) & 1)) * C;
   const int lane = lane_id(), wv = tid >> 6;
-  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   constexpr int kOrdPer = 32;
   int kept = 0;
   for (int j0 = 0; j0 < C; j0 += kSelThreads * kOrdPer) {
@@ -339,7 +360,7 @@ __global__ __launch_bounds__(kSelThreads) void k_select(DevState d, int32_t t,
     int wave_total = 0;
 #pragma unroll
     for (int e = 0; e < kOrdPer; ++e) {
-      const bool keep = v[e] >= 0 && !((sh.touched[v[e] >> 5] >> (v[e] & 31)) & 1u);
+      const bool keep = v[e] >= 0 && !((sh.u.lru.touched[v[e] >> 5] >> (v[e] & 31)) & 1u);
       if (!keep) v[e] = -1;
       wave_total += __popcll(__ballot(keep));
     }
@@ -357,7 +378,7 @@ __global__ __launch_bounds__(kSelThreads) void k_select(DevState d, int32_t t,
       const uint64_t bal = __ballot(v[e] >= 0);
       if (v[e] >= 0) {
         const int k = run + __popcll(bal & lt_mask);
-        if (k < m) sh.vic[k] = v[e];
+        if (k < m) sh.u.lru.vic[k] = v[e];
         else onxt[k - m] = v[e];
       }
       run += __popcll(bal);
@@ -365,13 +386,13 @@ __global__ __launch_bounds__(kSelThreads) void k_select(DevState d, int32_t t,
     kept += total;
   }
   __syncthreads();
-  for (int k = tid; k < m; k += kSelThreads) atomicOr(&sh.touched[sh.vic[k] >> 5], 1u << (sh.vic[k] & 31));
+  for (int k = tid; k < m; k += kSelThreads) atomicOr(&sh.u.lru.touched[sh.u.lru.vic[k] >> 5], 1u << (sh.u.lru.vic[k] & 31));
   __syncthreads();
   // this step's K slots, ascending, close the order list
   int base = C - K;
   for (int w0 = 0; w0 < nwords; w0 += kSelThreads) {
     const int w = w0 + tid;
-    uint32_t bits = w < nwords ? sh.touched[w] : 0u;
+    uint32_t bits = w < nwords ? sh.u.lru.touched[w] : 0u;
     int total;
     const int incl = block_incl_scan(__popc(bits), sh.wtot, total);
     int o = base + incl - __popc(bits);
@@ -393,7 +414,7 @@ __global__ __launch_bounds__(kSelThreads) void k_select(DevState d, int32_t t,
   int32_t* g_vic = d.victim + (size_t)u * K;
   int32_t* g_midx = d.miss_idx + (size_t)u * K;
   for (int k = tid; k < m; k += kSelThreads) {
-    const int32_t v = sh.vic[k], p = sh.mpos[k];
+    const int32_t v = sh.u.lru.vic[k], p = sh.mpos[k];
     const int32_t old = slot2pos[v];
     if (old >= 0) {
       pos2slot[old] = -1;
@@ -402,10 +423,10 @@ __global__ __launch_bounds__(kSelThreads) void k_select(DevState d, int32_t t,
     pos2slot[p] = v;
     slot2pos[v] = p;
     last_use[v] = t;
-    sh.sel[sh.midx[k]] = -(v + 1);
+    sh.sel[sh.u.lru.midx[k]] = -(v + 1);
     g_miss[k] = p;
     g_vic[k] = v;
-    g_midx[k] = sh.midx[k];
+    g_midx[k] = sh.u.lru.midx[k];
     if (tr) {
       tr[HC_TRACE_HEADER + K + k] = p;
       tr[HC_TRACE_HEADER + 2 * K + k] = v;
