@@ -112,6 +112,9 @@ def main():
     ap.add_argument("--workload", default="model78_50k")
     ap.add_argument("--cpu-steps", type=int, default=8)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run a plain 256 MiB device-to-device copy (reference for "
+                         "scaling rocprofv3 FETCH_SIZE / WRITE_SIZE readings)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -263,6 +266,13 @@ def main():
     }
     cache.close()
     del d_scores, trace, out, sel
+    if args.calibrate_copy:
+        a = torch.ones(256 << 20, dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
     if not args.no_cpu_baseline:
         log("cpu baseline: oracle on the first %d steps ..." % args.cpu_steps)
         result["cpu_baseline"] = run_cpu_baseline(wl, rows, args.cpu_steps)
