@@ -236,8 +236,7 @@ def main():
     kernels = {
         "gather": ("k_gather.hip", "hbm", gather_bytes, HBM_PEAK_GBS, "gather"),
         "fetch": ("k_gather.hip", "pcie", fetch_bytes, PCIE_PEAK_GBS, "gather"),
-        "topk_hist": ("k_topk.hip", "hbm", scan_bytes, HBM_PEAK_GBS, "topk_hist"),
-        "topk_filter": ("k_topk.hip", "hbm", scan_bytes, HBM_PEAK_GBS, "topk_filter"),
+        "topk_scan": ("k_topk.hip", "hbm", scan_bytes, HBM_PEAK_GBS, "topk_scan"),
         "select": ("k_select.hip", "hbm", U * (wl.cache_slots * 8 + K * 16), HBM_PEAK_GBS,
                    "select"),
     }

@@ -24,7 +24,7 @@ namespace {
 constexpr uint64_t kAlign = 256;
 
 struct Layout {
-  uint64_t pos2slot, slot2pos, last_use, order, hist, cnt, above, cand, sel_slot, miss_pos,
+  uint64_t pos2slot, slot2pos, last_use, order, cnt, above, cand, sel_slot, miss_pos,
       victim, miss_idx, host_tab, hot, total;
 };
 
@@ -60,7 +60,6 @@ Layout layout_of(const hc_config* c) {
   lo.slot2pos = take(U * C * 4);
   lo.last_use = take(U * C * 4);
   lo.order = take(U * 2 * C * 4);
-  lo.hist = take(U * kBins1 * 4);
   lo.cnt = take(U * kCnt * 4);
   lo.above = take(U * K * 4);
   lo.cand = take(U * hcap * 8);
@@ -100,8 +99,7 @@ __global__ void k_init(DevState d, int64_t n_pos, int64_t n_slots) {
   }
   const int64_t units = (int64_t)d.S * d.G;
   for (int64_t i = i0; i < units * d.K; i += stride) d.sel_slot[i] = 0;
-  for (int64_t i = i0; i < units * kBins1; i += stride) d.hist[i] = 0;
-  for (int64_t i = i0; i < units * kCnt; i += stride) d.cnt[i] = 0;
+  for (int64_t i = i0; i < units * kCnt; i += stride) d.cnt[i] = (i % kCnt) == kCntBin1 ? -1 : 0;
 }
 
 }  // namespace
@@ -210,7 +208,6 @@ hc_status hc_create(const hc_config* cfg, void* dev_workspace, uint64_t ws_bytes
   d.slot2pos = reinterpret_cast<int32_t*>(w + lo.slot2pos);
   d.last_use = reinterpret_cast<int32_t*>(w + lo.last_use);
   d.order = reinterpret_cast<int32_t*>(w + lo.order);
-  d.hist = reinterpret_cast<uint32_t*>(w + lo.hist);
   d.cnt = reinterpret_cast<int32_t*>(w + lo.cnt);
   d.above = reinterpret_cast<int32_t*>(w + lo.above);
   d.cand = reinterpret_cast<uint2*>(w + lo.cand);
@@ -274,15 +271,12 @@ hc_status hc_step(hc_ctx* c, void* stream, const float* d_scores, uint64_t score
   auto mark = [&](int i) { return prof ? hipEventRecord(ev[i], st) : hipSuccess; };
 
   hipError_t e = mark(0);
-  if (e == hipSuccess) e = launch_topk_hist(c->dev, a, d_scores, score_stride, n_chunks, vec4, st);
+  if (e == hipSuccess) e = launch_topk_scan(c->dev, a, d_scores, score_stride, n_chunks, vec4, st);
   if (e == hipSuccess) e = mark(1);
-  if (e == hipSuccess)
-    e = launch_topk_filter(c->dev, a, d_scores, score_stride, n_chunks, vec4, st);
+  if (e == hipSuccess) e = launch_select(c->dev, a, d_scores, score_stride, d_sel, d_trace, st);
   if (e == hipSuccess) e = mark(2);
-  if (e == hipSuccess) e = launch_select(c->dev, a.t, d_sel, d_trace, st);
-  if (e == hipSuccess) e = mark(3);
   if (e == hipSuccess) e = launch_gather(c->dev, d_out, st);
-  if (e == hipSuccess) e = mark(4);
+  if (e == hipSuccess) e = mark(3);
   if (e == hipSuccess) e = hipEventRecord(c->done, st);
   c->enqueued = true;
   if (e != hipSuccess) return fail_hip(c);

@@ -19,6 +19,7 @@ constexpr int kScanChunk = 8192;          // scores per workgroup in the scan ke
 constexpr int kMaxUnits = HC_MAX_UNITS;   // S * G: the per-unit miss prefix lives in LDS
 
 // Per-unit counters (int32 each): unit u owns cnt[u * kCnt .. +kCnt).
+// kCntBin1 is the cut bin of the unit's previous step (-1 before the first).
 enum { kCntAbove = 0, kCntCand = 1, kCntMiss = 2, kCntBin1 = 3, kCnt = 4 };
 
 // Device view of the caller's workspace.  Unit u = s * G + g; layer index
@@ -30,7 +31,6 @@ struct DevState {
   int32_t* slot2pos;   // [U][C]     position held by a slot, -1 if empty
   int32_t* last_use;   // [U][C]     step of the slot's last use, -1 if never
   int32_t* order;      // [U][2][C]  slots in ascending (last_use, slot); ping-pong by step parity
-  uint32_t* hist;      // [U][kBins1] top-digit histogram of the current step (zero between steps)
   int32_t* cnt;        // [U][kCnt]
   int32_t* above;      // [U][K]     positions whose top digit beats the cut bin
   uint2* cand;         // [U][hcap]  (key, position) of scores in the cut bin
@@ -56,14 +56,25 @@ __device__ __forceinline__ uint32_t order_key(float f) {
   return b ^ ((uint32_t)((int32_t)b >> 31) | 0x80000000u);
 }
 
+// Cut window of a unit's score scan: the previous step's cut bin +- 1, or every
+// bin when there is none yet (prev < 0).  The scan and the select kernel must
+// agree on it exactly.
+__device__ __forceinline__ void cut_window(int prev, uint32_t& lo, uint32_t& hi) {
+  if (prev < 0) {
+    lo = 0;
+    hi = kBins1 - 1;
+  } else {
+    lo = prev > 0 ? (uint32_t)(prev - 1) : 0u;
+    hi = prev < kBins1 - 1 ? (uint32_t)(prev + 1) : (uint32_t)(kBins1 - 1);
+  }
+}
+
 // Launchers (each defined next to its kernel).  All return hipGetLastError().
 hipError_t launch_init(const DevState& d, hipStream_t st);
-hipError_t launch_topk_hist(const DevState& d, const StepArgs& a, const float* scores,
+hipError_t launch_topk_scan(const DevState& d, const StepArgs& a, const float* scores,
                             uint64_t stride, int n_chunks, bool vec4, hipStream_t st);
-hipError_t launch_topk_filter(const DevState& d, const StepArgs& a, const float* scores,
-                              uint64_t stride, int n_chunks, bool vec4, hipStream_t st);
-hipError_t launch_select(const DevState& d, int32_t t, int32_t* d_sel, int32_t* d_trace,
-                         hipStream_t st);
+hipError_t launch_select(const DevState& d, const StepArgs& a, const float* scores,
+                         uint64_t stride, int32_t* d_sel, int32_t* d_trace, hipStream_t st);
 hipError_t launch_gather(const DevState& d, uint16_t* d_out, hipStream_t st);
 
 }  // namespace hc

@@ -39,7 +39,7 @@ constexpr int kWinWords = HC_MAX_SLOTS / 32;   // bitmap words per position wind
 constexpr int kWinPositions = kWinWords * 32;  // 262,144 positions per window
 
 struct SelShared {
-  uint32_t hist[2048];
+  uint32_t hist[kBins1];          // histograms of up to 4,096 bins
   int32_t sel[HC_MAX_TOPK];     // winners by ascending position, then the slot of each
   int32_t mpos[HC_MAX_TOPK];    // winners unordered (phase 2), then missing positions
   union {
@@ -138,41 +138,97 @@ __device__ __forceinline__ void clear_hist(SelShared& sh, int nb) {
   __syncthreads();
 }
 
-// Miss count of the step, and a clean histogram and list counters for the
-// next step's scan.
-__device__ __forceinline__ void reset_scan_state(const DevState& d, int u, int m) {
-  uint32_t* gh = d.hist + (size_t)u * kBins1;
-  for (int b = threadIdx.x; b < kBins1; b += kSelThreads) gh[b] = 0;
+// Miss count of the step, cleared list counters and the cut bin for the next
+// step's scan.
+__device__ __forceinline__ void reset_scan_state(const DevState& d, int u, int m, int cut_bin) {
   if (threadIdx.x == 0) {
     d.cnt[u * kCnt + kCntAbove] = 0;
     d.cnt[u * kCnt + kCntCand] = 0;
     d.cnt[u * kCnt + kCntMiss] = m;
+    d.cnt[u * kCnt + kCntBin1] = cut_bin;  // centre of the next step's cut window
   }
 }
 
-__global__ __launch_bounds__(kSelThreads) void k_select(DevState d, int32_t t,
+__global__ __launch_bounds__(kSelThreads) void k_select(DevState d, StepArgs a,
+                                                        const float* __restrict__ scores,
+                                                        uint64_t stride,
                                                         int32_t* __restrict__ d_sel,
                                                         int32_t* __restrict__ d_trace) {
   __shared__ SelShared sh;
   const int u = blockIdx.x, tid = threadIdx.x;
   const int K = d.K, C = d.C;
+  const int32_t t = a.t;
   int32_t* cnt = d.cnt + u * kCnt;
-  const int n_above = min(cnt[kCntAbove], K - 1);          // < K by construction
-  const int n_cand = (int)min((int64_t)cnt[kCntCand], d.hcap);
-  const uint32_t b1 = (uint32_t)cnt[kCntBin1];
-  const uint2* gcand = d.cand + (size_t)u * d.hcap;
-  int r = K - n_above;  // winners still to take from the cut bin, >= 1
+  int32_t* above_g = d.above + (size_t)u * K;
+  uint2* gcand = d.cand + (size_t)u * d.hcap;
 
-  // ---- 1. exact cut key T and position cut among keys equal to T ----------
-  // The first pass also copies the candidates into LDS when they fit.
+  // ---- 0. the cut bin b1: the 12-bit bin holding the K-th key ---------------
+  uint32_t b_lo, b_hi;
+  cut_window(cnt[kCntBin1], b_lo, b_hi);
+  int n_above = cnt[kCntAbove];                      // keys above the window
+  int n_cand = (int)min((int64_t)cnt[kCntCand], d.hcap);
+  if (!(n_above < K && (int64_t)n_above + n_cand >= K)) {
+    // The K-th key left the predicted window: rebuild both lists from the
+    // scores — a 12-bit histogram for b1, then bins above b1 -> above, bin
+    // b1 -> cand — and use the one-bin window [b1, b1].
+    const int64_t H = a.hist_len[u / d.G];
+    const float* src = scores + (uint64_t)u * stride;
+    clear_hist(sh, kBins1);
+    for (int64_t i = tid; i < H; i += kSelThreads)
+      atomicAdd(&sh.hist[order_key(src[i]) >> (32 - kBin1Bits)], 1u);
+    __syncthreads();
+    int bt, gt;
+    find_digit(sh.hist, kBins1, K, true, sh, bt, gt);
+    if (tid == 0) sh.bcast[2] = sh.bcast[3] = 0;
+    __syncthreads();
+    const uint64_t lt = (lane_id() == 0) ? 0ull : (~0ull >> (64 - lane_id()));
+    for (int64_t i0 = 0; i0 < H; i0 += kSelThreads) {
+      const int64_t i = i0 + tid;
+      uint32_t key = 0, b = 0;
+      if (i < H) {
+        key = order_key(src[i]);
+        b = key >> (32 - kBin1Bits);
+      }
+      const bool up = i < H && b > (uint32_t)bt, eq = i < H && b == (uint32_t)bt;
+      const uint64_t bu = __ballot(up), be = __ballot(eq);
+      int ou = 0, oe = 0;
+      if (lane_id() == 0) {
+        if (bu) ou = atomicAdd(&sh.bcast[2], __popcll(bu));
+        if (be) oe = atomicAdd(&sh.bcast[3], __popcll(be));
+      }
+      ou = __shfl(ou, 0, 64) + __popcll(bu & lt);
+      oe = __shfl(oe, 0, 64) + __popcll(be & lt);
+      if (up && ou < K) above_g[ou] = (int32_t)i;
+      if (eq && oe < d.hcap) gcand[oe] = make_uint2(key, (uint32_t)i);
+    }
+    __syncthreads();
+    n_above = min(sh.bcast[2], K - 1);   // = gt < K
+    n_cand = (int)min((int64_t)sh.bcast[3], d.hcap);
+    b_lo = b_hi = (uint32_t)bt;
+    __syncthreads();
+  }
+  // Copy the candidates into LDS when they fit, counting them per window bin;
+  // the bin where the count from the top reaches K is b1.
   const bool cached = n_cand <= kCandCache;
   const uint2* cand = cached ? sh.u.cand : gcand;
-  int d2, d3, skip;
-  clear_hist(sh, 1024);
+  clear_hist(sh, kBins1);
   for (int i = tid; i < n_cand; i += kSelThreads) {
     const uint2 c = gcand[i];
     if (cached) sh.u.cand[i] = c;
-    atomicAdd(&sh.hist[(c.x >> 10) & 1023], 1u);
+    atomicAdd(&sh.hist[(c.x >> (32 - kBin1Bits)) - b_lo], 1u);
+  }
+  __syncthreads();
+  int rel, beyond;
+  find_digit(sh.hist, kBins1, K - n_above, true, sh, rel, beyond);
+  const uint32_t b1 = b_lo + (uint32_t)rel;
+  int r = K - n_above - beyond;  // winners still to take from bin b1, >= 1
+
+  // ---- 1. exact cut key T and position cut among keys equal to T ----------
+  int d2, d3, skip;
+  clear_hist(sh, 1024);
+  for (int i = tid; i < n_cand; i += kSelThreads) {
+    const uint32_t k = cand[i].x;
+    if ((k >> 20) == b1) atomicAdd(&sh.hist[(k >> 10) & 1023], 1u);
   }
   __syncthreads();
   find_digit(sh.hist, 1024, r, true, sh, d2, skip);
@@ -180,7 +236,7 @@ __global__ __launch_bounds__(kSelThreads) void k_select(DevState d, int32_t t,
   clear_hist(sh, 1024);
   for (int i = tid; i < n_cand; i += kSelThreads) {
     const uint32_t k = cand[i].x;
-    if (((k >> 10) & 1023) == (uint32_t)d2) atomicAdd(&sh.hist[k & 1023], 1u);
+    if ((k >> 10) == ((b1 << 10) | (uint32_t)d2)) atomicAdd(&sh.hist[k & 1023], 1u);
   }
   __syncthreads();
   find_digit(sh.hist, 1024, r, true, sh, d3, skip);
@@ -225,7 +281,7 @@ __global__ __launch_bounds__(kSelThreads) void k_select(DevState d, int32_t t,
     sh.wmax = 0;
   }
   __syncthreads();
-  const int32_t* above = d.above + (size_t)u * K;
+  const int32_t* above = above_g;
   int32_t pmax = 0;
   for (int i = tid; i < n_above; i += kSelThreads) {
     const int32_t p = above[i];
@@ -264,7 +320,7 @@ __global__ __launch_bounds__(kSelThreads) void k_select(DevState d, int32_t t,
       d_sel[(size_t)u * K + i] = -1;
       d.sel_slot[(size_t)u * K + i] = 0;  // the gather then only reads slot 0
     }
-    reset_scan_state(d, u, 0);
+    reset_scan_state(d, u, 0, (int)b1);
     return;
   }
   {
@@ -454,12 +510,13 @@ __global__ __launch_bounds__(kSelThreads) void k_select(DevState d, int32_t t,
     tr[3] = 0;
   }
 
-  reset_scan_state(d, u, m);
+  reset_scan_state(d, u, m, (int)b1);
 }
 
-hipError_t launch_select(const DevState& d, int32_t t, int32_t* d_sel, int32_t* d_trace,
-                         hipStream_t st) {
-  hipLaunchKernelGGL(k_select, dim3(d.S * d.G), dim3(kSelThreads), 0, st, d, t, d_sel, d_trace);
+hipError_t launch_select(const DevState& d, const StepArgs& a, const float* scores,
+                         uint64_t stride, int32_t* d_sel, int32_t* d_trace, hipStream_t st) {
+  hipLaunchKernelGGL(k_select, dim3(d.S * d.G), dim3(kSelThreads), 0, st, d, a, scores, stride,
+                     d_sel, d_trace);
   return hipGetLastError();
 }
 

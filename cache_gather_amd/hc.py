@@ -22,8 +22,8 @@ HEADER = os.path.join(ROOT, "include", "hc.h")
 ROW_BYTES = 656
 OUT_ELEMS = 576
 TRACE_HEADER = 4
-NUM_STAGES = 4
-STAGES = ("topk_hist", "topk_filter", "select", "gather")
+NUM_STAGES = 3
+STAGES = ("topk_scan", "select", "gather")
 STATUS = {0: "HC_OK", -1: "HC_E_INVAL", -2: "HC_E_NOMEM", -3: "HC_E_HIP", -4: "HC_E_STATE"}
 
 

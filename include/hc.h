@@ -72,13 +72,12 @@ extern "C" {
 #define HC_TRACE_INTS(k) (HC_TRACE_HEADER + 4 * (k))
 
 /* Kernel stages timed by hc_profile_read, in launch order. */
-#define HC_STAGE_TOPK_HIST   0  /* score scan: top-12-bit key histogram     */
-#define HC_STAGE_TOPK_FILTER 1  /* score scan: bin filter and compaction    */
-#define HC_STAGE_SELECT      2  /* exact cut, lookup, miss compaction, LRU  */
-#define HC_STAGE_GATHER      3  /* hits from HBM slots, misses from host RAM
+#define HC_STAGE_TOPK_SCAN   0  /* score scan: key histogram + candidates   */
+#define HC_STAGE_SELECT      1  /* exact cut, lookup, miss compaction, LRU  */
+#define HC_STAGE_GATHER      2  /* hits from HBM slots, misses from host RAM
                                    (also written into their victim slots),
                                    dequantised into the bf16 buffer          */
-#define HC_NUM_STAGES        4
+#define HC_NUM_STAGES        3
 
 typedef enum {
   HC_OK      = 0,

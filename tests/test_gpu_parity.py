@@ -101,6 +101,19 @@ def test_signed_zeros_infinities_and_nans():
     _run_custom_scores(wl, mk)
 
 
+def test_cut_jumping_between_steps_rescans_exactly():
+    """Scores shifted far between steps move the cut bin outside the window
+    predicted from the previous step; the select kernel then rebuilds its
+    candidate lists from the scores.  Both paths must be exact."""
+    wl = W.Workload("jumping_cut", 2, 2, 1, 20000, 8, 2600, 1300, (1.0, 1.0), (1.0, 1.0), 11)
+
+    def mk(t, u, h):
+        rng = np.random.default_rng((t, u, 5))
+        x = rng.standard_normal(h).astype(np.float32)
+        return (x * np.float32(1 + 3 * (t % 3)) + np.float32((-1) ** t * 40.0 * t)).astype(np.float32)
+    _run_custom_scores(wl, mk)
+
+
 def test_dequant_every_int8_with_every_finite_fp16_scale():
     """Rows covering all 256 int8 values against all 63,488 finite fp16 scales,
     gathered 2,048 rows per step through hc_step."""
