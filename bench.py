@@ -98,6 +98,29 @@ def run_cpu_baseline(wl, rows, n_steps):
     }
 
 
+def copy_ceiling(torch, dev):
+    """Read+write rate (GB/s) of a plain 256 MiB device-to-device copy, median
+    of 5, each preceded by a read of an unrelated 1 GiB buffer: the copy starts
+    with neither its source nor dirty lines in the 256 MB Infinity Cache, the
+    state a gather of 1.6 GiB of slots meets."""
+    n = 256 << 20
+    a = torch.ones(n, dtype=torch.uint8, device=dev)
+    b = torch.empty_like(a)
+    flush = torch.ones(1 << 30, dtype=torch.uint8, device=dev)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ts = []
+    for _ in range(5):
+        flush.view(torch.int64).sum()
+        ev[0].record()
+        b.copy_(a)
+        ev[1].record()
+        torch.cuda.synchronize()
+        ts.append(ev[0].elapsed_time(ev[1]))
+    ms = sorted(ts)[2]
+    del a, b, flush
+    return round(2 * n / (ms * 1e-3) / 1e9, 1)
+
+
 def preload_kernels(hc, torch):
     """One step on a tiny throwaway context, so that loading the kernels'
     code objects is not counted in the cold step."""
@@ -201,6 +224,7 @@ def main():
             assert n_prof == args.steps
             res["stage_avg"] = {k: v / n_prof for k, v in stage_ms.items()}
             res["step_kernel_us"] = per_step.sum(axis=1) * 1e3
+            res["gather_us"] = per_step[:, list(hc.STAGES).index("gather")] * 1e3
             res["elapsed_with_events"] = elapsed
         cache.close()
         del out, sel, trace
@@ -241,6 +265,23 @@ def main():
                    "select"),
     }
 
+    # Per timed step: is the gather launch held by HBM or by PCIe?  Each step
+    # goes to the resource it drives closer to its peak.
+    g_us = kernels_pass["gather_us"]
+    hbm_frac_step = gather_bytes / (g_us * 1e-6) / 1e9 / HBM_PEAK_GBS
+    pcie_frac_step = timed_miss_rows * ROW / (g_us * 1e-6) / 1e9 / PCIE_PEAK_GBS
+    regimes = {}
+    for name, mask, frac in (("hbm_bound", hbm_frac_step >= pcie_frac_step, hbm_frac_step),
+                             ("pcie_bound", hbm_frac_step < pcie_frac_step, pcie_frac_step)):
+        if mask.any():
+            peak = HBM_PEAK_GBS if name == "hbm_bound" else PCIE_PEAK_GBS
+            nbytes = (gather_bytes * mask.sum() if name == "hbm_bound"
+                      else float(timed_miss_rows[mask].sum()) * ROW)
+            gbs = nbytes / (g_us[mask].sum() * 1e-6) / 1e9
+            regimes[name] = {"steps": int(mask.sum()),
+                             "gather_us_mean": round(float(g_us[mask].mean()), 2),
+                             "achieved_gbs": round(gbs, 2), "frac": round(gbs / peak, 4)}
+
     def roofline(stage):
         src, bound, nbytes, peak, timed_as = kernels[stage]
         ms = stage_avg[timed_as]
@@ -273,6 +314,7 @@ def main():
         "roofline_gather": roofline("gather"),
         "roofline_fetch": roofline("fetch"),
         "dominant_kernel": dominant,
+        "gather_regimes": regimes,
         "stage_us": {k: round(v * 1e3, 2) for k, v in stage_avg.items()},
         "kernel_sum_us": round(sum(stage_avg.values()) * 1e3, 2),
         "ms_per_step_with_kernel_events": round(
@@ -292,6 +334,7 @@ def main():
         "cpu_baseline": None,
     }
     del d_scores
+    result["hbm_copy_ceiling_gbs"] = copy_ceiling(torch, dev)
     if args.calibrate_copy:
         a = torch.ones(256 << 20, dtype=torch.uint8, device=dev)
         b = torch.empty_like(a)
