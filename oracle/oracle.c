@@ -128,6 +128,86 @@ void orc_dequant_table(uint16_t* table) {
       table[(size_t)(q + 128) * 65536 + s] = orc_dequant_elem((int8_t)q, (uint16_t)s);
 }
 
+/* ---------------------------------------------------------- recent ring -- */
+
+/* New rows of one (session, layer) (page "From 1M Total to 15+ × 1M Contexts:
+ * GLM-5.3 KV Cache Offloading", data-flow figure of "Decision three" and
+ * section "GPU cache management has hazards too"): a row appended on the GPU
+ * first lives in a recent ring that holds the last `rows` appended rows; it
+ * reaches host RAM only through a batched copyback.  Here the ring copies
+ * every complete batch of `batch` rows not yet in host RAM as soon as the
+ * batch is complete, and a flush copies whatever is left (section "Capacity
+ * optimization must survive the session lifecycle"). */
+struct orc_ring {
+  int32_t rows, batch;
+  int64_t first;     /* first appended position, -1 before the first append */
+  int64_t end;       /* one past the last appended position                */
+  int64_t copied;    /* appended rows [first, copied) are in host RAM      */
+  int64_t* pos;      /* ring entry -> position it holds, -1 if none        */
+  uint8_t* data;     /* ring entry -> row bytes                            */
+};
+
+orc_ring* orc_ring_new(int32_t rows, int32_t batch) {
+  if (rows < 1 || batch < 1 || batch > rows) return NULL;
+  orc_ring* r = (orc_ring*)calloc(1, sizeof *r);
+  if (!r) return NULL;
+  r->rows = rows;
+  r->batch = batch;
+  r->first = r->end = r->copied = -1;
+  r->pos = (int64_t*)malloc((size_t)rows * sizeof(int64_t));
+  r->data = (uint8_t*)calloc((size_t)rows, ORC_ROW_BYTES);
+  if (!r->pos || !r->data) {
+    orc_ring_free(r);
+    return NULL;
+  }
+  for (int32_t i = 0; i < rows; ++i) r->pos[i] = -1;
+  return r;
+}
+
+void orc_ring_free(orc_ring* r) {
+  if (!r) return;
+  free(r->pos);
+  free(r->data);
+  free(r);
+}
+
+/* Copies the appended rows not yet in host RAM out of the ring. */
+static void ring_copy_back(orc_ring* r, uint8_t* host_rows) {
+  for (int64_t p = r->copied; p < r->end; ++p) {
+    const int32_t e = (int32_t)(p % r->rows);
+    memcpy(host_rows + (size_t)p * ORC_ROW_BYTES, r->data + (size_t)e * ORC_ROW_BYTES,
+           ORC_ROW_BYTES);
+  }
+  r->copied = r->end;
+}
+
+int orc_ring_append(orc_ring* r, int64_t p, const uint8_t* row, uint8_t* host_rows) {
+  if (p < 0 || (r->first >= 0 && p != r->end)) return -1;
+  if (r->first < 0) r->first = r->end = r->copied = p;
+  const int32_t e = (int32_t)(p % r->rows);
+  /* the entry's previous row must already be in host RAM */
+  if (r->pos[e] >= 0 && r->pos[e] >= r->copied) return -1;
+  memcpy(r->data + (size_t)e * ORC_ROW_BYTES, row, ORC_ROW_BYTES);
+  r->pos[e] = p;
+  r->end = p + 1;
+  if (r->end - r->copied >= r->batch) ring_copy_back(r, host_rows);
+  return 0;
+}
+
+int64_t orc_ring_flush(orc_ring* r, uint8_t* host_rows) {
+  if (r->first < 0) return 0;
+  ring_copy_back(r, host_rows);
+  return r->copied;
+}
+
+const uint8_t* orc_ring_row(const orc_ring* r, int64_t p) {
+  if (!r || p < 0) return NULL;
+  const int32_t e = (int32_t)(p % r->rows);
+  return r->pos[e] == p ? r->data + (size_t)e * ORC_ROW_BYTES : NULL;
+}
+
+int64_t orc_ring_copied(const orc_ring* r) { return r->first < 0 ? 0 : r->copied; }
+
 /* ------------------------------------------------------------ LRU cache -- */
 
 struct orc_cache {
@@ -178,13 +258,17 @@ static int32_t lru_victim(const orc_cache* c, int32_t t) {
 }
 
 int orc_cache_step(orc_cache* c, int32_t t, const int32_t* sel, int32_t K,
-                   const uint8_t* host_rows, orc_step_info* info) {
+                   const uint8_t* host_rows, const orc_ring* ring, orc_step_info* info) {
   if (K < 1 || K > c->C) return -1;
   for (int32_t i = 0; i < K; ++i)
     if (sel[i] < 0 || sel[i] >= c->hcap) return -1;
-  int32_t n_hit = 0, n_miss = 0, n_evict = 0;
+  int32_t n_hit = 0, n_miss = 0, n_evict = 0, n_ring = 0;
+  /* Rows still in the recent ring are read from there and leave the cache
+   * alone. */
+  for (int32_t i = 0; i < K; ++i) n_ring += orc_ring_row(ring, sel[i]) != NULL;
   /* Hits: a selected position already resident is used in step t. */
   for (int32_t i = 0; i < K; ++i) {
+    if (orc_ring_row(ring, sel[i])) continue;
     int32_t s = c->slot_of[sel[i]];
     if (s >= 0) {
       c->last[s] = t;
@@ -194,7 +278,7 @@ int orc_cache_step(orc_cache* c, int32_t t, const int32_t* sel, int32_t K,
   /* Misses, one at a time in selection order. */
   for (int32_t i = 0; i < K; ++i) {
     int32_t p = sel[i];
-    if (c->slot_of[p] >= 0) continue;
+    if (orc_ring_row(ring, p) || c->slot_of[p] >= 0) continue;
     int32_t v = lru_victim(c, t);
     if (v < 0) return -1;
     int32_t old = c->pos_of[v];
@@ -215,19 +299,28 @@ int orc_cache_step(orc_cache* c, int32_t t, const int32_t* sel, int32_t K,
     ++n_miss;
   }
   if (info) {
-    for (int32_t i = 0; i < K; ++i) info->slot[i] = c->slot_of[sel[i]];
+    for (int32_t i = 0; i < K; ++i)
+      info->slot[i] = orc_ring_row(ring, sel[i]) ? c->C + (int32_t)(sel[i] % ring->rows)
+                                                 : c->slot_of[sel[i]];
     for (int32_t j = n_miss; j < K; ++j)
       info->miss_pos[j] = info->victim[j] = info->evicted[j] = -1;
     info->n_hit = n_hit;
     info->n_miss = n_miss;
     info->n_evict = n_evict;
+    info->n_ring = n_ring;
   }
   return 0;
 }
 
-int orc_gather(const orc_cache* c, const int32_t* sel, int32_t K, uint16_t* out) {
+int orc_gather(const orc_cache* c, const orc_ring* ring, const int32_t* sel, int32_t K,
+               uint16_t* out) {
   for (int32_t i = 0; i < K; ++i) {
     if (sel[i] < 0 || sel[i] >= c->hcap) return -1;
+    const uint8_t* rrow = orc_ring_row(ring, sel[i]);
+    if (rrow) {
+      orc_dequant_row(rrow, out + (size_t)i * ORC_OUT_ELEMS);
+      continue;
+    }
     int32_t s = c->slot_of[sel[i]];
     if (s < 0) return -1;
     orc_dequant_row(c->hot + (size_t)s * ORC_ROW_BYTES, out + (size_t)i * ORC_OUT_ELEMS);
@@ -245,6 +338,7 @@ const uint8_t* orc_cache_hot(const orc_cache* c) { return c->hot; }
 typedef struct {
   orc_cache* const* caches;
   const uint8_t* const* host_rows;
+  orc_ring* const* rings;
   int32_t S, L, R, K, G, t;
   const float* const* scores;
   const int64_t* hist_len;
@@ -264,9 +358,10 @@ static int run_unit(model_job* j, int32_t u) {
   for (int32_t l = g * j->R; l < l_end; ++l) {
     size_t sl = (size_t)s * j->L + l;
     orc_step_info* info = j->infos ? &j->infos[sl] : NULL;
-    if (orc_cache_step(j->caches[sl], j->t, sel, j->K, j->host_rows[sl], info)) return -1;
-    if (j->out &&
-        orc_gather(j->caches[sl], sel, j->K, j->out + sl * (size_t)j->K * ORC_OUT_ELEMS))
+    const orc_ring* ring = j->rings ? j->rings[sl] : NULL;
+    if (orc_cache_step(j->caches[sl], j->t, sel, j->K, j->host_rows[sl], ring, info)) return -1;
+    if (j->out && orc_gather(j->caches[sl], ring, sel, j->K,
+                             j->out + sl * (size_t)j->K * ORC_OUT_ELEMS))
       return -1;
   }
   return 0;
@@ -289,6 +384,7 @@ static void* model_worker(void* arg) {
 }
 
 int orc_model_step(orc_cache* const* caches, const uint8_t* const* host_rows,
+                   orc_ring* const* rings,
                    int32_t S, int32_t L, int32_t R, int32_t K, int32_t t,
                    const float* const* scores, const int64_t* hist_len,
                    int32_t* sel_out, uint16_t* out, orc_step_info* infos,
@@ -297,6 +393,7 @@ int orc_model_step(orc_cache* const* caches, const uint8_t* const* host_rows,
   model_job j;
   j.caches = caches;
   j.host_rows = host_rows;
+  j.rings = rings;
   j.S = S, j.L = L, j.R = R, j.K = K, j.G = (L + R - 1) / R, j.t = t;
   j.scores = scores;
   j.hist_len = hist_len;

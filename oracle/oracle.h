@@ -42,30 +42,62 @@ void orc_dequant_row(const uint8_t* row, uint16_t* out);
  * patterns (non-finite scales included; NaN results are 0x7FC0 | sign). */
 void orc_dequant_table(uint16_t* table);
 
+/* Recent ring of one (session, layer): rows appended by decode steps live
+ * here until a batched copyback writes them to host RAM.  It holds the last
+ * `rows` appended rows; after an append, once `batch` appended rows are not
+ * yet in host RAM, all of them are copied (batch <= rows, so a ring entry is
+ * in host RAM before it is reused). */
+typedef struct orc_ring orc_ring;
+
+orc_ring* orc_ring_new(int32_t rows, int32_t batch);
+void      orc_ring_free(orc_ring* r);
+
+/* Appends the row of position p: the first append fixes the ring's first
+ * position, later ones must continue it (p = previous p + 1).  host_rows is
+ * the (session, layer)'s host row store, written by copybacks.  Returns 0, or
+ * -1 for an out-of-order position. */
+int orc_ring_append(orc_ring* r, int64_t p, const uint8_t* row, uint8_t* host_rows);
+
+/* Copies every appended row not yet in host RAM; returns the host row
+ * frontier (one past the last appended row in host RAM; 0 if none). */
+int64_t orc_ring_flush(orc_ring* r, uint8_t* host_rows);
+
+/* The ring's row of position p, or NULL if the ring does not hold p (r may
+ * be NULL: no ring). */
+const uint8_t* orc_ring_row(const orc_ring* r, int64_t p);
+
+/* Host row frontier without copying (0 before the first append). */
+int64_t orc_ring_copied(const orc_ring* r);
+
 /* LRU hot cache of one (session, layer). */
 typedef struct orc_cache orc_cache;
 
 typedef struct orc_step_info {
   int32_t n_hit, n_miss, n_evict;
-  int32_t* slot;       /* [K]: slot of sel[i] after the step                 */
+  int32_t* slot;       /* [K]: slot of sel[i] after the step; C + (p % ring
+                          rows) for a row read from the recent ring         */
   int32_t* miss_pos;   /* [K]: misses in processing order (ascending pos)    */
   int32_t* victim;     /* [K]: slot given to miss i                          */
   int32_t* evicted;    /* [K]: position evicted from that slot, -1 if empty  */
+  int32_t n_ring;      /* selected rows read from the recent ring           */
 } orc_step_info;
 
 orc_cache* orc_cache_new(int32_t C, int64_t hcap);
 void       orc_cache_free(orc_cache* c);
 
 /* Step t for a selection sel[0..K) (distinct positions < hcap, ascending):
- * hits first (last = t), then each miss in order takes the slot minimising
- * (last, slot) among slots with last != t, evicting its position, and copies
- * the 656-B host row into the slot.  info may be NULL.  Returns 0 or -1. */
+ * positions the ring holds are left out; of the rest, hits first (last = t),
+ * then each miss in order takes the slot minimising (last, slot) among slots
+ * with last != t, evicting its position, and copies the 656-B host row into
+ * the slot.  ring and info may be NULL.  Returns 0 or -1. */
 int orc_cache_step(orc_cache* c, int32_t t, const int32_t* sel, int32_t K,
-                   const uint8_t* host_rows, orc_step_info* info);
+                   const uint8_t* host_rows, const orc_ring* ring, orc_step_info* info);
 
-/* Reads every selected row from its hot slot and dequantises it:
- * out[i][0..576).  Returns -1 if a selected position is not resident. */
-int orc_gather(const orc_cache* c, const int32_t* sel, int32_t K, uint16_t* out);
+/* Reads every selected row from the ring if it holds it, else from its hot
+ * slot, and dequantises it: out[i][0..576).  Returns -1 if a selected
+ * position is in neither. */
+int orc_gather(const orc_cache* c, const orc_ring* ring, const int32_t* sel, int32_t K,
+               uint16_t* out);
 
 /* State views (read-only, owned by the cache). */
 const int32_t* orc_cache_slot_of(const orc_cache* c);  /* [hcap] pos -> slot  */
@@ -75,11 +107,12 @@ const uint8_t* orc_cache_hot(const orc_cache* c);      /* [C][656] slot bytes */
 
 /* Whole decode step for S sessions x L layers with a selection per group of R
  * layers (G = ceil(L/R)), units processed on up to nthreads threads.
- *   caches[s*L + l], host_rows[s*L + l]
+ *   caches[s*L + l], host_rows[s*L + l], rings[s*L + l] (rings may be NULL)
  *   scores[s*G + g] -> that unit's fp32 scores, hist_len[s]
  *   sel_out [S*G*K], out [S*L*K*576] (NULL: skip the gather),
  *   infos[s*L + l] (NULL: none).  Returns 0, or the first failing unit's -1. */
 int orc_model_step(orc_cache* const* caches, const uint8_t* const* host_rows,
+                   orc_ring* const* rings,
                    int32_t S, int32_t L, int32_t R, int32_t K, int32_t t,
                    const float* const* scores, const int64_t* hist_len,
                    int32_t* sel_out, uint16_t* out, orc_step_info* infos,
