@@ -140,6 +140,11 @@ def main():
     ap.add_argument("--workload", default="model78_50k")
     ap.add_argument("--cpu-steps", type=int, default=8)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--ring", type=int, default=0, metavar="ROWS",
+                    help="decode with a recent ring of ROWS rows per layer: every step first "
+                         "appends the new position's row of every layer, and batches of "
+                         "--copyback-rows rows are copied back to host RAM")
+    ap.add_argument("--copyback-rows", type=int, default=64)
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 256 MiB device-to-device copy (reference for "
                          "scaling rocprofv3 FETCH_SIZE / WRITE_SIZE readings)")
@@ -174,6 +179,18 @@ def main():
     log("host rows generated (%.1f GiB) in %.1fs" % (
         S * L * wl.hcap * ROW / 2 ** 30, time.time() - t0))
 
+    # With a ring, prefill rows [0, H0 - 1) are in host RAM and step t appends
+    # position H0 - 1 + t (the newest token) before it runs, so hist_len(t) is
+    # the same as without a ring; the appended rows wait in HBM.
+    first = wl.hist0 - 1
+    d_new = None
+    if args.ring:
+        d_new = torch.empty((total, S, L, ROW), dtype=torch.uint8, device=dev)
+        for t in range(total):
+            d_new[t].copy_(torch.from_numpy(np.stack([np.stack([rows[s][l][first + t]
+                                                                for l in range(L)])
+                                                      for s in range(S)])))
+
     stride = (wl.hcap + 3) // 4 * 4
     t0 = time.time()
     scores = W.Scores(wl)
@@ -189,14 +206,30 @@ def main():
         timed steps.  With kernel_events, HIP events bracket every kernel of the
         timed steps on the step's stream (they add a few us per kernel, so the
         pass that produces `value` runs without them)."""
-        cache = hc.HotCache(S, L, wl.layers_per_select, wl.cache_slots, K, wl.hcap, 0)
+        cache = hc.HotCache(S, L, wl.layers_per_select, wl.cache_slots, K, wl.hcap, 0,
+                            ring_rows=args.ring,
+                            copyback_rows=args.copyback_rows if args.ring else 0)
         for s in range(S):
             for l in range(L):
-                np.copyto(cache.host_rows(s, l), rows[s][l])
+                h = cache.host_rows(s, l)
+                if args.ring:
+                    h[:first] = rows[s][l][:first]
+                    h[first:] = 0
+                else:
+                    np.copyto(h, rows[s][l])
         out, sel, _ = cache.alloc_outputs()
         trace = torch.empty((total, U, hc.trace_ints(K)), dtype=torch.int32, device=dev)
+        append_ev = ([(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                      for _ in range(total)] if args.ring and kernel_events else None)
 
         def step(t):
+            if args.ring:
+                timed_append = append_ev is not None and t >= args.warmup
+                if timed_append:
+                    append_ev[t][0].record()
+                cache.append(d_new[t], [first + t] * S)
+                if timed_append:
+                    append_ev[t][1].record()
             cache.step(d_scores[t], stride, wl.hist_len(t), out, sel, trace[t])
 
         # cold step (every row misses), then the rest of the warmup
@@ -219,6 +252,14 @@ def main():
         elapsed = time.perf_counter() - t0
         res = {"elapsed": elapsed, "cold_ms": cold_ms, "cold_stage_ms": cold_stage_ms,
                "trace": trace.cpu().numpy()}
+        if args.ring:
+            f0 = time.perf_counter()
+            status, counts = cache.flush()
+            res["flush_ms"] = (time.perf_counter() - f0) * 1e3
+            res["flush_ok"] = status == 0 and all(int(c) == first + total for c in counts)
+            if append_ev is not None:
+                res["append_us"] = np.array([append_ev[t][0].elapsed_time(append_ev[t][1]) * 1e3
+                                             for t in range(args.warmup, total)])
         if kernel_events:
             stage_ms, n_prof, per_step = hc.hc_profile_read(cache.ctx, args.steps)
             assert n_prof == args.steps
@@ -333,6 +374,26 @@ def main():
             cold_stage_ms["gather"] * 1e-3) / 1e9, 2),
         "cpu_baseline": None,
     }
+    if args.ring:
+        B = args.copyback_rows
+        timed_t = np.arange(args.warmup, total)
+        copies = (timed_t + 1) % B == 0     # t + 1 rows appended after step t
+        a_us = kernels_pass["append_us"]
+        plain = float(a_us[~copies].mean()) if (~copies).any() else None
+        with_copy = float(a_us[copies].mean()) if copies.any() else None
+        batch_bytes = S * L * B * ROW
+        result["config"]["ring_rows"] = args.ring
+        result["config"]["copyback_rows"] = B
+        result["recent_ring"] = {
+            "append_us_mean": round(plain, 2) if plain is not None else None,
+            "append_with_copyback_us": round(with_copy, 2) if with_copy is not None else None,
+            "copybacks_in_timed_steps": int(copies.sum()),
+            "copyback_bytes": batch_bytes,
+            "copyback_pcie_write_gbs": (round(batch_bytes / ((with_copy - plain) * 1e-6) / 1e9, 2)
+                                        if plain is not None and with_copy is not None else None),
+            "flush_ms": round(timed["flush_ms"], 3),
+            "flush_host_count_ok": bool(timed["flush_ok"] and kernels_pass["flush_ok"]),
+        }
     del d_scores
     result["hbm_copy_ceiling_gbs"] = copy_ceiling(torch, dev)
     if args.calibrate_copy:

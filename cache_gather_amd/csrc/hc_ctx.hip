@@ -12,6 +12,8 @@
 // page "Making KV offload correct", sections "A grouped allocation is a
 // transaction" and "Response completion is not copy completion").
 #include <algorithm>
+#include <cstddef>
+#include <cstring>
 #include <new>
 #include <vector>
 
@@ -25,13 +27,37 @@ constexpr uint64_t kAlign = 256;
 
 struct Layout {
   uint64_t pos2slot, slot2pos, last_use, order, cnt, above, cand, sel_slot, miss_pos,
-      victim, miss_idx, host_tab, hot, total;
+      victim, miss_idx, host_tab, hot, ring, total;
 };
+
+// Size of hc_config before the recent-ring fields were added.
+constexpr uint32_t kConfigSizeNoRing = offsetof(hc_config, ring_rows);
+
+// A full-size copy of the caller's config (ring fields zero for the short
+// form); false if the struct size is neither form.
+bool normalize(const hc_config* in, hc_config* out) {
+  if (!in) return false;
+  if (in->struct_size == sizeof(hc_config)) {
+    *out = *in;
+    return true;
+  }
+  if (in->struct_size == kConfigSizeNoRing) {
+    *out = hc_config{};
+    std::memcpy(out, in, kConfigSizeNoRing);
+    out->struct_size = sizeof(hc_config);
+    return true;
+  }
+  return false;
+}
 
 uint64_t align_up(uint64_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 bool valid_config(const hc_config* c) {
   if (!c || c->struct_size != sizeof(hc_config)) return false;
+  if (c->ring_rows == 0 ? c->copyback_rows != 0
+                        : (c->ring_rows > HC_MAX_RING_ROWS || c->copyback_rows < 1 ||
+                           c->copyback_rows > c->ring_rows))
+    return false;
   if (c->n_sessions < 1 || c->n_sessions > (uint32_t)kMaxSessions) return false;
   if (c->n_layers < 1 || c->layers_per_select < 1) return false;
   if (c->top_k < 1 || c->top_k > HC_MAX_TOPK) return false;
@@ -69,6 +95,7 @@ Layout layout_of(const hc_config* c) {
   lo.miss_idx = take(U * K * 4);
   lo.host_tab = take(S * L * 8);
   lo.hot = take(S * L * C * kSlotStride);
+  lo.ring = take(S * L * (uint64_t)c->ring_rows * kRow);
   lo.total = align_up(off);
   return lo;
 }
@@ -120,6 +147,11 @@ struct hc_ctx {
   std::vector<uint8_t*> host_rows;   // S*L pinned buffers
   uint64_t t = 0;                    // steps issued
   std::vector<uint64_t> last_len;    // previous hist_len per session
+  // recent ring, per session: appended positions [first, end), of which
+  // [first, copied) have a copyback enqueued; first = -1 before any append
+  std::vector<int64_t> first, end, copied;
+  uint64_t* host_count = nullptr;    // pinned [S], written by the device after copybacks
+  uint64_t* host_count_dev = nullptr;
   bool poisoned = false;
   bool enqueued = false;
   hipEvent_t done = nullptr;         // recorded after every step
@@ -134,6 +166,8 @@ void free_host(hc_ctx* c) {
   for (uint8_t* p : c->host_rows)
     if (p) (void)hipHostFree(p);
   c->host_rows.clear();
+  if (c->host_count) (void)hipHostFree(c->host_count);
+  c->host_count = c->host_count_dev = nullptr;
 }
 
 void free_prof(hc_ctx* c) {
@@ -148,19 +182,43 @@ hc_status fail_hip(hc_ctx* c) {
   return HC_E_HIP;
 }
 
+// Enqueues the copyback of every session with at least `min_pending` appended
+// rows not yet in host RAM (plus the count update) and marks them copied.
+hipError_t copy_back(hc_ctx* c, hipStream_t st, int64_t min_pending) {
+  CopybackArgs a{};
+  for (uint32_t s = 0; s < c->cfg.n_sessions; ++s) {
+    const int64_t pending = c->end[s] - c->copied[s];
+    if (c->first[s] < 0 || pending == 0 || pending < min_pending) continue;
+    a.lo[s] = (uint32_t)c->copied[s];
+    a.hi[s] = (uint32_t)c->end[s];
+    a.max_rows = std::max(a.max_rows, a.hi[s] - a.lo[s]);
+  }
+  hipError_t e = launch_copyback(c->dev, a, c->host_count_dev, st);
+  if (e == hipSuccess)
+    for (uint32_t s = 0; s < c->cfg.n_sessions; ++s)
+      if (a.hi[s] > a.lo[s]) c->copied[s] = a.hi[s];
+  return e;
+}
+
 }  // namespace
 
 extern "C" {
 
-hc_status hc_workspace_bytes(const hc_config* cfg, uint64_t* bytes) {
-  if (!valid_config(cfg) || !bytes) return HC_E_INVAL;
+hc_status hc_workspace_bytes(const hc_config* cfg_in, uint64_t* bytes) {
+  hc_config full;
+  const hc_config* cfg = &full;
+  if (!normalize(cfg_in, &full) || !valid_config(cfg) || !bytes) return HC_E_INVAL;
   *bytes = layout_of(cfg).total;
   return HC_OK;
 }
 
-hc_status hc_create(const hc_config* cfg, void* dev_workspace, uint64_t ws_bytes, hc_ctx** out) {
+hc_status hc_create(const hc_config* cfg_in, void* dev_workspace, uint64_t ws_bytes,
+                    hc_ctx** out) {
   if (out) *out = nullptr;
-  if (!valid_config(cfg) || !out || !dev_workspace) return HC_E_INVAL;
+  hc_config full;
+  const hc_config* cfg = &full;
+  if (!normalize(cfg_in, &full) || !valid_config(cfg) || !out || !dev_workspace)
+    return HC_E_INVAL;
   if (reinterpret_cast<uintptr_t>(dev_workspace) % kAlign) return HC_E_INVAL;
   const Layout lo = layout_of(cfg);
   if (ws_bytes < lo.total) return HC_E_NOMEM;
@@ -175,6 +233,9 @@ hc_status hc_create(const hc_config* cfg, void* dev_workspace, uint64_t ws_bytes
   const uint32_t S = cfg->n_sessions, L = cfg->n_layers, R = cfg->layers_per_select;
   const uint32_t G = (L + R - 1) / R;
   c->last_len.assign(S, 0);
+  c->first.assign(S, -1);
+  c->end.assign(S, 0);
+  c->copied.assign(S, 0);
 
   // pinned, mapped host rows: one exact-size buffer per (session, layer)
   const uint64_t row_bytes = cfg->max_positions * (uint64_t)kRow;
@@ -191,6 +252,18 @@ hc_status hc_create(const hc_config* cfg, void* dev_workspace, uint64_t ws_bytes
     void* dp = nullptr;
     if (hipHostGetDevicePointer(&dp, p, 0) != hipSuccess || !dp) st = HC_E_HIP;
     dev_ptrs[i] = static_cast<const uint8_t*>(dp);
+  }
+  if (st == HC_OK && cfg->ring_rows) {
+    void* p = nullptr;
+    if (hipHostMalloc(&p, S * sizeof(uint64_t), hipHostMallocMapped) != hipSuccess || !p) {
+      st = HC_E_NOMEM;
+    } else {
+      c->host_count = static_cast<uint64_t*>(p);
+      std::memset(c->host_count, 0, S * sizeof(uint64_t));
+      void* dp = nullptr;
+      if (hipHostGetDevicePointer(&dp, p, 0) != hipSuccess || !dp) st = HC_E_HIP;
+      c->host_count_dev = static_cast<uint64_t*>(dp);
+    }
   }
   if (st == HC_OK && hipEventCreateWithFlags(&c->done, hipEventDisableTiming) != hipSuccess)
     st = HC_E_HIP;
@@ -217,6 +290,8 @@ hc_status hc_create(const hc_config* cfg, void* dev_workspace, uint64_t ws_bytes
   d.miss_idx = reinterpret_cast<int32_t*>(w + lo.miss_idx);
   d.host = reinterpret_cast<const uint8_t* const*>(w + lo.host_tab);
   d.hot = w + lo.hot;
+  d.ring = w + lo.ring;
+  d.ring_rows = (int32_t)cfg->ring_rows;
 
   if (st == HC_OK &&
       hipMemcpy(w + lo.host_tab, dev_ptrs.data(), dev_ptrs.size() * sizeof(void*),
@@ -249,6 +324,7 @@ hc_status hc_step(hc_ctx* c, void* stream, const float* d_scores, uint64_t score
   for (uint32_t s = 0; s < S; ++s) {
     const uint64_t h = hist_len[s];
     if (h < c->cfg.top_k || h > c->cfg.max_positions || h < c->last_len[s]) return HC_E_INVAL;
+    if (c->first[s] >= 0 && h > (uint64_t)c->end[s]) return HC_E_INVAL;  // rows not appended yet
     max_len = std::max(max_len, h);
   }
   if (score_stride < max_len) return HC_E_INVAL;
@@ -260,8 +336,13 @@ hc_status hc_step(hc_ctx* c, void* stream, const float* d_scores, uint64_t score
   hipStream_t st = static_cast<hipStream_t>(stream);
   StepArgs a;
   a.t = (int32_t)c->t;
-  for (uint32_t s = 0; s < (uint32_t)kMaxSessions; ++s)
+  for (uint32_t s = 0; s < (uint32_t)kMaxSessions; ++s) {
     a.hist_len[s] = s < S ? (uint32_t)hist_len[s] : 0u;
+    a.ring_lo[s] = kNoRing;
+    // the ring holds the session's last ring_rows appended positions
+    if (s < S && c->first[s] >= 0)
+      a.ring_lo[s] = (uint32_t)std::max(c->first[s], c->end[s] - (int64_t)c->cfg.ring_rows);
+  }
   const int n_chunks = (int)((max_len + kScanChunk - 1) / kScanChunk);
   const bool vec4 =
       (reinterpret_cast<uintptr_t>(d_scores) % 16 == 0) && (score_stride % 4 == 0);
@@ -284,6 +365,66 @@ hc_status hc_step(hc_ctx* c, void* stream, const float* d_scores, uint64_t score
   for (uint32_t s = 0; s < S; ++s) c->last_len[s] = hist_len[s];
   ++c->t;
   return HC_OK;
+}
+
+hc_status hc_append(hc_ctx* c, void* stream, const uint8_t* d_rows, const uint64_t* pos) {
+  if (!c) return HC_E_INVAL;
+  if (c->poisoned) return HC_E_STATE;
+  if (!c->cfg.ring_rows || !d_rows || !pos) return HC_E_INVAL;
+  if (reinterpret_cast<uintptr_t>(d_rows) % 16) return HC_E_INVAL;
+  const uint32_t S = c->cfg.n_sessions;
+  AppendArgs a{};
+  for (uint32_t s = 0; s < (uint32_t)kMaxSessions; ++s) a.entry[s] = kNoRing;
+  for (uint32_t s = 0; s < S; ++s) {
+    const uint64_t p = pos[s];
+    if (p == HC_NO_APPEND) continue;
+    if (p >= c->cfg.max_positions) return HC_E_INVAL;
+    if (c->first[s] < 0 ? p < c->last_len[s] : p != (uint64_t)c->end[s]) return HC_E_INVAL;
+    a.entry[s] = (uint32_t)(p % c->cfg.ring_rows);
+  }
+  DeviceGuard dg(c->cfg.device);
+  if (!dg.ok) return HC_E_INVAL;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  // the entry being overwritten left the ring copyback_rows <= ring_rows
+  // appends ago, so its copyback is already enqueued ahead of this launch
+  hipError_t e = launch_append(c->dev, a, d_rows, st);
+  c->enqueued = true;
+  if (e == hipSuccess) {
+    for (uint32_t s = 0; s < S; ++s) {
+      if (pos[s] == HC_NO_APPEND) continue;
+      if (c->first[s] < 0) c->first[s] = c->copied[s] = (int64_t)pos[s];
+      c->end[s] = (int64_t)pos[s] + 1;
+    }
+    const int64_t batch = c->cfg.copyback_rows;
+    e = copy_back(c, st, batch);
+  }
+  if (e == hipSuccess) e = hipEventRecord(c->done, st);
+  return e == hipSuccess ? HC_OK : fail_hip(c);
+}
+
+hc_status hc_flush(hc_ctx* c, void* stream, uint64_t* host_count) {
+  if (!c) return HC_E_INVAL;
+  if (c->poisoned) return HC_E_STATE;
+  DeviceGuard dg(c->cfg.device);
+  if (!dg.ok) return HC_E_INVAL;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const uint32_t S = c->cfg.n_sessions;
+  if (c->cfg.ring_rows) {
+    hipError_t e = copy_back(c, st, 1);
+    if (e == hipSuccess) e = hipEventRecord(c->done, st);
+    c->enqueued = true;
+    if (e != hipSuccess) return fail_hip(c);
+  }
+  // wait for the copy itself, not for its submission
+  if (c->enqueued && hipEventSynchronize(c->done) != hipSuccess) return fail_hip(c);
+  if (hipStreamSynchronize(st) != hipSuccess) return fail_hip(c);
+  hc_status r = HC_OK;
+  for (uint32_t s = 0; s < S; ++s) {
+    const uint64_t n = c->host_count ? reinterpret_cast<volatile uint64_t*>(c->host_count)[s] : 0;
+    if (host_count) host_count[s] = c->first[s] >= 0 ? n : 0;
+    if (c->first[s] >= 0 && n != (uint64_t)c->end[s]) r = HC_E_CONSISTENCY;
+  }
+  return r;
 }
 
 hc_status hc_export_state(hc_ctx* c, uint32_t session, uint32_t layer, int32_t* slot2pos,
@@ -376,6 +517,7 @@ const char* hc_status_str(hc_status s) {
     case HC_E_NOMEM: return "out of memory or workspace too small";
     case HC_E_HIP: return "HIP error (context poisoned)";
     case HC_E_STATE: return "context poisoned by an earlier HIP error";
+    case HC_E_CONSISTENCY: return "host row count differs from the logical row count";
   }
   return "unknown status";
 }

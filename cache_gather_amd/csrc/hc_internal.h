@@ -40,11 +40,28 @@ struct DevState {
   int32_t* miss_idx;   // [U][K]     index in the selection of miss k
   const uint8_t* const* host;  // [S*L] device-visible pointers of the pinned host rows
   uint8_t* hot;        // [S*L][C][kSlotStride], a row in the first 656 B of its slot
+  uint8_t* ring;       // [S*L][ring_rows][kRow] recent ring; position p at p % ring_rows
+  int32_t ring_rows;   // 0: no ring
 };
 
 struct StepArgs {
   int32_t t;                          // step number (last-use stamp)
   uint32_t hist_len[kMaxSessions];    // positions per session this step
+  uint32_t ring_lo[kMaxSessions];     // positions >= ring_lo[s] are read from the ring
+};
+
+constexpr uint32_t kNoRing = 0xFFFFFFFFu;  // ring_lo / append slot of a session without one
+
+// hc_append: ring entry written for each session (kNoRing: none).
+struct AppendArgs {
+  uint32_t entry[kMaxSessions];
+};
+
+// Copyback: session s copies positions [lo[s], hi[s]) (empty when equal).
+struct CopybackArgs {
+  uint32_t lo[kMaxSessions];
+  uint32_t hi[kMaxSessions];
+  uint32_t max_rows;                  // max_s hi[s] - lo[s]
 };
 
 // 16-byte vector usable with the nontemporal load/store builtins.
@@ -76,5 +93,11 @@ hipError_t launch_topk_scan(const DevState& d, const StepArgs& a, const float* s
 hipError_t launch_select(const DevState& d, const StepArgs& a, const float* scores,
                          uint64_t stride, int32_t* d_sel, int32_t* d_trace, hipStream_t st);
 hipError_t launch_gather(const DevState& d, uint16_t* d_out, hipStream_t st);
+hipError_t launch_append(const DevState& d, const AppendArgs& a, const uint8_t* d_rows,
+                         hipStream_t st);
+// Copies the rows and then writes hi[s] into host_count[s] (device pointer of
+// pinned host memory) for every session with rows to copy.
+hipError_t launch_copyback(const DevState& d, const CopybackArgs& a, uint64_t* host_count,
+                           hipStream_t st);
 
 }  // namespace hc

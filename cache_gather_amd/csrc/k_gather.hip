@@ -15,8 +15,9 @@
 //     (zero-copy), written into its victim slot, and dequantised from the same
 //     registers — so its slot is only ever read in later steps, and all PCIe
 //     reads are issued as soon as the launch starts;
-//   * the remaining workgroups stream the hit rows out of the HBM slots (rows
-//     that missed are skipped; the miss workgroups write them).
+//   * the remaining workgroups stream the hit rows out of the HBM slots, and
+//     the rows of the recent ring out of the ring (rows that missed are
+//     skipped; the miss workgroups write them).
 // The PCIe transfer of the few missing rows thus overlaps the HBM stream of
 // the many hits.
 //
@@ -210,7 +211,9 @@ __global__ __launch_bounds__(kGatherThreads) void k_gather(DevState d,
     if (i >= d.K) continue;
     const int32_t enc = slot[i];
     if (enc < 0) continue;  // missed this step: written by a miss workgroup
-    j.src[p] = hot + (size_t)enc * kSlotStride;
+    // enc >= C: a row of the recent ring (entry enc - C)
+    j.src[p] = enc < d.C ? hot + (size_t)enc * kSlotStride
+                         : d.ring + ((size_t)sl * d.ring_rows + (enc - d.C)) * kRow;
     j.dst[p] = orow + (size_t)i * out_row_bytes;
   }
   run_rows(j, item);

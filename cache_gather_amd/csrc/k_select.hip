@@ -17,13 +17,15 @@
 //  2. Emit the K winners in ascending position order: per window of 262,144
 //     positions, set one bit per winner in an LDS bitmap and read the set bits
 //     back in order with one block-wide prefix sum.
-//  3. Lookup pos2slot; hits get last_use = t and are marked in an LDS bitmap of
+//  3. Positions the recent ring holds (a suffix of the ascending selection)
+//     are read from the ring and skip the cache.  For the rest, look up
+//     pos2slot; hits get last_use = t and are marked in an LDS bitmap of
 //     touched slots; misses are compacted in ascending order by wave ballot +
 //     mbcnt prefix.
 //  4. LRU without any search: `order` holds all C slots sorted by
 //     (last_use, slot).  Dropping the hit slots keeps it sorted, so the victims
 //     are its first m entries.  The next order is the rest of the list followed
-//     by this step's K touched slots (all now last_use = t) in slot order, read
+//     by this step's touched slots (all now last_use = t) in slot order, read
 //     out of the bitmap.  One stable partition of C entries per step.
 //  5. Apply the m (miss, victim) pairs to pos2slot / slot2pos / last_use in
 //     parallel (an evicted position is never one of this step's misses).
@@ -54,6 +56,7 @@ struct SelShared {
   int32_t wtot[kWaves];
   int32_t bcast[4];
   int32_t wmax;
+  int32_t n_ring;                 // selected rows the recent ring holds
 };
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
@@ -279,6 +282,7 @@ __global__ __launch_bounds__(kSelThreads) void k_select(DevState d, StepArgs a,
   if (tid == 0) {
     sh.bcast[2] = 0;
     sh.wmax = 0;
+    sh.n_ring = 0;
   }
   __syncthreads();
   const int32_t* above = above_g;
@@ -367,26 +371,35 @@ __global__ __launch_bounds__(kSelThreads) void k_select(DevState d, StepArgs a,
   int32_t* slot2pos = d.slot2pos + (size_t)u * C;
   int32_t* last_use = d.last_use + (size_t)u * C;
   constexpr int kLookRounds = HC_MAX_TOPK / kSelThreads;
+  const uint32_t ring_lo = a.ring_lo[u / d.G];
   int32_t lp[kLookRounds], ls[kLookRounds];
 #pragma unroll
   for (int r = 0; r < kLookRounds; ++r) {   // all map reads in flight together
     const int i = r * kSelThreads + tid;
     lp[r] = i < K ? sh.sel[i] : 0;
-    ls[r] = i < K ? pos2slot[lp[r]] : 0;
+    const bool in_ring = i < K && (uint32_t)lp[r] >= ring_lo;
+    ls[r] = i < K && !in_ring ? pos2slot[lp[r]] : 0;
+    // the first ring row of the ascending selection counts the suffix
+    if (in_ring && (i == 0 || (uint32_t)sh.sel[i - 1] < ring_lo)) sh.n_ring = K - i;
   }
   __syncthreads();
+  const int n_ring = sh.n_ring;
+  const int first_ring = K - n_ring;
   int m = 0;
 #pragma unroll
   for (int r = 0; r < kLookRounds; ++r) {
     if (r * kSelThreads >= K) break;
     const int i = r * kSelThreads + tid;
     const bool valid = i < K;
-    const bool miss = valid && ls[r] < 0;
-    if (valid && !miss) {
+    const bool in_ring = valid && i >= first_ring;
+    const bool miss = valid && !in_ring && ls[r] < 0;
+    if (valid && !in_ring && !miss) {
       last_use[ls[r]] = t;
       atomicOr(&sh.u.lru.touched[ls[r] >> 5], 1u << (ls[r] & 31));
     }
-    if (valid) sh.sel[i] = ls[r];  // from here on sel[] holds slots (-1 = miss, filled below)
+    // from here on sel[] holds slots: C + ring entry for ring rows, -1 for a
+    // miss (its victim is filled in below)
+    if (valid) sh.sel[i] = in_ring ? d.C + (int32_t)((uint32_t)lp[r] % (uint32_t)d.ring_rows) : ls[r];
     int total;
     const int k = m + block_flag_rank(miss, sh.wtot, total);
     if (miss) {
@@ -444,8 +457,9 @@ __global__ __launch_bounds__(kSelThreads) void k_select(DevState d, StepArgs a,
   __syncthreads();
   for (int k = tid; k < m; k += kSelThreads) atomicOr(&sh.u.lru.touched[sh.u.lru.vic[k] >> 5], 1u << (sh.u.lru.vic[k] & 31));
   __syncthreads();
-  // this step's K slots, ascending, close the order list
-  int base = C - K;
+  // this step's K - n_ring slots (hits and victims), ascending, close the
+  // order list
+  int base = C - (K - n_ring);
   for (int w0 = 0; w0 < nwords; w0 += kSelThreads) {
     const int w = w0 + tid;
     uint32_t bits = w < nwords ? sh.u.lru.touched[w] : 0u;
@@ -504,10 +518,10 @@ __global__ __launch_bounds__(kSelThreads) void k_select(DevState d, StepArgs a,
     }
   }
   if (tr && tid == 0) {
-    tr[0] = K - m;
+    tr[0] = K - m - n_ring;
     tr[1] = m;
     tr[2] = sh.bcast[3];
-    tr[3] = 0;
+    tr[3] = n_ring;
   }
 
   reset_scan_state(d, u, m, (int)b1);

@@ -24,7 +24,9 @@ OUT_ELEMS = 576
 TRACE_HEADER = 4
 NUM_STAGES = 3
 STAGES = ("topk_scan", "select", "gather")
-STATUS = {0: "HC_OK", -1: "HC_E_INVAL", -2: "HC_E_NOMEM", -3: "HC_E_HIP", -4: "HC_E_STATE"}
+STATUS = {0: "HC_OK", -1: "HC_E_INVAL", -2: "HC_E_NOMEM", -3: "HC_E_HIP", -4: "HC_E_STATE",
+          -5: "HC_E_CONSISTENCY"}
+NO_APPEND = (1 << 64) - 1
 
 
 def trace_ints(k: int) -> int:
@@ -42,13 +44,18 @@ class hc_config(ctypes.Structure):
                 ("n_layers", ctypes.c_uint32), ("layers_per_select", ctypes.c_uint32),
                 ("cache_slots", ctypes.c_uint32), ("top_k", ctypes.c_uint32),
                 ("max_positions", ctypes.c_uint64), ("device", ctypes.c_int32),
-                ("flags", ctypes.c_uint32)]
+                ("flags", ctypes.c_uint32), ("ring_rows", ctypes.c_uint32),
+                ("copyback_rows", ctypes.c_uint32)]
+
+
+CONFIG_SIZE_NO_RING = hc_config.ring_rows.offset
 
 
 def make_config(n_sessions, n_layers, layers_per_select, cache_slots, top_k, max_positions,
-                device=0, flags=0) -> hc_config:
+                device=0, flags=0, ring_rows=0, copyback_rows=0) -> hc_config:
     return hc_config(ctypes.sizeof(hc_config), n_sessions, n_layers, layers_per_select,
-                     cache_slots, top_k, max_positions, device, flags)
+                     cache_slots, top_k, max_positions, device, flags, ring_rows,
+                     copyback_rows)
 
 
 _LIB = None
@@ -74,6 +81,10 @@ def lib():
     L.hc_step.argtypes = [_vp, _vp, _vp, ctypes.c_uint64, ctypes.POINTER(ctypes.c_uint64),
                           _vp, _vp, _vp]
     L.hc_step.restype = st
+    L.hc_append.argtypes = [_vp, _vp, _vp, ctypes.POINTER(ctypes.c_uint64)]
+    L.hc_append.restype = st
+    L.hc_flush.argtypes = [_vp, _vp, _vp]
+    L.hc_flush.restype = st
     L.hc_export_state.argtypes = [_vp, ctypes.c_uint32, ctypes.c_uint32, _vp, _vp, _vp, _vp]
     L.hc_export_state.restype = st
     L.hc_profile_enable.argtypes = [_vp, ctypes.c_uint32]
@@ -147,6 +158,23 @@ def hc_step(ctx: int, stream, d_scores, score_stride: int, hist_len, d_out, d_se
                                     _ptr(d_out), _ptr(d_sel), _ptr(d_trace)))
 
 
+def hc_append(ctx: int, stream, d_rows, pos) -> None:
+    """pos: one position per session, or NO_APPEND (None is accepted too)."""
+    p = np.array([NO_APPEND if x is None else x for x in pos], dtype=np.uint64)
+    _check("hc_append", lib().hc_append(ctx, _ptr(stream), _ptr(d_rows),
+                                        p.ctypes.data_as(ctypes.POINTER(ctypes.c_uint64))))
+
+
+def hc_flush(ctx: int, stream, n_sessions: int, check=True):
+    """Returns (status, host row count per session); raises on a failure other
+    than HC_E_CONSISTENCY unless check is False."""
+    counts = np.zeros(n_sessions, np.uint64)
+    r = lib().hc_flush(ctx, _ptr(stream), _ptr(counts))
+    if check and r not in (0, -5):
+        raise HcError("hc_flush", r)
+    return r, counts
+
+
 def hc_export_state(ctx: int, session: int, layer: int, slots: int, max_positions: int,
                     pos2slot=False, hot_rows=False):
     slot2pos = np.empty(slots, np.int32)
@@ -197,10 +225,10 @@ class HotCache:
     """
 
     def __init__(self, n_sessions, n_layers, layers_per_select, cache_slots, top_k,
-                 max_positions, device=0):
+                 max_positions, device=0, ring_rows=0, copyback_rows=0):
         import torch
         self.cfg = make_config(n_sessions, n_layers, layers_per_select, cache_slots, top_k,
-                               max_positions, device)
+                               max_positions, device, 0, ring_rows, copyback_rows)
         self.S, self.L, self.R = n_sessions, n_layers, layers_per_select
         self.G = -(-n_layers // layers_per_select)
         self.C, self.K, self.hcap = cache_slots, top_k, max_positions
@@ -217,6 +245,18 @@ class HotCache:
         import torch
         st = stream if stream is not None else torch.cuda.current_stream(self.device)
         hc_step(self.ctx, st.cuda_stream, scores, score_stride, hist_len, out, sel, trace)
+
+    def _stream(self, stream):
+        import torch
+        return (stream if stream is not None else torch.cuda.current_stream(self.device)).cuda_stream
+
+    def append(self, rows, pos, stream=None):
+        """rows: device uint8 [S, L, 656]; pos: position per session or None."""
+        hc_append(self.ctx, self._stream(stream), rows, pos)
+
+    def flush(self, stream=None):
+        """(status, host row count per session) after the consistency boundary."""
+        return hc_flush(self.ctx, self._stream(stream), self.S)
 
     def export_state(self, s, l, pos2slot=False, hot_rows=False):
         return hc_export_state(self.ctx, s, l, self.C, self.hcap, pos2slot, hot_rows)

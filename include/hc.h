@@ -29,6 +29,21 @@
  *      for j < 512, out[512 + k] = RoPE bf16 k for k < 64.
  * t is the number of earlier hc_step calls on the context (0-based).
  *
+ * Recent ring (optional, hc_config.ring_rows > 0): new rows made by decode
+ * steps enter an HBM ring and reach host RAM through a batched copyback (the
+ * page's data-flow figure of "Decision three"; "GPU cache management has
+ * hazards too": the ring protects rows that have not reached RAM yet).
+ * hc_append adds one position per session; the ring of every (session,
+ * layer) holds that session's last ring_rows appended rows.  Once
+ * copyback_rows appended rows of a session are not yet in host RAM, one
+ * launch copies all of them, for every layer, into the pinned host rows.  A
+ * selected position the ring holds — first appended <= p and
+ * p >= appended end - ring_rows — is read from the ring and is neither a hit
+ * nor a miss: it does not touch the slot map or last-use steps.  hc_flush is
+ * the consistency boundary of the page's section "Capacity optimization must
+ * survive the session lifecycle": it submits the remaining rows, waits for the
+ * copy, and checks the host row count written by the device.
+ *
  * Row format (Q8G64 MLA row, 656 B; the page's payload description): bytes
  * [0,512) int8 latent, [512,528) 8 little-endian fp16 scales (scale g covers
  * latent bytes [64g, 64g+64)), [528,656) 64 little-endian bf16 RoPE values.
@@ -59,12 +74,15 @@ extern "C" {
 #define HC_MAX_SLOTS     262144 /* largest supported cache_slots            */
 #define HC_MAX_SESSIONS  256   /* largest supported n_sessions              */
 #define HC_MAX_UNITS     4096  /* largest S * ceil(L / R) (selection units) */
+#define HC_MAX_RING_ROWS 65536 /* largest recent ring per (session, layer)  */
+#define HC_NO_APPEND     (~(uint64_t)0)  /* hc_append: this session appends nothing */
 
 /* Per-unit trace record: HC_TRACE_INTS(K) int32 values per (session, group),
  * units ordered u = s * G + g.  Layout:
  *   [0] n_hit   [1] n_miss   [2] n_evict (victims whose slot held a position)
- *   [3] reserved (0)
- *   [4 + 0K .. 4 + 1K)  slot of selected row i after the step (sel order)
+ *   [3] n_ring  (selected rows read from the recent ring)
+ *   [4 + 0K .. 4 + 1K)  slot of selected row i after the step (sel order);
+ *                       C + p % ring_rows for a row read from the ring
  *   [4 + 1K .. 4 + 2K)  miss_pos: missing positions, ascending; -1 past n_miss
  *   [4 + 2K .. 4 + 3K)  victim slot paired with miss i; -1 past n_miss
  *   [4 + 3K .. 4 + 4K)  position evicted from that slot, -1 if it was empty   */
@@ -84,11 +102,14 @@ typedef enum {
   HC_E_INVAL = -1,  /* bad argument or configuration; nothing was changed   */
   HC_E_NOMEM = -2,  /* workspace too small or host allocation failed        */
   HC_E_HIP   = -3,  /* a HIP call failed; the context is now poisoned       */
-  HC_E_STATE = -4   /* the context is poisoned; only hc_destroy is allowed  */
+  HC_E_STATE = -4,  /* the context is poisoned; only hc_destroy is allowed  */
+  HC_E_CONSISTENCY = -5  /* hc_flush: a host row count differs from the
+                            logical row count                               */
 } hc_status;
 
 typedef struct hc_config {
-  uint32_t struct_size;       /* sizeof(hc_config)                              */
+  uint32_t struct_size;       /* sizeof(hc_config); the size without the ring
+                                 fields (40) is accepted and means no ring      */
   uint32_t n_sessions;        /* S, 1 <= S <= HC_MAX_SESSIONS                   */
   uint32_t n_layers;          /* L >= 1 layers per session                      */
   uint32_t layers_per_select; /* R >= 1; S * ceil(L / R) <= HC_MAX_UNITS        */
@@ -98,6 +119,11 @@ typedef struct hc_config {
                                  K <= Hcap < 2^31                               */
   int32_t  device;            /* HIP device ordinal                             */
   uint32_t flags;             /* must be 0                                      */
+  uint32_t ring_rows;         /* recent ring rows per (session, layer); 0 = no
+                                 ring (the caller writes every host row),
+                                 else <= HC_MAX_RING_ROWS                       */
+  uint32_t copyback_rows;     /* rows per copyback batch, 1 <= copyback_rows <=
+                                 ring_rows (0 when ring_rows is 0)              */
 } hc_config;
 
 typedef struct hc_ctx hc_ctx;
@@ -118,7 +144,9 @@ hc_status hc_create(const hc_config* cfg, void* dev_workspace, uint64_t ws_bytes
 /* Host pointer to the pinned row store of (session, layer): Hcap rows of
  * HC_ROW_BYTES, row p at offset p * 656.  Owned by the library, valid until
  * hc_destroy.  The caller writes row p before the first hc_step whose
- * hist_len exceeds p and never changes it afterwards.  NULL on a bad index. */
+ * hist_len exceeds p and never changes it afterwards — except rows at or
+ * beyond the session's first hc_append position, which only the library's
+ * copyback writes.  NULL on a bad index. */
 uint8_t* hc_host_rows(hc_ctx* ctx, uint32_t session, uint32_t layer);
 
 /* One decode step, enqueued on `stream` (a hipStream_t; NULL = default stream).
@@ -127,7 +155,8 @@ uint8_t* hc_host_rows(hc_ctx* ctx, uint32_t session, uint32_t layer);
  *   score_stride elements between units, >= max_s hist_len[s].
  *   hist_len     host uint64 [S]: positions in each session's history this
  *                step; K <= hist_len[s] <= Hcap, never smaller than at the
- *                previous step.
+ *                previous step, and at most the end of the appended
+ *                positions once the session has appended.
  *   d_out        device bf16 bits [S][L][K][576], rows in selection order.
  *   d_sel        device int32 [S][G][K]: selected positions, ascending.
  *   d_trace      NULL, or device int32 [S*G][HC_TRACE_INTS(K)] (see above).
@@ -138,6 +167,29 @@ uint8_t* hc_host_rows(hc_ctx* ctx, uint32_t session, uint32_t layer);
 hc_status hc_step(hc_ctx* ctx, void* stream, const float* d_scores,
                   uint64_t score_stride, const uint64_t* hist_len,
                   uint16_t* d_out, int32_t* d_sel, int32_t* d_trace);
+
+/* Appends one position per session to the recent ring, enqueued on `stream`.
+ *   d_rows  device [S][L][656], 16-B aligned: row of position pos[s] for every
+ *           layer of session s (sessions skipped by HC_NO_APPEND are ignored).
+ *   pos     host uint64 [S]: the session's first call fixes its first appended
+ *           position (>= every hist_len it has had, < Hcap); later calls must
+ *           continue it (previous pos[s] + 1), or pass HC_NO_APPEND.
+ * When a session then has copyback_rows appended rows that are not in host
+ * RAM yet, one launch copies all such rows of all sessions and layers to the
+ * pinned host rows (GPU stores over PCIe), after which they are in host RAM
+ * for every later operation on the stream.  Asynchronous; all arguments are
+ * checked before anything is enqueued (HC_E_INVAL changes nothing); HC_E_INVAL
+ * also when the context has no ring.  d_rows may be reused once the stream
+ * has passed this call. */
+hc_status hc_append(hc_ctx* ctx, void* stream, const uint8_t* d_rows, const uint64_t* pos);
+
+/* Consistency boundary: enqueues the copyback of every appended row not yet
+ * in host RAM, waits until the stream has completed it (and everything before
+ * it), then reads the per-session host row counts the device wrote after the
+ * copies (one past the last appended position in host RAM; 0 for a session
+ * that has not appended) into host_count[S] if non-NULL.  HC_OK if every
+ * appended session's count equals its appended end, else HC_E_CONSISTENCY. */
+hc_status hc_flush(hc_ctx* ctx, void* stream, uint64_t* host_count);
 
 /* Synchronous snapshot for tests: waits for all enqueued steps, then copies
  * the state that layer `layer` of `session` sees into host buffers:

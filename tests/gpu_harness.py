@@ -84,7 +84,7 @@ class Pair:
                 info = o_inf[s * wl.n_layers + gi * wl.layers_per_select]
                 msg = "step %d unit %d" % (t, u)
                 assert tr[0] == info["n_hit"] and tr[1] == info["n_miss"], msg
-                assert tr[2] == info["n_evict"], msg
+                assert tr[2] == info["n_evict"] and tr[3] == info["n_ring"], msg
                 base = hc.TRACE_HEADER
                 np.testing.assert_array_equal(tr[base:base + K], info["slot"], err_msg=msg)
                 np.testing.assert_array_equal(tr[base + K:base + 2 * K], info["miss_pos"],
@@ -125,3 +125,104 @@ class Pair:
     def close(self):
         self.hc.close()
         self.orc.close()
+
+
+class RingPair(Pair):
+    """Both sides with a recent ring.  Prefill rows [0, H0 - 1) are written to
+    host RAM up front; step t first appends position H0 - 1 + t for every
+    layer (so hist_len(t) = H0 + t as without a ring), and those rows reach
+    host RAM only through the copybacks.  recent_boost is added to the scores
+    of appended positions so that the ring is selected from."""
+
+    def __init__(self, wl, ring_rows, copyback_rows, recent_boost=1.0, device=0, skip=None):
+        self.ring_rows, self.copyback_rows = ring_rows, copyback_rows
+        self.first = wl.hist0 - 1
+        self.recent_boost = np.float32(recent_boost)
+        self.skip = skip or (lambda t, s: False)  # session s appends nothing at step t
+        self.wl = wl
+        self.dev = torch.device("cuda", device)
+        say("ring workload", wl.name, "S=%d L=%d K=%d C=%d H0=%d steps=%d ring=%d batch=%d" % (
+            wl.n_sessions, wl.n_layers, wl.top_k, wl.cache_slots, wl.hist0, wl.steps,
+            ring_rows, copyback_rows))
+        self.stride = align4(wl.hcap)
+        self.hc = hc.HotCache(wl.n_sessions, wl.n_layers, wl.layers_per_select,
+                              wl.cache_slots, wl.top_k, wl.hcap, device,
+                              ring_rows=ring_rows, copyback_rows=copyback_rows)
+        S, L = wl.n_sessions, wl.n_layers
+        self.rows = [[W.fill_rows(wl, s, l) for l in range(L)] for s in range(S)]
+        self.orc_host = [[np.zeros_like(self.rows[s][l]) for l in range(L)] for s in range(S)]
+        for s in range(S):
+            for l in range(L):
+                h = self.hc.host_rows(s, l)
+                h[:self.first] = self.rows[s][l][:self.first]
+                h[self.first:] = 0
+                self.orc_host[s][l][:self.first] = self.rows[s][l][:self.first]
+        self.orc = oracle.Model(S, L, wl.layers_per_select, wl.top_k, wl.cache_slots, wl.hcap,
+                                self.orc_host, ring_rows=ring_rows, copyback_rows=copyback_rows)
+        self.end = [self.first] * S
+        self.scores = W.Scores(wl)
+        self.out, self.sel, self.trace = self.hc.alloc_outputs(trace=True)
+        self.d_scores = torch.empty((wl.n_units, self.stride), dtype=torch.float32,
+                                    device=self.dev)
+        self.d_new = torch.empty((S, L, 656), dtype=torch.uint8, device=self.dev)
+
+    def step(self, t, scores_np=None, hist_len=None, gather=True, nthreads=16):
+        wl = self.wl
+        S, L = wl.n_sessions, wl.n_layers
+        pos = [None if self.skip(t, s) else self.end[s] for s in range(S)]
+        new = np.zeros((S, L, 656), np.uint8)
+        for s in range(S):
+            if pos[s] is not None:
+                for l in range(L):
+                    new[s, l] = self.rows[s][l][pos[s]]
+        self.d_new.copy_(torch.from_numpy(new))
+        self.hc.append(self.d_new, pos)
+        self.orc.append(pos, new)
+        for s in range(S):
+            if pos[s] is not None:
+                self.end[s] += 1
+        if hist_len is None:
+            hist_len = np.array(self.end, np.uint64)
+        if scores_np is None:
+            scores_np = self.scores_for(t)
+            for u in range(wl.n_units):
+                scores_np[u, self.first:self.end[u // wl.n_groups]] += self.recent_boost
+        return Pair.step(self, t, scores_np, hist_len, gather, nthreads)
+
+    def compare_host(self, margin=8):
+        """Pinned host rows around the appended range equal the oracle's host
+        store: copied rows equal, rows not copied yet still zero."""
+        torch.cuda.synchronize()
+        for s in range(self.wl.n_sessions):
+            lo, hi = self.first, min(self.wl.hcap, self.end[s] + margin)
+            for l in range(self.wl.n_layers):
+                g = self.hc.host_rows(s, l)[lo:hi]
+                o = self.orc_host[s][l][lo:hi]
+                if not np.array_equal(g, o):
+                    bad = np.flatnonzero((g != o).any(axis=1))
+                    raise AssertionError("host rows differ: session %d layer %d positions %s"
+                                         % (s, l, (lo + bad[:8]).tolist()))
+
+    def flush_both(self):
+        status, counts = self.hc.flush()
+        o_counts = self.orc.flush()
+        return status, counts, o_counts
+
+    def run(self, steps=None, gather_every=1, nthreads=16, host_every=1):
+        steps = self.wl.steps if steps is None else steps
+        t0 = time.time()
+        for t in range(steps):
+            gather = gather_every and (t % gather_every == 0 or t == steps - 1)
+            g, o = self.step(t, gather=bool(gather), nthreads=nthreads)
+            self.compare(t, g, o, gather=bool(gather))
+            if host_every and t % host_every == 0:
+                self.compare_host()
+        n_ring = int(sum(self.trace.cpu().numpy()[:, 3]))
+        say("%s ring: %d steps bit-exact in %.1fs (last step read %d rows from the ring)" % (
+            self.wl.name, steps, time.time() - t0, n_ring))
+        status, counts, o_counts = self.flush_both()
+        assert status == 0, hc.STATUS.get(status)
+        np.testing.assert_array_equal(counts, o_counts)
+        np.testing.assert_array_equal(counts, self.end)
+        self.compare_host()
+        self.compare_state()

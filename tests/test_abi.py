@@ -10,6 +10,7 @@ from cache_gather_amd import hc
 def test_library_exports_every_declared_function():
     names = hc.declared_functions()
     assert set(names) >= {"hc_workspace_bytes", "hc_create", "hc_host_rows", "hc_step",
+                          "hc_append", "hc_flush",
                           "hc_export_state", "hc_profile_enable", "hc_profile_read",
                           "hc_steps_done", "hc_destroy", "hc_status_str"}
     L = hc.lib()
@@ -18,7 +19,7 @@ def test_library_exports_every_declared_function():
 
 
 def test_status_strings():
-    for code in (0, -1, -2, -3, -4):
+    for code in (0, -1, -2, -3, -4, -5):
         assert hc.hc_status_str(code)
     assert hc.hc_status_str(-99) == "unknown status"
 
@@ -38,6 +39,8 @@ def test_workspace_grows_with_the_configuration_and_holds_the_hot_rows():
     dict(n_sessions=0), dict(n_sessions=257), dict(n_layers=0), dict(layers_per_select=0),
     dict(max_positions=100, top_k=200, cache_slots=300), dict(max_positions=1 << 31),
     dict(flags=1), dict(cache_slots=262145),
+    dict(ring_rows=64, copyback_rows=0), dict(ring_rows=64, copyback_rows=65),
+    dict(ring_rows=0, copyback_rows=8), dict(ring_rows=65537, copyback_rows=64),
 ])
 def test_invalid_configurations_are_rejected(bad):
     kw = dict(n_sessions=1, n_layers=2, layers_per_select=1, cache_slots=1024, top_k=256,
@@ -47,6 +50,22 @@ def test_invalid_configurations_are_rejected(bad):
     with pytest.raises(hc.HcError) as e:
         hc.hc_workspace_bytes(cfg)
     assert e.value.status == -1
+
+
+def test_ring_adds_its_rows_to_the_workspace():
+    base = hc.hc_workspace_bytes(hc.make_config(2, 78, 4, 32768, 2048, 51047))
+    ring = hc.hc_workspace_bytes(hc.make_config(2, 78, 4, 32768, 2048, 51047,
+                                                ring_rows=128, copyback_rows=64))
+    assert ring - base == 2 * 78 * 128 * 656
+
+
+def test_config_without_the_ring_fields_is_accepted():
+    cfg = hc.make_config(1, 3, 2, 1024, 256, 5000)
+    full = hc.hc_workspace_bytes(cfg)
+    assert hc.CONFIG_SIZE_NO_RING == 40
+    cfg.struct_size = hc.CONFIG_SIZE_NO_RING
+    cfg.ring_rows, cfg.copyback_rows = 99, 7   # ignored: beyond the short struct
+    assert hc.hc_workspace_bytes(cfg) == full
 
 
 def test_bad_struct_size_is_rejected():
@@ -61,6 +80,8 @@ def test_null_handles():
     assert L.hc_destroy(None) == 0
     assert L.hc_host_rows(None, 0, 0) is None
     assert L.hc_step(None, None, None, 0, None, None, None, None) == -1
+    assert L.hc_append(None, None, None, None) == -1
+    assert L.hc_flush(None, None, None) == -1
     n = ctypes.c_uint64()
     assert L.hc_steps_done(None, ctypes.byref(n)) == -1
     cfg = hc.make_config(1, 1, 1, 1024, 256, 5000)

@@ -46,13 +46,16 @@ MUTANTS = {
     # dequant: scale group of 32 instead of 64 values
     "scale_group_of_32": ("    int g = j / 64;", "    int g = (j / 32) & 7;",
                           "test_oracle_format.py"),
-    # gather: RoPE read two bytes early
+    # ring: the copyback moves no bytes
     "ring_copyback_skips_rows": ("    memcpy(host_rows + (size_t)p * ORC_ROW_BYTES, r->data + (size_t)e * ORC_ROW_BYTES,\n           ORC_ROW_BYTES);\n",
                                  "", "test_oracle_ring.py"),
+    # ring: rows the ring holds go through the LRU cache anyway
     "ring_rows_through_cache": ("    if (orc_ring_row(ring, p) || c->slot_of[p] >= 0) continue;",
                                 "    if (c->slot_of[p] >= 0) continue;", "test_oracle_ring.py"),
+    # ring: a batch is copied one append late
     "ring_batch_off_by_one": ("if (r->end - r->copied >= r->batch)",
                               "if (r->end - r->copied > r->batch)", "test_oracle_ring.py"),
+    # gather: RoPE read two bytes early
     "rope_offset": ("out[512 + k] = (uint16_t)(row[528 + 2 * k] | (row[528 + 2 * k + 1] << 8));",
                     "out[512 + k] = (uint16_t)(row[526 + 2 * k] | (row[526 + 2 * k + 1] << 8));",
                     "test_oracle_format.py"),
