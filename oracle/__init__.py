@@ -75,7 +75,7 @@ def lib():
         L.orc_model_step.argtypes = [
             ctypes.POINTER(ctypes.c_void_p), ctypes.POINTER(_u8p), ctypes.POINTER(ctypes.c_void_p),
             ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
-            ctypes.POINTER(_f32p), ctypes.POINTER(ctypes.c_int64),
+            ctypes.c_int32, ctypes.POINTER(_f32p), ctypes.POINTER(ctypes.c_int64),
             _i32p, _u16p, ctypes.POINTER(StepInfo), ctypes.c_int32]
         L.orc_model_step.restype = ctypes.c_int
         _LIB = L
@@ -226,10 +226,11 @@ class Model:
     then be writable C-contiguous uint8 arrays: they are used in place)."""
 
     def __init__(self, n_sessions, n_layers, layers_per_select, top_k, slots, hcap, host_rows,
-                 ring_rows=0, copyback_rows=0):
+                 ring_rows=0, copyback_rows=0, queries=1):
         self.S, self.L, self.R = int(n_sessions), int(n_layers), int(layers_per_select)
         self.G = -(-self.L // self.R)
         self.K, self.C, self.hcap = int(top_k), int(slots), int(hcap)
+        self.Q = int(queries)
         self.caches = [Cache(slots, hcap) for _ in range(self.S * self.L)]
         self.rows = [np.ascontiguousarray(host_rows[s][l], dtype=np.uint8)
                      for s in range(self.S) for l in range(self.L)]
@@ -274,22 +275,26 @@ class Model:
         return out
 
     def step(self, t, scores, hist_len, gather=True, info=True, nthreads=1):
-        """scores[s*G + g]: fp32 array of at least hist_len[s] entries.
-        Returns (sel [S,G,K], out [S,L,K,576] or None, infos list or None)."""
-        units = self.S * self.G
+        """scores[(s*G + g)*Q + q]: fp32 array of at least hist_len[s] entries.
+        Returns (sel [S,G,K] or [S,G,Q,K] when Q > 1, out [S,L,K,576] or
+        [S,L,Q,K,576] or None, infos list or None); with Q > 1 the infos cover
+        the union of the group's Q selections (Q*K entries per array)."""
+        units = self.S * self.G * self.Q
         sc = [np.ascontiguousarray(x, dtype=np.float32) for x in scores]
         assert len(sc) == units
         for u, x in enumerate(sc):
-            assert x.size >= hist_len[u // self.G]
+            assert x.size >= hist_len[u // (self.G * self.Q)]
         sc_arr = (_f32p * units)(*[_ptr(x, _f32p) for x in sc])
         hl = np.ascontiguousarray(hist_len, dtype=np.int64)
-        sel = np.empty((self.S, self.G, self.K), np.int32)
-        out = np.empty((self.S, self.L, self.K, OUT_ELEMS), np.uint16) if gather else None
-        bufs = [_InfoBufs(self.K) for _ in range(self.S * self.L)] if info else None
+        QK = self.Q * self.K
+        sel = np.empty((self.S, self.G, self.Q, self.K), np.int32)
+        out = (np.empty((self.S, self.L, self.Q, self.K, OUT_ELEMS), np.uint16)
+               if gather else None)
+        bufs = [_InfoBufs(QK) for _ in range(self.S * self.L)] if info else None
         info_arr = (StepInfo * (self.S * self.L))(*[b.info for b in bufs]) if info else None
         rc = lib().orc_model_step(
-            self._cache_arr, self._rows_arr, self._ring_arr, self.S, self.L, self.R, self.K, int(t),
-            sc_arr, _ptr(hl, ctypes.POINTER(ctypes.c_int64)), _ptr(sel, _i32p),
+            self._cache_arr, self._rows_arr, self._ring_arr, self.S, self.L, self.R, self.K,
+            self.Q, int(t), sc_arr, _ptr(hl, ctypes.POINTER(ctypes.c_int64)), _ptr(sel, _i32p),
             _ptr(out, _u16p) if gather else None, info_arr, int(nthreads))
         if rc != 0:
             raise ValueError("orc_model_step failed")
@@ -300,6 +305,9 @@ class Model:
             for i, b in enumerate(bufs):
                 b.info = info_arr[i]
                 infos.append(b.result())
+        if self.Q == 1:
+            sel = sel[:, :, 0]
+            out = out[:, :, 0] if gather else None
         return sel, out, infos
 
     def close(self):

@@ -339,7 +339,7 @@ typedef struct {
   orc_cache* const* caches;
   const uint8_t* const* host_rows;
   orc_ring* const* rings;
-  int32_t S, L, R, K, G, t;
+  int32_t S, L, R, K, G, Q, t;
   const float* const* scores;
   const int64_t* hist_len;
   int32_t* sel_out;
@@ -350,21 +350,43 @@ typedef struct {
   int status;
 } model_job;
 
+/* One selection unit (session s, group g) of a round: every query's top-K,
+ * the ascending union of the Q selections, one cache step on the union for
+ * each layer of the group, then each query's rows gathered in its own order. */
 static int run_unit(model_job* j, int32_t u) {
   int32_t s = u / j->G, g = u % j->G;
-  int32_t* sel = j->sel_out + (size_t)u * j->K;
-  if (orc_topk(j->scores[u], j->hist_len[s], j->K, sel)) return -1;
+  const int32_t QK = j->Q * j->K;
+  int32_t* sel = j->sel_out + (size_t)u * QK;     /* [Q][K] */
+  for (int32_t q = 0; q < j->Q; ++q)
+    if (orc_topk(j->scores[(size_t)u * j->Q + q], j->hist_len[s], j->K, sel + (size_t)q * j->K))
+      return -1;
+  int32_t* uni = (int32_t*)malloc((size_t)QK * sizeof(int32_t));
+  if (!uni) return -1;
+  memcpy(uni, sel, (size_t)QK * sizeof(int32_t));
+  qsort(uni, (size_t)QK, sizeof(int32_t), cmp_int32);
+  int32_t n = 0;
+  for (int32_t i = 0; i < QK; ++i)
+    if (n == 0 || uni[i] != uni[n - 1]) uni[n++] = uni[i];
+  int status = 0;
   int32_t l_end = (g + 1) * j->R < j->L ? (g + 1) * j->R : j->L;
-  for (int32_t l = g * j->R; l < l_end; ++l) {
+  for (int32_t l = g * j->R; l < l_end && !status; ++l) {
     size_t sl = (size_t)s * j->L + l;
     orc_step_info* info = j->infos ? &j->infos[sl] : NULL;
     const orc_ring* ring = j->rings ? j->rings[sl] : NULL;
-    if (orc_cache_step(j->caches[sl], j->t, sel, j->K, j->host_rows[sl], ring, info)) return -1;
-    if (j->out && orc_gather(j->caches[sl], ring, sel, j->K,
-                             j->out + sl * (size_t)j->K * ORC_OUT_ELEMS))
-      return -1;
+    if (orc_cache_step(j->caches[sl], j->t, uni, n, j->host_rows[sl], ring, info)) {
+      status = -1;
+      break;
+    }
+    if (info)
+      for (int32_t i = n; i < QK; ++i)
+        info->slot[i] = info->miss_pos[i] = info->victim[i] = info->evicted[i] = -1;
+    for (int32_t q = 0; q < j->Q && j->out; ++q)
+      if (orc_gather(j->caches[sl], ring, sel + (size_t)q * j->K, j->K,
+                     j->out + (sl * j->Q + q) * (size_t)j->K * ORC_OUT_ELEMS))
+        status = -1;
   }
-  return 0;
+  free(uni);
+  return status;
 }
 
 static void* model_worker(void* arg) {
@@ -385,16 +407,16 @@ static void* model_worker(void* arg) {
 
 int orc_model_step(orc_cache* const* caches, const uint8_t* const* host_rows,
                    orc_ring* const* rings,
-                   int32_t S, int32_t L, int32_t R, int32_t K, int32_t t,
+                   int32_t S, int32_t L, int32_t R, int32_t K, int32_t Q, int32_t t,
                    const float* const* scores, const int64_t* hist_len,
                    int32_t* sel_out, uint16_t* out, orc_step_info* infos,
                    int32_t nthreads) {
-  if (S < 1 || L < 1 || R < 1 || K < 1) return -1;
+  if (S < 1 || L < 1 || R < 1 || K < 1 || Q < 1) return -1;
   model_job j;
   j.caches = caches;
   j.host_rows = host_rows;
   j.rings = rings;
-  j.S = S, j.L = L, j.R = R, j.K = K, j.G = (L + R - 1) / R, j.t = t;
+  j.S = S, j.L = L, j.R = R, j.K = K, j.G = (L + R - 1) / R, j.Q = Q, j.t = t;
   j.scores = scores;
   j.hist_len = hist_len;
   j.sel_out = sel_out;

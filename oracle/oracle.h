@@ -105,15 +105,23 @@ const int32_t* orc_cache_pos_of(const orc_cache* c);   /* [C] slot -> pos     */
 const int32_t* orc_cache_last(const orc_cache* c);     /* [C] last-use step   */
 const uint8_t* orc_cache_hot(const orc_cache* c);      /* [C][656] slot bytes */
 
-/* Whole decode step for S sessions x L layers with a selection per group of R
- * layers (G = ceil(L/R)), units processed on up to nthreads threads.
+/* Whole decode round for S sessions x L layers with a selection per group of R
+ * layers (G = ceil(L/R)) and Q query rows per round (MTP verification: the
+ * page's section "GPU cache management has hazards too"), units processed on
+ * up to nthreads threads.  Every query selects its own top-K over the same
+ * history; the cache step of each layer runs once on the ascending union of
+ * the group's Q selections (so a position several queries select is one hit,
+ * or one miss with one victim); each query's rows are gathered in its own
+ * selection order.
  *   caches[s*L + l], host_rows[s*L + l], rings[s*L + l] (rings may be NULL)
- *   scores[s*G + g] -> that unit's fp32 scores, hist_len[s]
- *   sel_out [S*G*K], out [S*L*K*576] (NULL: skip the gather),
- *   infos[s*L + l] (NULL: none).  Returns 0, or the first failing unit's -1. */
+ *   scores[(s*G + g)*Q + q] -> that query's fp32 scores, hist_len[s]
+ *   sel_out [S*G*Q*K], out [S*L*Q*K*576] (NULL: skip the gather),
+ *   infos[s*L + l] (NULL: none), each with Q*K entries per array: the union's
+ *   entries first, -1 past the union.  Returns 0, or the first failing unit's
+ *   -1. */
 int orc_model_step(orc_cache* const* caches, const uint8_t* const* host_rows,
                    orc_ring* const* rings,
-                   int32_t S, int32_t L, int32_t R, int32_t K, int32_t t,
+                   int32_t S, int32_t L, int32_t R, int32_t K, int32_t Q, int32_t t,
                    const float* const* scores, const int64_t* hist_len,
                    int32_t* sel_out, uint16_t* out, orc_step_info* infos,
                    int32_t nthreads);

@@ -55,6 +55,9 @@ MUTANTS = {
     # ring: a batch is copied one append late
     "ring_batch_off_by_one": ("if (r->end - r->copied >= r->batch)",
                               "if (r->end - r->copied > r->batch)", "test_oracle_ring.py"),
+    # multi-query round: the union keeps duplicate positions
+    "union_keeps_duplicates": ("    if (n == 0 || uni[i] != uni[n - 1]) uni[n++] = uni[i];",
+                               "    uni[n++] = uni[i];", "test_oracle_mtp.py"),
     # gather: RoPE read two bytes early
     "rope_offset": ("out[512 + k] = (uint16_t)(row[528 + 2 * k] | (row[528 + 2 * k + 1] << 8));",
                     "out[512 + k] = (uint16_t)(row[526 + 2 * k] | (row[526 + 2 * k + 1] << 8));",
