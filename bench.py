@@ -122,14 +122,19 @@ def copy_ceiling(torch, dev):
 
 
 def preload_kernels(hc, torch):
-    """One step on a tiny throwaway context, so that loading the kernels'
-    code objects is not counted in the cold step."""
-    c = hc.HotCache(1, 1, 1, 64, 8, 64, 0)
-    out, sel, _ = c.alloc_outputs()
-    sc = torch.zeros(64, dtype=torch.float32, device="cuda")
-    c.step(sc, 64, [64], out, sel)
-    torch.cuda.synchronize()
-    c.close()
+    """Steps on tiny throwaway contexts — one query, two queries, and a ring
+    append with its copyback — so that loading the kernels' code objects is
+    not counted in the cold step."""
+    for q in (1, 2):
+        c = hc.HotCache(1, 1, 1, 64, 8, 64, 0, ring_rows=2, copyback_rows=1, queries=q)
+        out, sel, _ = c.alloc_outputs()
+        sc = torch.zeros(64 * q, dtype=torch.float32, device="cuda")
+        rows = torch.zeros((1, 1, ROW), dtype=torch.uint8, device="cuda")
+        c.step(sc, 64, [63], out, sel)
+        c.append(rows, [63])
+        c.step(sc, 64, [64], out, sel)
+        torch.cuda.synchronize()
+        c.close()
 
 
 def main():
@@ -145,6 +150,9 @@ def main():
                          "appends the new position's row of every layer, and batches of "
                          "--copyback-rows rows are copied back to host RAM")
     ap.add_argument("--copyback-rows", type=int, default=64)
+    ap.add_argument("--queries", type=int, default=1, metavar="Q",
+                    help="query rows per round (MTP verification: Q = MTP depth + 1); every "
+                         "query selects its own top-K and the cache round runs on their union")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 256 MiB device-to-device copy (reference for "
                          "scaling rocprofv3 FETCH_SIZE / WRITE_SIZE readings)")
@@ -194,9 +202,10 @@ def main():
     stride = (wl.hcap + 3) // 4 * 4
     t0 = time.time()
     scores = W.Scores(wl)
-    d_scores = torch.empty((total, U, stride), dtype=torch.float32, device=dev)
+    Q = args.queries
+    d_scores = torch.empty((total, U * Q, stride), dtype=torch.float32, device=dev)
     for t in range(total):
-        d_scores[t].copy_(torch.from_numpy(scores.step(t, stride)))
+        d_scores[t].copy_(torch.from_numpy(scores.step(t, stride, queries=Q)))
     torch.cuda.synchronize()
     log("scores for %d steps resident in HBM (%.2f GiB) in %.1fs" % (
         total, d_scores.numel() * 4 / 2 ** 30, time.time() - t0))
@@ -208,7 +217,7 @@ def main():
         pass that produces `value` runs without them)."""
         cache = hc.HotCache(S, L, wl.layers_per_select, wl.cache_slots, K, wl.hcap, 0,
                             ring_rows=args.ring,
-                            copyback_rows=args.copyback_rows if args.ring else 0)
+                            copyback_rows=args.copyback_rows if args.ring else 0, queries=Q)
         for s in range(S):
             for l in range(L):
                 h = cache.host_rows(s, l)
@@ -218,7 +227,7 @@ def main():
                 else:
                     np.copyto(h, rows[s][l])
         out, sel, _ = cache.alloc_outputs()
-        trace = torch.empty((total, U, hc.trace_ints(K)), dtype=torch.int32, device=dev)
+        trace = torch.empty((total, U, hc.trace_ints(Q * K)), dtype=torch.int32, device=dev)
         append_ev = ([(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                       for _ in range(total)] if args.ring and kernel_events else None)
 
@@ -281,7 +290,7 @@ def main():
         raise SystemExit("the two passes disagree")
 
     ms_per_step = elapsed * 1e3 / args.steps
-    rows_per_step = S * L * K
+    rows_per_step = S * L * Q * K       # every query row's K rows of every layer
     value = rows_per_step / (ms_per_step / 1e3)
 
     # misses per step from the trace (n_miss of each unit x layers of its group)
@@ -350,7 +359,8 @@ def main():
         "config": {"workload": wl.name, "sessions": S, "layers": L,
                    "layers_per_select": wl.layers_per_select, "history0": wl.hist0,
                    "cache_slots": wl.cache_slots, "top_k": K,
-                   "rows_per_step": rows_per_step, "output": "bf16 [S][L][K][576]"},
+                   "rows_per_step": rows_per_step,
+                   "output": "bf16 [S][L][Q][K][576]" if Q > 1 else "bf16 [S][L][K][576]"},
         "roofline": roofline(dominant),
         "roofline_gather": roofline("gather"),
         "roofline_fetch": roofline("fetch"),
@@ -374,6 +384,10 @@ def main():
             cold_stage_ms["gather"] * 1e-3) / 1e9, 2),
         "cpu_baseline": None,
     }
+    if Q > 1:
+        result["config"]["queries"] = Q
+        # fetch bytes count one PCIe read per distinct missing position; further
+        # query rows of the same missing position read host RAM again
     if args.ring:
         B = args.copyback_rows
         timed_t = np.arange(args.warmup, total)
@@ -403,7 +417,9 @@ def main():
             b.copy_(a)
         torch.cuda.synchronize()
         del a, b
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and (Q > 1 or args.ring):
+        log("cpu baseline: timed only for the single-query step without a ring")
+    elif not args.no_cpu_baseline:
         log("cpu baseline: oracle on the first %d steps ..." % args.cpu_steps)
         result["cpu_baseline"] = run_cpu_baseline(wl, rows, args.cpu_steps)
     print(json.dumps(result), flush=True)

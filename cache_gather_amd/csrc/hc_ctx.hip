@@ -30,24 +30,22 @@ struct Layout {
       victim, miss_idx, host_tab, hot, ring, total;
 };
 
-// Size of hc_config before the recent-ring fields were added.
+// Sizes of hc_config before the recent-ring fields and before `queries` were
+// added; both are accepted (no ring, one query).
 constexpr uint32_t kConfigSizeNoRing = offsetof(hc_config, ring_rows);
+constexpr uint32_t kConfigSizeOneQuery = offsetof(hc_config, queries);
 
-// A full-size copy of the caller's config (ring fields zero for the short
-// form); false if the struct size is neither form.
+// A full-size copy of the caller's config (missing fields zero); false if the
+// struct size is none of the known forms.
 bool normalize(const hc_config* in, hc_config* out) {
   if (!in) return false;
-  if (in->struct_size == sizeof(hc_config)) {
-    *out = *in;
-    return true;
-  }
-  if (in->struct_size == kConfigSizeNoRing) {
-    *out = hc_config{};
-    std::memcpy(out, in, kConfigSizeNoRing);
-    out->struct_size = sizeof(hc_config);
-    return true;
-  }
-  return false;
+  const uint32_t n = in->struct_size;
+  if (n != sizeof(hc_config) && n != kConfigSizeNoRing && n != kConfigSizeOneQuery) return false;
+  *out = hc_config{};
+  std::memcpy(out, in, n);
+  out->struct_size = sizeof(hc_config);
+  if (out->queries == 0) out->queries = 1;
+  return true;
 }
 
 uint64_t align_up(uint64_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
@@ -61,11 +59,15 @@ bool valid_config(const hc_config* c) {
   if (c->n_sessions < 1 || c->n_sessions > (uint32_t)kMaxSessions) return false;
   if (c->n_layers < 1 || c->layers_per_select < 1) return false;
   if (c->top_k < 1 || c->top_k > HC_MAX_TOPK) return false;
-  if (c->cache_slots < c->top_k || c->cache_slots > HC_MAX_SLOTS) return false;
-  if (c->max_positions < c->top_k || c->max_positions >= (1ull << 31)) return false;
+  if (c->queries < 1 || c->queries > HC_MAX_QUERIES) return false;
+  const uint64_t qk = (uint64_t)c->queries * c->top_k;
+  if (qk > HC_MAX_ROUND_ROWS) return false;
+  if (c->cache_slots < qk || c->cache_slots > HC_MAX_SLOTS) return false;
+  // positions < 2^31 - 2^19 keep -(C + 1 + position) inside int32
+  if (c->max_positions < c->top_k || c->max_positions > (1ull << 31) - (1ull << 19)) return false;
   if (c->flags != 0) return false;
   const uint64_t layers = (uint64_t)c->n_sessions * c->n_layers;
-  if (layers > 60000) return false;  // one gather grid row per layer
+  if (layers * c->queries > 60000) return false;  // one gather grid row per layer and query
   const uint64_t G = (c->n_layers + c->layers_per_select - 1) / c->layers_per_select;
   if ((uint64_t)c->n_sessions * G > (uint64_t)kMaxUnits) return false;
   return true;
@@ -75,6 +77,7 @@ Layout layout_of(const hc_config* c) {
   const uint64_t S = c->n_sessions, L = c->n_layers;
   const uint64_t G = (L + c->layers_per_select - 1) / c->layers_per_select;
   const uint64_t U = S * G, C = c->cache_slots, K = c->top_k, hcap = c->max_positions;
+  const uint64_t Q = c->queries, SU = U * Q;  // selection units: one per query row
   Layout lo{};
   uint64_t off = 0;
   auto take = [&](uint64_t bytes) {
@@ -86,13 +89,13 @@ Layout layout_of(const hc_config* c) {
   lo.slot2pos = take(U * C * 4);
   lo.last_use = take(U * C * 4);
   lo.order = take(U * 2 * C * 4);
-  lo.cnt = take(U * kCnt * 4);
-  lo.above = take(U * K * 4);
-  lo.cand = take(U * hcap * 8);
-  lo.sel_slot = take(U * K * 4);
-  lo.miss_pos = take(U * K * 4);
-  lo.victim = take(U * K * 4);
-  lo.miss_idx = take(U * K * 4);
+  lo.cnt = take(SU * kCnt * 4);
+  lo.above = take(SU * K * 4);
+  lo.cand = take(SU * hcap * 8);
+  lo.sel_slot = take(SU * K * 4);
+  lo.miss_pos = take(SU * K * 4);
+  lo.victim = take(SU * K * 4);
+  lo.miss_idx = take(SU * K * 4);
   lo.host_tab = take(S * L * 8);
   lo.hot = take(S * L * C * kSlotStride);
   lo.ring = take(S * L * (uint64_t)c->ring_rows * kRow);
@@ -124,9 +127,10 @@ __global__ void k_init(DevState d, int64_t n_pos, int64_t n_slots) {
     d.order[(u * 2) * d.C + v] = (int32_t)v;      // step 0 reads parity 0
     d.order[(u * 2 + 1) * d.C + v] = (int32_t)v;
   }
-  const int64_t units = (int64_t)d.S * d.G;
-  for (int64_t i = i0; i < units * d.K; i += stride) d.sel_slot[i] = 0;
-  for (int64_t i = i0; i < units * kCnt; i += stride) d.cnt[i] = (i % kCnt) == kCntBin1 ? -1 : 0;
+  const int64_t sel_units = (int64_t)d.S * d.G * d.Q;
+  for (int64_t i = i0; i < sel_units * d.K; i += stride) d.sel_slot[i] = 0;
+  for (int64_t i = i0; i < sel_units * kCnt; i += stride)
+    d.cnt[i] = (i % kCnt) == kCntBin1 ? -1 : 0;
 }
 
 }  // namespace
@@ -275,6 +279,7 @@ hc_status hc_create(const hc_config* cfg_in, void* dev_workspace, uint64_t ws_by
   d.G = (int32_t)G;
   d.K = (int32_t)cfg->top_k;
   d.C = (int32_t)cfg->cache_slots;
+  d.Q = (int32_t)cfg->queries;
   d.hcap = (int64_t)cfg->max_positions;
   uint8_t* w = c->ws;
   d.pos2slot = reinterpret_cast<int32_t*>(w + lo.pos2slot);
@@ -355,6 +360,7 @@ hc_status hc_step(hc_ctx* c, void* stream, const float* d_scores, uint64_t score
   if (e == hipSuccess) e = launch_topk_scan(c->dev, a, d_scores, score_stride, n_chunks, vec4, st);
   if (e == hipSuccess) e = mark(1);
   if (e == hipSuccess) e = launch_select(c->dev, a, d_scores, score_stride, d_sel, d_trace, st);
+  if (e == hipSuccess && c->dev.Q > 1) e = launch_round(c->dev, a, d_sel, d_trace, st);
   if (e == hipSuccess) e = mark(2);
   if (e == hipSuccess) e = launch_gather(c->dev, d_out, st);
   if (e == hipSuccess) e = mark(3);

@@ -26,18 +26,21 @@ enum { kCntAbove = 0, kCntCand = 1, kCntMiss = 2, kCntBin1 = 3, kCnt = 4 };
 // sl = s * L + l.  All arrays are carved from one allocation (see hc_ctx.hip).
 struct DevState {
   int32_t S, L, R, G, K, C;
+  int32_t Q;           // query rows per round; selection unit su = u * Q + q
   int64_t hcap;
   int32_t* pos2slot;   // [U][hcap]  slot holding a position, -1 if none
   int32_t* slot2pos;   // [U][C]     position held by a slot, -1 if empty
   int32_t* last_use;   // [U][C]     step of the slot's last use, -1 if never
   int32_t* order;      // [U][2][C]  slots in ascending (last_use, slot); ping-pong by step parity
-  int32_t* cnt;        // [U][kCnt]
-  int32_t* above;      // [U][K]     positions whose top digit beats the cut bin
-  uint2* cand;         // [U][hcap]  (key, position) of scores in the cut bin
-  int32_t* sel_slot;   // [U][K]     slot of selected row i; -(slot + 1) if it missed this step
-  int32_t* miss_pos;   // [U][K]     position of miss k (ascending), k < cnt[u][kCntMiss]
-  int32_t* victim;     // [U][K]     slot that miss k fills
-  int32_t* miss_idx;   // [U][K]     index in the selection of miss k
+  int32_t* cnt;        // [U*Q][kCnt] per selection unit; the round's miss count at su = u*Q
+  int32_t* above;      // [U*Q][K]   positions whose top digit beats the cut bin
+  uint2* cand;         // [U*Q][hcap] (key, position) of scores in the cut bin
+  int32_t* sel_slot;   // [U*Q][K]   source of selected row i: slot, C + ring entry,
+                       //            -(slot + 1) if it missed and this row fills the slot,
+                       //            -(C + 1 + position) for a further row of that miss
+  int32_t* miss_pos;   // [U][Q*K]   position of miss k (ascending), k < cnt[u*Q][kCntMiss]
+  int32_t* victim;     // [U][Q*K]   slot that miss k fills
+  int32_t* miss_idx;   // [U][Q*K]   output row (q * K + i) that miss k fills
   const uint8_t* const* host;  // [S*L] device-visible pointers of the pinned host rows
   uint8_t* hot;        // [S*L][C][kSlotStride], a row in the first 656 B of its slot
   uint8_t* ring;       // [S*L][ring_rows][kRow] recent ring; position p at p % ring_rows
@@ -90,8 +93,12 @@ __device__ __forceinline__ void cut_window(int prev, uint32_t& lo, uint32_t& hi)
 hipError_t launch_init(const DevState& d, hipStream_t st);
 hipError_t launch_topk_scan(const DevState& d, const StepArgs& a, const float* scores,
                             uint64_t stride, int n_chunks, bool vec4, hipStream_t st);
+// Q == 1: the fused per-unit selection + cache kernel.  Q > 1: the top-K part
+// per selection unit, then launch_round per unit.
 hipError_t launch_select(const DevState& d, const StepArgs& a, const float* scores,
                          uint64_t stride, int32_t* d_sel, int32_t* d_trace, hipStream_t st);
+hipError_t launch_round(const DevState& d, const StepArgs& a, const int32_t* d_sel,
+                        int32_t* d_trace, hipStream_t st);
 hipError_t launch_gather(const DevState& d, uint16_t* d_out, hipStream_t st);
 hipError_t launch_append(const DevState& d, const AppendArgs& a, const uint8_t* d_rows,
                          hipStream_t st);

@@ -17,7 +17,10 @@
 //     reads are issued as soon as the launch starts;
 //   * the remaining workgroups stream the hit rows out of the HBM slots, and
 //     the rows of the recent ring out of the ring (rows that missed are
-//     skipped; the miss workgroups write them).
+//     skipped; the miss workgroups write them).  In a multi-query round a
+//     position several queries missed is filled by its first query's row; the
+//     other queries' rows of it read host RAM directly (the page's rule for
+//     duplicate misses), never the slot being filled.
 // The PCIe transfer of the few missing rows thus overlaps the HBM stream of
 // the many hits.
 //
@@ -32,7 +35,8 @@
 // keeping several rows per thread in flight streams slower).  Grid rows
 // [0, miss_rows) are the miss workgroups, dispatched first; grid row
 // miss_rows + sl holds layer sl's hit rows, so no per-row index division is
-// needed.  HBM-bound: 656 B read (hit) or written (miss) + 1,152 B written per
+// needed (with Q query rows, grid row miss_rows + sl * Q + q).  HBM-bound:
+// 656 B read (hit) or written (miss) + 1,152 B written per
 // selected row; PCIe: 656 B per missing row.  bf16 rounding by
 // v_cvt_pk_bf16_f32.
 #include "hc_internal.h"
@@ -142,7 +146,8 @@ __global__ __launch_bounds__(kGatherThreads) void k_gather(DevState d,
     int running = 0;
     for (int u0 = 0; u0 < U; u0 += kGatherThreads) {
       const int u = u0 + threadIdx.x;
-      const int c = u < U ? d.cnt[u * kCnt + kCntMiss] * layers_in_group(d, u % d.G) : 0;
+      const int c = u < U ? d.cnt[(size_t)u * d.Q * kCnt + kCntMiss] * layers_in_group(d, u % d.G)
+                          : 0;
       // block inclusive scan of c
       int x = c;
       const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -186,22 +191,24 @@ __global__ __launch_bounds__(kGatherThreads) void k_gather(DevState d,
         const int r = q - pref[u], m = (pref[u + 1] - pref[u]) / nl;
         const int lig = r / m, k = r - lig * m;
         const int64_t sl = (int64_t)s * d.L + g * d.R + lig;
-        const size_t uk = (size_t)u * d.K + k;
+        const size_t QK = (size_t)d.Q * d.K;
+        const size_t uk = (size_t)u * QK + k;
         j.src[p] = d.host[sl] + (size_t)d.miss_pos[uk] * kRow;
         j.fill[p] = d.hot + ((size_t)sl * d.C + d.victim[uk]) * kSlotStride;
-        j.dst[p] = out_b + ((size_t)sl * d.K + d.miss_idx[uk]) * out_row_bytes;
+        j.dst[p] = out_b + ((size_t)sl * QK + d.miss_idx[uk]) * out_row_bytes;
       }
       run_rows(j, item);
     }
     return;
   }
 
-  // ---- hit rows of layer sl = blockIdx.y - miss_rows, in output order -----
-  const int sl = blockIdx.y - miss_rows;
+  // ---- rows of (layer sl, query q), hr = blockIdx.y - miss_rows = sl * Q + q --
+  const int hr = blockIdx.y - miss_rows;
+  const int sl = hr / d.Q, q = hr - sl * d.Q;
   const int s = sl / d.L, l = sl - s * d.L;           // uniform per workgroup
-  const int32_t* slot = d.sel_slot + (size_t)(s * d.G + l / d.R) * d.K;
+  const int32_t* slot = d.sel_slot + ((size_t)(s * d.G + l / d.R) * d.Q + q) * d.K;
   const uint8_t* hot = d.hot + (size_t)sl * d.C * kSlotStride;
-  uint8_t* orow = out_b + (size_t)sl * d.K * out_row_bytes;
+  uint8_t* orow = out_b + (size_t)hr * d.K * out_row_bytes;
   const int i0 = blockIdx.x * kRowsPerRound + lrow;
 #pragma unroll
   for (int p = 0; p < kPasses; ++p) {
@@ -210,10 +217,13 @@ __global__ __launch_bounds__(kGatherThreads) void k_gather(DevState d,
     j.fill[p] = nullptr;
     if (i >= d.K) continue;
     const int32_t enc = slot[i];
-    if (enc < 0) continue;  // missed this step: written by a miss workgroup
-    // enc >= C: a row of the recent ring (entry enc - C)
-    j.src[p] = enc < d.C ? hot + (size_t)enc * kSlotStride
-                         : d.ring + ((size_t)sl * d.ring_rows + (enc - d.C)) * kRow;
+    if (enc < 0 && enc >= -d.C) continue;  // missed this step: written by a miss workgroup
+    if (enc >= d.C)                        // a row of the recent ring (entry enc - C)
+      j.src[p] = d.ring + ((size_t)sl * d.ring_rows + (enc - d.C)) * kRow;
+    else if (enc >= 0)                     // a hit
+      j.src[p] = hot + (size_t)enc * kSlotStride;
+    else                                   // another query's row of a miss: host RAM
+      j.src[p] = d.host[sl] + (size_t)(-(int64_t)enc - d.C - 1) * kRow;
     j.dst[p] = orow + (size_t)i * out_row_bytes;
   }
   run_rows(j, item);
@@ -225,8 +235,8 @@ hipError_t launch_gather(const DevState& d, uint16_t* d_out, hipStream_t st) {
   const int gx = (d.K + kRowsPerRound - 1) / kRowsPerRound;
   const int miss_rows = (kMissBlocks + gx - 1) / gx;
   const size_t lds = ((size_t)d.S * d.G + 1) * sizeof(int32_t);
-  hipLaunchKernelGGL(k_gather, dim3(gx, d.S * d.L + miss_rows), dim3(kGatherThreads), lds, st, d,
-                     d_out, miss_rows);
+  hipLaunchKernelGGL(k_gather, dim3(gx, d.S * d.L * d.Q + miss_rows), dim3(kGatherThreads), lds,
+                     st, d, d_out, miss_rows);
   return hipGetLastError();
 }
 

@@ -29,12 +29,9 @@
 //     out of the bitmap.  One stable partition of C entries per step.
 //  5. Apply the m (miss, victim) pairs to pos2slot / slot2pos / last_use in
 //     parallel (an evicted position is never one of this step's misses).
-#include "hc_internal.h"
+#include "hc_block.h"
 
 namespace hc {
-
-constexpr int kSelThreads = 1024;
-constexpr int kWaves = kSelThreads / 64;
 
 constexpr int kCandCache = 8192;               // cut-bin candidates kept in LDS (64 KB)
 constexpr int kWinWords = HC_MAX_SLOTS / 32;   // bitmap words per position window
@@ -58,50 +55,6 @@ struct SelShared {
   int32_t wmax;
   int32_t n_ring;                 // selected rows the recent ring holds
 };
-
-__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
-
-// Inclusive prefix over the block (thread order); `total` gets the block sum.
-__device__ __forceinline__ int block_incl_scan(int v, int32_t* wtot, int& total) {
-  const int lane = lane_id(), w = threadIdx.x >> 6;
-  int x = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    int y = __shfl_up(x, o, 64);
-    if (lane >= o) x += y;
-  }
-  if (lane == 63) wtot[w] = x;
-  __syncthreads();
-  int off = 0, tot = 0;
-#pragma unroll
-  for (int i = 0; i < kWaves; ++i) {
-    off += i < w ? wtot[i] : 0;
-    tot += wtot[i];
-  }
-  __syncthreads();
-  total = tot;
-  return x + off;
-}
-
-// Rank of this lane's flag among set flags of the block, in thread order, with
-// the block count in `total` (wave ballot + mbcnt, then wave offsets).
-__device__ __forceinline__ int block_flag_rank(bool f, int32_t* wtot, int& total) {
-  const uint64_t bal = __ballot(f);
-  const int w = threadIdx.x >> 6;
-  const int below = __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32),
-                                               __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0));
-  if (lane_id() == 0) wtot[w] = __popcll(bal);
-  __syncthreads();
-  int off = 0, tot = 0;
-#pragma unroll
-  for (int i = 0; i < kWaves; ++i) {
-    off += i < w ? wtot[i] : 0;
-    tot += wtot[i];
-  }
-  __syncthreads();
-  total = tot;
-  return off + below;
-}
 
 // Digit d (of nb bins, nb = 1024 or 2048) such that the count in bins above d
 // is < r and the count in bins >= d is >= r; *gt = count in bins above d.
@@ -152,6 +105,10 @@ __device__ __forceinline__ void reset_scan_state(const DevState& d, int u, int m
   }
 }
 
+// kTopkOnly (multi-query rounds): workgroup u is selection unit (s, g, q) and
+// stops after writing its selection; k_round then runs steps 3-5 on the union
+// of the group's selections.  Otherwise (one query) u is the unit (s, g).
+template <bool kTopkOnly>
 __global__ __launch_bounds__(kSelThreads) void k_select(DevState d, StepArgs a,
                                                         const float* __restrict__ scores,
                                                         uint64_t stride,
@@ -159,6 +116,7 @@ __global__ __launch_bounds__(kSelThreads) void k_select(DevState d, StepArgs a,
                                                         int32_t* __restrict__ d_trace) {
   __shared__ SelShared sh;
   const int u = blockIdx.x, tid = threadIdx.x;
+  const int session = u / (d.G * d.Q);
   const int K = d.K, C = d.C;
   const int32_t t = a.t;
   int32_t* cnt = d.cnt + u * kCnt;
@@ -174,7 +132,7 @@ __global__ __launch_bounds__(kSelThreads) void k_select(DevState d, StepArgs a,
     // The K-th key left the predicted window: rebuild both lists from the
     // scores — a 12-bit histogram for b1, then bins above b1 -> above, bin
     // b1 -> cand — and use the one-bin window [b1, b1].
-    const int64_t H = a.hist_len[u / d.G];
+    const int64_t H = a.hist_len[session];
     const float* src = scores + (uint64_t)u * stride;
     clear_hist(sh, kBins1);
     for (int64_t i = tid; i < H; i += kSelThreads)
@@ -363,6 +321,10 @@ __global__ __launch_bounds__(kSelThreads) void k_select(DevState d, StepArgs a,
   }
   __syncthreads();
   for (int i = tid; i < K; i += kSelThreads) d_sel[(size_t)u * K + i] = sh.sel[i];
+  if (kTopkOnly) {
+    reset_scan_state(d, u, 0, (int)b1);
+    return;
+  }
 
   // ---- 3. lookup, hits, ascending miss compaction ------------------------
   const int nwords = (C + 31) >> 5;
@@ -371,7 +333,7 @@ __global__ __launch_bounds__(kSelThreads) void k_select(DevState d, StepArgs a,
   int32_t* slot2pos = d.slot2pos + (size_t)u * C;
   int32_t* last_use = d.last_use + (size_t)u * C;
   constexpr int kLookRounds = HC_MAX_TOPK / kSelThreads;
-  const uint32_t ring_lo = a.ring_lo[u / d.G];
+  const uint32_t ring_lo = a.ring_lo[session];
   int32_t lp[kLookRounds], ls[kLookRounds];
 #pragma unroll
   for (int r = 0; r < kLookRounds; ++r) {   // all map reads in flight together
@@ -410,69 +372,7 @@ __global__ __launch_bounds__(kSelThreads) void k_select(DevState d, StepArgs a,
   }
 
   // ---- 4. LRU victims: first m untouched entries of the order list --------
-  // Wave w of a round owns 2,048 consecutive entries, lane-interleaved so every
-  // load is coalesced; ranks inside the wave come from ballots, and one block
-  // scan of the 16 wave totals orders the waves.
-  const int32_t* ocur = d.order + ((size_t)u * 2 + (t & 1)) * C;
-  int32_t* onxt = d.order + ((size_t)u * 2 + ((t + 1) & 1)) * C;
-  const int lane = lane_id(), wv = tid >> 6;
-  constexpr int kOrdPer = 32;
-  int kept = 0;
-  for (int j0 = 0; j0 < C; j0 += kSelThreads * kOrdPer) {
-    const int wb = j0 + wv * 64 * kOrdPer;
-    int32_t v[kOrdPer];
-#pragma unroll
-    for (int e = 0; e < kOrdPer; ++e) {
-      const int j = wb + e * 64 + lane;
-      v[e] = j < C ? ocur[j] : -1;
-    }
-    int wave_total = 0;
-#pragma unroll
-    for (int e = 0; e < kOrdPer; ++e) {
-      const bool keep = v[e] >= 0 && !((sh.u.lru.touched[v[e] >> 5] >> (v[e] & 31)) & 1u);
-      if (!keep) v[e] = -1;
-      wave_total += __popcll(__ballot(keep));
-    }
-    if (lane == 0) sh.wtot[wv] = wave_total;
-    __syncthreads();
-    int run = kept, total = 0;
-#pragma unroll
-    for (int i = 0; i < kWaves; ++i) {
-      run += i < wv ? sh.wtot[i] : 0;
-      total += sh.wtot[i];
-    }
-    __syncthreads();
-#pragma unroll
-    for (int e = 0; e < kOrdPer; ++e) {
-      const uint64_t bal = __ballot(v[e] >= 0);
-      if (v[e] >= 0) {
-        const int k = run + __popcll(bal & lt_mask);
-        if (k < m) sh.u.lru.vic[k] = v[e];
-        else onxt[k - m] = v[e];
-      }
-      run += __popcll(bal);
-    }
-    kept += total;
-  }
-  __syncthreads();
-  for (int k = tid; k < m; k += kSelThreads) atomicOr(&sh.u.lru.touched[sh.u.lru.vic[k] >> 5], 1u << (sh.u.lru.vic[k] & 31));
-  __syncthreads();
-  // this step's K - n_ring slots (hits and victims), ascending, close the
-  // order list
-  int base = C - (K - n_ring);
-  for (int w0 = 0; w0 < nwords; w0 += kSelThreads) {
-    const int w = w0 + tid;
-    uint32_t bits = w < nwords ? sh.u.lru.touched[w] : 0u;
-    int total;
-    const int incl = block_incl_scan(__popc(bits), sh.wtot, total);
-    int o = base + incl - __popc(bits);
-    while (bits) {
-      const int b = __ffs(bits) - 1;
-      bits &= bits - 1;
-      onxt[o++] = w * 32 + b;
-    }
-    base += total;
-  }
+  lru_victims(d, u, t, m, K - n_ring, sh.u.lru.touched, sh.u.lru.vic, sh.wtot);
 
   // ---- 5. apply (miss, victim) pairs --------------------------------------
   // A miss row is marked in sel_slot as -(slot + 1): the gather then reads it
@@ -529,8 +429,12 @@ __global__ __launch_bounds__(kSelThreads) void k_select(DevState d, StepArgs a,
 
 hipError_t launch_select(const DevState& d, const StepArgs& a, const float* scores,
                          uint64_t stride, int32_t* d_sel, int32_t* d_trace, hipStream_t st) {
-  hipLaunchKernelGGL(k_select, dim3(d.S * d.G), dim3(kSelThreads), 0, st, d, a, scores, stride,
-                     d_sel, d_trace);
+  if (d.Q == 1)
+    hipLaunchKernelGGL(k_select<false>, dim3(d.S * d.G), dim3(kSelThreads), 0, st, d, a, scores,
+                       stride, d_sel, d_trace);
+  else
+    hipLaunchKernelGGL(k_select<true>, dim3(d.S * d.G * d.Q), dim3(kSelThreads), 0, st, d, a,
+                       scores, stride, d_sel, d_trace);
   return hipGetLastError();
 }
 

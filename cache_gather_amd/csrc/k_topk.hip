@@ -21,8 +21,9 @@
 // from one appended position), so the window almost always holds and a step
 // reads the history once.
 //
-// Grid = (chunks of 8,192 positions) x (units), 256 threads; HBM-bound
-// streaming read of 4 B per position.
+// Grid = (chunks of 8,192 positions) x (selection units: one per query row of
+// each session and group), 256 threads; HBM-bound streaming read of 4 B per
+// position.
 #include "hc_internal.h"
 
 namespace hc {
@@ -84,8 +85,8 @@ __global__ __launch_bounds__(kScanThreads) void k_topk_scan(DevState d, StepArgs
                                                             uint64_t stride) {
   __shared__ int wtot[kScanThreads / 64];
   __shared__ int off_above, off_cand;
-  const int u = blockIdx.y;
-  const int64_t H = a.hist_len[u / d.G];
+  const int u = blockIdx.y;  // selection unit (s, g, q)
+  const int64_t H = a.hist_len[u / (d.G * d.Q)];
   const int64_t base = (int64_t)blockIdx.x * kScanChunk;
   if (base >= H) return;
   const int n = (int)(H - base < kScanChunk ? H - base : kScanChunk);
@@ -139,7 +140,7 @@ __global__ __launch_bounds__(kScanThreads) void k_topk_scan(DevState d, StepArgs
 
 hipError_t launch_topk_scan(const DevState& d, const StepArgs& a, const float* scores,
                             uint64_t stride, int n_chunks, bool vec4, hipStream_t st) {
-  dim3 grid(n_chunks, d.S * d.G);
+  dim3 grid(n_chunks, d.S * d.G * d.Q);
   if (vec4)
     hipLaunchKernelGGL(k_topk_scan<true>, grid, dim3(kScanThreads), 0, st, d, a, scores, stride);
   else

@@ -45,17 +45,18 @@ class hc_config(ctypes.Structure):
                 ("cache_slots", ctypes.c_uint32), ("top_k", ctypes.c_uint32),
                 ("max_positions", ctypes.c_uint64), ("device", ctypes.c_int32),
                 ("flags", ctypes.c_uint32), ("ring_rows", ctypes.c_uint32),
-                ("copyback_rows", ctypes.c_uint32)]
+                ("copyback_rows", ctypes.c_uint32), ("queries", ctypes.c_uint32)]
 
 
 CONFIG_SIZE_NO_RING = hc_config.ring_rows.offset
+CONFIG_SIZE_ONE_QUERY = hc_config.queries.offset
 
 
 def make_config(n_sessions, n_layers, layers_per_select, cache_slots, top_k, max_positions,
-                device=0, flags=0, ring_rows=0, copyback_rows=0) -> hc_config:
+                device=0, flags=0, ring_rows=0, copyback_rows=0, queries=1) -> hc_config:
     return hc_config(ctypes.sizeof(hc_config), n_sessions, n_layers, layers_per_select,
                      cache_slots, top_k, max_positions, device, flags, ring_rows,
-                     copyback_rows)
+                     copyback_rows, queries)
 
 
 _LIB = None
@@ -225,10 +226,11 @@ class HotCache:
     """
 
     def __init__(self, n_sessions, n_layers, layers_per_select, cache_slots, top_k,
-                 max_positions, device=0, ring_rows=0, copyback_rows=0):
+                 max_positions, device=0, ring_rows=0, copyback_rows=0, queries=1):
         import torch
         self.cfg = make_config(n_sessions, n_layers, layers_per_select, cache_slots, top_k,
-                               max_positions, device, 0, ring_rows, copyback_rows)
+                               max_positions, device, 0, ring_rows, copyback_rows, queries)
+        self.Q = queries
         self.S, self.L, self.R = n_sessions, n_layers, layers_per_select
         self.G = -(-n_layers // layers_per_select)
         self.C, self.K, self.hcap = cache_slots, top_k, max_positions
@@ -262,11 +264,15 @@ class HotCache:
         return hc_export_state(self.ctx, s, l, self.C, self.hcap, pos2slot, hot_rows)
 
     def alloc_outputs(self, trace=False):
+        """out [S, L, K, 576] and sel [S, G, K]; with Q > 1 query rows per
+        round, out [S, L, Q, K, 576] and sel [S, G, Q, K]."""
         import torch
-        out = torch.empty((self.S, self.L, self.K, OUT_ELEMS), dtype=torch.int16,
+        q = (self.Q,) if self.Q > 1 else ()
+        out = torch.empty((self.S, self.L) + q + (self.K, OUT_ELEMS), dtype=torch.int16,
                           device=self.device)
-        sel = torch.empty((self.S, self.G, self.K), dtype=torch.int32, device=self.device)
-        tr = (torch.empty((self.S * self.G, trace_ints(self.K)), dtype=torch.int32,
+        sel = torch.empty((self.S, self.G) + q + (self.K,), dtype=torch.int32,
+                          device=self.device)
+        tr = (torch.empty((self.S * self.G, trace_ints(self.Q * self.K)), dtype=torch.int32,
                           device=self.device) if trace else None)
         return out, sel, tr
 

@@ -22,6 +22,10 @@ Recipe (all seeded; numpy PCG64 via default_rng with a tuple seed):
   noise of step t:       sigma_n * N(0,1) float32, H_t values, rng((seed, 3, s, g, t))
   scores(s, g, t) = bias[:H_t] + noise   (one float32 add)
   H_t = H0 + t: one position is appended per decode step; Hcap = H0 + steps.
+  Multi-query rounds (MTP verification, Q query rows): query 0 has the scores
+  above; query q > 0 adds its own draft noise, one more float32 add:
+      sigma_draft * N(0,1) float32, H_t values, rng((seed, 4, s, g, q, t))
+  so the Q selections overlap heavily without being equal.
 """
 from __future__ import annotations
 
@@ -186,19 +190,26 @@ class Scores:
         noise = np.float32(self.wl.sigma_noise[s]) * rng.standard_normal(h, dtype=np.float32)
         return self.bias(s, g)[:h] + noise
 
-    def step(self, t: int, stride: int | None = None) -> np.ndarray:
-        """float32 [S*G, stride] for step t (entries past H_t are zero)."""
+    def step(self, t: int, stride: int | None = None, queries: int = 1,
+             sigma_draft: float = 0.1) -> np.ndarray:
+        """float32 [S*G*Q, stride] for step t (entries past H_t are zero);
+        row (s*G + g)*Q + q is query q of unit (s, g)."""
         wl = self.wl
         stride = wl.hcap if stride is None else stride
-        out = np.zeros((wl.n_units, stride), dtype=np.float32)
+        out = np.zeros((wl.n_units * queries, stride), dtype=np.float32)
 
-        def one(u):
+        def one(uq):
+            u, q = divmod(uq, queries)
             s, g = divmod(u, wl.n_groups)
             x = self.unit(s, g, t)
-            out[u, :x.size] = x
+            if q:
+                h = x.size
+                rng = np.random.default_rng((self.wl.seed, 4, s, g, q, t))
+                x = x + np.float32(sigma_draft) * rng.standard_normal(h, dtype=np.float32)
+            out[uq, :x.size] = x
 
         for u in range(wl.n_units):   # bias vectors first, then parallel noise
             self.bias(*divmod(u, wl.n_groups))
         with ThreadPoolExecutor(_workers()) as ex:
-            list(ex.map(one, range(wl.n_units)))
+            list(ex.map(one, range(wl.n_units * queries)))
         return out

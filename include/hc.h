@@ -44,6 +44,17 @@
  * survive the session lifecycle": it submits the remaining rows, waits for the
  * copy, and checks the host row count written by the device.
  *
+ * Multi-query rounds (hc_config.queries = Q > 1; MTP verification, the
+ * page's section "GPU cache management has hazards too"): each of the Q query
+ * rows of a round has its own scores and selects its own top-K over the same
+ * history.  Steps 2-4 run once on the ascending union of a group's Q
+ * selections: a position several queries select is one hit or one miss (one
+ * victim, one fill); slots used by any query are pinned; a slot filled in the
+ * round is only read in later rounds, and every query row whose position
+ * missed — beyond the one that fills the slot — reads host RAM directly.
+ * Step 5 gathers each query's rows in its own selection order.  Q = 1 is the
+ * single-query step described above.
+ *
  * Row format (Q8G64 MLA row, 656 B; the page's payload description): bytes
  * [0,512) int8 latent, [512,528) 8 little-endian fp16 scales (scale g covers
  * latent bytes [64g, 64g+64)), [528,656) 64 little-endian bf16 RoPE values.
@@ -75,14 +86,19 @@ extern "C" {
 #define HC_MAX_SESSIONS  256   /* largest supported n_sessions              */
 #define HC_MAX_UNITS     4096  /* largest S * ceil(L / R) (selection units) */
 #define HC_MAX_RING_ROWS 65536 /* largest recent ring per (session, layer)  */
+#define HC_MAX_QUERIES   16    /* largest number of query rows per round    */
+#define HC_MAX_ROUND_ROWS 8192 /* largest queries * top_k                   */
 #define HC_NO_APPEND     (~(uint64_t)0)  /* hc_append: this session appends nothing */
 
-/* Per-unit trace record: HC_TRACE_INTS(K) int32 values per (session, group),
- * units ordered u = s * G + g.  Layout:
+/* Per-unit trace record: HC_TRACE_INTS(Q * K) int32 values per (session,
+ * group), units ordered u = s * G + g, describing the round's selection
+ * union (for Q = 1, the selection itself; N = n_hit + n_miss + n_ring entries
+ * in ascending position order, below written with K meaning Q * K).  Layout:
  *   [0] n_hit   [1] n_miss   [2] n_evict (victims whose slot held a position)
  *   [3] n_ring  (selected rows read from the recent ring)
- *   [4 + 0K .. 4 + 1K)  slot of selected row i after the step (sel order);
- *                       C + p % ring_rows for a row read from the ring
+ *   [4 + 0K .. 4 + 1K)  slot of union entry j after the step (ascending
+ *                       position); C + p % ring_rows for a row read from the
+ *                       ring; -1 past the N entries
  *   [4 + 1K .. 4 + 2K)  miss_pos: missing positions, ascending; -1 past n_miss
  *   [4 + 2K .. 4 + 3K)  victim slot paired with miss i; -1 past n_miss
  *   [4 + 3K .. 4 + 4K)  position evicted from that slot, -1 if it was empty   */
@@ -108,15 +124,16 @@ typedef enum {
 } hc_status;
 
 typedef struct hc_config {
-  uint32_t struct_size;       /* sizeof(hc_config); the size without the ring
-                                 fields (40) is accepted and means no ring      */
+  uint32_t struct_size;       /* sizeof(hc_config); the sizes without the ring
+                                 fields (40) or without `queries` (48) are
+                                 accepted: no ring, one query                   */
   uint32_t n_sessions;        /* S, 1 <= S <= HC_MAX_SESSIONS                   */
   uint32_t n_layers;          /* L >= 1 layers per session                      */
   uint32_t layers_per_select; /* R >= 1; S * ceil(L / R) <= HC_MAX_UNITS        */
   uint32_t cache_slots;       /* C, top_k <= C <= HC_MAX_SLOTS                  */
   uint32_t top_k;             /* K, 1 <= K <= HC_MAX_TOPK                       */
   uint64_t max_positions;     /* Hcap: host rows per (session, layer),
-                                 K <= Hcap < 2^31                               */
+                                 K <= Hcap <= 2^31 - 2^19                       */
   int32_t  device;            /* HIP device ordinal                             */
   uint32_t flags;             /* must be 0                                      */
   uint32_t ring_rows;         /* recent ring rows per (session, layer); 0 = no
@@ -124,6 +141,10 @@ typedef struct hc_config {
                                  else <= HC_MAX_RING_ROWS                       */
   uint32_t copyback_rows;     /* rows per copyback batch, 1 <= copyback_rows <=
                                  ring_rows (0 when ring_rows is 0)              */
+  uint32_t queries;           /* Q query rows per round, 0 or 1 = one query;
+                                 Q <= HC_MAX_QUERIES, Q * K <= HC_MAX_ROUND_ROWS,
+                                 Q * K <= C; the struct without this field
+                                 (48 B) means Q = 1                             */
 } hc_config;
 
 typedef struct hc_ctx hc_ctx;
@@ -149,17 +170,18 @@ hc_status hc_create(const hc_config* cfg, void* dev_workspace, uint64_t ws_bytes
  * copyback writes.  NULL on a bad index. */
 uint8_t* hc_host_rows(hc_ctx* ctx, uint32_t session, uint32_t layer);
 
-/* One decode step, enqueued on `stream` (a hipStream_t; NULL = default stream).
- *   d_scores     device fp32 [S][G][score_stride]; unit (s,g) uses entries
- *                [0, hist_len[s]).
+/* One decode step (round), enqueued on `stream` (a hipStream_t; NULL = default
+ * stream).  Q = queries (1 if not set).
+ *   d_scores     device fp32 [S][G][Q][score_stride]; query (s,g,q) uses
+ *                entries [0, hist_len[s]).
  *   score_stride elements between units, >= max_s hist_len[s].
  *   hist_len     host uint64 [S]: positions in each session's history this
  *                step; K <= hist_len[s] <= Hcap, never smaller than at the
  *                previous step, and at most the end of the appended
  *                positions once the session has appended.
- *   d_out        device bf16 bits [S][L][K][576], rows in selection order.
- *   d_sel        device int32 [S][G][K]: selected positions, ascending.
- *   d_trace      NULL, or device int32 [S*G][HC_TRACE_INTS(K)] (see above).
+ *   d_out        device bf16 bits [S][L][Q][K][576], rows in selection order.
+ *   d_sel        device int32 [S][G][Q][K]: selected positions, ascending.
+ *   d_trace      NULL, or device int32 [S*G][HC_TRACE_INTS(Q*K)] (see above).
  * Asynchronous: results are valid once the stream has completed the step.
  * All arguments are checked before anything is enqueued; a rejected call
  * (HC_E_INVAL) changes nothing.  A HIP launch failure returns HC_E_HIP and

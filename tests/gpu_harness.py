@@ -25,15 +25,16 @@ def align4(n):
 
 
 class Pair:
-    def __init__(self, wl: W.Workload, score_stride=None, rows_fn=None, device=0):
+    def __init__(self, wl: W.Workload, score_stride=None, rows_fn=None, device=0, queries=1):
         self.wl = wl
+        self.Q = queries
         self.dev = torch.device("cuda", device)
         say("workload", wl.name, "S=%d L=%d R=%d K=%d C=%d H0=%d steps=%d" % (
             wl.n_sessions, wl.n_layers, wl.layers_per_select, wl.top_k, wl.cache_slots,
             wl.hist0, wl.steps))
         self.stride = align4(wl.hcap) if score_stride is None else score_stride
         self.hc = hc.HotCache(wl.n_sessions, wl.n_layers, wl.layers_per_select,
-                              wl.cache_slots, wl.top_k, wl.hcap, device)
+                              wl.cache_slots, wl.top_k, wl.hcap, device, queries=queries)
         t0 = time.time()
         self.rows = [[None] * wl.n_layers for _ in range(wl.n_sessions)]
         for s in range(wl.n_sessions):
@@ -43,14 +44,14 @@ class Pair:
                 np.copyto(self.hc.host_rows(s, l), r)
         say("rows ready in %.1fs" % (time.time() - t0))
         self.orc = oracle.Model(wl.n_sessions, wl.n_layers, wl.layers_per_select, wl.top_k,
-                                wl.cache_slots, wl.hcap, self.rows)
+                                wl.cache_slots, wl.hcap, self.rows, queries=queries)
         self.scores = W.Scores(wl)
         self.out, self.sel, self.trace = self.hc.alloc_outputs(trace=True)
-        self.d_scores = torch.empty((wl.n_units, self.stride), dtype=torch.float32,
+        self.d_scores = torch.empty((wl.n_units * queries, self.stride), dtype=torch.float32,
                                     device=self.dev)
 
     def scores_for(self, t):
-        return self.scores.step(t, self.stride)
+        return self.scores.step(t, self.stride, queries=self.Q)
 
     def gpu_step(self, t, scores_np, hist_len):
         self.d_scores.copy_(torch.from_numpy(scores_np))
@@ -75,7 +76,7 @@ class Pair:
     def compare(self, t, g, o, gather=True):
         wl = self.wl
         o_sel, o_out, o_inf = o
-        K = wl.top_k
+        K = wl.top_k * self.Q    # trace entries per unit: the round's union
         np.testing.assert_array_equal(g["sel"], o_sel, err_msg="selection, step %d" % t)
         for s in range(wl.n_sessions):
             for gi in range(wl.n_groups):
@@ -134,8 +135,10 @@ class RingPair(Pair):
     host RAM only through the copybacks.  recent_boost is added to the scores
     of appended positions so that the ring is selected from."""
 
-    def __init__(self, wl, ring_rows, copyback_rows, recent_boost=1.0, device=0, skip=None):
+    def __init__(self, wl, ring_rows, copyback_rows, recent_boost=1.0, device=0, skip=None,
+                 queries=1):
         self.ring_rows, self.copyback_rows = ring_rows, copyback_rows
+        self.Q = queries
         self.first = wl.hist0 - 1
         self.recent_boost = np.float32(recent_boost)
         self.skip = skip or (lambda t, s: False)  # session s appends nothing at step t
@@ -147,7 +150,7 @@ class RingPair(Pair):
         self.stride = align4(wl.hcap)
         self.hc = hc.HotCache(wl.n_sessions, wl.n_layers, wl.layers_per_select,
                               wl.cache_slots, wl.top_k, wl.hcap, device,
-                              ring_rows=ring_rows, copyback_rows=copyback_rows)
+                              ring_rows=ring_rows, copyback_rows=copyback_rows, queries=queries)
         S, L = wl.n_sessions, wl.n_layers
         self.rows = [[W.fill_rows(wl, s, l) for l in range(L)] for s in range(S)]
         self.orc_host = [[np.zeros_like(self.rows[s][l]) for l in range(L)] for s in range(S)]
@@ -158,11 +161,12 @@ class RingPair(Pair):
                 h[self.first:] = 0
                 self.orc_host[s][l][:self.first] = self.rows[s][l][:self.first]
         self.orc = oracle.Model(S, L, wl.layers_per_select, wl.top_k, wl.cache_slots, wl.hcap,
-                                self.orc_host, ring_rows=ring_rows, copyback_rows=copyback_rows)
+                                self.orc_host, ring_rows=ring_rows, copyback_rows=copyback_rows,
+                                queries=queries)
         self.end = [self.first] * S
         self.scores = W.Scores(wl)
         self.out, self.sel, self.trace = self.hc.alloc_outputs(trace=True)
-        self.d_scores = torch.empty((wl.n_units, self.stride), dtype=torch.float32,
+        self.d_scores = torch.empty((wl.n_units * queries, self.stride), dtype=torch.float32,
                                     device=self.dev)
         self.d_new = torch.empty((S, L, 656), dtype=torch.uint8, device=self.dev)
 
@@ -185,8 +189,9 @@ class RingPair(Pair):
             hist_len = np.array(self.end, np.uint64)
         if scores_np is None:
             scores_np = self.scores_for(t)
-            for u in range(wl.n_units):
-                scores_np[u, self.first:self.end[u // wl.n_groups]] += self.recent_boost
+            for uq in range(wl.n_units * self.Q):
+                s_ = uq // (wl.n_groups * self.Q)
+                scores_np[uq, self.first:self.end[s_]] += self.recent_boost
         return Pair.step(self, t, scores_np, hist_len, gather, nthreads)
 
     def compare_host(self, margin=8):

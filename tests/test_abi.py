@@ -41,6 +41,9 @@ def test_workspace_grows_with_the_configuration_and_holds_the_hot_rows():
     dict(flags=1), dict(cache_slots=262145),
     dict(ring_rows=64, copyback_rows=0), dict(ring_rows=64, copyback_rows=65),
     dict(ring_rows=0, copyback_rows=8), dict(ring_rows=65537, copyback_rows=64),
+    dict(queries=17), dict(queries=4, cache_slots=1000), dict(queries=8, top_k=2048,
+                                                              cache_slots=32768),
+    dict(max_positions=(1 << 31) - (1 << 19) + 1),
 ])
 def test_invalid_configurations_are_rejected(bad):
     kw = dict(n_sessions=1, n_layers=2, layers_per_select=1, cache_slots=1024, top_k=256,
@@ -66,6 +69,24 @@ def test_config_without_the_ring_fields_is_accepted():
     cfg.struct_size = hc.CONFIG_SIZE_NO_RING
     cfg.ring_rows, cfg.copyback_rows = 99, 7   # ignored: beyond the short struct
     assert hc.hc_workspace_bytes(cfg) == full
+
+
+def test_config_without_queries_means_one_query():
+    cfg = hc.make_config(1, 3, 2, 1024, 256, 5000, ring_rows=16, copyback_rows=8)
+    full = hc.hc_workspace_bytes(cfg)
+    assert hc.CONFIG_SIZE_ONE_QUERY == 48 and ctypes.sizeof(hc.hc_config) == 56
+    cfg.struct_size = hc.CONFIG_SIZE_ONE_QUERY
+    cfg.queries = 9                         # ignored: beyond the short struct
+    assert hc.hc_workspace_bytes(cfg) == full
+    zero = hc.make_config(1, 3, 2, 1024, 256, 5000, ring_rows=16, copyback_rows=8, queries=0)
+    assert hc.hc_workspace_bytes(zero) == full
+
+
+def test_queries_grow_the_selection_arrays():
+    one = hc.hc_workspace_bytes(hc.make_config(1, 78, 4, 32768, 2048, 51047))
+    four = hc.hc_workspace_bytes(hc.make_config(1, 78, 4, 32768, 2048, 51047, queries=4))
+    # per extra query and unit: cand (8 B per position) + 5 arrays of K ints + counters
+    assert four - one >= 20 * 3 * (51047 * 8 + 5 * 2048 * 4)
 
 
 def test_bad_struct_size_is_rejected():
