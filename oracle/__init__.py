@@ -20,6 +20,7 @@ _f32p = ctypes.POINTER(ctypes.c_float)
 
 ROW_BYTES = 656
 OUT_ELEMS = 576
+LRU, CIRCULAR, CLOCK = 0, 1, 2   # replacement policies
 
 
 class StepInfo(ctypes.Structure):
@@ -48,6 +49,12 @@ def lib():
         L.orc_dequant_table.restype = None
         L.orc_cache_new.argtypes = [ctypes.c_int32, ctypes.c_int64]
         L.orc_cache_new.restype = ctypes.c_void_p
+        L.orc_cache_new_policy.argtypes = [ctypes.c_int32, ctypes.c_int64, ctypes.c_int32]
+        L.orc_cache_new_policy.restype = ctypes.c_void_p
+        L.orc_cache_ref.argtypes = [ctypes.c_void_p]
+        L.orc_cache_ref.restype = _u8p
+        L.orc_cache_hand.argtypes = [ctypes.c_void_p]
+        L.orc_cache_hand.restype = ctypes.c_int32
         L.orc_cache_free.argtypes = [ctypes.c_void_p]
         L.orc_cache_free.restype = None
         L.orc_cache_step.argtypes = [ctypes.c_void_p, ctypes.c_int32, _i32p, ctypes.c_int32,
@@ -168,11 +175,11 @@ class Ring:
 
 
 class Cache:
-    """LRU hot cache of one (session, layer)."""
+    """Hot cache of one (session, layer); replacement LRU, CIRCULAR or CLOCK."""
 
-    def __init__(self, slots, hcap):
+    def __init__(self, slots, hcap, policy=LRU):
         self.C, self.hcap = int(slots), int(hcap)
-        self._p = lib().orc_cache_new(self.C, self.hcap)
+        self._p = lib().orc_cache_new_policy(self.C, self.hcap, int(policy))
         if not self._p:
             raise MemoryError("orc_cache_new failed")
 
@@ -217,6 +224,12 @@ class Cache:
         return np.ctypeslib.as_array(lib().orc_cache_hot(self._p),
                                      (self.C, ROW_BYTES)).copy()
 
+    def ref(self):
+        return np.ctypeslib.as_array(lib().orc_cache_ref(self._p), (self.C,)).copy()
+
+    def hand(self):
+        return int(lib().orc_cache_hand(self._p))
+
 
 class Model:
     """S sessions x L layers, one selection per group of R layers; each layer
@@ -226,12 +239,12 @@ class Model:
     then be writable C-contiguous uint8 arrays: they are used in place)."""
 
     def __init__(self, n_sessions, n_layers, layers_per_select, top_k, slots, hcap, host_rows,
-                 ring_rows=0, copyback_rows=0, queries=1):
+                 ring_rows=0, copyback_rows=0, queries=1, replacement=LRU):
         self.S, self.L, self.R = int(n_sessions), int(n_layers), int(layers_per_select)
         self.G = -(-self.L // self.R)
         self.K, self.C, self.hcap = int(top_k), int(slots), int(hcap)
         self.Q = int(queries)
-        self.caches = [Cache(slots, hcap) for _ in range(self.S * self.L)]
+        self.caches = [Cache(slots, hcap, replacement) for _ in range(self.S * self.L)]
         self.rows = [np.ascontiguousarray(host_rows[s][l], dtype=np.uint8)
                      for s in range(self.S) for l in range(self.L)]
         for r in self.rows:

@@ -217,10 +217,15 @@ struct orc_cache {
   int32_t* pos_of;   /* slot -> position, -1 if empty        */
   int32_t* last;     /* slot -> last-use step, -1 if unused  */
   uint8_t* hot;      /* slot contents                        */
+  int32_t policy;    /* ORC_LRU, ORC_CIRCULAR or ORC_CLOCK    */
+  int32_t hand;      /* circular / clock hand                 */
+  uint8_t* ref;      /* clock reference bits                  */
 };
 
-orc_cache* orc_cache_new(int32_t C, int64_t hcap) {
-  if (C < 1 || hcap < 1) return NULL;
+orc_cache* orc_cache_new(int32_t C, int64_t hcap) { return orc_cache_new_policy(C, hcap, ORC_LRU); }
+
+orc_cache* orc_cache_new_policy(int32_t C, int64_t hcap, int32_t policy) {
+  if (C < 1 || hcap < 1 || policy < ORC_LRU || policy > ORC_CLOCK) return NULL;
   orc_cache* c = (orc_cache*)calloc(1, sizeof *c);
   if (!c) return NULL;
   c->C = C;
@@ -229,7 +234,10 @@ orc_cache* orc_cache_new(int32_t C, int64_t hcap) {
   c->pos_of = (int32_t*)malloc((size_t)C * sizeof(int32_t));
   c->last = (int32_t*)malloc((size_t)C * sizeof(int32_t));
   c->hot = (uint8_t*)calloc((size_t)C, ORC_ROW_BYTES);
-  if (!c->slot_of || !c->pos_of || !c->last || !c->hot) {
+  c->ref = (uint8_t*)calloc((size_t)C, 1);
+  c->policy = policy;
+  c->hand = 0;
+  if (!c->slot_of || !c->pos_of || !c->last || !c->hot || !c->ref) {
     orc_cache_free(c);
     return NULL;
   }
@@ -244,6 +252,7 @@ void orc_cache_free(orc_cache* c) {
   free(c->pos_of);
   free(c->last);
   free(c->hot);
+  free(c->ref);
   free(c);
 }
 
@@ -255,6 +264,36 @@ static int32_t lru_victim(const orc_cache* c, int32_t t) {
     if (best < 0 || c->last[v] < c->last[best]) best = v;
   }
   return best;
+}
+
+/* Circular eviction that skips pinned slots (page "From 1M Total to 15+ × 1M
+ * Contexts: GLM-5.3 KV Cache Offloading", section "GPU cache management has
+ * hazards too"): the hand moves to the next slot not used in step t, which is
+ * the victim, and passes it. */
+static int32_t circular_victim(orc_cache* c, int32_t t) {
+  for (int32_t n = 0; n < c->C; ++n) {
+    int32_t v = c->hand;
+    c->hand = (c->hand + 1) % c->C;
+    if (c->last[v] != t) return v;
+  }
+  return -1;
+}
+
+/* Clock with reference bits (same section): the hand skips slots used in step
+ * t, clears and skips slots whose reference bit is set, and takes the first
+ * slot whose bit is clear.  Two revolutions always suffice. */
+static int32_t clock_victim(orc_cache* c, int32_t t) {
+  for (int32_t n = 0; n < 2 * c->C; ++n) {
+    int32_t v = c->hand;
+    c->hand = (c->hand + 1) % c->C;
+    if (c->last[v] == t) continue;
+    if (c->ref[v]) {
+      c->ref[v] = 0;
+      continue;
+    }
+    return v;
+  }
+  return -1;
 }
 
 int orc_cache_step(orc_cache* c, int32_t t, const int32_t* sel, int32_t K,
@@ -273,13 +312,16 @@ int orc_cache_step(orc_cache* c, int32_t t, const int32_t* sel, int32_t K,
     if (s >= 0) {
       c->last[s] = t;
       ++n_hit;
+      c->ref[s] = 1;
     }
   }
   /* Misses, one at a time in selection order. */
   for (int32_t i = 0; i < K; ++i) {
     int32_t p = sel[i];
     if (orc_ring_row(ring, p) || c->slot_of[p] >= 0) continue;
-    int32_t v = lru_victim(c, t);
+    int32_t v = c->policy == ORC_CIRCULAR ? circular_victim(c, t)
+              : c->policy == ORC_CLOCK    ? clock_victim(c, t)
+                                          : lru_victim(c, t);
     if (v < 0) return -1;
     int32_t old = c->pos_of[v];
     if (old >= 0) {
@@ -289,6 +331,7 @@ int orc_cache_step(orc_cache* c, int32_t t, const int32_t* sel, int32_t K,
     c->pos_of[v] = p;
     c->slot_of[p] = v;
     c->last[v] = t;
+    c->ref[v] = 1;
     memcpy(c->hot + (size_t)v * ORC_ROW_BYTES, host_rows + (size_t)p * ORC_ROW_BYTES,
            ORC_ROW_BYTES);
     if (info) {
@@ -332,6 +375,8 @@ const int32_t* orc_cache_slot_of(const orc_cache* c) { return c->slot_of; }
 const int32_t* orc_cache_pos_of(const orc_cache* c) { return c->pos_of; }
 const int32_t* orc_cache_last(const orc_cache* c) { return c->last; }
 const uint8_t* orc_cache_hot(const orc_cache* c) { return c->hot; }
+const uint8_t* orc_cache_ref(const orc_cache* c) { return c->ref; }
+int32_t orc_cache_hand(const orc_cache* c) { return c->hand; }
 
 /* --------------------------------------------------- whole-model driver -- */
 

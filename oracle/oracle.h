@@ -82,7 +82,18 @@ typedef struct orc_step_info {
   int32_t n_ring;      /* selected rows read from the recent ring           */
 } orc_step_info;
 
-orc_cache* orc_cache_new(int32_t C, int64_t hcap);
+/* Replacement policies.  LRU: the slot with the oldest last-use step, ties to
+ * the lowest slot.  Circular: a hand moves over the slots and takes the next
+ * one not used in the current step.  Clock: hits and fills set a slot's
+ * reference bit; the hand skips slots used in the current step, clears and
+ * skips set bits, and takes the first slot with a clear bit.  Both hands
+ * start at slot 0 and stop just past their last victim. */
+#define ORC_LRU      0
+#define ORC_CIRCULAR 1
+#define ORC_CLOCK    2
+
+orc_cache* orc_cache_new(int32_t C, int64_t hcap);   /* LRU */
+orc_cache* orc_cache_new_policy(int32_t C, int64_t hcap, int32_t policy);
 void       orc_cache_free(orc_cache* c);
 
 /* Step t for a selection sel[0..K) (distinct positions < hcap, ascending):
@@ -104,6 +115,8 @@ const int32_t* orc_cache_slot_of(const orc_cache* c);  /* [hcap] pos -> slot  */
 const int32_t* orc_cache_pos_of(const orc_cache* c);   /* [C] slot -> pos     */
 const int32_t* orc_cache_last(const orc_cache* c);     /* [C] last-use step   */
 const uint8_t* orc_cache_hot(const orc_cache* c);      /* [C][656] slot bytes */
+const uint8_t* orc_cache_ref(const orc_cache* c);      /* [C] clock reference bits */
+int32_t        orc_cache_hand(const orc_cache* c);     /* circular / clock hand */
 
 /* Whole decode round for S sessions x L layers with a selection per group of R
  * layers (G = ceil(L/R)) and Q query rows per round (MTP verification: the

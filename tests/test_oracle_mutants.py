@@ -58,6 +58,16 @@ MUTANTS = {
     # multi-query round: the union keeps duplicate positions
     "union_keeps_duplicates": ("    if (n == 0 || uni[i] != uni[n - 1]) uni[n++] = uni[i];",
                                "    uni[n++] = uni[i];", "test_oracle_mtp.py"),
+    # circular replacement: the hand takes pinned slots too
+    "circular_ignores_pins": ("    if (c->last[v] != t) return v;", "    return v;",
+                              "test_oracle_replacement.py"),
+    # clock replacement: hits do not set the reference bit
+    "clock_hits_keep_bit": ("      ++n_hit;\n      c->ref[s] = 1;", "      ++n_hit;",
+                            "test_oracle_replacement.py"),
+    # clock replacement: a set bit is skipped without being cleared
+    "clock_bits_not_cleared": ("    if (c->ref[v]) {\n      c->ref[v] = 0;\n      continue;",
+                               "    if (c->ref[v]) {\n      continue;",
+                               "test_oracle_replacement.py"),
     # gather: RoPE read two bytes early
     "rope_offset": ("out[512 + k] = (uint16_t)(row[528 + 2 * k] | (row[528 + 2 * k + 1] << 8));",
                     "out[512 + k] = (uint16_t)(row[526 + 2 * k] | (row[526 + 2 * k + 1] << 8));",
