@@ -121,6 +121,59 @@ def copy_ceiling(torch, dev):
     return round(2 * n / (ms * 1e-3) / 1e9, 1)
 
 
+def replacement_probe(hc, W, np, torch, reps=10):
+    """The page's probe (section "GPU cache management has hazards too"): a
+    full hot cache of 32,768 slots whose reference bits are all set, then one
+    gather of 2,048 rows with 1% (20) misses.  Each repetition builds the
+    state on a fresh context (16 steps of disjoint 2,048-position blocks fill
+    every slot; fills set the bits) and times the probe step's kernels with
+    HIP events.  One layer, one session, history 131,072 positions."""
+    K, C, H = 2048, 32768, 131072
+    wl = W.Workload("replacement_probe", 1, 1, 1, H, 17, C, K, (1.0,), (1.0,), 77)
+    rows = W.fill_rows(wl, 0, 0)
+    stride = (wl.hcap + 3) // 4 * 4
+    dev = torch.device("cuda", 0)
+    preload_kernels(hc, torch)
+    blocks = torch.zeros((C // K, stride), dtype=torch.float32, device=dev)
+    for t in range(C // K):
+        blocks[t, t * K:(t + 1) * K] = 1.0
+    rng = np.random.default_rng(3)
+    probes = []
+    for r in range(reps):
+        x = np.zeros(stride, np.float32)
+        x[np.sort(rng.choice(C, K - 20, replace=False))] = 1.0
+        x[np.sort(rng.choice(np.arange(C, H), 20, replace=False))] = 1.0
+        probes.append(torch.from_numpy(x).to(dev))
+    out_res = {}
+    for name, policy in (("lru", hc.LRU), ("circular", hc.CIRCULAR), ("clock", hc.CLOCK)):
+        stage = {k: [] for k in hc.STAGES}
+        misses = []
+        for r in range(reps):
+            cache = hc.HotCache(1, 1, 1, C, K, wl.hcap, 0, replacement=policy)
+            np.copyto(cache.host_rows(0, 0), rows)
+            out, sel, tr = cache.alloc_outputs(trace=True)
+            for t in range(C // K):
+                cache.step(blocks[t], stride, [H], out, sel)
+            hc.hc_profile_enable(cache.ctx, 1)
+            cache.step(probes[r], stride, [H], out, sel, tr)
+            ms, n, _ = hc.hc_profile_read(cache.ctx)
+            misses.append(int(tr[0, 1].item()))
+            for k in hc.STAGES:
+                stage[k].append(ms[k] * 1e3)
+            cache.close()
+        med = {k: round(float(np.median(v)), 2) for k, v in stage.items()}
+        out_res[name] = {"stage_us_median": med,
+                         "select_plus_gather_us": round(med["select"] + med["gather"], 2),
+                         "misses": int(np.median(misses))}
+    return {"metric": "replacement probe: us per 2,048-row step, full cache, all reference "
+                      "bits set, 1% misses",
+            "unit": "us", "higher_is_better": False, "n_gpus": 1, "reps": reps,
+            "config": {"workload": "replacement_probe", "cache_slots": C, "top_k": K,
+                       "history": H, "layers": 1},
+            "policies": out_res,
+            "page_context_w7900d": {"clock_ms": [1.03, 1.07], "circular_ms": 0.032}}
+
+
 def preload_kernels(hc, torch):
     """Steps on tiny throwaway contexts — one query, two queries, and a ring
     append with its copyback — so that loading the kernels' code objects is
@@ -153,6 +206,10 @@ def main():
     ap.add_argument("--queries", type=int, default=1, metavar="Q",
                     help="query rows per round (MTP verification: Q = MTP depth + 1); every "
                          "query selects its own top-K and the cache round runs on their union")
+    ap.add_argument("--replacement-probe", action="store_true",
+                    help="time the page's replacement probe instead: a full 32,768-slot hot "
+                         "cache with every reference bit set, then one 2,048-row step with 1%% "
+                         "misses, for LRU, circular and clock replacement")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 256 MiB device-to-device copy (reference for "
                          "scaling rocprofv3 FETCH_SIZE / WRITE_SIZE readings)")
@@ -171,6 +228,10 @@ def main():
     import torch
     from cache_gather_amd import hc
     from cache_gather_amd import workload as W
+
+    if args.replacement_probe:
+        print(json.dumps(replacement_probe(hc, W, np, torch)), flush=True)
+        return
 
     base = W.ALL[args.workload]
     total = args.warmup + args.steps

@@ -129,4 +129,114 @@ __device__ __forceinline__ void lru_victims(const DevState& d, int u, int32_t t,
   }
 }
 
+// Hand-based victims of unit u at step t: circular (clock = false) or clock
+// with reference bits (clock = true).  Sequentially the hand walks the slots
+// from its position h, skipping slots used this step (`touched`); circular
+// takes every slot it reaches, clock clears and skips slots whose reference
+// bit is set and takes slots whose bit is clear.  In parallel: in circular
+// order from h, let A be the unpinned slots with a clear bit (all unpinned
+// slots for circular) and B those with a set bit.  The m victims are the first
+// m of A in that order, and if A is shorter, the first m - |A| of B (the
+// second revolution, after the first cleared every bit of B).  The hand stops
+// just past the last victim.  Clock's new bits: set for pinned slots and
+// victims (hits and fills), clear for every other slot the hand passed (all
+// of B in the second case), unchanged beyond.  The circular order is cut into
+// nwords + 1 pieces: the word holding h from h on, the following words, and
+// that word's bits below h last.  `last` is LDS scratch of one int.
+__device__ __forceinline__ void hand_victims(const DevState& d, int u, int m, bool clock,
+                                             const uint32_t* touched, int32_t* vic,
+                                             int32_t* wtot, int32_t* last) {
+  const int C = d.C, tid = threadIdx.x;
+  const int nwords = (C + 31) >> 5, npieces = nwords + 1;
+  int32_t* hand = d.cnt + (size_t)u * d.Q * kCnt + kCntHand;
+  uint32_t* ref = d.refbits + (size_t)u * nwords;
+  const int h = *hand, hw = h >> 5, hb = h & 31;
+  const int per = (npieces + kSelThreads - 1) / kSelThreads;
+  const int p0 = tid * per;
+  constexpr int kMaxPer = (HC_MAX_SLOTS / 32 + 1 + kSelThreads - 1) / kSelThreads;  // 9
+  uint32_t pa[kMaxPer], pb[kMaxPer], pm[kMaxPer];
+  int pw[kMaxPer];
+  int ca = 0, cb = 0;
+#pragma unroll
+  for (int i = 0; i < kMaxPer; ++i) {
+    const int p = p0 + i;
+    pa[i] = pb[i] = pm[i] = 0;
+    pw[i] = 0;
+    if (i >= per || p >= npieces) continue;
+    const int w = p < nwords ? (hw + p) % nwords : hw;
+    uint32_t mk = 0xFFFFFFFFu;
+    if (w == nwords - 1 && (C & 31)) mk &= (1u << (C & 31)) - 1u;
+    if (p == 0) mk &= ~((1u << hb) - 1u);
+    if (p == nwords) mk &= (1u << hb) - 1u;
+    const uint32_t avail = ~touched[w] & mk;
+    const uint32_t r = clock ? ref[w] : 0u;
+    pw[i] = w;
+    pm[i] = mk;
+    pa[i] = avail & ~r;
+    pb[i] = avail & r;
+    ca += __popc(pa[i]);
+    cb += __popc(pb[i]);
+  }
+  int a_tot, b_tot = 0;
+  const int a_ex = block_incl_scan(ca, wtot, a_tot) - ca;
+  int b_ex = 0;
+  if (clock) b_ex = block_incl_scan(cb, wtot, b_tot) - cb;
+  const int mA = m < a_tot ? m : a_tot;   // victims of the first revolution
+  const int mB = m - mA;                  // of the second (clock only)
+  if (tid == 0) *last = -1;
+  __syncthreads();
+  uint32_t vbits[kMaxPer];
+  int ra = a_ex, rb = b_ex;
+#pragma unroll
+  for (int i = 0; i < kMaxPer; ++i) {
+    vbits[i] = 0;
+    uint32_t bits = pa[i];
+    while (bits && ra < mA) {
+      const int b = __ffs(bits) - 1;
+      bits &= bits - 1;
+      const int v = pw[i] * 32 + b;
+      vic[ra] = v;
+      vbits[i] |= 1u << b;
+      if (ra == m - 1) *last = v;
+      ++ra;
+    }
+    bits = pb[i];
+    while (bits && rb < mB) {
+      const int b = __ffs(bits) - 1;
+      bits &= bits - 1;
+      const int v = pw[i] * 32 + b;
+      vic[mA + rb] = v;
+      vbits[i] |= 1u << b;
+      if (mA + rb == m - 1) *last = v;
+      ++rb;
+    }
+  }
+  __syncthreads();
+  const int vl = *last;
+  if (m > 0 && tid == 0) *hand = (vl + 1) % C;
+  if (!clock) return;
+  // new reference bits of this thread's pieces (the hand's word is split over
+  // two pieces, so each piece changes only its own bits)
+  const int cl = m > 0 ? (vl - h + C) % C : -1;   // circular position of the last victim
+#pragma unroll
+  for (int i = 0; i < kMaxPer; ++i) {
+    if (!pm[i]) continue;
+    const uint32_t pinned = touched[pw[i]] & pm[i];
+    uint32_t keep = 0;   // bits of B the hand did not pass
+    if (m == 0) {
+      keep = pb[i];
+    } else if (mB == 0) {
+      uint32_t bits = pb[i];
+      while (bits) {
+        const int b = __ffs(bits) - 1;
+        bits &= bits - 1;
+        if ((pw[i] * 32 + b - h + C) % C > cl) keep |= 1u << b;
+      }
+    }
+    const uint32_t nb = pinned | vbits[i] | keep;
+    atomicAnd(&ref[pw[i]], ~pm[i]);
+    atomicOr(&ref[pw[i]], nb);
+  }
+}
+
 }  // namespace hc

@@ -27,7 +27,7 @@ constexpr uint64_t kAlign = 256;
 
 struct Layout {
   uint64_t pos2slot, slot2pos, last_use, order, cnt, above, cand, sel_slot, miss_pos,
-      victim, miss_idx, host_tab, hot, ring, total;
+      victim, miss_idx, host_tab, hot, ring, refbits, total;
 };
 
 // Sizes of hc_config before the recent-ring fields and before `queries` were
@@ -66,6 +66,7 @@ bool valid_config(const hc_config* c) {
   // positions < 2^31 - 2^19 keep -(C + 1 + position) inside int32
   if (c->max_positions < c->top_k || c->max_positions > (1ull << 31) - (1ull << 19)) return false;
   if (c->flags != 0) return false;
+  if (c->replacement > HC_REPLACE_CLOCK) return false;
   const uint64_t layers = (uint64_t)c->n_sessions * c->n_layers;
   if (layers * c->queries > 60000) return false;  // one gather grid row per layer and query
   const uint64_t G = (c->n_layers + c->layers_per_select - 1) / c->layers_per_select;
@@ -99,6 +100,7 @@ Layout layout_of(const hc_config* c) {
   lo.host_tab = take(S * L * 8);
   lo.hot = take(S * L * C * kSlotStride);
   lo.ring = take(S * L * (uint64_t)c->ring_rows * kRow);
+  lo.refbits = take(U * ((C + 31) / 32) * 4);
   lo.total = align_up(off);
   return lo;
 }
@@ -131,6 +133,8 @@ __global__ void k_init(DevState d, int64_t n_pos, int64_t n_slots) {
   for (int64_t i = i0; i < sel_units * d.K; i += stride) d.sel_slot[i] = 0;
   for (int64_t i = i0; i < sel_units * kCnt; i += stride)
     d.cnt[i] = (i % kCnt) == kCntBin1 ? -1 : 0;
+  const int64_t ref_words = (int64_t)d.S * d.G * ((d.C + 31) / 32);
+  for (int64_t i = i0; i < ref_words; i += stride) d.refbits[i] = 0;
 }
 
 }  // namespace
@@ -297,6 +301,8 @@ hc_status hc_create(const hc_config* cfg_in, void* dev_workspace, uint64_t ws_by
   d.hot = w + lo.hot;
   d.ring = w + lo.ring;
   d.ring_rows = (int32_t)cfg->ring_rows;
+  d.policy = (int32_t)cfg->replacement;
+  d.refbits = reinterpret_cast<uint32_t*>(w + lo.refbits);
 
   if (st == HC_OK &&
       hipMemcpy(w + lo.host_tab, dev_ptrs.data(), dev_ptrs.size() * sizeof(void*),

@@ -18,9 +18,10 @@ constexpr int kMaxSessions = HC_MAX_SESSIONS;  // session lengths travel as kern
 constexpr int kScanChunk = 8192;          // scores per workgroup in the scan kernels
 constexpr int kMaxUnits = HC_MAX_UNITS;   // S * G: the per-unit miss prefix lives in LDS
 
-// Per-unit counters (int32 each): unit u owns cnt[u * kCnt .. +kCnt).
-// kCntBin1 is the cut bin of the unit's previous step (-1 before the first).
-enum { kCntAbove = 0, kCntCand = 1, kCntMiss = 2, kCntBin1 = 3, kCnt = 4 };
+// Per-selection-unit counters (int32 each): unit su owns cnt[su * kCnt .. +kCnt).
+// kCntBin1 is the cut bin of the unit's previous step (-1 before the first);
+// kCntMiss and kCntHand (circular / clock hand) are kept at su = u * Q.
+enum { kCntAbove = 0, kCntCand = 1, kCntMiss = 2, kCntBin1 = 3, kCntHand = 4, kCnt = 5 };
 
 // Device view of the caller's workspace.  Unit u = s * G + g; layer index
 // sl = s * L + l.  All arrays are carved from one allocation (see hc_ctx.hip).
@@ -45,6 +46,8 @@ struct DevState {
   uint8_t* hot;        // [S*L][C][kSlotStride], a row in the first 656 B of its slot
   uint8_t* ring;       // [S*L][ring_rows][kRow] recent ring; position p at p % ring_rows
   int32_t ring_rows;   // 0: no ring
+  int32_t policy;      // HC_REPLACE_LRU, HC_REPLACE_CIRCULAR or HC_REPLACE_CLOCK
+  uint32_t* refbits;   // [U][ceil(C / 32)] clock reference bits
 };
 
 struct StepArgs {

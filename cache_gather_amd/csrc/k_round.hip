@@ -192,7 +192,10 @@ __global__ __launch_bounds__(kSelThreads) void k_round(DevState d, StepArgs a,
   block_incl_scan(my_miss, sh.wtot, m);
 
   // ---- 4. LRU victims ------------------------------------------------------
-  lru_victims(d, u, t, m, n - n_ring, touched, sh.vic, sh.wtot);
+  if (d.policy == HC_REPLACE_LRU)
+    lru_victims(d, u, t, m, n - n_ring, touched, sh.vic, sh.wtot);
+  else
+    hand_victims(d, u, m, d.policy == HC_REPLACE_CLOCK, touched, sh.vic, sh.wtot, &sh.wmin);
 
   // ---- 5. apply (miss, victim) pairs in ascending position order ----------
   int32_t* tr = d_trace ? d_trace + (size_t)u * HC_TRACE_INTS(QK) : nullptr;

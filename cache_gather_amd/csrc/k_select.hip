@@ -372,7 +372,11 @@ __global__ __launch_bounds__(kSelThreads) void k_select(DevState d, StepArgs a,
   }
 
   // ---- 4. LRU victims: first m untouched entries of the order list --------
-  lru_victims(d, u, t, m, K - n_ring, sh.u.lru.touched, sh.u.lru.vic, sh.wtot);
+  if (d.policy == HC_REPLACE_LRU)
+    lru_victims(d, u, t, m, K - n_ring, sh.u.lru.touched, sh.u.lru.vic, sh.wtot);
+  else
+    hand_victims(d, u, m, d.policy == HC_REPLACE_CLOCK, sh.u.lru.touched, sh.u.lru.vic, sh.wtot,
+                 &sh.bcast[0]);
 
   // ---- 5. apply (miss, victim) pairs --------------------------------------
   // A miss row is marked in sel_slot as -(slot + 1): the gather then reads it

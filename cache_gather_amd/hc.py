@@ -45,18 +45,21 @@ class hc_config(ctypes.Structure):
                 ("cache_slots", ctypes.c_uint32), ("top_k", ctypes.c_uint32),
                 ("max_positions", ctypes.c_uint64), ("device", ctypes.c_int32),
                 ("flags", ctypes.c_uint32), ("ring_rows", ctypes.c_uint32),
-                ("copyback_rows", ctypes.c_uint32), ("queries", ctypes.c_uint32)]
+                ("copyback_rows", ctypes.c_uint32), ("queries", ctypes.c_uint32),
+                ("replacement", ctypes.c_uint32)]
 
 
 CONFIG_SIZE_NO_RING = hc_config.ring_rows.offset
 CONFIG_SIZE_ONE_QUERY = hc_config.queries.offset
+LRU, CIRCULAR, CLOCK = 0, 1, 2   # hc_config.replacement
 
 
 def make_config(n_sessions, n_layers, layers_per_select, cache_slots, top_k, max_positions,
-                device=0, flags=0, ring_rows=0, copyback_rows=0, queries=1) -> hc_config:
+                device=0, flags=0, ring_rows=0, copyback_rows=0, queries=1,
+                replacement=LRU) -> hc_config:
     return hc_config(ctypes.sizeof(hc_config), n_sessions, n_layers, layers_per_select,
                      cache_slots, top_k, max_positions, device, flags, ring_rows,
-                     copyback_rows, queries)
+                     copyback_rows, queries, replacement)
 
 
 _LIB = None
@@ -226,10 +229,12 @@ class HotCache:
     """
 
     def __init__(self, n_sessions, n_layers, layers_per_select, cache_slots, top_k,
-                 max_positions, device=0, ring_rows=0, copyback_rows=0, queries=1):
+                 max_positions, device=0, ring_rows=0, copyback_rows=0, queries=1,
+                 replacement=LRU):
         import torch
         self.cfg = make_config(n_sessions, n_layers, layers_per_select, cache_slots, top_k,
-                               max_positions, device, 0, ring_rows, copyback_rows, queries)
+                               max_positions, device, 0, ring_rows, copyback_rows, queries,
+                               replacement)
         self.Q = queries
         self.S, self.L, self.R = n_sessions, n_layers, layers_per_select
         self.G = -(-n_layers // layers_per_select)

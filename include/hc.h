@@ -20,8 +20,9 @@
  *   2. a lookup of each selected position in the group's slot map; hits get
  *      last_use = t;
  *   3. the i-th miss (ascending position) takes the i-th victim in ascending
- *      (last_use, slot) order among slots with last_use != t; the evicted
- *      position leaves the map;
+ *      (last_use, slot) order among slots with last_use != t (LRU; see
+ *      HC_REPLACE_* for the other policies); the evicted position leaves the
+ *      map;
  *   4. for every layer of the group, the missing rows are copied from pinned
  *      host RAM into the victim slots;
  *   5. every selected row is read from its hot slot and dequantised:
@@ -90,6 +91,18 @@ extern "C" {
 #define HC_MAX_ROUND_ROWS 8192 /* largest queries * top_k                   */
 #define HC_NO_APPEND     (~(uint64_t)0)  /* hc_append: this session appends nothing */
 
+/* hc_config.replacement.  LRU: the victim is the slot with the oldest
+ * last-use step, ties to the lowest slot.  The two policies of the page's
+ * section "GPU cache management has hazards too", as probes: CIRCULAR — a
+ * hand moves over the slots and takes the next slot not used in the current
+ * step; CLOCK — hits and fills set a slot's reference bit, the hand skips
+ * slots used in the current step, clears and skips set bits, and takes the
+ * first slot with a clear bit.  Hands start at slot 0 and stop just past
+ * their last victim; misses are served in ascending position order. */
+#define HC_REPLACE_LRU      0
+#define HC_REPLACE_CIRCULAR 1
+#define HC_REPLACE_CLOCK    2
+
 /* Per-unit trace record: HC_TRACE_INTS(Q * K) int32 values per (session,
  * group), units ordered u = s * G + g, describing the round's selection
  * union (for Q = 1, the selection itself; N = n_hit + n_miss + n_ring entries
@@ -145,6 +158,7 @@ typedef struct hc_config {
                                  Q <= HC_MAX_QUERIES, Q * K <= HC_MAX_ROUND_ROWS,
                                  Q * K <= C; the struct without this field
                                  (48 B) means Q = 1                             */
+  uint32_t replacement;       /* HC_REPLACE_* (0 = LRU)                         */
 } hc_config;
 
 typedef struct hc_ctx hc_ctx;

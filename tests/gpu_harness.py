@@ -25,7 +25,8 @@ def align4(n):
 
 
 class Pair:
-    def __init__(self, wl: W.Workload, score_stride=None, rows_fn=None, device=0, queries=1):
+    def __init__(self, wl: W.Workload, score_stride=None, rows_fn=None, device=0, queries=1,
+                 replacement=0):
         self.wl = wl
         self.Q = queries
         self.dev = torch.device("cuda", device)
@@ -34,7 +35,8 @@ class Pair:
             wl.hist0, wl.steps))
         self.stride = align4(wl.hcap) if score_stride is None else score_stride
         self.hc = hc.HotCache(wl.n_sessions, wl.n_layers, wl.layers_per_select,
-                              wl.cache_slots, wl.top_k, wl.hcap, device, queries=queries)
+                              wl.cache_slots, wl.top_k, wl.hcap, device, queries=queries,
+                              replacement=replacement)
         t0 = time.time()
         self.rows = [[None] * wl.n_layers for _ in range(wl.n_sessions)]
         for s in range(wl.n_sessions):
@@ -44,7 +46,8 @@ class Pair:
                 np.copyto(self.hc.host_rows(s, l), r)
         say("rows ready in %.1fs" % (time.time() - t0))
         self.orc = oracle.Model(wl.n_sessions, wl.n_layers, wl.layers_per_select, wl.top_k,
-                                wl.cache_slots, wl.hcap, self.rows, queries=queries)
+                                wl.cache_slots, wl.hcap, self.rows, queries=queries,
+                                replacement=replacement)
         self.scores = W.Scores(wl)
         self.out, self.sel, self.trace = self.hc.alloc_outputs(trace=True)
         self.d_scores = torch.empty((wl.n_units * queries, self.stride), dtype=torch.float32,
