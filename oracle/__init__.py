@@ -45,6 +45,9 @@ def lib():
         L.orc_dequant_elem.restype = ctypes.c_uint16
         L.orc_dequant_row.argtypes = [_u8p, _u16p]
         L.orc_dequant_row.restype = None
+        L.orc_attend.argtypes = [_u16p, _u16p, ctypes.c_int32, ctypes.c_int32, ctypes.c_double,
+                                 ctypes.POINTER(ctypes.c_double)]
+        L.orc_attend.restype = None
         L.orc_dequant_table.argtypes = [_u16p]
         L.orc_dequant_table.restype = None
         L.orc_cache_new.argtypes = [ctypes.c_int32, ctypes.c_int64]
@@ -112,6 +115,19 @@ def dequant_row(row):
     assert r.size == ROW_BYTES
     out = np.empty(OUT_ELEMS, dtype=np.uint16)
     lib().orc_dequant_row(_ptr(r, _u8p), _ptr(out, _u16p))
+    return out
+
+
+def attend(q, rows, scale):
+    """MLA decode attention: q uint16 bf16 bits [H, 576], rows uint16 bf16
+    bits [K, 576] -> float64 [H, 512]."""
+    q = np.ascontiguousarray(q, dtype=np.uint16)
+    rows = np.ascontiguousarray(rows, dtype=np.uint16)
+    H, K = q.shape[0], rows.shape[0]
+    assert q.shape[1] == OUT_ELEMS and rows.shape[1] == OUT_ELEMS
+    out = np.empty((H, 512), np.float64)
+    lib().orc_attend(_ptr(q, _u16p), _ptr(rows, _u16p), H, K, float(scale),
+                     out.ctypes.data_as(ctypes.POINTER(ctypes.c_double)))
     return out
 
 

@@ -208,6 +208,50 @@ const uint8_t* orc_ring_row(const orc_ring* r, int64_t p) {
 
 int64_t orc_ring_copied(const orc_ring* r) { return r->first < 0 ? 0 : r->copied; }
 
+/* ------------------------------------------------------------ attention -- */
+
+/* Value of a bfloat16 bit pattern (the upper half of an IEEE binary32). */
+static double bf16_value(uint16_t b) {
+  uint32_t u = (uint32_t)b << 16;
+  float f;
+  memcpy(&f, &u, sizeof f);
+  return (double)f;
+}
+
+/* MLA decode attention over K gathered rows, in double precision.  For each
+ * head h: z_i = scale * sum over all 576 values of q[h] * row_i, weights =
+ * softmax(z) (largest score subtracted first), out[h][d] = sum_i w_i *
+ * row_i[d] for the 512 latent values. */
+void orc_attend(const uint16_t* q, const uint16_t* rows, int32_t H, int32_t K, double scale,
+                double* out) {
+  double* z = (double*)malloc((size_t)K * sizeof(double));
+  if (!z) return;
+  for (int32_t h = 0; h < H; ++h) {
+    const uint16_t* qh = q + (size_t)h * ORC_OUT_ELEMS;
+    double zmax = -INFINITY;
+    for (int32_t i = 0; i < K; ++i) {
+      const uint16_t* x = rows + (size_t)i * ORC_OUT_ELEMS;
+      double acc = 0.0;
+      for (int d = 0; d < ORC_OUT_ELEMS; ++d) acc += bf16_value(qh[d]) * bf16_value(x[d]);
+      z[i] = scale * acc;
+      if (z[i] > zmax) zmax = z[i];
+    }
+    double sum = 0.0;
+    for (int32_t i = 0; i < K; ++i) {
+      z[i] = exp(z[i] - zmax);
+      sum += z[i];
+    }
+    double* oh = out + (size_t)h * 512;
+    for (int d = 0; d < 512; ++d) oh[d] = 0.0;
+    for (int32_t i = 0; i < K; ++i) {
+      const uint16_t* x = rows + (size_t)i * ORC_OUT_ELEMS;
+      const double w = z[i] / sum;
+      for (int d = 0; d < 512; ++d) oh[d] += w * bf16_value(x[d]);
+    }
+  }
+  free(z);
+}
+
 /* ------------------------------------------------------------ LRU cache -- */
 
 struct orc_cache {

@@ -69,6 +69,14 @@ const uint8_t* orc_ring_row(const orc_ring* r, int64_t p);
 /* Host row frontier without copying (0 before the first append). */
 int64_t orc_ring_copied(const orc_ring* r);
 
+/* MLA decode attention over K gathered rows (the consumer of the gather):
+ * q [H][576] and rows [K][576] are bf16 bit patterns (rows as the gather
+ * writes them: 512 dequantised latent values, 64 RoPE values).  For each head
+ * h: z_i = scale * <q[h], row_i> over all 576 values, w = softmax(z),
+ * out[h][d] = sum_i w_i * row_i[d] for the 512 latent values (double). */
+void orc_attend(const uint16_t* q, const uint16_t* rows, int32_t H, int32_t K, double scale,
+                double* out);
+
 /* LRU hot cache of one (session, layer). */
 typedef struct orc_cache orc_cache;
 

@@ -68,6 +68,15 @@ MUTANTS = {
     "clock_bits_not_cleared": ("    if (c->ref[v]) {\n      c->ref[v] = 0;\n      continue;",
                                "    if (c->ref[v]) {\n      continue;",
                                "test_oracle_replacement.py"),
+    # attention: the RoPE values left out of the scores
+    "attend_scores_without_rope": ("      for (int d = 0; d < ORC_OUT_ELEMS; ++d) acc += bf16_value(qh[d]) * bf16_value(x[d]);",
+                                   "      for (int d = 0; d < 512; ++d) acc += bf16_value(qh[d]) * bf16_value(x[d]);",
+                                   "test_oracle_attend.py"),
+    # attention: exponentials taken without subtracting the largest score
+    "attend_no_max_shift": ("      z[i] = exp(z[i] - zmax);", "      z[i] = exp(z[i]);",
+                            "test_oracle_attend.py"),
+    # attention: the softmax scale not applied
+    "attend_scale_ignored": ("      z[i] = scale * acc;", "      z[i] = acc;", "test_oracle_attend.py"),
     # gather: RoPE read two bytes early
     "rope_offset": ("out[512 + k] = (uint16_t)(row[528 + 2 * k] | (row[528 + 2 * k + 1] << 8));",
                     "out[512 + k] = (uint16_t)(row[526 + 2 * k] | (row[526 + 2 * k + 1] << 8));",
