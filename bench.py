@@ -210,6 +210,10 @@ def main():
                     help="time the page's replacement probe instead: a full 32,768-slot hot "
                          "cache with every reference bit set, then one 2,048-row step with 1%% "
                          "misses, for LRU, circular and clock replacement")
+    ap.add_argument("--attend", type=int, default=0, metavar="HEADS",
+                    help="follow every step with MLA decode attention of HEADS heads over the "
+                         "selected rows, once through the bf16 buffer and once fused (the step "
+                         "skips the buffer, attention reads the slots)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 256 MiB device-to-device copy (reference for "
                          "scaling rocprofv3 FETCH_SIZE / WRITE_SIZE readings)")
@@ -271,7 +275,16 @@ def main():
     log("scores for %d steps resident in HBM (%.2f GiB) in %.1fs" % (
         total, d_scores.numel() * 4 / 2 ** 30, time.time() - t0))
 
-    def run_pass(kernel_events):
+    att = None
+    if args.attend:
+        import math
+        d_q = torch.empty((total,) + W.queries(wl, 0, args.attend, Q).shape, dtype=torch.int16,
+                          device=dev)
+        for t in range(total):
+            d_q[t].copy_(torch.from_numpy(W.queries(wl, t, args.attend, Q).view(np.int16)))
+        att = {"heads": args.attend, "scale": 1.0 / math.sqrt(576.0), "q": d_q}
+
+    def run_pass(kernel_events, variant=None):
         """A fresh context over the same inputs: cold step, warmup, then the
         timed steps.  With kernel_events, HIP events bracket every kernel of the
         timed steps on the step's stream (they add a few us per kernel, so the
@@ -292,7 +305,18 @@ def main():
         append_ev = ([(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                       for _ in range(total)] if args.ring and kernel_events else None)
 
+        if variant:
+            work, att_out = cache.attention_buffers(att["heads"])
+
         def step(t):
+            if variant == "fused":
+                cache.step(d_scores[t], stride, wl.hist_len(t), None, sel, trace[t])
+                cache.attend_cached(att["q"][t], att["heads"], att["scale"], work, att_out)
+                return
+            if variant == "buffer":
+                cache.step(d_scores[t], stride, wl.hist_len(t), out, sel, trace[t])
+                cache.attend(att["q"][t], att["heads"], att["scale"], out, work, att_out)
+                return
             if args.ring:
                 timed_append = append_ev is not None and t >= args.warmup
                 if timed_append:
@@ -341,6 +365,24 @@ def main():
         del out, sel, trace
         return res
 
+    if att:
+        res_att = {}
+        for variant in ("buffer", "fused"):
+            r = run_pass(False, variant)
+            res_att[variant] = {"ms_per_step": round(r["elapsed"] * 1e3 / args.steps, 5)}
+        heads = att["heads"]
+        rows = S * L * Q * K
+        flops = 2.0 * rows * heads * (576 + 512)
+        for v in res_att.values():
+            v["attention_tflops_incl_step"] = round(flops / (v["ms_per_step"] * 1e-3) / 1e12, 2)
+        print(json.dumps({
+            "metric": "decode step + MLA attention over the selected rows (ms per step)",
+            "unit": "ms", "higher_is_better": False, "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "dtype": "bf16 (fp32 accumulate)", "data": "synthetic",
+            "config": {"workload": wl.name, "heads": heads, "queries": Q, "top_k": K,
+                       "layers": L, "attention_gflop_per_step": round(flops / 1e9, 2)},
+            "variants": res_att}), flush=True)
+        return
     timed = run_pass(False)
     kernels_pass = run_pass(True)
     elapsed = timed["elapsed"]

@@ -13,7 +13,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libhc.so")
-SOURCES = ["hc_ctx.hip", "k_topk.hip", "k_select.hip", "k_gather.hip", "k_ring.hip", "k_round.hip"]
+SOURCES = ["hc_ctx.hip", "k_topk.hip", "k_select.hip", "k_gather.hip", "k_ring.hip", "k_round.hip", "k_attend.hip"]
 ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 CFLAGS = [

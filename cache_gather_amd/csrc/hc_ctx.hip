@@ -329,7 +329,7 @@ hc_status hc_step(hc_ctx* c, void* stream, const float* d_scores, uint64_t score
                   const uint64_t* hist_len, uint16_t* d_out, int32_t* d_sel, int32_t* d_trace) {
   if (!c) return HC_E_INVAL;
   if (c->poisoned) return HC_E_STATE;
-  if (!d_scores || !hist_len || !d_out || !d_sel) return HC_E_INVAL;
+  if (!d_scores || !hist_len || !d_sel) return HC_E_INVAL;   // d_out may be NULL
   const uint32_t S = c->cfg.n_sessions;
   uint64_t max_len = 0;
   for (uint32_t s = 0; s < S; ++s) {
@@ -437,6 +437,46 @@ hc_status hc_flush(hc_ctx* c, void* stream, uint64_t* host_count) {
     if (c->first[s] >= 0 && n != (uint64_t)c->end[s]) r = HC_E_CONSISTENCY;
   }
   return r;
+}
+
+hc_status hc_attend_workspace_bytes(const hc_ctx* c, uint32_t heads, uint64_t* bytes) {
+  if (!c || !bytes || heads == 0 || heads % 64 || heads > 4096) return HC_E_INVAL;
+  *bytes = attend_work_bytes(c->dev, (int)heads);
+  return HC_OK;
+}
+
+namespace {
+
+hc_status attend(hc_ctx* c, void* stream, bool from_slots, const uint16_t* d_q, uint32_t heads,
+                 float scale, const uint16_t* d_rows, void* d_work, uint64_t work_bytes,
+                 float* d_out) {
+  if (!c) return HC_E_INVAL;
+  if (c->poisoned) return HC_E_STATE;
+  if (!d_q || !d_work || !d_out || (!from_slots && !d_rows)) return HC_E_INVAL;
+  if (heads == 0 || heads % 64 || heads > 4096) return HC_E_INVAL;
+  if (reinterpret_cast<uintptr_t>(d_q) % 16 || (d_rows && reinterpret_cast<uintptr_t>(d_rows) % 16))
+    return HC_E_INVAL;
+  if (work_bytes < attend_work_bytes(c->dev, (int)heads)) return HC_E_NOMEM;
+  if (c->t == 0) return HC_E_INVAL;   // no step has selected rows yet
+  DeviceGuard dg(c->cfg.device);
+  if (!dg.ok) return HC_E_INVAL;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e = launch_attend(c->dev, from_slots, d_q, (int)heads, scale, d_rows, d_work, d_out, st);
+  if (e == hipSuccess) e = hipEventRecord(c->done, st);
+  c->enqueued = true;
+  return e == hipSuccess ? HC_OK : fail_hip(c);
+}
+
+}  // namespace
+
+hc_status hc_attend(hc_ctx* c, void* stream, const uint16_t* d_q, uint32_t heads, float scale,
+                    const uint16_t* d_rows, void* d_work, uint64_t work_bytes, float* d_out) {
+  return attend(c, stream, false, d_q, heads, scale, d_rows, d_work, work_bytes, d_out);
+}
+
+hc_status hc_attend_cached(hc_ctx* c, void* stream, const uint16_t* d_q, uint32_t heads,
+                           float scale, void* d_work, uint64_t work_bytes, float* d_out) {
+  return attend(c, stream, true, d_q, heads, scale, nullptr, d_work, work_bytes, d_out);
 }
 
 hc_status hc_export_state(hc_ctx* c, uint32_t session, uint32_t layer, int32_t* slot2pos,

@@ -102,8 +102,15 @@ hipError_t launch_select(const DevState& d, const StepArgs& a, const float* scor
                          uint64_t stride, int32_t* d_sel, int32_t* d_trace, hipStream_t st);
 hipError_t launch_round(const DevState& d, const StepArgs& a, const int32_t* d_sel,
                         int32_t* d_trace, hipStream_t st);
+// d_out == nullptr: only the missing rows are fetched into their slots.
 hipError_t launch_gather(const DevState& d, uint16_t* d_out, hipStream_t st);
 hipError_t launch_append(const DevState& d, const AppendArgs& a, const uint8_t* d_rows,
+                         hipStream_t st);
+// Attention over the last step's selection: rows from the gathered bf16
+// buffer, or (from_slots) straight from the slots / ring / host RAM.
+uint64_t attend_work_bytes(const DevState& d, int heads);
+hipError_t launch_attend(const DevState& d, bool from_slots, const uint16_t* q, int heads,
+                         float scale, const uint16_t* rows, void* work, float* out,
                          hipStream_t st);
 // Copies the rows and then writes hi[s] into host_count[s] (device pointer of
 // pinned host memory) for every session with rows to copy.

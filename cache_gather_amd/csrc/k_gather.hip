@@ -90,17 +90,18 @@ __device__ __forceinline__ void run_rows(const RowJob& j, int item) {
   const int off = item < 32 ? 16 * item : HC_ROPE_OFFSET + 16 * (item - 32);
 #pragma unroll
   for (int p = 0; p < kPasses; ++p) {
-    if (!j.dst[p]) continue;
+    if (!j.dst[p] && !j.fill[p]) continue;
     v[p] = *reinterpret_cast<const u32x4*>(j.src[p] + off);
     if (item < 32) sblk[p] = *reinterpret_cast<const u32x4*>(j.src[p] + HC_SCALE_OFFSET);
   }
 #pragma unroll
   for (int p = 0; p < kPasses; ++p) {
-    if (!j.dst[p]) continue;
+    if (!j.dst[p] && !j.fill[p]) continue;
     if (j.fill[p]) {
       *reinterpret_cast<u32x4*>(j.fill[p] + off) = v[p];
       if (item == 0) *reinterpret_cast<u32x4*>(j.fill[p] + HC_SCALE_OFFSET) = sblk[p];
     }
+    if (!j.dst[p]) continue;   // fill only: no gathered output
     if (item < 32) {
       const float sc = scale_of(sblk[p], item >> 2);
       const u32x4 q = v[p];
@@ -179,6 +180,7 @@ __global__ __launch_bounds__(kGatherThreads) void k_gather(DevState d,
       for (int p = 0; p < kPasses; ++p) {
         const int q = base + p * kRowsPerPass + lrow;
         j.dst[p] = nullptr;
+        j.fill[p] = nullptr;
         if (q >= M) continue;
         int lo = 0, hi = U;  // largest u with pref[u] <= q
         while (hi - lo > 1) {
@@ -195,7 +197,7 @@ __global__ __launch_bounds__(kGatherThreads) void k_gather(DevState d,
         const size_t uk = (size_t)u * QK + k;
         j.src[p] = d.host[sl] + (size_t)d.miss_pos[uk] * kRow;
         j.fill[p] = d.hot + ((size_t)sl * d.C + d.victim[uk]) * kSlotStride;
-        j.dst[p] = out_b + ((size_t)sl * QK + d.miss_idx[uk]) * out_row_bytes;
+        j.dst[p] = out ? out_b + ((size_t)sl * QK + d.miss_idx[uk]) * out_row_bytes : nullptr;
       }
       run_rows(j, item);
     }
@@ -235,8 +237,10 @@ hipError_t launch_gather(const DevState& d, uint16_t* d_out, hipStream_t st) {
   const int gx = (d.K + kRowsPerRound - 1) / kRowsPerRound;
   const int miss_rows = (kMissBlocks + gx - 1) / gx;
   const size_t lds = ((size_t)d.S * d.G + 1) * sizeof(int32_t);
-  hipLaunchKernelGGL(k_gather, dim3(gx, d.S * d.L * d.Q + miss_rows), dim3(kGatherThreads), lds,
-                     st, d, d_out, miss_rows);
+  // without an output buffer only the miss workgroups run (they fill slots)
+  const int rows = d_out ? d.S * d.L * d.Q + miss_rows : miss_rows;
+  hipLaunchKernelGGL(k_gather, dim3(gx, rows), dim3(kGatherThreads), lds, st, d, d_out,
+                     miss_rows);
   return hipGetLastError();
 }
 

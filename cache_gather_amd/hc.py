@@ -89,6 +89,14 @@ def lib():
     L.hc_append.restype = st
     L.hc_flush.argtypes = [_vp, _vp, _vp]
     L.hc_flush.restype = st
+    L.hc_attend_workspace_bytes.argtypes = [_vp, ctypes.c_uint32, ctypes.POINTER(ctypes.c_uint64)]
+    L.hc_attend_workspace_bytes.restype = st
+    L.hc_attend.argtypes = [_vp, _vp, _vp, ctypes.c_uint32, ctypes.c_float, _vp, _vp,
+                            ctypes.c_uint64, _vp]
+    L.hc_attend.restype = st
+    L.hc_attend_cached.argtypes = [_vp, _vp, _vp, ctypes.c_uint32, ctypes.c_float, _vp,
+                                   ctypes.c_uint64, _vp]
+    L.hc_attend_cached.restype = st
     L.hc_export_state.argtypes = [_vp, ctypes.c_uint32, ctypes.c_uint32, _vp, _vp, _vp, _vp]
     L.hc_export_state.restype = st
     L.hc_profile_enable.argtypes = [_vp, ctypes.c_uint32]
@@ -179,6 +187,24 @@ def hc_flush(ctx: int, stream, n_sessions: int, check=True):
     return r, counts
 
 
+def hc_attend_workspace_bytes(ctx: int, heads: int) -> int:
+    n = ctypes.c_uint64()
+    _check("hc_attend_workspace_bytes", lib().hc_attend_workspace_bytes(ctx, heads, ctypes.byref(n)))
+    return n.value
+
+
+def hc_attend(ctx: int, stream, d_q, heads: int, scale: float, d_rows, d_work, work_bytes: int,
+              d_out) -> None:
+    _check("hc_attend", lib().hc_attend(ctx, _ptr(stream), _ptr(d_q), heads, scale,
+                                        _ptr(d_rows), _ptr(d_work), work_bytes, _ptr(d_out)))
+
+
+def hc_attend_cached(ctx: int, stream, d_q, heads: int, scale: float, d_work, work_bytes: int,
+                     d_out) -> None:
+    _check("hc_attend_cached", lib().hc_attend_cached(ctx, _ptr(stream), _ptr(d_q), heads, scale,
+                                                      _ptr(d_work), work_bytes, _ptr(d_out)))
+
+
 def hc_export_state(ctx: int, session: int, layer: int, slots: int, max_positions: int,
                     pos2slot=False, hot_rows=False):
     slot2pos = np.empty(slots, np.int32)
@@ -264,6 +290,24 @@ class HotCache:
     def flush(self, stream=None):
         """(status, host row count per session) after the consistency boundary."""
         return hc_flush(self.ctx, self._stream(stream), self.S)
+
+    def attention_buffers(self, heads):
+        """(scratch, out fp32 [S, L, (Q,) heads, 512]) for hc_attend*."""
+        import torch
+        nbytes = hc_attend_workspace_bytes(self.ctx, heads)
+        work = torch.empty(nbytes, dtype=torch.uint8, device=self.device)
+        q = (self.Q,) if self.Q > 1 else ()
+        out = torch.empty((self.S, self.L) + q + (heads, 512), dtype=torch.float32,
+                          device=self.device)
+        return work, out
+
+    def attend(self, q, heads, scale, rows, work, out, stream=None):
+        """Attention over the last step's gathered bf16 rows."""
+        hc_attend(self.ctx, self._stream(stream), q, heads, scale, rows, work, work.numel(), out)
+
+    def attend_cached(self, q, heads, scale, work, out, stream=None):
+        """Attention reading the last step's rows from the slots (no bf16 buffer)."""
+        hc_attend_cached(self.ctx, self._stream(stream), q, heads, scale, work, work.numel(), out)
 
     def export_state(self, s, l, pos2slot=False, hot_rows=False):
         return hc_export_state(self.ctx, s, l, self.C, self.hcap, pos2slot, hot_rows)

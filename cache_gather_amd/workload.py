@@ -26,6 +26,9 @@ Recipe (all seeded; numpy PCG64 via default_rng with a tuple seed):
   above; query q > 0 adds its own draft noise, one more float32 add:
       sigma_draft * N(0,1) float32, H_t values, rng((seed, 4, s, g, q, t))
   so the Q selections overlap heavily without being equal.
+  Attention queries (the consumer of the gathered rows), per (s, l, t):
+      bf16 of N(0,1) float32 (torch float32 -> bfloat16), [Q][heads][576],
+      rng((seed, 5, s, l, t)).
 """
 from __future__ import annotations
 
@@ -213,3 +216,15 @@ class Scores:
         with ThreadPoolExecutor(_workers()) as ex:
             list(ex.map(one, range(wl.n_units * queries)))
         return out
+
+
+def queries(wl: Workload, t: int, heads: int, n_queries: int = 1) -> np.ndarray:
+    """bf16 bit patterns (uint16) [S, L, Q, heads, 576] of step t's attention
+    queries (or [S, L, heads, 576] for one query row)."""
+    out = np.empty((wl.n_sessions, wl.n_layers, n_queries, heads, 576), np.uint16)
+    for s in range(wl.n_sessions):
+        for l in range(wl.n_layers):
+            rng = np.random.default_rng((wl.seed, 5, s, l, t))
+            x = rng.standard_normal((n_queries, heads, 576), dtype=np.float32)
+            out[s, l] = _bf16_bits(x).view(np.uint16)
+    return out if n_queries > 1 else out[:, :, 0]

@@ -193,7 +193,9 @@ uint8_t* hc_host_rows(hc_ctx* ctx, uint32_t session, uint32_t layer);
  *                step; K <= hist_len[s] <= Hcap, never smaller than at the
  *                previous step, and at most the end of the appended
  *                positions once the session has appended.
- *   d_out        device bf16 bits [S][L][Q][K][576], rows in selection order.
+ *   d_out        device bf16 bits [S][L][Q][K][576], rows in selection order;
+ *                NULL: the step only fetches the missing rows into their slots
+ *                (no gathered output), for hc_attend_cached.
  *   d_sel        device int32 [S][G][Q][K]: selected positions, ascending.
  *   d_trace      NULL, or device int32 [S*G][HC_TRACE_INTS(Q*K)] (see above).
  * Asynchronous: results are valid once the stream has completed the step.
@@ -226,6 +228,30 @@ hc_status hc_append(hc_ctx* ctx, void* stream, const uint8_t* d_rows, const uint
  * that has not appended) into host_count[S] if non-NULL.  HC_OK if every
  * appended session's count equals its appended end, else HC_E_CONSISTENCY. */
 hc_status hc_flush(hc_ctx* ctx, void* stream, uint64_t* host_count);
+
+/* MLA decode attention over the last step's selection (the consumer of the
+ * gather; the page's data-flow figure of "Decision three": the compact
+ * selection feeds GPU attention).  For every session, layer, query row q and
+ * head h: z_i = scale * <query, row_i> over the 576 values of each selected
+ * row (512 latent + 64 RoPE, as the gather writes them), w = softmax(z) over
+ * the K rows, out = sum_i w_i * (the row's 512 latent values).  bf16 matrix
+ * products on the matrix cores with fp32 accumulation; the softmax weights
+ * are rounded to bf16 for the second product.
+ *   d_q      device bf16 bits [S][L][Q][heads][576], 16-B aligned.
+ *   heads    a multiple of 64, at most 4096.
+ *   d_work   caller-owned device scratch of hc_attend_workspace_bytes(heads).
+ *   d_out    device fp32 [S][L][Q][heads][512].
+ * hc_attend reads the rows from d_rows, the bf16 [S][L][Q][K][576] output of
+ * the last hc_step; hc_attend_cached reads them from the hot slots, the recent
+ * ring and host RAM (a further query row of a miss), dequantising on the way,
+ * so a step with d_out = NULL plus hc_attend_cached never writes the bf16
+ * buffer.  Both give the same result bit for bit.  Asynchronous on `stream`;
+ * HC_E_INVAL before any hc_step; HC_E_NOMEM if work_bytes is too small. */
+hc_status hc_attend_workspace_bytes(const hc_ctx* ctx, uint32_t heads, uint64_t* bytes);
+hc_status hc_attend(hc_ctx* ctx, void* stream, const uint16_t* d_q, uint32_t heads, float scale,
+                    const uint16_t* d_rows, void* d_work, uint64_t work_bytes, float* d_out);
+hc_status hc_attend_cached(hc_ctx* ctx, void* stream, const uint16_t* d_q, uint32_t heads,
+                           float scale, void* d_work, uint64_t work_bytes, float* d_out);
 
 /* Synchronous snapshot for tests: waits for all enqueued steps, then copies
  * the state that layer `layer` of `session` sees into host buffers:

@@ -56,9 +56,12 @@ class Pair:
     def scores_for(self, t):
         return self.scores.step(t, self.stride, queries=self.Q)
 
+    fill_only = False   # steps without a gathered output (hc_step with d_out = NULL)
+
     def gpu_step(self, t, scores_np, hist_len):
         self.d_scores.copy_(torch.from_numpy(scores_np))
-        self.hc.step(self.d_scores, self.stride, hist_len, self.out, self.sel, self.trace)
+        self.hc.step(self.d_scores, self.stride, hist_len, None if self.fill_only else self.out,
+                     self.sel, self.trace)
 
     def step(self, t, scores_np=None, hist_len=None, gather=True, nthreads=16):
         """One step on both sides; returns (gpu dict, oracle tuple)."""
@@ -72,7 +75,7 @@ class Pair:
                                             gather=gather, nthreads=nthreads)
         torch.cuda.synchronize()
         g = {"sel": self.sel.cpu().numpy(), "trace": self.trace.cpu().numpy()}
-        if gather:
+        if gather and not self.fill_only:
             g["out"] = self.out.cpu().numpy().view(np.uint16)
         return g, (o_sel, o_out, o_inf)
 
@@ -97,7 +100,7 @@ class Pair:
                                               err_msg=msg)
                 np.testing.assert_array_equal(tr[base + 3 * K:base + 4 * K], info["evicted"],
                                               err_msg=msg)
-        if gather:
+        if gather and "out" in g:
             bad = np.argwhere(g["out"] != o_out)
             assert bad.size == 0, "output differs at step %d, first [s,l,i,j]=%s (%d values)" % (
                 t, bad[0].tolist(), bad.shape[0])
