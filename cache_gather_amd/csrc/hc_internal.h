@@ -15,7 +15,7 @@ constexpr int kOut = HC_OUT_ELEMS;        // 576 bf16 per gathered row
 constexpr int kBin1Bits = 12;             // first radix digit: key bits [20, 32)
 constexpr int kBins1 = 1 << kBin1Bits;    // 4096 histogram bins per unit
 constexpr int kMaxSessions = HC_MAX_SESSIONS;  // session lengths travel as kernel args
-constexpr int kScanChunk = 8192;          // scores per workgroup in the scan kernels
+constexpr int kScanChunk = 4096;          // scores per workgroup of the score scan (16 per thread)
 constexpr int kMaxUnits = HC_MAX_UNITS;   // S * G: the per-unit miss prefix lives in LDS
 
 // Per-selection-unit counters (int32 each): unit su owns cnt[su * kCnt .. +kCnt).

@@ -21,7 +21,7 @@
 // from one appended position), so the window almost always holds and a step
 // reads the history once.
 //
-// Grid = (chunks of 8,192 positions) x (selection units: one per query row of
+// Grid = (chunks of 4,096 positions) x (selection units: one per query row of
 // each session and group), 256 threads; HBM-bound streaming read of 4 B per
 // position.
 #include "hc_internal.h"
@@ -29,7 +29,7 @@
 namespace hc {
 
 constexpr int kScanThreads = 256;
-constexpr int kPerThread = kScanChunk / kScanThreads;  // 32 scores per thread
+constexpr int kPerThread = kScanChunk / kScanThreads;  // 16 scores per thread
 
 // Loads this thread's scores of the chunk: element j of the thread is position
 // base + pos[j]; positions >= n are invalid.
@@ -109,7 +109,7 @@ __global__ __launch_bounds__(kScanThreads) void k_topk_scan(DevState d, StepArgs
     na += ok && b > b_hi;
     nc += ok && b >= b_lo && b <= b_hi;
   }
-  // both counts fit 16 bits (at most 8,192 per block): scan them packed
+  // both counts fit 16 bits (at most 4,096 per block): scan them packed
   const int packed = (na << 16) | nc;
   const int pincl = block_incl_scan256(packed, wtot);
   if (tid == kScanThreads - 1) {
