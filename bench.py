@@ -221,8 +221,8 @@ def main():
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py runs on one GPU only: the decode step has no multi-GPU path "
-              "in this build (asked for --gpus %d, WORLD_SIZE=%d)" % (args.gpus, world),
+        print("bench.py measures one GPU; runs on several GPUs are not supported "
+              "(asked for --gpus %d, WORLD_SIZE=%d)" % (args.gpus, world),
               file=sys.stderr)
         sys.exit(2)
     if args.warmup < 1 or args.steps < 1:

@@ -148,7 +148,7 @@ __device__ __forceinline__ void hand_victims(const DevState& d, int u, int m, bo
                                              int32_t* wtot, int32_t* last) {
   const int C = d.C, tid = threadIdx.x;
   const int nwords = (C + 31) >> 5, npieces = nwords + 1;
-  int32_t* hand = d.cnt + (size_t)u * d.Q * kCnt + kCntHand;
+  int32_t* hand = d.cnt + (size_t)u * d.Q * kCntStride + kCntHand;
   uint32_t* ref = d.refbits + (size_t)u * nwords;
   const int h = *hand, hw = h >> 5, hb = h & 31;
   const int per = (npieces + kSelThreads - 1) / kSelThreads;

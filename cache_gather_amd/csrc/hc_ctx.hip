@@ -90,7 +90,7 @@ Layout layout_of(const hc_config* c) {
   lo.slot2pos = take(U * C * 4);
   lo.last_use = take(U * C * 4);
   lo.order = take(U * 2 * C * 4);
-  lo.cnt = take(SU * kCnt * 4);
+  lo.cnt = take(SU * kCntStride * 4);
   lo.above = take(SU * K * 4);
   lo.cand = take(SU * hcap * 8);
   lo.sel_slot = take(SU * K * 4);
@@ -131,8 +131,12 @@ __global__ void k_init(DevState d, int64_t n_pos, int64_t n_slots) {
   }
   const int64_t sel_units = (int64_t)d.S * d.G * d.Q;
   for (int64_t i = i0; i < sel_units * d.K; i += stride) d.sel_slot[i] = 0;
-  for (int64_t i = i0; i < sel_units * kCnt; i += stride)
-    d.cnt[i] = (i % kCnt) == kCntBin1 ? -1 : 0;
+  for (int64_t i = i0; i < sel_units * kCntStride; i += stride)
+    d.cnt[i] = (i % kCntStride) == kCntBin1 ? -1 : 0;
+  // the first step's cut histograms (see launch_cold_cut)
+  if (d.hcap >= kColdMinPositions)
+    for (int64_t i = i0; i < sel_units * kBins1; i += stride)
+      reinterpret_cast<uint32_t*>(d.cand + (i / kBins1) * d.hcap)[i % kBins1] = 0u;
   const int64_t ref_words = (int64_t)d.S * d.G * ((d.C + 31) / 32);
   for (int64_t i = i0; i < ref_words; i += stride) d.refbits[i] = 0;
 }
@@ -363,6 +367,8 @@ hc_status hc_step(hc_ctx* c, void* stream, const float* d_scores, uint64_t score
   auto mark = [&](int i) { return prof ? hipEventRecord(ev[i], st) : hipSuccess; };
 
   hipError_t e = mark(0);
+  if (e == hipSuccess && c->t == 0 && c->dev.hcap >= kColdMinPositions)
+    e = launch_cold_cut(c->dev, a, d_scores, score_stride, (int64_t)max_len, st);
   if (e == hipSuccess) e = launch_topk_scan(c->dev, a, d_scores, score_stride, n_chunks, vec4, st);
   if (e == hipSuccess) e = mark(1);
   if (e == hipSuccess) e = launch_select(c->dev, a, d_scores, score_stride, d_sel, d_trace, st);

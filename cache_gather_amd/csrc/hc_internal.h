@@ -18,10 +18,16 @@ constexpr int kMaxSessions = HC_MAX_SESSIONS;  // session lengths travel as kern
 constexpr int kScanChunk = 4096;          // scores per workgroup of the score scan (16 per thread)
 constexpr int kMaxUnits = HC_MAX_UNITS;   // S * G: the per-unit miss prefix lives in LDS
 
-// Per-selection-unit counters (int32 each): unit su owns cnt[su * kCnt .. +kCnt).
-// kCntBin1 is the cut bin of the unit's previous step (-1 before the first);
-// kCntMiss and kCntHand (circular / clock hand) are kept at su = u * Q.
+// Per-selection-unit counters (int32 each): unit su owns cnt[su * kCntStride ..
+// + kCnt).  kCntBin1 is the cut bin of the unit's previous step (-1 before the
+// first); kCntMiss and kCntHand (circular / clock hand) are kept at su = u * Q.
+// kCntAbove and kCntCand form one 8-byte word that every scan workgroup bumps
+// with a single atomic; each unit's counters sit on a 256-byte line of their
+// own, because atomics on neighbouring addresses queue behind each other
+// (measured: 16 units x 257 workgroups took 58 us packed, 20 us spread, 13 us
+// without atomics).
 enum { kCntAbove = 0, kCntCand = 1, kCntMiss = 2, kCntBin1 = 3, kCntHand = 4, kCnt = 5 };
+constexpr int kCntStride = 64;
 
 // Device view of the caller's workspace.  Unit u = s * G + g; layer index
 // sl = s * L + l.  All arrays are carved from one allocation (see hc_ctx.hip).
@@ -33,7 +39,7 @@ struct DevState {
   int32_t* slot2pos;   // [U][C]     position held by a slot, -1 if empty
   int32_t* last_use;   // [U][C]     step of the slot's last use, -1 if never
   int32_t* order;      // [U][2][C]  slots in ascending (last_use, slot); ping-pong by step parity
-  int32_t* cnt;        // [U*Q][kCnt] per selection unit; the round's miss count at su = u*Q
+  int32_t* cnt;        // [U*Q][kCntStride] per selection unit; the round's miss count at su = u*Q
   int32_t* above;      // [U*Q][K]   positions whose top digit beats the cut bin
   uint2* cand;         // [U*Q][hcap] (key, position) of scores in the cut bin
   int32_t* sel_slot;   // [U*Q][K]   source of selected row i: slot, C + ring entry,
@@ -96,6 +102,11 @@ __device__ __forceinline__ void cut_window(int prev, uint32_t& lo, uint32_t& hi)
 hipError_t launch_init(const DevState& d, hipStream_t st);
 hipError_t launch_topk_scan(const DevState& d, const StepArgs& a, const float* scores,
                             uint64_t stride, int n_chunks, bool vec4, hipStream_t st);
+// First step only (needs hcap >= kColdMinPositions): sets every selection
+// unit's cut bin from a histogram of its scores.
+constexpr int64_t kColdMinPositions = 2048;   // the histogram borrows 16 KB of `cand`
+hipError_t launch_cold_cut(const DevState& d, const StepArgs& a, const float* scores,
+                           uint64_t stride, int64_t max_len, hipStream_t st);
 // Q == 1: the fused per-unit selection + cache kernel.  Q > 1: the top-K part
 // per selection unit, then launch_round per unit.
 hipError_t launch_select(const DevState& d, const StepArgs& a, const float* scores,

@@ -147,7 +147,7 @@ __global__ __launch_bounds__(kGatherThreads) void k_gather(DevState d,
     int running = 0;
     for (int u0 = 0; u0 < U; u0 += kGatherThreads) {
       const int u = u0 + threadIdx.x;
-      const int c = u < U ? d.cnt[(size_t)u * d.Q * kCnt + kCntMiss] * layers_in_group(d, u % d.G)
+      const int c = u < U ? d.cnt[(size_t)u * d.Q * kCntStride + kCntMiss] * layers_in_group(d, u % d.G)
                           : 0;
       // block inclusive scan of c
       int x = c;

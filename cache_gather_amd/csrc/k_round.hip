@@ -65,7 +65,7 @@ __global__ __launch_bounds__(kSelThreads) void k_round(DevState d, StepArgs a,
     // a query's selection was abandoned (inconsistent scan state): touch
     // nothing, the gather reads slot 0
     for (int e = tid; e < QK; e += kSelThreads) g_slot[e] = 0;
-    if (tid == 0) d.cnt[(size_t)u * Q * kCnt + kCntMiss] = 0;
+    if (tid == 0) d.cnt[(size_t)u * Q * kCntStride + kCntMiss] = 0;
     return;
   }
 
@@ -267,7 +267,7 @@ __global__ __launch_bounds__(kSelThreads) void k_round(DevState d, StepArgs a,
       tr[3] = n_ring;
     }
   }
-  if (tid == 0) d.cnt[(size_t)u * Q * kCnt + kCntMiss] = m;
+  if (tid == 0) d.cnt[(size_t)u * Q * kCntStride + kCntMiss] = m;
 }
 
 hipError_t launch_round(const DevState& d, const StepArgs& a, const int32_t* d_sel,

@@ -98,10 +98,10 @@ __device__ __forceinline__ void clear_hist(SelShared& sh, int nb) {
 // step's scan.
 __device__ __forceinline__ void reset_scan_state(const DevState& d, int u, int m, int cut_bin) {
   if (threadIdx.x == 0) {
-    d.cnt[u * kCnt + kCntAbove] = 0;
-    d.cnt[u * kCnt + kCntCand] = 0;
-    d.cnt[u * kCnt + kCntMiss] = m;
-    d.cnt[u * kCnt + kCntBin1] = cut_bin;  // centre of the next step's cut window
+    d.cnt[u * kCntStride + kCntAbove] = 0;
+    d.cnt[u * kCntStride + kCntCand] = 0;
+    d.cnt[u * kCntStride + kCntMiss] = m;
+    d.cnt[u * kCntStride + kCntBin1] = cut_bin;  // centre of the next step's cut window
   }
 }
 
@@ -119,7 +119,7 @@ __global__ __launch_bounds__(kSelThreads) void k_select(DevState d, StepArgs a,
   const int session = u / (d.G * d.Q);
   const int K = d.K, C = d.C;
   const int32_t t = a.t;
-  int32_t* cnt = d.cnt + u * kCnt;
+  int32_t* cnt = d.cnt + u * kCntStride;
   int32_t* above_g = d.above + (size_t)u * K;
   uint2* gcand = d.cand + (size_t)u * d.hcap;
 

@@ -21,6 +21,13 @@
 // from one appended position), so the window almost always holds and a step
 // reads the history once.
 //
+// A context's first step has no previous cut bin.  Rather than classify every
+// key as a candidate (which leaves one k_select workgroup to rank the whole
+// history: 1.4 ms at a million positions), k_cold_hist counts the keys of
+// every 12-bit bin over many workgroups and k_cold_cut places the window on
+// the bin holding the K-th key, so the first step's lists are as small as any
+// other step's.
+//
 // Grid = (chunks of 4,096 positions) x (selection units: one per query row of
 // each session and group), 256 threads; HBM-bound streaming read of 4 B per
 // position.
@@ -94,7 +101,7 @@ __global__ __launch_bounds__(kScanThreads) void k_topk_scan(DevState d, StepArgs
 
   // predicted cut window from the previous step's cut bin (-1: none yet)
   uint32_t b_lo, b_hi;
-  cut_window(d.cnt[u * kCnt + kCntBin1], b_lo, b_hi);
+  cut_window(d.cnt[u * kCntStride + kCntBin1], b_lo, b_hi);
 
   float x[kPerThread];
   int pos[kPerThread];
@@ -113,8 +120,15 @@ __global__ __launch_bounds__(kScanThreads) void k_topk_scan(DevState d, StepArgs
   const int packed = (na << 16) | nc;
   const int pincl = block_incl_scan256(packed, wtot);
   if (tid == kScanThreads - 1) {
-    off_above = atomicAdd(&d.cnt[u * kCnt + kCntAbove], pincl >> 16);
-    off_cand = atomicAdd(&d.cnt[u * kCnt + kCntCand], pincl & 0xFFFF);
+    // one atomic reserves both lists: above count in the low word, candidate
+    // count in the high word (neither total exceeds 2^31, so no carry)
+    static_assert(kCntCand == kCntAbove + 1 && kCntAbove % 2 == 0, "counter pair");
+    const uint64_t add = ((uint64_t)(pincl & 0xFFFF) << 32) | (uint32_t)(pincl >> 16);
+    const uint64_t old = atomicAdd(
+        reinterpret_cast<unsigned long long*>(&d.cnt[u * kCntStride + kCntAbove]),
+        (unsigned long long)add);
+    off_above = (int)(uint32_t)old;
+    off_cand = (int)(old >> 32);
   }
   __syncthreads();
   int ia = off_above + ((pincl - packed) >> 16);
@@ -136,6 +150,81 @@ __global__ __launch_bounds__(kScanThreads) void k_topk_scan(DevState d, StepArgs
       ++ic;
     }
   }
+}
+
+constexpr int kColdChunk = 16384;   // positions per workgroup of the cold histogram
+constexpr int kColdBatch = 16;      // loads in flight per thread
+
+// The cold histogram of selection unit u lives in the first 16 KB of the
+// unit's candidate list (zeroed by k_init; the scan overwrites it afterwards).
+__device__ __forceinline__ uint32_t* cold_hist(const DevState& d, int u) {
+  return reinterpret_cast<uint32_t*>(d.cand + (size_t)u * d.hcap);
+}
+
+__global__ __launch_bounds__(kScanThreads) void k_cold_hist(DevState d, StepArgs a,
+                                                            const float* __restrict__ scores,
+                                                            uint64_t stride) {
+  __shared__ uint32_t h[kBins1];
+  const int u = blockIdx.y, tid = threadIdx.x;
+  const int64_t H = a.hist_len[u / (d.G * d.Q)];
+  const int64_t base = (int64_t)blockIdx.x * kColdChunk;
+  if (base >= H) return;
+  const int n = (int)(H - base < kColdChunk ? H - base : kColdChunk);
+  for (int b = tid; b < kBins1; b += kScanThreads) h[b] = 0;
+  __syncthreads();
+  const float* src = scores + (uint64_t)u * stride + base;
+  for (int i0 = 0; i0 < n; i0 += kScanThreads * kColdBatch) {
+    uint32_t bin[kColdBatch];
+#pragma unroll
+    for (int j = 0; j < kColdBatch; ++j) {
+      const int i = i0 + j * kScanThreads + tid;
+      bin[j] = i < n ? order_key(src[i]) >> (32 - kBin1Bits) : kBins1;
+    }
+#pragma unroll
+    for (int j = 0; j < kColdBatch; ++j)
+      if (bin[j] < (uint32_t)kBins1) atomicAdd(&h[bin[j]], 1u);
+  }
+  __syncthreads();
+  uint32_t* g = cold_hist(d, u);
+  for (int b = tid; b < kBins1; b += kScanThreads)
+    if (h[b]) atomicAdd(&g[b], h[b]);
+}
+
+// One workgroup per selection unit: the bin where the count from the top
+// reaches K becomes the unit's cut bin (H >= K, so it exists).
+__global__ __launch_bounds__(kScanThreads) void k_cold_cut(DevState d) {
+  __shared__ int wtot[kScanThreads / 64];
+  constexpr int kPer = kBins1 / kScanThreads;   // 16 bins per thread, from the top
+  const int u = blockIdx.x, tid = threadIdx.x;
+  const uint32_t* g = cold_hist(d, u);
+  int c[kPer];
+  int sum = 0;
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    c[j] = (int)g[kBins1 - 1 - (tid * kPer + j)];
+    sum += c[j];
+  }
+  const int incl = block_incl_scan256(sum, wtot);
+  int cum = incl - sum;
+  if (cum < d.K && incl >= d.K) {
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      if (cum < d.K && cum + c[j] >= d.K)
+        d.cnt[u * kCntStride + kCntBin1] = kBins1 - 1 - (tid * kPer + j);
+      cum += c[j];
+    }
+  }
+}
+
+hipError_t launch_cold_cut(const DevState& d, const StepArgs& a, const float* scores,
+                           uint64_t stride, int64_t max_len, hipStream_t st) {
+  const int units = d.S * d.G * d.Q;
+  dim3 grid((unsigned)((max_len + kColdChunk - 1) / kColdChunk), units);
+  hipLaunchKernelGGL(k_cold_hist, grid, dim3(kScanThreads), 0, st, d, a, scores, stride);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_cold_cut, dim3(units), dim3(kScanThreads), 0, st, d);
+  return hipGetLastError();
 }
 
 hipError_t launch_topk_scan(const DevState& d, const StepArgs& a, const float* scores,
