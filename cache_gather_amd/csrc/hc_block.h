@@ -53,79 +53,158 @@ __device__ __forceinline__ int block_flag_rank(bool f, int32_t* wtot, int& total
   return off + below;
 }
 
-// LRU victims of unit u at step t without any search.  The unit's order list
-// (parity t & 1) holds all C slots in ascending (last_use, slot); `touched`
-// (LDS bitmap) marks the slots this step's hits use.  Dropping them keeps the
-// list sorted, so the m victims are its first m untouched entries (written to
-// vic[0, m)); the next list (parity t + 1) is the remaining entries followed by
-// the step's n_touched slots — hits and victims, all now last used at t — in
-// slot order, read out of the bitmap after the victims are added to it.
-// Wave w of a round owns 2,048 consecutive entries, lane-interleaved so every
-// load is coalesced; ranks inside the wave come from ballots, and one block
-// scan of the 16 wave totals orders the waves.
+// LRU victims of unit u at step t without any search.  The unit's queue holds
+// (slot, step) entries in ascending (step, slot) order between a head and a
+// tail: each step appends the slots it used (hits and victims) at the tail in
+// slot order, stamped with the step.  An entry is live while the slot's
+// last_use still equals its stamp; a slot used again later has a newer entry,
+// so the old one is dead without being touched.  The callers stamp the hits'
+// last_use before this runs and the victims' after it.  `touched` (LDS bitmap)
+// marks the slots the step's hits use; the m victims are the first m live,
+// untouched entries from the head (written to vic[0, m)), and everything
+// before the last of them is dead afterwards, so the head moves past it.  A
+// step reads about m entries instead of C.  When the tail would pass the
+// buffer's end (2C entries: once every C / K steps or so) the live entries are
+// compacted into the other buffer, followed by the step's slots.
+// n_touched = hits + m; `scratch` is one int of LDS.
 __device__ __forceinline__ void lru_victims(const DevState& d, int u, int32_t t, int m,
                                             int n_touched, uint32_t* touched, int32_t* vic,
-                                            int32_t* wtot) {
-  const int C = d.C, tid = threadIdx.x;
-  const int nwords = (C + 31) >> 5;
-  const int32_t* ocur = d.order + ((size_t)u * 2 + (t & 1)) * C;
-  int32_t* onxt = d.order + ((size_t)u * 2 + ((t + 1) & 1)) * C;
-  const int lane = lane_id(), wv = tid >> 6;
-  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  constexpr int kOrdPer = 32;
-  int kept = 0;
-  for (int j0 = 0; j0 < C; j0 += kSelThreads * kOrdPer) {
-    const int wb = j0 + wv * 64 * kOrdPer;
-    int32_t v[kOrdPer];
-#pragma unroll
-    for (int e = 0; e < kOrdPer; ++e) {
-      const int j = wb + e * 64 + lane;
-      v[e] = j < C ? ocur[j] : -1;
+                                            int32_t* wtot, int32_t* scratch) {
+  const int C = d.C, QC = d.qcap, tid = threadIdx.x;
+  constexpr int kPer = 4;   // queue entries per thread and window (two 16-byte loads)
+  int32_t* cnt = d.cnt + (size_t)u * d.Q * kCntStride;
+  const int h = cnt[kCntQHead], e = cnt[kCntQTail], b = cnt[kCntQBuf];
+  const int2* q = d.oq + ((size_t)u * 2 + b) * QC;
+  const int32_t* last = d.last_use + (size_t)u * C;
+  auto pinned = [&](int v) { return (touched[v >> 5] >> (v & 31)) & 1u; };
+  // entries jb .. jb + n - 1 (n a multiple of 2, jb even) of this thread
+  auto load = [&](int jb, int n, int2* ent) {
+    for (int x = 0; x < n; x += 2) {
+      int4 w = make_int4(-1, -1, -1, -1);
+      if (jb + x < e) w = *reinterpret_cast<const int4*>(q + jb + x);   // QC % 4 == 0
+      ent[x] = make_int2(w.x, w.y);
+      ent[x + 1] = make_int2(w.z, w.w);
     }
-    int wave_total = 0;
+  };
+
+  // the first m live, untouched entries from the head
+  if (tid == 0) *scratch = h - 1;   // queue index of the last victim
+  int found = 0;
+  for (int j0 = h & ~(kPer - 1); found < m && j0 < e; j0 += kSelThreads * kPer) {
+    const int jb = j0 + tid * kPer;
+    int2 ent[kPer];
+    load(jb, kPer, ent);
+    bool f[kPer];
 #pragma unroll
-    for (int e = 0; e < kOrdPer; ++e) {
-      const bool keep = v[e] >= 0 && !((touched[v[e] >> 5] >> (v[e] & 31)) & 1u);
-      if (!keep) v[e] = -1;
-      wave_total += __popcll(__ballot(keep));
+    for (int k = 0; k < kPer; ++k) {
+      const int j = jb + k;
+      f[k] = j >= h && j < e && ent[k].x >= 0 && ent[k].x < C && !pinned(ent[k].x);
     }
-    if (lane == 0) wtot[wv] = wave_total;
-    __syncthreads();
-    int run = kept, total = 0;
+    int lu[kPer];
 #pragma unroll
-    for (int i = 0; i < kWaves; ++i) {
-      run += i < wv ? wtot[i] : 0;
-      total += wtot[i];
+    for (int k = 0; k < kPer; ++k) lu[k] = f[k] ? last[ent[k].x] : 0;
+    int c = 0;
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+      f[k] = f[k] && lu[k] == ent[k].y;
+      c += f[k];
     }
-    __syncthreads();
+    int total;
+    int k0 = found + block_incl_scan(c, wtot, total) - c;
 #pragma unroll
-    for (int e = 0; e < kOrdPer; ++e) {
-      const uint64_t bal = __ballot(v[e] >= 0);
-      if (v[e] >= 0) {
-        const int k = run + __popcll(bal & lt_mask);
-        if (k < m) vic[k] = v[e];
-        else onxt[k - m] = v[e];
+    for (int k = 0; k < kPer; ++k) {
+      if (!f[k]) continue;
+      if (k0 < m) {
+        vic[k0] = ent[k].x;
+        if (k0 == m - 1) *scratch = jb + k;
       }
-      run += __popcll(bal);
+      ++k0;
     }
-    kept += total;
+    found += total;
   }
+  // fewer than m candidates means a corrupted queue: keep every index in range
+  for (int k = found + tid; k < m; k += kSelThreads) vic[k] = 0;
   __syncthreads();
+  const int hn = *scratch + 1;
   for (int k = tid; k < m; k += kSelThreads) atomicOr(&touched[vic[k] >> 5], 1u << (vic[k] & 31));
   __syncthreads();
-  int base = C - n_touched;
+
+  const bool fits = e + n_touched <= QC;
+  int2* qw = const_cast<int2*>(fits ? q : d.oq + ((size_t)u * 2 + (b ^ 1)) * QC);
+  int base = e;
+  if (!fits) {
+    // survivors: the live entries after the last victim that this step did
+    // not use, in order, to the front of the other buffer.  Wave w of a
+    // window owns 1,024 consecutive entries, lane-interleaved so that loads
+    // and stores coalesce; ranks inside the wave come from ballots and one
+    // block scan of the wave totals orders the waves.
+    constexpr int kCPer = 16;
+    const int lane = lane_id(), wv = tid >> 6;
+    const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    int kept = 0;
+    for (int j0 = hn; j0 < e; j0 += kSelThreads * kCPer) {
+      const int wb = j0 + wv * 64 * kCPer;
+      int2 ent[kCPer];
+#pragma unroll
+      for (int k = 0; k < kCPer; ++k) {
+        const int j = wb + k * 64 + lane;
+        ent[k] = j < e ? q[j] : make_int2(-1, -1);
+      }
+      bool f[kCPer];
+#pragma unroll
+      for (int k = 0; k < kCPer; ++k)
+        f[k] = ent[k].x >= 0 && ent[k].x < C && !pinned(ent[k].x);
+      int lu[kCPer];
+#pragma unroll
+      for (int k = 0; k < kCPer; ++k) lu[k] = f[k] ? last[ent[k].x] : 0;
+      int wave_total = 0;
+#pragma unroll
+      for (int k = 0; k < kCPer; ++k) {
+        f[k] = f[k] && lu[k] == ent[k].y;
+        wave_total += __popcll(__ballot(f[k]));
+      }
+      if (lane == 0) wtot[wv] = wave_total;
+      __syncthreads();
+      int run = kept, total = 0;
+#pragma unroll
+      for (int i = 0; i < kWaves; ++i) {
+        run += i < wv ? wtot[i] : 0;
+        total += wtot[i];
+      }
+      __syncthreads();
+#pragma unroll
+      for (int k = 0; k < kCPer; ++k) {
+        const uint64_t bal = __ballot(f[k]);
+        if (f[k]) {
+          const int o = run + __popcll(bal & lt_mask);
+          if (o < QC) qw[o] = ent[k];
+        }
+        run += __popcll(bal);
+      }
+      kept += total;
+    }
+    base = kept;
+  }
+  // the step's slots in slot order at the tail
+  const int nwords = (C + 31) >> 5;
+  int o0 = base;
   for (int w0 = 0; w0 < nwords; w0 += kSelThreads) {
     const int w = w0 + tid;
     uint32_t bits = w < nwords ? touched[w] : 0u;
     int total;
-    const int incl = block_incl_scan(__popc(bits), wtot, total);
-    int o = base + incl - __popc(bits);
+    int o = o0 + block_incl_scan(__popc(bits), wtot, total) - __popc(bits);
     while (bits) {
-      const int b = __ffs(bits) - 1;
+      const int v = w * 32 + __ffs(bits) - 1;
       bits &= bits - 1;
-      onxt[o++] = w * 32 + b;
+      if (o < QC) qw[o] = make_int2(v, t);
+      ++o;
     }
-    base += total;
+    o0 += total;
+  }
+  if (tid == 0) {
+    cnt[kCntQHead] = fits ? hn : 0;
+    cnt[kCntQTail] = o0 < QC ? o0 : QC;
+    cnt[kCntQBuf] = fits ? b : (b ^ 1);
   }
 }
 

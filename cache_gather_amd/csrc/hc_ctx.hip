@@ -26,7 +26,7 @@ namespace {
 constexpr uint64_t kAlign = 256;
 
 struct Layout {
-  uint64_t pos2slot, slot2pos, last_use, order, cnt, above, cand, sel_slot, miss_pos,
+  uint64_t pos2slot, slot2pos, last_use, oq, cnt, above, cand, sel_slot, miss_pos,
       victim, miss_idx, host_tab, hot, ring, refbits, total;
 };
 
@@ -74,6 +74,8 @@ bool valid_config(const hc_config* c) {
   return true;
 }
 
+uint64_t queue_cap(uint64_t C) { return (2 * C + 3) / 4 * 4; }
+
 Layout layout_of(const hc_config* c) {
   const uint64_t S = c->n_sessions, L = c->n_layers;
   const uint64_t G = (L + c->layers_per_select - 1) / c->layers_per_select;
@@ -89,7 +91,7 @@ Layout layout_of(const hc_config* c) {
   lo.pos2slot = take(U * hcap * 4);
   lo.slot2pos = take(U * C * 4);
   lo.last_use = take(U * C * 4);
-  lo.order = take(U * 2 * C * 4);
+  lo.oq = take(U * 2 * queue_cap(C) * 8);
   lo.cnt = take(SU * kCntStride * 4);
   lo.above = take(SU * K * 4);
   lo.cand = take(SU * hcap * 8);
@@ -126,13 +128,14 @@ __global__ void k_init(DevState d, int64_t n_pos, int64_t n_slots) {
     d.slot2pos[i] = -1;
     d.last_use[i] = -1;
     const int64_t u = i / d.C, v = i - u * d.C;
-    d.order[(u * 2) * d.C + v] = (int32_t)v;      // step 0 reads parity 0
-    d.order[(u * 2 + 1) * d.C + v] = (int32_t)v;
+    d.oq[(u * 2) * (int64_t)d.qcap + v] = make_int2((int32_t)v, -1);   // buffer 0: every slot, never used
   }
   const int64_t sel_units = (int64_t)d.S * d.G * d.Q;
   for (int64_t i = i0; i < sel_units * d.K; i += stride) d.sel_slot[i] = 0;
-  for (int64_t i = i0; i < sel_units * kCntStride; i += stride)
-    d.cnt[i] = (i % kCntStride) == kCntBin1 ? -1 : 0;
+  for (int64_t i = i0; i < sel_units * kCntStride; i += stride) {
+    const int64_t f = i % kCntStride;
+    d.cnt[i] = f == kCntBin1 ? -1 : f == kCntQTail ? d.C : 0;   // queue [0, C) in buffer 0
+  }
   // the first step's cut histograms (see launch_cold_cut)
   if (d.hcap >= kColdMinPositions)
     for (int64_t i = i0; i < sel_units * kBins1; i += stride)
@@ -293,7 +296,8 @@ hc_status hc_create(const hc_config* cfg_in, void* dev_workspace, uint64_t ws_by
   d.pos2slot = reinterpret_cast<int32_t*>(w + lo.pos2slot);
   d.slot2pos = reinterpret_cast<int32_t*>(w + lo.slot2pos);
   d.last_use = reinterpret_cast<int32_t*>(w + lo.last_use);
-  d.order = reinterpret_cast<int32_t*>(w + lo.order);
+  d.oq = reinterpret_cast<int2*>(w + lo.oq);
+  d.qcap = (int32_t)queue_cap(cfg->cache_slots);
   d.cnt = reinterpret_cast<int32_t*>(w + lo.cnt);
   d.above = reinterpret_cast<int32_t*>(w + lo.above);
   d.cand = reinterpret_cast<uint2*>(w + lo.cand);

@@ -26,7 +26,11 @@ constexpr int kMaxUnits = HC_MAX_UNITS;   // S * G: the per-unit miss prefix liv
 // own, because atomics on neighbouring addresses queue behind each other
 // (measured: 16 units x 257 workgroups took 58 us packed, 20 us spread, 13 us
 // without atomics).
-enum { kCntAbove = 0, kCntCand = 1, kCntMiss = 2, kCntBin1 = 3, kCntHand = 4, kCnt = 5 };
+// kCntQHead / kCntQTail / kCntQBuf: the LRU queue of the unit (at su = u * Q).
+enum {
+  kCntAbove = 0, kCntCand = 1, kCntMiss = 2, kCntBin1 = 3, kCntHand = 4,
+  kCntQHead = 5, kCntQTail = 6, kCntQBuf = 7, kCnt = 8
+};
 constexpr int kCntStride = 64;
 
 // Device view of the caller's workspace.  Unit u = s * G + g; layer index
@@ -38,7 +42,9 @@ struct DevState {
   int32_t* pos2slot;   // [U][hcap]  slot holding a position, -1 if none
   int32_t* slot2pos;   // [U][C]     position held by a slot, -1 if empty
   int32_t* last_use;   // [U][C]     step of the slot's last use, -1 if never
-  int32_t* order;      // [U][2][C]  slots in ascending (last_use, slot); ping-pong by step parity
+  int2* oq;            // [U][2][qcap] LRU queue of (slot, step) in ascending (step, slot);
+                       //            an entry is live while last_use[slot] == step
+  int32_t qcap;        // entries per queue buffer: 2 C rounded up to a multiple of 4
   int32_t* cnt;        // [U*Q][kCntStride] per selection unit; the round's miss count at su = u*Q
   int32_t* above;      // [U*Q][K]   positions whose top digit beats the cut bin
   uint2* cand;         // [U*Q][hcap] (key, position) of scores in the cut bin

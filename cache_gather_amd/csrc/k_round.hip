@@ -193,7 +193,7 @@ __global__ __launch_bounds__(kSelThreads) void k_round(DevState d, StepArgs a,
 
   // ---- 4. LRU victims ------------------------------------------------------
   if (d.policy == HC_REPLACE_LRU)
-    lru_victims(d, u, t, m, n - n_ring, touched, sh.vic, sh.wtot);
+    lru_victims(d, u, t, m, n - n_ring, touched, sh.vic, sh.wtot, &sh.wmin);
   else
     hand_victims(d, u, m, d.policy == HC_REPLACE_CLOCK, touched, sh.vic, sh.wtot, &sh.wmin);
 

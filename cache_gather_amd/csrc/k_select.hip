@@ -14,9 +14,11 @@
 //     candidates of the cut bin (kept in LDS when they fit); if more keys
 //     equal the cut key than are needed, radix-select the position cut among
 //     them (lower positions win).
-//  2. Emit the K winners in ascending position order: per window of 262,144
-//     positions, set one bit per winner in an LDS bitmap and read the set bits
-//     back in order with one block-wide prefix sum.
+//  2. Emit the K winners in ascending position order without a sort: count
+//     them into at most 8,192 buckets of 2^s consecutive positions, place
+//     each bucket at its prefix offset, and give each winner its rank inside
+//     its bucket by comparing it with the bucket's other members (rarely more
+//     than a few: 8 positions per bucket at 50K, 128 at a million).
 //  3. Positions the recent ring holds (a suffix of the ascending selection)
 //     are read from the ring and skip the cache.  For the rest, look up
 //     pos2slot; hits get last_use = t and are marked in an LDS bitmap of
@@ -34,8 +36,7 @@
 namespace hc {
 
 constexpr int kCandCache = 8192;               // cut-bin candidates kept in LDS (64 KB)
-constexpr int kWinWords = HC_MAX_SLOTS / 32;   // bitmap words per position window
-constexpr int kWinPositions = kWinWords * 32;  // 262,144 positions per window
+constexpr int kOrdBuckets = 8192;              // position buckets of the ordering phase
 
 struct SelShared {
   uint32_t hist[kBins1];          // histograms of up to 4,096 bins
@@ -43,7 +44,10 @@ struct SelShared {
   int32_t mpos[HC_MAX_TOPK];    // winners unordered (phase 2), then missing positions
   union {
     uint2 cand[kCandCache];       // phase 1: (key, position) of the cut bin
-    uint32_t posbits[kWinWords];  // phase 2: winners of one position window
+    struct {
+      uint32_t start[kOrdBuckets];  // winners per bucket, then each bucket's offset
+      int32_t member[HC_MAX_TOPK];  // winners grouped by bucket
+    } ord;                        // phase 2
     struct {
       int32_t midx[HC_MAX_TOPK];  // index in sel of miss k
       int32_t vic[HC_MAX_TOPK];   // victim slot of miss k
@@ -286,37 +290,57 @@ __global__ __launch_bounds__(kSelThreads) void k_select(DevState d, StepArgs a,
     return;
   }
   {
-    constexpr int kWordsPerThread = kWinWords / kSelThreads;  // 8
+    // buckets of 2^shift positions, at most kOrdBuckets of them
     const int wmax = sh.wmax;
-    int emitted = 0;
-    for (int64_t w0 = 0; w0 <= wmax; w0 += kWinPositions) {
-      for (int i = tid; i < kWinWords; i += kSelThreads) sh.u.posbits[i] = 0;
-      __syncthreads();
-      for (int i = tid; i < K; i += kSelThreads) {
-        const int p = sh.mpos[i];
-        if (p >= w0 && p - w0 < kWinPositions)
-          atomicOr(&sh.u.posbits[(int)(p - w0) >> 5], 1u << (p & 31));
-      }
-      __syncthreads();
-      uint32_t wd[kWordsPerThread];
-      int n = 0;
+    int shift = 0;
+    while ((wmax >> shift) >= kOrdBuckets) ++shift;
+    const int nb = (wmax >> shift) + 1;
+    constexpr int kRounds = HC_MAX_TOPK / kSelThreads;   // winners per thread
+    constexpr int kBPer = kOrdBuckets / kSelThreads;     // buckets per thread
+    for (int b = tid; b < nb; b += kSelThreads) sh.u.ord.start[b] = 0;
+    __syncthreads();
+    int32_t wp[kRounds];
+    int arrival[kRounds];
 #pragma unroll
-      for (int e = 0; e < kWordsPerThread; ++e) {
-        wd[e] = sh.u.posbits[kWordsPerThread * tid + e];
-        n += __popc(wd[e]);
-      }
-      int total;
-      int o = emitted + block_incl_scan(n, sh.wtot, total) - n;
+    for (int r = 0; r < kRounds; ++r) {
+      const int i = r * kSelThreads + tid;
+      wp[r] = i < K ? sh.mpos[i] : 0;
+      arrival[r] = i < K ? (int)atomicAdd(&sh.u.ord.start[wp[r] >> shift], 1u) : 0;
+    }
+    __syncthreads();
+    int cnt8[kBPer];
+    int sum = 0;
 #pragma unroll
-      for (int e = 0; e < kWordsPerThread; ++e) {
-        uint32_t bits = wd[e];
-        while (bits) {
-          const int b = __ffs(bits) - 1;
-          bits &= bits - 1;
-          sh.sel[o++] = (int32_t)(w0 + (kWordsPerThread * tid + e) * 32 + b);
-        }
-      }
-      emitted += total;
+    for (int j = 0; j < kBPer; ++j) {
+      const int b = tid * kBPer + j;
+      cnt8[j] = b < nb ? (int)sh.u.ord.start[b] : 0;
+      sum += cnt8[j];
+    }
+    int total;
+    int off = block_incl_scan(sum, sh.wtot, total) - sum;
+#pragma unroll
+    for (int j = 0; j < kBPer; ++j) {
+      const int b = tid * kBPer + j;
+      if (b < nb) sh.u.ord.start[b] = (uint32_t)off;
+      off += cnt8[j];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < kRounds; ++r) {
+      const int i = r * kSelThreads + tid;
+      if (i < K) sh.u.ord.member[sh.u.ord.start[wp[r] >> shift] + arrival[r]] = wp[r];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < kRounds; ++r) {
+      const int i = r * kSelThreads + tid;
+      if (i >= K) continue;
+      const int b = wp[r] >> shift;
+      const int lo = (int)sh.u.ord.start[b];
+      const int hi = b + 1 < nb ? (int)sh.u.ord.start[b + 1] : K;
+      int rank = 0;
+      for (int q = lo; q < hi; ++q) rank += sh.u.ord.member[q] < wp[r];
+      sh.sel[lo + rank] = wp[r];
     }
   }
   __syncthreads();
@@ -373,7 +397,7 @@ __global__ __launch_bounds__(kSelThreads) void k_select(DevState d, StepArgs a,
 
   // ---- 4. LRU victims: first m untouched entries of the order list --------
   if (d.policy == HC_REPLACE_LRU)
-    lru_victims(d, u, t, m, K - n_ring, sh.u.lru.touched, sh.u.lru.vic, sh.wtot);
+    lru_victims(d, u, t, m, K - n_ring, sh.u.lru.touched, sh.u.lru.vic, sh.wtot, &sh.bcast[0]);
   else
     hand_victims(d, u, m, d.policy == HC_REPLACE_CLOCK, sh.u.lru.touched, sh.u.lru.vic, sh.wtot,
                  &sh.bcast[0]);
