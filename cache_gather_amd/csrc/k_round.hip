@@ -16,8 +16,8 @@
 //  2. finds each union entry's first row (lowest query, by an LDS atomic
 //     minimum): the row that fills a missing slot;
 //  3. runs the single-query method on the union: lookup (ring rows skip the
-//     cache), hits stamped and marked, LRU victims from the order list, and
-//     the (miss, victim) pairs applied;
+//     cache), hits stamped and marked, LRU victims from the stamped queue,
+//     and the (miss, victim) pairs applied;
 //  4. gives every query row its source for the gather: the hit slot, the ring
 //     entry, -(victim + 1) for the row that fills the slot, and
 //     -(C + 1 + position) — read host RAM directly — for any other row of the

@@ -24,11 +24,11 @@
 //     pos2slot; hits get last_use = t and are marked in an LDS bitmap of
 //     touched slots; misses are compacted in ascending order by wave ballot +
 //     mbcnt prefix.
-//  4. LRU without any search: `order` holds all C slots sorted by
-//     (last_use, slot).  Dropping the hit slots keeps it sorted, so the victims
-//     are its first m entries.  The next order is the rest of the list followed
-//     by this step's touched slots (all now last_use = t) in slot order, read
-//     out of the bitmap.  One stable partition of C entries per step.
+//  4. LRU without any search: a queue of (slot, step) entries in ascending
+//     (step, slot) order, live while the slot's last use equals the entry's
+//     step.  The victims are the first m live entries the step's hits do not
+//     pin; the step's slots are appended in slot order; the queue is
+//     compacted into its second buffer once every C / K steps or so.
 //  5. Apply the m (miss, victim) pairs to pos2slot / slot2pos / last_use in
 //     parallel (an evicted position is never one of this step's misses).
 #include "hc_block.h"
@@ -395,7 +395,7 @@ __global__ __launch_bounds__(kSelThreads) void k_select(DevState d, StepArgs a,
     m += total;
   }
 
-  // ---- 4. LRU victims: first m untouched entries of the order list --------
+  // ---- 4. LRU victims: first m live, unpinned entries of the queue -------
   if (d.policy == HC_REPLACE_LRU)
     lru_victims(d, u, t, m, K - n_ring, sh.u.lru.touched, sh.u.lru.vic, sh.wtot, &sh.bcast[0]);
   else
