@@ -15,37 +15,50 @@
 //     buffer is never written.  The staged values are the same bf16 numbers
 //     either way, so both sources give the same result bit for bit.
 //
-// Workgroup = (256-row split of one (session, layer, query row), 64-head
-// group): 4 wave64, 16 heads each.  Per 64-row sub-chunk the rows are staged
-// in LDS twice — row-major (the B operand of Q.K^T over 576 values) and the
-// latent part transposed (the B operand of P.V) — and each wave runs
-// v_mfma_f32_16x16x32_bf16: Q.K^T in 18 k-steps x 4 row tiles, online softmax
-// in fp32 (each lane holds 4 heads of one row per tile), P rounded to bf16
-// through LDS, P.V in 2 k-steps x 32 dim tiles accumulating 16 x 512 fp32 per
-// wave.  Each split writes (max, sum, unnormalised output) per head; a second
-// kernel merges the splits.
+// Workgroup = (split of up to 1,024 rows of one (session, layer, query row),
+// 64-head group): 8 wave64 in pairs.  Wave w serves head tile w % 4 (16 heads) and
+// half w / 4: for Q.K^T the half of the 576 values it multiplies, for P.V the
+// half of the 512 output values it accumulates — so a wave keeps 9 query
+// fragments and 16 x 256 fp32 accumulators, and two waves fit on each SIMD.
+// Per 64-row sub-chunk the rows are staged once in LDS, row-major (dequantised
+// while staging for the slot source), and each wave runs
+// v_mfma_f32_16x16x32_bf16: its half of Q.K^T in 9 k-steps x 4 row tiles; the
+// pair adds its two partial scores through LDS (fp32 addition commutes, so
+// both waves hold the same sums); online softmax in fp32 (each lane holds 4
+// heads of one row per tile); P rounded to bf16 through LDS; P.V in 2 k-steps
+// x 16 dim tiles, its B operand read from the row-major rows with the gfx950
+// transposing LDS load (ds_read_b64_tr_b16: within each 16-lane group, lane j
+// receives value j % 4 of what lane 4k + j / 4 addressed, so four lanes
+// addressing four consecutive rows give every lane four consecutive rows of
+// one column).  Each split writes (max, sum, unnormalised output) per head; a
+// second kernel merges the splits.
 #include "hc_internal.h"
 
 namespace hc {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x8 __attribute__((ext_vector_type(8)));
 
-constexpr int kAttThreads = 256;                  // 4 wave64
-constexpr int kHeadsPerGroup = 64;                // 16 per wave
-constexpr int kSplitRows = 256;                   // rows per workgroup
+constexpr int kAttThreads = 512;                  // 8 wave64
+constexpr int kHeadsPerGroup = 64;                // 4 tiles of 16
+constexpr int kMaxSplitRows = 1024;              // rows per workgroup, at most
+constexpr int kResident = 256;                    // workgroups the chip runs at once (1 per CU)
 constexpr int kSub = 64;                          // rows per LDS sub-chunk
 constexpr int kRowLd = HC_OUT_ELEMS + 8;          // 584 bf16: padded row-major row
-constexpr int kVtLd = kSub + 8;                   // 72 bf16: padded transposed row
 constexpr int kPLd = kSub + 8;
 constexpr int kPartStride = 516;                  // floats per (head) partial: 512 + m + l + pad
+constexpr int kHalfK = HC_OUT_ELEMS / 32 / 2;     // 9 Q.K^T k-steps per half
+constexpr int kDimTiles = 512 / 2 / 16;           // 16 P.V dim tiles per half
 
 enum { kFromBuffer = 0, kFromSlots = 1 };
 
 struct AttShared {
   alignas(16) __bf16 rows[kSub * kRowLd];         // 74,752 B
-  alignas(16) __bf16 vt[512 * kVtLd];             // 73,728 B
-  alignas(16) __bf16 p[4 * 16 * kPLd];            //  9,216 B
+  alignas(16) float sx[8 * 4 * 4 * 64];           // 32,768 B: partial scores [wave][n][i][lane]
+  alignas(16) __bf16 p[4 * 16 * kPLd];            //  9,216 B: weights [head tile][head][row]
+  const uint8_t* src[kMaxSplitRows];              //  8,192 B: slot source of each row
 };
 
 __device__ __forceinline__ uint32_t bf16x2_rne(float lo, float hi) {
@@ -66,11 +79,9 @@ __device__ __forceinline__ const uint8_t* slot_row(const DevState& d, int64_t sl
   return d.host[sl] + (size_t)(-(int64_t)enc - d.C - 1) * kRow;                     // host RAM
 }
 
-// 8 int8 latent values times fp16 scale g of the row's scale block, as bf16.
-__device__ __forceinline__ u32x4 dequant8(const uint2& qq, const u32x4& sblk, int g) {
-  const uint32_t sw = (g >> 1) == 0 ? sblk.x : (g >> 1) == 1 ? sblk.y : (g >> 1) == 2 ? sblk.z : sblk.w;
-  const uint16_t hs = (uint16_t)((g & 1) ? (sw >> 16) : (sw & 0xFFFFu));
-  const float sc = (float)__builtin_bit_cast(_Float16, hs);
+// 8 int8 latent values times an fp16 scale (low 16 bits of hs), as bf16.
+__device__ __forceinline__ u32x4 dequant8(const uint2& qq, uint32_t hs) {
+  const float sc = (float)__builtin_bit_cast(_Float16, (uint16_t)(hs & 0xFFFFu));
   u32x4 w;
   w.x = bf16x2_rne(i8f(qq.x, 0) * sc, i8f(qq.x, 1) * sc);
   w.y = bf16x2_rne(i8f(qq.x, 2) * sc, i8f(qq.x, 3) * sc);
@@ -79,28 +90,39 @@ __device__ __forceinline__ u32x4 dequant8(const uint2& qq, const u32x4& sblk, in
   return w;
 }
 
+// Four consecutive bf16 of LDS per lane, transposed across each 16-lane group.
+__device__ __forceinline__ i16x4 lds_tr4(const __bf16* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) i16x4*)(p));
+}
+
 template <int SRC>
 __global__ __launch_bounds__(kAttThreads) void k_attend(DevState d, const uint16_t* __restrict__ q,
-                                                        int heads, float scale,
+                                                        int heads, float scale, int split_rows,
                                                         const uint16_t* __restrict__ rows_buf,
                                                         float* __restrict__ part) {
   __shared__ AttShared sh;
   const int split = blockIdx.x, hg = blockIdx.y, slq = blockIdx.z;  // slq = sl * Q + qi
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int ht = wave & 3, half = wave >> 2;
   const int K = d.K, Q = d.Q;
   const int sl = slq / Q, qi = slq - sl * Q;
   const int s = sl / d.L, l = sl - s * d.L;
   const int32_t* enc_row = d.sel_slot + ((size_t)(s * d.G + l / d.R) * Q + qi) * K;
-  const int r_begin = split * kSplitRows;
-  const int r_end = min(K, r_begin + kSplitRows);
-  // this lane's query fragment base: head row lane % 16 of the wave's 16
-  const int head0 = hg * kHeadsPerGroup + wave * 16;
+  const int r_begin = split * split_rows;
+  const int r_end = min(K, r_begin + split_rows);
+  // this lane's query fragments: head row lane % 16 of the tile, this half's k
+  const int head0 = hg * kHeadsPerGroup + ht * 16;
   const uint16_t* qrow = q + ((size_t)slq * heads + head0 + (lane & 15)) * HC_OUT_ELEMS +
-                         8 * (lane >> 4);
-
-  f32x4 o[32];
+                         32 * kHalfK * half + 8 * (lane >> 4);
+  bf16x8 qa[kHalfK];
 #pragma unroll
-  for (int n = 0; n < 32; ++n) o[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int ks = 0; ks < kHalfK; ++ks)
+    qa[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qrow + 32 * ks));
+
+  f32x4 o[kDimTiles];
+#pragma unroll
+  for (int n = 0; n < kDimTiles; ++n) o[n] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_run[4], l_run[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -108,120 +130,84 @@ __global__ __launch_bounds__(kAttThreads) void k_attend(DevState d, const uint16
     l_run[i] = 0.f;
   }
 
-  // the 18 query fragments of this lane (A operands of Q.K^T), kept in registers
-  bf16x8 qa[HC_OUT_ELEMS / 32];
-#pragma unroll
-  for (int ks = 0; ks < HC_OUT_ELEMS / 32; ++ks)
-    qa[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qrow + 32 * ks));
-
-  // staging: thread tid always handles rows 2 * rp and 2 * rp + 1 of a
-  // sub-chunk (rp = tid % 32) and chunks ch0, ch0 + 8, ..., ch0 + 64 of 8
-  // values (ch0 = tid / 32): 8 latent chunks and one RoPE chunk per row.
-  // Consecutive lanes take consecutive row pairs, so the transposed latent is
-  // written as consecutive 32-bit words, free of bank conflicts.  Software
-  // pipeline: the raw loads of sub-chunk j + 1 are issued before the matrix
-  // work of sub-chunk j and only converted and stored after it.
-  const int rp = tid & 31, ch0 = tid >> 5;
-  const int ra = 2 * rp, rb = 2 * rp + 1;
-  uint32_t* vt32 = reinterpret_cast<uint32_t*>(sh.vt);
+  // staging: thread tid handles row rr = tid / 8 of a sub-chunk and chunks
+  // cc, cc + 8, ..., cc + 64 of 8 values (cc = tid % 8): 8 latent chunks, chunk
+  // k in scale group k, and one RoPE chunk.  Eight consecutive lanes cover 128
+  // contiguous bytes of a row.  Software pipeline: the raw loads of sub-chunk
+  // j + 1 are issued before the matrix work of sub-chunk j.
   const int nsub = (r_end - r_begin + kSub - 1) / kSub;
-  constexpr int kMaxSub = kSplitRows / kSub;       // 4
-  constexpr int kLat = 8;                          // latent chunks per row and thread
-  int32_t enca[kMaxSub], encb[kMaxSub];            // slot codes of this thread's rows
-#pragma unroll
-  for (int j = 0; j < kMaxSub; ++j) {
-    enca[j] = encb[j] = 0;
-    if (SRC == kFromSlots) {
-      if (j < nsub && r_begin + j * kSub + ra < r_end) enca[j] = enc_row[r_begin + j * kSub + ra];
-      if (j < nsub && r_begin + j * kSub + rb < r_end) encb[j] = enc_row[r_begin + j * kSub + rb];
-    }
+  constexpr int kLat = 8;
+  const int rr = tid >> 3, cc = tid & 7;
+  if (SRC == kFromSlots) {
+    for (int r = tid; r < r_end - r_begin; r += kAttThreads)
+      sh.src[r] = slot_row(d, sl, enc_row[r_begin + r]);
+    __syncthreads();
   }
-  // raw data of the sub-chunk in flight
-  u32x4 ba[kLat + 1], bb[kLat + 1];                // buffer source: 9 chunks of 16 B per row
-  uint2 qa8[kLat], qb8[kLat];                      // slot source: 8 latent chunks of 8 B
-  u32x4 ropea, ropeb, sca, scb;                    // slot source: RoPE chunk and scale block
-  bool va = false, vb = false;
+  u32x4 bv[kLat + 1];                              // buffer source: 9 chunks of 16 B
+  uint2 q8[kLat];                                  // slot source: 8 latent chunks of 8 B
+  u32x4 rope, scb;                                 // slot source: RoPE chunk, scale block
   auto fetch = [&](int j) {
     const int r0 = r_begin + j * kSub;
-    va = r0 + ra < r_end;
-    vb = r0 + rb < r_end;
+    const bool vr = r0 + rr < r_end;
     if (SRC == kFromBuffer) {
-      const uint16_t* base = rows_buf + ((size_t)slq * K + r0) * HC_OUT_ELEMS + 8 * ch0;
+      const uint16_t* base = rows_buf + ((size_t)slq * K + r0 + rr) * HC_OUT_ELEMS + 8 * cc;
 #pragma unroll
-      for (int k = 0; k <= kLat; ++k) {
-        ba[k] = va ? *reinterpret_cast<const u32x4*>(base + (size_t)ra * HC_OUT_ELEMS + 64 * k)
-                   : u32x4{0u, 0u, 0u, 0u};
-        bb[k] = vb ? *reinterpret_cast<const u32x4*>(base + (size_t)rb * HC_OUT_ELEMS + 64 * k)
-                   : u32x4{0u, 0u, 0u, 0u};
-      }
+      for (int k = 0; k <= kLat; ++k)
+        bv[k] = vr ? *reinterpret_cast<const u32x4*>(base + 64 * k) : u32x4{0u, 0u, 0u, 0u};
     } else {
-      const uint8_t* sa = va ? slot_row(d, sl, enca[j]) : nullptr;
-      const uint8_t* sb = vb ? slot_row(d, sl, encb[j]) : nullptr;
+      const uint8_t* src = vr ? sh.src[j * kSub + rr] : nullptr;
 #pragma unroll
-      for (int k = 0; k < kLat; ++k) {
-        qa8[k] = va ? *reinterpret_cast<const uint2*>(sa + 8 * (ch0 + 8 * k)) : uint2{0u, 0u};
-        qb8[k] = vb ? *reinterpret_cast<const uint2*>(sb + 8 * (ch0 + 8 * k)) : uint2{0u, 0u};
-      }
-      ropea = va ? *reinterpret_cast<const u32x4*>(sa + HC_ROPE_OFFSET + 16 * ch0) : u32x4{0u, 0u, 0u, 0u};
-      ropeb = vb ? *reinterpret_cast<const u32x4*>(sb + HC_ROPE_OFFSET + 16 * ch0) : u32x4{0u, 0u, 0u, 0u};
-      sca = va ? *reinterpret_cast<const u32x4*>(sa + HC_SCALE_OFFSET) : u32x4{0u, 0u, 0u, 0u};
-      scb = vb ? *reinterpret_cast<const u32x4*>(sb + HC_SCALE_OFFSET) : u32x4{0u, 0u, 0u, 0u};
+      for (int k = 0; k < kLat; ++k)
+        q8[k] = vr ? *reinterpret_cast<const uint2*>(src + 8 * (cc + 8 * k)) : uint2{0u, 0u};
+      rope = vr ? *reinterpret_cast<const u32x4*>(src + HC_ROPE_OFFSET + 16 * cc)
+                : u32x4{0u, 0u, 0u, 0u};
+      scb = vr ? *reinterpret_cast<const u32x4*>(src + HC_SCALE_OFFSET) : u32x4{0u, 0u, 0u, 0u};
     }
   };
-  // chunk k (ch = ch0 + 8k) of this thread's two rows, as bf16
-  auto chunk = [&](int k, u32x4& wa, u32x4& wb) {
-    if (SRC == kFromBuffer) {
-      wa = ba[k];
-      wb = bb[k];
-    } else if (k < kLat) {
-      wa = dequant8(qa8[k], sca, k);   // latent chunk ch0 + 8k is in scale group k
-      wb = dequant8(qb8[k], scb, k);
-    } else {
-      wa = ropea;
-      wb = ropeb;
-    }
+  auto chunk = [&](int k) -> u32x4 {
+    if (SRC == kFromBuffer) return bv[k];
+    if (k == kLat) return rope;
+    const uint32_t sw = (k >> 1) == 0 ? scb.x : (k >> 1) == 1 ? scb.y : (k >> 1) == 2 ? scb.z : scb.w;
+    return dequant8(q8[k], (k & 1) ? (sw >> 16) : sw);
   };
 
   fetch(0);
   for (int j = 0; j < nsub; ++j) {
-    const int r0 = r_begin + j * kSub;
-    const int nvalid = min(kSub, r_end - r0);
+    const int nvalid = min(kSub, r_end - (r_begin + j * kSub));
     __syncthreads();   // the previous sub-chunk's matrix work is done with LDS
 #pragma unroll
-    for (int k = 0; k <= kLat; ++k) {
-      const int ch = ch0 + 8 * k;
-      u32x4 wa, wb;
-      chunk(k, wa, wb);
-      *reinterpret_cast<u32x4*>(&sh.rows[ra * kRowLd + 8 * ch]) = wa;
-      *reinterpret_cast<u32x4*>(&sh.rows[rb * kRowLd + 8 * ch]) = wb;
-      if (k < kLat) {
-        const uint32_t xa[4] = {wa.x, wa.y, wa.z, wa.w};
-        const uint32_t xb[4] = {wb.x, wb.y, wb.z, wb.w};
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const uint32_t lo = (xa[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
-          const uint32_t hi = (xb[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
-          vt32[(8 * ch + e) * (kVtLd / 2) + rp] = lo | (hi << 16);
-        }
-      }
-    }
+    for (int k = 0; k <= kLat; ++k)
+      *reinterpret_cast<u32x4*>(&sh.rows[rr * kRowLd + 8 * (cc + 8 * k)]) = chunk(k);
     __syncthreads();
     if (j + 1 < nsub) fetch(j + 1);   // in flight during this sub-chunk's matrix work
 
-    // ---- S = Q K^T for this wave's 16 heads and the 64 rows ---------------
+    // ---- this wave's half of S = Q K^T: 16 heads x 64 rows ----------------
     f32x4 sacc[4];
 #pragma unroll
     for (int n = 0; n < 4; ++n) sacc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int ks = 0; ks < HC_OUT_ELEMS / 32; ++ks) {
-      const bf16x8 a = qa[ks];
+    for (int ks = 0; ks < kHalfK; ++ks) {
+      const int kk = kHalfK * half + ks;
 #pragma unroll
       for (int n = 0; n < 4; ++n) {
         const bf16x8 b = *reinterpret_cast<const bf16x8*>(
-            &sh.rows[(16 * n + (lane & 15)) * kRowLd + 32 * ks + 8 * (lane >> 4)]);
-        sacc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, sacc[n], 0, 0, 0);
+            &sh.rows[(16 * n + (lane & 15)) * kRowLd + 32 * kk + 8 * (lane >> 4)]);
+        sacc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[ks], b, sacc[n], 0, 0, 0);
       }
     }
+    // ---- the pair's two halves added through LDS ----------------------------
+    float* mine = sh.sx + wave * 1024;
+#pragma unroll
+    for (int n = 0; n < 4; ++n)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) mine[n * 256 + i * 64 + lane] = sacc[n][i];
+    __syncthreads();
+    const float* other = sh.sx + (wave ^ 4) * 1024;
+#pragma unroll
+    for (int n = 0; n < 4; ++n)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sacc[n][i] += other[n * 256 + i * 64 + lane];
+
     // ---- online softmax: lane holds heads 4*(lane/16)+i of row 16n + lane%16
     float mx[4];
 #pragma unroll
@@ -254,26 +240,32 @@ __global__ __launch_bounds__(kAttThreads) void k_attend(DevState d, const uint16
       m_run[i] = m_new;
     }
 #pragma unroll
-    for (int n = 0; n < 32; ++n)
+    for (int n = 0; n < kDimTiles; ++n)
 #pragma unroll
       for (int i = 0; i < 4; ++i) o[n][i] *= factor[i];
-    // P (bf16) to LDS as [head][row] for the A operand of P.V
-    __bf16* pw = sh.p + wave * 16 * kPLd;
+    // P (bf16) of the head tile to LDS as [head][row], written by half 0
+    __bf16* pw = sh.p + ht * 16 * kPLd;
+    if (half == 0) {
 #pragma unroll
-    for (int n = 0; n < 4; ++n)
+      for (int n = 0; n < 4; ++n)
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        pw[(4 * (lane >> 4) + i) * kPLd + 16 * n + (lane & 15)] = (__bf16)sacc[n][i];
+        for (int i = 0; i < 4; ++i)
+          pw[(4 * (lane >> 4) + i) * kPLd + 16 * n + (lane & 15)] = (__bf16)sacc[n][i];
+    }
     __syncthreads();
-    // ---- O += P V ------------------------------------------------------------
+    // ---- O[:, this half] += P V -------------------------------------------
+    const int grp = lane >> 4, gl = lane & 15;
 #pragma unroll
     for (int ks = 0; ks < kSub / 32; ++ks) {
-      const bf16x8 a = *reinterpret_cast<const bf16x8*>(&pw[(lane & 15) * kPLd + 32 * ks + 8 * (lane >> 4)]);
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(&pw[gl * kPLd + 32 * ks + 8 * grp]);
+      const __bf16* vb = &sh.rows[(32 * ks + 8 * grp + (gl >> 2)) * kRowLd + 256 * half + 4 * (gl & 3)];
 #pragma unroll
-      for (int n = 0; n < 32; ++n) {
-        const bf16x8 b = *reinterpret_cast<const bf16x8*>(
-            &sh.vt[(16 * n + (lane & 15)) * kVtLd + 32 * ks + 8 * (lane >> 4)]);
-        o[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, o[n], 0, 0, 0);
+      for (int n = 0; n < kDimTiles; ++n) {
+        const i16x4 lo = lds_tr4(vb + 16 * n);
+        const i16x4 hi = lds_tr4(vb + 4 * kRowLd + 16 * n);
+        const i16x8 v8 = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        o[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8, v8), o[n],
+                                                      0, 0, 0);
       }
     }
   }
@@ -283,11 +275,11 @@ __global__ __launch_bounds__(kAttThreads) void k_attend(DevState d, const uint16
   float* base = part + (((size_t)slq * gridDim.y + hg) * nsplit + split) * kHeadsPerGroup * kPartStride;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int h = wave * 16 + 4 * (lane >> 4) + i;
+    const int h = ht * 16 + 4 * (lane >> 4) + i;
     float* ph = base + (size_t)h * kPartStride;
 #pragma unroll
-    for (int n = 0; n < 32; ++n) ph[16 * n + (lane & 15)] = o[n][i];
-    if ((lane & 15) == 0) {
+    for (int n = 0; n < kDimTiles; ++n) ph[256 * half + 16 * n + (lane & 15)] = o[n][i];
+    if (half == 0 && (lane & 15) == 0) {
       ph[512] = m_run[i];
       ph[513] = l_run[i];
     }
@@ -315,8 +307,35 @@ __global__ __launch_bounds__(512) void k_attend_merge(const float* __restrict__ 
   out[((size_t)slq * heads + h) * 512 + dd] = acc / L;
 }
 
+// Splits of the K rows: as few as fill the chip in the fewest rounds.  The
+// cost of a choice is (rounds of resident workgroups) x (sub-chunks per split
+// + about one sub-chunk of fixed work per workgroup); ties go to fewer splits,
+// which also means fewer partials to merge.
+struct AttSplit {
+  int nsplit, rows;
+};
+
+AttSplit attend_split(const DevState& d, int heads) {
+  const int64_t units = (int64_t)d.S * d.L * d.Q * (heads / kHeadsPerGroup);
+  AttSplit best{0, 0};
+  double best_cost = 0.0;
+  const int max_split = (d.K + kSub - 1) / kSub;
+  for (int ns = (d.K + kMaxSplitRows - 1) / kMaxSplitRows; ns <= max_split; ++ns) {
+    const int rows = ((d.K + ns - 1) / ns + kSub - 1) / kSub * kSub;
+    const int n = (d.K + rows - 1) / rows;
+    if (n != ns) continue;
+    const int64_t rounds = (units * n + kResident - 1) / kResident;
+    const double cost = (double)rounds * (rows / kSub + 1.2);
+    if (best.nsplit == 0 || cost < best_cost - 1e-9) {
+      best = AttSplit{n, rows};
+      best_cost = cost;
+    }
+  }
+  return best;
+}
+
 uint64_t attend_work_bytes(const DevState& d, int heads) {
-  const uint64_t nsplit = (d.K + kSplitRows - 1) / kSplitRows;
+  const uint64_t nsplit = attend_split(d, heads).nsplit;
   return (uint64_t)d.S * d.L * d.Q * (heads / kHeadsPerGroup) * nsplit * kHeadsPerGroup *
          kPartStride * sizeof(float);
 }
@@ -324,19 +343,19 @@ uint64_t attend_work_bytes(const DevState& d, int heads) {
 hipError_t launch_attend(const DevState& d, bool from_slots, const uint16_t* q, int heads,
                          float scale, const uint16_t* rows, void* work, float* out,
                          hipStream_t st) {
-  const int nsplit = (d.K + kSplitRows - 1) / kSplitRows;
-  dim3 grid(nsplit, heads / kHeadsPerGroup, d.S * d.L * d.Q);
+  const AttSplit sp = attend_split(d, heads);
+  dim3 grid(sp.nsplit, heads / kHeadsPerGroup, d.S * d.L * d.Q);
   float* part = static_cast<float*>(work);
   if (from_slots)
     hipLaunchKernelGGL(k_attend<kFromSlots>, grid, dim3(kAttThreads), 0, st, d, q, heads, scale,
-                       rows, part);
+                       sp.rows, rows, part);
   else
     hipLaunchKernelGGL(k_attend<kFromBuffer>, grid, dim3(kAttThreads), 0, st, d, q, heads, scale,
-                       rows, part);
+                       sp.rows, rows, part);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_attend_merge, dim3(heads, d.S * d.L * d.Q), dim3(512), 0, st, part, heads,
-                     nsplit, out);
+                     sp.nsplit, out);
   return hipGetLastError();
 }
 
