@@ -67,13 +67,15 @@ def traffic_from_profile(kernel_file, workload):
     return float(b.group(1))
 
 
-def run_cpu_baseline(wl, rows, n_steps):
+def run_cpu_baseline(wl, rows, n_steps, threads=0):
     """The oracle as it stands, on the first n_steps of the workload; the rate
-    is taken over steps 1..n_steps-1 (step 0 is the cold fill)."""
+    is taken over steps 1..n_steps-1 (step 0 is the cold fill).  threads = 0:
+    one per selection group, at most 16 (the machine's CPU share)."""
     import numpy as np
     import oracle
     from cache_gather_amd import workload as W
-    threads = max(1, min(16, os.cpu_count() or 1, wl.n_units))
+    if threads <= 0:
+        threads = max(1, min(16, os.cpu_count() or 1, wl.n_units))
     model = oracle.Model(wl.n_sessions, wl.n_layers, wl.layers_per_select, wl.top_k,
                          wl.cache_slots, wl.hcap, rows)
     sc = W.Scores(wl)
@@ -84,6 +86,7 @@ def run_cpu_baseline(wl, rows, n_steps):
         model.step(t, list(s), wl.hist_len(t).astype(np.int64), gather=True, info=False,
                    nthreads=threads)
         times.append(time.perf_counter() - t0)
+        log("cpu baseline: step %d took %.2f s" % (t, times[-1]))
     model.close()
     rows_per_step = wl.n_sessions * wl.n_layers * wl.top_k
     warm = times[1:] if len(times) > 1 else times
@@ -92,10 +95,21 @@ def run_cpu_baseline(wl, rows, n_steps):
         "unit": "rows/s",
         "cores": threads,
         "kind": "oracle",
-        "sample": "first %d decode steps of %s on %d threads (one per selection group); "
-                  "rate over steps 1-%d, cold step 0 took %.2f s" % (
+        "sample": "first %d decode steps of %s on %d threads (at most one per selection "
+                  "group); rate over steps 1-%d, cold step 0 took %.2f s" % (
                       n_steps, wl.name, threads, n_steps - 1, times[0]),
     }
+
+
+def cpu_model():
+    """The host CPU's model name (from /proc/cpuinfo), or None."""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 def copy_ceiling(torch, dev):
@@ -198,6 +212,12 @@ def main():
     ap.add_argument("--workload", default="model78_50k")
     ap.add_argument("--cpu-steps", type=int, default=8)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-threads", type=int, default=0,
+                    help="threads of the CPU oracle baseline (0: one per selection group, "
+                         "at most 16)")
+    ap.add_argument("--cpu-only", action="store_true",
+                    help="time only the CPU oracle baseline on --workload (first --cpu-steps "
+                         "steps, --cpu-threads threads); no GPU work")
     ap.add_argument("--ring", type=int, default=0, metavar="ROWS",
                     help="decode with a recent ring of ROWS rows per layer: every step first "
                          "appends the new position's row of every layer, and batches of "
@@ -227,6 +247,19 @@ def main():
         sys.exit(2)
     if args.warmup < 1 or args.steps < 1:
         sys.exit("need --warmup >= 1 (the cold step) and --steps >= 1")
+
+    if args.cpu_only:
+        from cache_gather_amd import workload as W
+        wl = W.ALL[args.workload]
+        t0 = time.time()
+        rows = W.fill_all_rows(wl)
+        log("host rows generated in %.1fs" % (time.time() - t0))
+        res = run_cpu_baseline(wl, rows, args.cpu_steps, args.cpu_threads)
+        print(json.dumps({"metric": "oracle rows/s (CPU)", "workload": wl.name,
+                          "cpu_baseline": res, "ms_per_step": round(
+                              wl.n_sessions * wl.n_layers * wl.top_k / res["value"] * 1e3, 2),
+                          "nproc": os.cpu_count(), "cpu_model": cpu_model()}), flush=True)
+        return
 
     import numpy as np
     import torch
@@ -524,7 +557,7 @@ def main():
         log("cpu baseline: timed only for the single-query step without a ring")
     elif not args.no_cpu_baseline:
         log("cpu baseline: oracle on the first %d steps ..." % args.cpu_steps)
-        result["cpu_baseline"] = run_cpu_baseline(wl, rows, args.cpu_steps)
+        result["cpu_baseline"] = run_cpu_baseline(wl, rows, args.cpu_steps, args.cpu_threads)
     print(json.dumps(result), flush=True)
 
 
