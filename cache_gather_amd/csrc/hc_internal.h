@@ -84,6 +84,18 @@ struct CopybackArgs {
 
 // 16-byte vector usable with the nontemporal load/store builtins.
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// Global-memory views of row pointers (hot slots, ring, pinned host rows
+// mapped for the device).  Loads through them compile to global loads; through
+// a pointer fetched from a table the compiler emits flat loads, which also
+// count against the LDS counter and so hold up every later LDS wait.
+typedef const __attribute__((address_space(1))) uint8_t gbyte;
+__device__ __forceinline__ gbyte* to_global(const uint8_t* p) { return (gbyte*)p; }
+template <class T>
+__device__ __forceinline__ T gload(gbyte* p) {
+  return *reinterpret_cast<const __attribute__((address_space(1))) T*>(p);
+}
 
 // IEEE-754 totalOrder of a float as an unsigned integer key.
 __device__ __forceinline__ uint32_t order_key(float f) {

@@ -155,13 +155,15 @@ __global__ __launch_bounds__(kAttThreads) void k_attend(DevState d, const uint16
       for (int k = 0; k <= kLat; ++k)
         bv[k] = vr ? *reinterpret_cast<const u32x4*>(base + 64 * k) : u32x4{0u, 0u, 0u, 0u};
     } else {
-      const uint8_t* src = vr ? sh.src[j * kSub + rr] : nullptr;
+      gbyte* src = to_global(vr ? sh.src[j * kSub + rr] : nullptr);
 #pragma unroll
       for (int k = 0; k < kLat; ++k)
-        q8[k] = vr ? *reinterpret_cast<const uint2*>(src + 8 * (cc + 8 * k)) : uint2{0u, 0u};
-      rope = vr ? *reinterpret_cast<const u32x4*>(src + HC_ROPE_OFFSET + 16 * cc)
-                : u32x4{0u, 0u, 0u, 0u};
-      scb = vr ? *reinterpret_cast<const u32x4*>(src + HC_SCALE_OFFSET) : u32x4{0u, 0u, 0u, 0u};
+      {
+        const u32x2 w = vr ? gload<u32x2>(src + 8 * (cc + 8 * k)) : u32x2{0u, 0u};
+        q8[k] = uint2{w.x, w.y};
+      }
+      rope = vr ? gload<u32x4>(src + HC_ROPE_OFFSET + 16 * cc) : u32x4{0u, 0u, 0u, 0u};
+      scb = vr ? gload<u32x4>(src + HC_SCALE_OFFSET) : u32x4{0u, 0u, 0u, 0u};
     }
   };
   auto chunk = [&](int k) -> u32x4 {

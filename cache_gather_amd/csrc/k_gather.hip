@@ -69,7 +69,7 @@ __device__ __forceinline__ float i8f(uint32_t w, int k) {
 // Where pass p of this thread reads its row, where it writes the output row,
 // and (misses only) which slot it fills.
 struct RowJob {
-  const uint8_t* src[kPasses];
+  gbyte* src[kPasses];
   uint8_t* dst[kPasses];
   uint8_t* fill[kPasses];
 };
@@ -91,8 +91,8 @@ __device__ __forceinline__ void run_rows(const RowJob& j, int item) {
 #pragma unroll
   for (int p = 0; p < kPasses; ++p) {
     if (!j.dst[p] && !j.fill[p]) continue;
-    v[p] = *reinterpret_cast<const u32x4*>(j.src[p] + off);
-    if (item < 32) sblk[p] = *reinterpret_cast<const u32x4*>(j.src[p] + HC_SCALE_OFFSET);
+    v[p] = gload<u32x4>(j.src[p] + off);
+    if (item < 32) sblk[p] = gload<u32x4>(j.src[p] + HC_SCALE_OFFSET);
   }
 #pragma unroll
   for (int p = 0; p < kPasses; ++p) {
@@ -195,7 +195,7 @@ __global__ __launch_bounds__(kGatherThreads) void k_gather(DevState d,
         const int64_t sl = (int64_t)s * d.L + g * d.R + lig;
         const size_t QK = (size_t)d.Q * d.K;
         const size_t uk = (size_t)u * QK + k;
-        j.src[p] = d.host[sl] + (size_t)d.miss_pos[uk] * kRow;
+        j.src[p] = to_global(d.host[sl] + (size_t)d.miss_pos[uk] * kRow);
         j.fill[p] = d.hot + ((size_t)sl * d.C + d.victim[uk]) * kSlotStride;
         j.dst[p] = out ? out_b + ((size_t)sl * QK + d.miss_idx[uk]) * out_row_bytes : nullptr;
       }
@@ -221,11 +221,11 @@ __global__ __launch_bounds__(kGatherThreads) void k_gather(DevState d,
     const int32_t enc = slot[i];
     if (enc < 0 && enc >= -d.C) continue;  // missed this step: written by a miss workgroup
     if (enc >= d.C)                        // a row of the recent ring (entry enc - C)
-      j.src[p] = d.ring + ((size_t)sl * d.ring_rows + (enc - d.C)) * kRow;
+      j.src[p] = to_global(d.ring + ((size_t)sl * d.ring_rows + (enc - d.C)) * kRow);
     else if (enc >= 0)                     // a hit
-      j.src[p] = hot + (size_t)enc * kSlotStride;
+      j.src[p] = to_global(hot + (size_t)enc * kSlotStride);
     else                                   // another query's row of a miss: host RAM
-      j.src[p] = d.host[sl] + (size_t)(-(int64_t)enc - d.C - 1) * kRow;
+      j.src[p] = to_global(d.host[sl] + (size_t)(-(int64_t)enc - d.C - 1) * kRow);
     j.dst[p] = orow + (size_t)i * out_row_bytes;
   }
   run_rows(j, item);

@@ -175,12 +175,38 @@ __global__ __launch_bounds__(kSelThreads) void k_select(DevState d, StepArgs a,
   // Copy the candidates into LDS when they fit, counting them per window bin;
   // the bin where the count from the top reaches K is b1.
   const bool cached = n_cand <= kCandCache;
-  const uint2* cand = cached ? sh.u.cand : gcand;
+  // Every pass below visits the candidates through each_cand, with the loop
+  // written once for LDS and once for global memory: through one pointer that
+  // may be either, the compiler emits generic loads that wait for every
+  // outstanding load and LDS operation, one candidate at a time.
+  auto each_cand = [&](auto&& f) {
+    if (cached) {
+#pragma unroll 4
+      for (int i = tid; i < n_cand; i += kSelThreads) f(sh.u.cand[i]);
+    } else {
+      for (int i = tid; i < n_cand; i += kSelThreads) f(gcand[i]);
+    }
+  };
   clear_hist(sh, kBins1);
-  for (int i = tid; i < n_cand; i += kSelThreads) {
-    const uint2 c = gcand[i];
-    if (cached) sh.u.cand[i] = c;
-    atomicAdd(&sh.hist[(c.x >> (32 - kBin1Bits)) - b_lo], 1u);
+  if (cached) {
+    // all of this thread's global reads in flight together
+    constexpr int kCopy = kCandCache / kSelThreads;   // 8
+    uint2 c[kCopy];
+#pragma unroll
+    for (int r = 0; r < kCopy; ++r) {
+      const int i = r * kSelThreads + tid;
+      c[r] = i < n_cand ? gcand[i] : uint2{0u, 0u};
+    }
+#pragma unroll
+    for (int r = 0; r < kCopy; ++r) {
+      const int i = r * kSelThreads + tid;
+      if (i >= n_cand) continue;
+      sh.u.cand[i] = c[r];
+      atomicAdd(&sh.hist[(c[r].x >> (32 - kBin1Bits)) - b_lo], 1u);
+    }
+  } else {
+    for (int i = tid; i < n_cand; i += kSelThreads)
+      atomicAdd(&sh.hist[(gcand[i].x >> (32 - kBin1Bits)) - b_lo], 1u);
   }
   __syncthreads();
   int rel, beyond;
@@ -191,18 +217,16 @@ __global__ __launch_bounds__(kSelThreads) void k_select(DevState d, StepArgs a,
   // ---- 1. exact cut key T and position cut among keys equal to T ----------
   int d2, d3, skip;
   clear_hist(sh, 1024);
-  for (int i = tid; i < n_cand; i += kSelThreads) {
-    const uint32_t k = cand[i].x;
-    if ((k >> 20) == b1) atomicAdd(&sh.hist[(k >> 10) & 1023], 1u);
-  }
+  each_cand([&](const uint2 c) {
+    if ((c.x >> 20) == b1) atomicAdd(&sh.hist[(c.x >> 10) & 1023], 1u);
+  });
   __syncthreads();
   find_digit(sh.hist, 1024, r, true, sh, d2, skip);
   r -= skip;
   clear_hist(sh, 1024);
-  for (int i = tid; i < n_cand; i += kSelThreads) {
-    const uint32_t k = cand[i].x;
-    if ((k >> 10) == ((b1 << 10) | (uint32_t)d2)) atomicAdd(&sh.hist[k & 1023], 1u);
-  }
+  each_cand([&](const uint2 c) {
+    if ((c.x >> 10) == ((b1 << 10) | (uint32_t)d2)) atomicAdd(&sh.hist[c.x & 1023], 1u);
+  });
   __syncthreads();
   find_digit(sh.hist, 1024, r, true, sh, d3, skip);
   r -= skip;
@@ -214,27 +238,24 @@ __global__ __launch_bounds__(kSelThreads) void k_select(DevState d, StepArgs a,
     int e1, e2, e3, below;
     __syncthreads();
     clear_hist(sh, 2048);
-    for (int i = tid; i < n_cand; i += kSelThreads) {
-      const uint2 c = cand[i];
+    each_cand([&](const uint2 c) {
       if (c.x == T) atomicAdd(&sh.hist[c.y >> 20], 1u);
-    }
+    });
     __syncthreads();
     find_digit(sh.hist, 2048, r, false, sh, e1, below);
     r -= below;
     clear_hist(sh, 1024);
-    for (int i = tid; i < n_cand; i += kSelThreads) {
-      const uint2 c = cand[i];
+    each_cand([&](const uint2 c) {
       if (c.x == T && (int)(c.y >> 20) == e1) atomicAdd(&sh.hist[(c.y >> 10) & 1023], 1u);
-    }
+    });
     __syncthreads();
     find_digit(sh.hist, 1024, r, false, sh, e2, below);
     r -= below;
     clear_hist(sh, 1024);
     const uint32_t hi = ((uint32_t)e1 << 10) | (uint32_t)e2;
-    for (int i = tid; i < n_cand; i += kSelThreads) {
-      const uint2 c = cand[i];
+    each_cand([&](const uint2 c) {
       if (c.x == T && (c.y >> 10) == hi) atomicAdd(&sh.hist[c.y & 1023], 1u);
-    }
+    });
     __syncthreads();
     find_digit(sh.hist, 1024, r, false, sh, e3, below);
     pcut = (int32_t)((hi << 10) | (uint32_t)e3);
@@ -247,34 +268,51 @@ __global__ __launch_bounds__(kSelThreads) void k_select(DevState d, StepArgs a,
     sh.n_ring = 0;
   }
   __syncthreads();
-  const int32_t* above = above_g;
   int32_t pmax = 0;
-  for (int i = tid; i < n_above; i += kSelThreads) {
-    const int32_t p = above[i];
-    sh.mpos[i] = p;
-    pmax = max(pmax, p);
+  {
+    // n_above < K: at most 4 per thread, all reads in flight together
+    constexpr int kAbove = HC_MAX_TOPK / kSelThreads;
+    int32_t ap[kAbove];
+#pragma unroll
+    for (int r = 0; r < kAbove; ++r) {
+      const int i = r * kSelThreads + tid;
+      ap[r] = i < n_above ? above_g[i] : 0;
+    }
+#pragma unroll
+    for (int r = 0; r < kAbove; ++r) {
+      const int i = r * kSelThreads + tid;
+      if (i >= n_above) continue;
+      sh.mpos[i] = ap[r];
+      pmax = max(pmax, ap[r]);
+    }
   }
   // candidates that win, compacted per wave: one LDS atomic per wave
   const uint64_t lt_mask = (lane_id() == 0) ? 0ull : (~0ull >> (64 - lane_id()));
-  for (int i0 = 0; i0 < n_cand; i0 += kSelThreads) {
-    const int i = i0 + tid;
-    bool win = false;
-    int32_t p = 0;
-    if (i < n_cand) {
-      const uint2 c = cand[i];
-      p = (int32_t)c.y;
-      win = c.x > T || (c.x == T && p <= pcut);
+  auto win_pass = [&](auto&& cand_at) {
+    for (int i0 = 0; i0 < n_cand; i0 += kSelThreads) {
+      const int i = i0 + tid;
+      bool win = false;
+      int32_t p = 0;
+      if (i < n_cand) {
+        const uint2 c = cand_at(i);
+        p = (int32_t)c.y;
+        win = c.x > T || (c.x == T && p <= pcut);
+      }
+      const uint64_t bal = __ballot(win);
+      int base = 0;
+      if (lane_id() == 0 && bal) base = atomicAdd(&sh.bcast[2], __popcll(bal));
+      base = __shfl(base, 0, 64);
+      if (win) {
+        const int o = n_above + base + __popcll(bal & lt_mask);
+        if (o < K) sh.mpos[o] = p;  // exactly K - n_above winners by construction
+        pmax = max(pmax, p);
+      }
     }
-    const uint64_t bal = __ballot(win);
-    int base = 0;
-    if (lane_id() == 0 && bal) base = atomicAdd(&sh.bcast[2], __popcll(bal));
-    base = __shfl(base, 0, 64);
-    if (win) {
-      const int o = n_above + base + __popcll(bal & lt_mask);
-      if (o < K) sh.mpos[o] = p;  // exactly K - n_above winners by construction
-      pmax = max(pmax, p);
-    }
-  }
+  };
+  if (cached)
+    win_pass([&](int i) { return sh.u.cand[i]; });
+  else
+    win_pass([&](int i) { return gcand[i]; });
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) pmax = max(pmax, __shfl_xor(pmax, o, 64));
   if (lane_id() == 0) atomicMax(&sh.wmax, pmax);
