@@ -52,6 +52,7 @@ class Pair:
         self.out, self.sel, self.trace = self.hc.alloc_outputs(trace=True)
         self.d_scores = torch.empty((wl.n_units * queries, self.stride), dtype=torch.float32,
                                     device=self.dev)
+        self.evictions = 0   # over all compared steps and units, as the oracle counts them
 
     def scores_for(self, t):
         return self.scores.step(t, self.stride, queries=self.Q)
@@ -92,6 +93,7 @@ class Pair:
                 msg = "step %d unit %d" % (t, u)
                 assert tr[0] == info["n_hit"] and tr[1] == info["n_miss"], msg
                 assert tr[2] == info["n_evict"] and tr[3] == info["n_ring"], msg
+                self.evictions += int(info["n_evict"])
                 base = hc.TRACE_HEADER
                 np.testing.assert_array_equal(tr[base:base + K], info["slot"], err_msg=msg)
                 np.testing.assert_array_equal(tr[base + K:base + 2 * K], info["miss_pos"],
@@ -166,6 +168,7 @@ class RingPair(Pair):
                 h[:self.first] = self.rows[s][l][:self.first]
                 h[self.first:] = 0
                 self.orc_host[s][l][:self.first] = self.rows[s][l][:self.first]
+        self.evictions = 0
         self.orc = oracle.Model(S, L, wl.layers_per_select, wl.top_k, wl.cache_slots, wl.hcap,
                                 self.orc_host, ring_rows=ring_rows, copyback_rows=copyback_rows,
                                 queries=queries)

@@ -51,6 +51,17 @@ def test_eight_queries_groups_and_sessions():
     p.close()
 
 
+def test_slots_equal_to_the_round_rows():
+    """C = Q * K, the smallest cache a round is allowed: a round with Q
+    disjoint selections uses every slot."""
+    wl = W.TINY.with_(name="mtp_min_slots", top_k=64, cache_slots=256, steps=20,
+                      sigma_bias=(0.3,), sigma_noise=(1.0,))
+    p = _pair(wl, 4)
+    p.run()
+    assert p.evictions > 0
+    p.close()
+
+
 def test_identical_queries_share_every_miss():
     """All Q queries select the same positions: every miss is one fill plus
     Q - 1 rows read from host RAM, and all queries' rows are equal."""

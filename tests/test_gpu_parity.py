@@ -43,6 +43,10 @@ SMALL_CASES = [
     ("h_equals_k", 1, 1, 1, 2048, 1, 2048, 2048, 1.0, 1.0),
     ("many_sessions", 9, 1, 1, 9000, 6, 1100, 1000, 0.5, 1.0),
     ("wide_slots", 1, 1, 1, 90000, 6, 65536, 2048, 0.2, 1.0),
+    # the LRU queue: compaction nearly every step with live and dead entries mixed
+    ("lru_churn", 1, 2, 1, 6000, 60, 400, 300, 0.6, 1.0),
+    # the LRU queue: long runs between compactions, evictions once the cache is full
+    ("lru_long_queue", 1, 1, 1, 20000, 80, 2048, 64, 0.5, 1.0),
 ]
 
 
@@ -52,6 +56,8 @@ def test_small_configurations(case):
     wl = W.Workload(name, S, L, R, H0, steps, C, K, (sb,) * S, (sn,) * S, 4242)
     p = _pair(wl)
     p.run()
+    if name.startswith("lru_"):
+        assert p.evictions > 0, "the case must evict to exercise the LRU queue"
     p.close()
 
 
