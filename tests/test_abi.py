@@ -10,8 +10,8 @@ from cache_gather_amd import hc
 def test_library_exports_every_declared_function():
     names = hc.declared_functions()
     assert set(names) >= {"hc_workspace_bytes", "hc_create", "hc_host_rows", "hc_step",
-                          "hc_append", "hc_flush",
-                          "hc_export_state", "hc_profile_enable", "hc_profile_read",
+                          "hc_append", "hc_flush", "hc_attend_workspace_bytes", "hc_attend",
+                          "hc_attend_cached", "hc_export_state", "hc_profile_enable", "hc_profile_read",
                           "hc_steps_done", "hc_destroy", "hc_status_str"}
     L = hc.lib()
     for n in names:
