@@ -362,7 +362,6 @@ hc_status hc_step(hc_ctx* c, void* stream, const float* d_scores, uint64_t score
     if (s < S && c->first[s] >= 0)
       a.ring_lo[s] = (uint32_t)std::max(c->first[s], c->end[s] - (int64_t)c->cfg.ring_rows);
   }
-  const int n_chunks = (int)((max_len + kScanChunk - 1) / kScanChunk);
   const bool vec4 =
       (reinterpret_cast<uintptr_t>(d_scores) % 16 == 0) && (score_stride % 4 == 0);
 
@@ -373,7 +372,7 @@ hc_status hc_step(hc_ctx* c, void* stream, const float* d_scores, uint64_t score
   hipError_t e = mark(0);
   if (e == hipSuccess && c->t == 0 && c->dev.hcap >= kColdMinPositions)
     e = launch_cold_cut(c->dev, a, d_scores, score_stride, (int64_t)max_len, st);
-  if (e == hipSuccess) e = launch_topk_scan(c->dev, a, d_scores, score_stride, n_chunks, vec4, st);
+  if (e == hipSuccess) e = launch_topk_scan(c->dev, a, d_scores, score_stride, (int64_t)max_len, vec4, st);
   if (e == hipSuccess) e = mark(1);
   if (e == hipSuccess) e = launch_select(c->dev, a, d_scores, score_stride, d_sel, d_trace, st);
   if (e == hipSuccess && c->dev.Q > 1) e = launch_round(c->dev, a, d_sel, d_trace, st);

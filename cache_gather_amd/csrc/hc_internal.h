@@ -15,7 +15,7 @@ constexpr int kOut = HC_OUT_ELEMS;        // 576 bf16 per gathered row
 constexpr int kBin1Bits = 12;             // first radix digit: key bits [20, 32)
 constexpr int kBins1 = 1 << kBin1Bits;    // 4096 histogram bins per unit
 constexpr int kMaxSessions = HC_MAX_SESSIONS;  // session lengths travel as kernel args
-constexpr int kScanChunk = 4096;          // scores per workgroup of the score scan (16 per thread)
+constexpr int64_t kScanSmallMax = 131072;  // histories up to this scan in 2,048-score chunks, longer in 4,096
 constexpr int kMaxUnits = HC_MAX_UNITS;   // S * G: the per-unit miss prefix lives in LDS
 
 // Per-selection-unit counters (int32 each): unit su owns cnt[su * kCntStride ..
@@ -119,7 +119,7 @@ __device__ __forceinline__ void cut_window(int prev, uint32_t& lo, uint32_t& hi)
 // Launchers (each defined next to its kernel).  All return hipGetLastError().
 hipError_t launch_init(const DevState& d, hipStream_t st);
 hipError_t launch_topk_scan(const DevState& d, const StepArgs& a, const float* scores,
-                            uint64_t stride, int n_chunks, bool vec4, hipStream_t st);
+                            uint64_t stride, int64_t max_len, bool vec4, hipStream_t st);
 // First step only (needs hcap >= kColdMinPositions): sets every selection
 // unit's cut bin from a histogram of its scores.
 constexpr int64_t kColdMinPositions = 2048;   // the histogram borrows 16 KB of `cand`

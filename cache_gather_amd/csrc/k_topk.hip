@@ -28,7 +28,7 @@
 // the bin holding the K-th key, so the first step's lists are as small as any
 // other step's.
 //
-// Grid = (chunks of 4,096 positions) x (selection units: one per query row of
+// Grid = (chunks of 2,048 or 4,096 positions) x (selection units: one per query row of
 // each session and group), 256 threads; HBM-bound streaming read of 4 B per
 // position.
 #include "hc_internal.h"
@@ -36,11 +36,10 @@
 namespace hc {
 
 constexpr int kScanThreads = 256;
-constexpr int kPerThread = kScanChunk / kScanThreads;  // 16 scores per thread
 
 // Loads this thread's scores of the chunk: element j of the thread is position
 // base + pos[j]; positions >= n are invalid.
-template <bool VEC>
+template <bool VEC, int kPerThread>
 __device__ __forceinline__ void load_chunk(const float* src, int n, float (&x)[kPerThread],
                                            int (&pos)[kPerThread]) {
   const int tid = threadIdx.x;
@@ -86,7 +85,8 @@ __device__ __forceinline__ int block_incl_scan256(int v, int* wtot) {
   return x + off;
 }
 
-template <bool VEC>
+// CHUNK scores per workgroup (2,048 or 4,096), CHUNK / 256 per thread.
+template <bool VEC, int CHUNK>
 __global__ __launch_bounds__(kScanThreads) void k_topk_scan(DevState d, StepArgs a,
                                                             const float* __restrict__ scores,
                                                             uint64_t stride) {
@@ -94,9 +94,10 @@ __global__ __launch_bounds__(kScanThreads) void k_topk_scan(DevState d, StepArgs
   __shared__ int off_above, off_cand;
   const int u = blockIdx.y;  // selection unit (s, g, q)
   const int64_t H = a.hist_len[u / (d.G * d.Q)];
-  const int64_t base = (int64_t)blockIdx.x * kScanChunk;
+  constexpr int kPerThread = CHUNK / kScanThreads;
+  const int64_t base = (int64_t)blockIdx.x * CHUNK;
   if (base >= H) return;
-  const int n = (int)(H - base < kScanChunk ? H - base : kScanChunk);
+  const int n = (int)(H - base < CHUNK ? H - base : CHUNK);
   const int tid = threadIdx.x;
 
   // predicted cut window from the previous step's cut bin (-1: none yet)
@@ -105,7 +106,7 @@ __global__ __launch_bounds__(kScanThreads) void k_topk_scan(DevState d, StepArgs
 
   float x[kPerThread];
   int pos[kPerThread];
-  load_chunk<VEC>(scores + (uint64_t)u * stride + base, n, x, pos);
+  load_chunk<VEC, kPerThread>(scores + (uint64_t)u * stride + base, n, x, pos);
   uint32_t key[kPerThread];
   int na = 0, nc = 0;
 #pragma unroll
@@ -228,12 +229,22 @@ hipError_t launch_cold_cut(const DevState& d, const StepArgs& a, const float* sc
 }
 
 hipError_t launch_topk_scan(const DevState& d, const StepArgs& a, const float* scores,
-                            uint64_t stride, int n_chunks, bool vec4, hipStream_t st) {
-  dim3 grid(n_chunks, d.S * d.G * d.Q);
-  if (vec4)
-    hipLaunchKernelGGL(k_topk_scan<true>, grid, dim3(kScanThreads), 0, st, d, a, scores, stride);
+                            uint64_t stride, int64_t max_len, bool vec4, hipStream_t st) {
+  // Short histories: more, smaller workgroups (the scan is latency-bound);
+  // long ones: fewer, because every workgroup bumps its unit's list counters
+  // (measured: 2,048-score chunks 4.95 vs 6.2 us at 50K positions x 20 units,
+  // but 39 vs 25 us at 1M positions x 16 units).
+  const bool small = max_len <= kScanSmallMax;
+  const int chunk = small ? 2048 : 4096;
+  dim3 grid((unsigned)((max_len + chunk - 1) / chunk), d.S * d.G * d.Q);
+  if (vec4 && small)
+    hipLaunchKernelGGL((k_topk_scan<true, 2048>), grid, dim3(kScanThreads), 0, st, d, a, scores, stride);
+  else if (vec4)
+    hipLaunchKernelGGL((k_topk_scan<true, 4096>), grid, dim3(kScanThreads), 0, st, d, a, scores, stride);
+  else if (small)
+    hipLaunchKernelGGL((k_topk_scan<false, 2048>), grid, dim3(kScanThreads), 0, st, d, a, scores, stride);
   else
-    hipLaunchKernelGGL(k_topk_scan<false>, grid, dim3(kScanThreads), 0, st, d, a, scores, stride);
+    hipLaunchKernelGGL((k_topk_scan<false, 4096>), grid, dim3(kScanThreads), 0, st, d, a, scores, stride);
   return hipGetLastError();
 }
 
