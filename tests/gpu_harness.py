@@ -144,7 +144,7 @@ class RingPair(Pair):
     of appended positions so that the ring is selected from."""
 
     def __init__(self, wl, ring_rows, copyback_rows, recent_boost=1.0, device=0, skip=None,
-                 queries=1):
+                 queries=1, replacement=0, score_stride=None):
         self.ring_rows, self.copyback_rows = ring_rows, copyback_rows
         self.Q = queries
         self.first = wl.hist0 - 1
@@ -155,10 +155,11 @@ class RingPair(Pair):
         say("ring workload", wl.name, "S=%d L=%d K=%d C=%d H0=%d steps=%d ring=%d batch=%d" % (
             wl.n_sessions, wl.n_layers, wl.top_k, wl.cache_slots, wl.hist0, wl.steps,
             ring_rows, copyback_rows))
-        self.stride = align4(wl.hcap)
+        self.stride = align4(wl.hcap) if score_stride is None else score_stride
         self.hc = hc.HotCache(wl.n_sessions, wl.n_layers, wl.layers_per_select,
                               wl.cache_slots, wl.top_k, wl.hcap, device,
-                              ring_rows=ring_rows, copyback_rows=copyback_rows, queries=queries)
+                              ring_rows=ring_rows, copyback_rows=copyback_rows, queries=queries,
+                              replacement=replacement)
         S, L = wl.n_sessions, wl.n_layers
         self.rows = [[W.fill_rows(wl, s, l) for l in range(L)] for s in range(S)]
         self.orc_host = [[np.zeros_like(self.rows[s][l]) for l in range(L)] for s in range(S)]
@@ -171,7 +172,7 @@ class RingPair(Pair):
         self.evictions = 0
         self.orc = oracle.Model(S, L, wl.layers_per_select, wl.top_k, wl.cache_slots, wl.hcap,
                                 self.orc_host, ring_rows=ring_rows, copyback_rows=copyback_rows,
-                                queries=queries)
+                                queries=queries, replacement=replacement)
         self.end = [self.first] * S
         self.scores = W.Scores(wl)
         self.out, self.sel, self.trace = self.hc.alloc_outputs(trace=True)
