@@ -89,7 +89,18 @@ __device__ __forceinline__ void lru_victims(const DevState& d, int u, int32_t t,
 
   // the first m live, untouched entries from the head
   if (tid == 0) *scratch = h - 1;   // queue index of the last victim
+  const int fill = cnt[kCntFill];
   int found = 0;
+  if (fill + m <= C) {
+    // Never-used slots remain for every miss.  They are the oldest (last use
+    // -1, none of them touched this step) and were entered in slot order
+    // before anything else, so the head entry is (fill, -1), followed by
+    // (fill + 1, -1) ...: the victims are fill .. fill + m - 1 and the head
+    // moves past m entries, without reading the queue.
+    for (int k = tid; k < m; k += kSelThreads) vic[k] = fill + k;
+    if (tid == 0) *scratch = h + m - 1;
+    found = m;
+  }
   for (int j0 = h & ~(kPer - 1); found < m && j0 < e; j0 += kSelThreads * kPer) {
     const int jb = j0 + tid * kPer;
     int2 ent[kPer];
@@ -205,6 +216,7 @@ __device__ __forceinline__ void lru_victims(const DevState& d, int u, int32_t t,
     cnt[kCntQHead] = fits ? hn : 0;
     cnt[kCntQTail] = o0 < QC ? o0 : QC;
     cnt[kCntQBuf] = fits ? b : (b ^ 1);
+    cnt[kCntFill] = fill + m < C ? fill + m : C;
   }
 }
 

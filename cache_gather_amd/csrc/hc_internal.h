@@ -26,10 +26,12 @@ constexpr int kMaxUnits = HC_MAX_UNITS;   // S * G: the per-unit miss prefix liv
 // own, because atomics on neighbouring addresses queue behind each other
 // (measured: 16 units x 257 workgroups took 58 us packed, 20 us spread, 13 us
 // without atomics).
-// kCntQHead / kCntQTail / kCntQBuf: the LRU queue of the unit (at su = u * Q).
+// kCntQHead / kCntQTail / kCntQBuf: the LRU queue of the unit (at su = u * Q);
+// kCntFill: slots the unit's LRU has filled so far (slots [fill, C) were never
+// used).
 enum {
   kCntAbove = 0, kCntCand = 1, kCntMiss = 2, kCntBin1 = 3, kCntHand = 4,
-  kCntQHead = 5, kCntQTail = 6, kCntQBuf = 7, kCnt = 8
+  kCntQHead = 5, kCntQTail = 6, kCntQBuf = 7, kCntFill = 8, kCnt = 9
 };
 constexpr int kCntStride = 64;
 
