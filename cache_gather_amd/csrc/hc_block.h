@@ -53,20 +53,24 @@ __device__ __forceinline__ int block_flag_rank(bool f, int32_t* wtot, int& total
   return off + below;
 }
 
-// LRU victims of unit u at step t without any search.  The unit's queue holds
-// (slot, step) entries in ascending (step, slot) order between a head and a
-// tail: each step appends the slots it used (hits and victims) at the tail in
-// slot order, stamped with the step.  An entry is live while the slot's
-// last_use still equals its stamp; a slot used again later has a newer entry,
-// so the old one is dead without being touched.  The callers stamp the hits'
-// last_use before this runs and the victims' after it.  `touched` (LDS bitmap)
-// marks the slots the step's hits use; the m victims are the first m live,
-// untouched entries from the head (written to vic[0, m)), and everything
-// before the last of them is dead afterwards, so the head moves past it.  A
-// step reads about m entries instead of C.  When the tail would pass the
-// buffer's end (2C entries: once every C / K steps or so) the live entries are
-// compacted into the other buffer, followed by the step's slots.
-// n_touched = hits + m; `scratch` is one int of LDS.
+// LRU victims of unit u at step t without any search.  Slots are filled in
+// slot order while never-used ones remain: slots [fill, C) have never been
+// used, they are the oldest (last use -1) and no hit touches them, so they come
+// first, lowest slot first, and are not stored anywhere.  The used slots are
+// ordered by the unit's queue of (slot, step) entries in ascending (step, slot)
+// order between a head and a tail: each step appends the slots it used (hits
+// and victims) at the tail in slot order, stamped with the step.  An entry is
+// live while the slot's last_use still equals its stamp; a slot used again
+// later has a newer entry, so the old one is dead without being touched.  The
+// callers stamp the hits' last_use before this runs and the victims' after it.
+// `touched` (LDS bitmap) marks the slots the step's hits use; the m victims
+// (written to vic[0, m)) are the never-used slots from `fill` on, then the
+// first live, untouched queue entries from the head, and everything before the
+// last of those is dead afterwards, so the head moves past it.  A step reads
+// about as many queue entries as it takes victims from the queue, instead of C.
+// When the tail would pass the buffer's end (2C entries: once every C / K
+// steps or so) the live entries are compacted into the other buffer, followed
+// by the step's slots.  n_touched = hits + m; `scratch` is one int of LDS.
 __device__ __forceinline__ void lru_victims(const DevState& d, int u, int32_t t, int m,
                                             int n_touched, uint32_t* touched, int32_t* vic,
                                             int32_t* wtot, int32_t* scratch) {
@@ -87,20 +91,12 @@ __device__ __forceinline__ void lru_victims(const DevState& d, int u, int32_t t,
     }
   };
 
-  // the first m live, untouched entries from the head
-  if (tid == 0) *scratch = h - 1;   // queue index of the last victim
+  // never-used slots first, then the first live, untouched entries from the head
+  if (tid == 0) *scratch = h - 1;   // queue index of the last victim taken from the queue
   const int fill = cnt[kCntFill];
-  int found = 0;
-  if (fill + m <= C) {
-    // Never-used slots remain for every miss.  They are the oldest (last use
-    // -1, none of them touched this step) and were entered in slot order
-    // before anything else, so the head entry is (fill, -1), followed by
-    // (fill + 1, -1) ...: the victims are fill .. fill + m - 1 and the head
-    // moves past m entries, without reading the queue.
-    for (int k = tid; k < m; k += kSelThreads) vic[k] = fill + k;
-    if (tid == 0) *scratch = h + m - 1;
-    found = m;
-  }
+  const int n_new = m < C - fill ? m : C - fill;
+  for (int k = tid; k < n_new; k += kSelThreads) vic[k] = fill + k;
+  int found = n_new;
   for (int j0 = h & ~(kPer - 1); found < m && j0 < e; j0 += kSelThreads * kPer) {
     const int jb = j0 + tid * kPer;
     int2 ent[kPer];
@@ -216,7 +212,7 @@ __device__ __forceinline__ void lru_victims(const DevState& d, int u, int32_t t,
     cnt[kCntQHead] = fits ? hn : 0;
     cnt[kCntQTail] = o0 < QC ? o0 : QC;
     cnt[kCntQBuf] = fits ? b : (b ^ 1);
-    cnt[kCntFill] = fill + m < C ? fill + m : C;
+    cnt[kCntFill] = fill + n_new;
   }
 }
 

@@ -127,14 +127,12 @@ __global__ void k_init(DevState d, int64_t n_pos, int64_t n_slots) {
   for (int64_t i = i0; i < n_slots; i += stride) {
     d.slot2pos[i] = -1;
     d.last_use[i] = -1;
-    const int64_t u = i / d.C, v = i - u * d.C;
-    d.oq[(u * 2) * (int64_t)d.qcap + v] = make_int2((int32_t)v, -1);   // buffer 0: every slot, never used
   }
   const int64_t sel_units = (int64_t)d.S * d.G * d.Q;
   for (int64_t i = i0; i < sel_units * d.K; i += stride) d.sel_slot[i] = 0;
   for (int64_t i = i0; i < sel_units * kCntStride; i += stride) {
     const int64_t f = i % kCntStride;
-    d.cnt[i] = f == kCntBin1 ? -1 : f == kCntQTail ? d.C : 0;   // queue [0, C) in buffer 0
+    d.cnt[i] = f == kCntBin1 ? -1 : 0;   // empty LRU queues, no slot filled
   }
   // the first step's cut histograms (see launch_cold_cut)
   if (d.hcap >= kColdMinPositions)

@@ -44,8 +44,9 @@ struct DevState {
   int32_t* pos2slot;   // [U][hcap]  slot holding a position, -1 if none
   int32_t* slot2pos;   // [U][C]     position held by a slot, -1 if empty
   int32_t* last_use;   // [U][C]     step of the slot's last use, -1 if never
-  int2* oq;            // [U][2][qcap] LRU queue of (slot, step) in ascending (step, slot);
-                       //            an entry is live while last_use[slot] == step
+  int2* oq;            // [U][2][qcap] LRU queue of (slot, step) in ascending (step, slot)
+                       //            over the used slots; an entry is live while
+                       //            last_use[slot] == step
   int32_t qcap;        // entries per queue buffer: 2 C rounded up to a multiple of 4
   int32_t* cnt;        // [U*Q][kCntStride] per selection unit; the round's miss count at su = u*Q
   int32_t* above;      // [U*Q][K]   positions whose top digit beats the cut bin
