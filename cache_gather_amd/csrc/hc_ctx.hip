@@ -461,7 +461,8 @@ hc_status attend(hc_ctx* c, void* stream, bool from_slots, const uint16_t* d_q, 
   if (c->poisoned) return HC_E_STATE;
   if (!d_q || !d_work || !d_out || (!from_slots && !d_rows)) return HC_E_INVAL;
   if (heads == 0 || heads % 64 || heads > 4096) return HC_E_INVAL;
-  if (reinterpret_cast<uintptr_t>(d_q) % 16 || (d_rows && reinterpret_cast<uintptr_t>(d_rows) % 16))
+  if (reinterpret_cast<uintptr_t>(d_q) % 16 || (d_rows && reinterpret_cast<uintptr_t>(d_rows) % 16) ||
+      reinterpret_cast<uintptr_t>(d_work) % 16 || reinterpret_cast<uintptr_t>(d_out) % 16)
     return HC_E_INVAL;
   if (work_bytes < attend_work_bytes(c->dev, (int)heads)) return HC_E_NOMEM;
   if (c->t == 0) return HC_E_INVAL;   // no step has selected rows yet

@@ -49,6 +49,7 @@ constexpr int kSub = 64;                          // rows per LDS sub-chunk
 constexpr int kRowLd = HC_OUT_ELEMS + 8;          // 584 bf16: padded row-major row
 constexpr int kPLd = kSub + 8;
 constexpr int kPartStride = 516;                  // floats per (head) partial: 512 + m + l + pad
+static_assert(kPartStride % 4 == 0, "partials stay 16-byte aligned");
 constexpr int kHalfK = HC_OUT_ELEMS / 32 / 2;     // 9 Q.K^T k-steps per half
 constexpr int kDimTiles = 512 / 2 / 16;           // 16 P.V dim tiles per half
 
@@ -288,10 +289,14 @@ __global__ __launch_bounds__(kAttThreads) void k_attend(DevState d, const uint16
   }
 }
 
-// Merges the splits of one (slq, head): out = sum_c e^(m_c - M) O_c / sum_c e^(m_c - M) l_c.
+// Merges the splits of four heads of one slq: out = sum_c e^(m_c - M) O_c /
+// sum_c e^(m_c - M) l_c.  128 threads per head, four output values each
+// (16-byte loads and stores; a partial's 516-float stride keeps them aligned).
+constexpr int kMergeHeads = 4;
 __global__ __launch_bounds__(512) void k_attend_merge(const float* __restrict__ part, int heads,
                                                       int nsplit, float* __restrict__ out) {
-  const int h = blockIdx.x, slq = blockIdx.y, dd = threadIdx.x;
+  const int h = blockIdx.x * kMergeHeads + (threadIdx.x >> 7), slq = blockIdx.y;
+  const int dd = 4 * (threadIdx.x & 127);
   const int hg = h / kHeadsPerGroup, hh = h - hg * kHeadsPerGroup;
   const int ngroups = heads / kHeadsPerGroup;
   const float* base = part + (((size_t)slq * ngroups + hg) * nsplit) * kHeadsPerGroup * kPartStride +
@@ -299,14 +304,20 @@ __global__ __launch_bounds__(512) void k_attend_merge(const float* __restrict__ 
   const size_t cstride = (size_t)kHeadsPerGroup * kPartStride;
   float M = -INFINITY;
   for (int c = 0; c < nsplit; ++c) M = fmaxf(M, base[c * cstride + 512]);
-  float L = 0.f, acc = 0.f;
+  float L = 0.f;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
   for (int c = 0; c < nsplit; ++c) {
     const float mc = base[c * cstride + 512];
     const float w = mc == -INFINITY ? 0.f : __expf(mc - M);
     L += w * base[c * cstride + 513];
-    acc += w * base[c * cstride + dd];
+    const float4 o = *reinterpret_cast<const float4*>(base + c * cstride + dd);
+    acc.x += w * o.x;
+    acc.y += w * o.y;
+    acc.z += w * o.z;
+    acc.w += w * o.w;
   }
-  out[((size_t)slq * heads + h) * 512 + dd] = acc / L;
+  *reinterpret_cast<float4*>(out + ((size_t)slq * heads + h) * 512 + dd) =
+      make_float4(acc.x / L, acc.y / L, acc.z / L, acc.w / L);
 }
 
 // Splits of the K rows: as few as fill the chip in the fewest rounds.  The
@@ -356,8 +367,8 @@ hipError_t launch_attend(const DevState& d, bool from_slots, const uint16_t* q, 
                        sp.rows, rows, part);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_attend_merge, dim3(heads, d.S * d.L * d.Q), dim3(512), 0, st, part, heads,
-                     sp.nsplit, out);
+  hipLaunchKernelGGL(k_attend_merge, dim3(heads / kMergeHeads, d.S * d.L * d.Q), dim3(512), 0, st,
+                     part, heads, sp.nsplit, out);
   return hipGetLastError();
 }
 

@@ -239,14 +239,16 @@ hc_status hc_flush(hc_ctx* ctx, void* stream, uint64_t* host_count);
  * are rounded to bf16 for the second product.
  *   d_q      device bf16 bits [S][L][Q][heads][576], 16-B aligned.
  *   heads    a multiple of 64, at most 4096.
- *   d_work   caller-owned device scratch of hc_attend_workspace_bytes(heads).
- *   d_out    device fp32 [S][L][Q][heads][512].
+ *   d_work   caller-owned device scratch of hc_attend_workspace_bytes(heads),
+ *            16-B aligned.
+ *   d_out    device fp32 [S][L][Q][heads][512], 16-B aligned.
  * hc_attend reads the rows from d_rows, the bf16 [S][L][Q][K][576] output of
  * the last hc_step; hc_attend_cached reads them from the hot slots, the recent
  * ring and host RAM (a further query row of a miss), dequantising on the way,
  * so a step with d_out = NULL plus hc_attend_cached never writes the bf16
  * buffer.  Both give the same result bit for bit.  Asynchronous on `stream`;
- * HC_E_INVAL before any hc_step; HC_E_NOMEM if work_bytes is too small. */
+ * HC_E_INVAL before any hc_step or for a pointer that is NULL or not aligned
+ * as stated; HC_E_NOMEM if work_bytes is too small. */
 hc_status hc_attend_workspace_bytes(const hc_ctx* ctx, uint32_t heads, uint64_t* bytes);
 hc_status hc_attend(hc_ctx* ctx, void* stream, const uint16_t* d_q, uint32_t heads, float scale,
                     const uint16_t* d_rows, void* d_work, uint64_t work_bytes, float* d_out);

@@ -139,3 +139,41 @@ def test_model78_page_shape():
     p = Pair(W.MODEL78_50K.with_(steps=3))
     _run(p, 3, 64, layers=[0, 1, 13, 38, 76, 77])
     p.close()
+
+
+def test_invalid_attention_arguments_are_rejected():
+    """Checked on the host before anything is enqueued (HC_E_INVAL, or
+    HC_E_NOMEM for a scratch area that is too small): a call before the first
+    step, heads not a multiple of 64, scratch or output not 16-byte aligned;
+    a valid call afterwards still matches the buffer path."""
+    import torch
+    from cache_gather_amd import hc
+    from gpu_harness import Pair
+    p = Pair(W.TINY.with_(steps=1))
+    heads = 64
+    work, out = p.hc.attention_buffers(heads)
+    q = torch.from_numpy(W.queries(p.wl, 0, heads, 1).view(np.int16)).cuda()
+    st = torch.cuda.current_stream().cuda_stream
+
+    def status(*args):
+        try:
+            hc.hc_attend_cached(p.hc.ctx, st, *args)
+        except hc.HcError as e:
+            return e.status
+        return 0
+
+    assert status(q, heads, SCALE, work, work.numel(), out) == -1      # no step yet
+    g, o = p.step(0)
+    p.compare(0, g, o)
+    assert status(q, 96, SCALE, work, work.numel(), out) == -1         # heads % 64
+    assert status(q, heads, SCALE, work, work.numel() - 1, out) == -2  # scratch too small
+    assert status(q, heads, SCALE, work[4:], work.numel() - 4, out) == -1
+    flat = torch.empty(out.numel() + 4, dtype=torch.float32, device="cuda")
+    assert status(q, heads, SCALE, work, work.numel(), flat[1:]) == -1
+    assert status(q, heads, SCALE, work, work.numel(), out) == 0
+    torch.cuda.synchronize()
+    cached = out.cpu().numpy().copy()
+    p.hc.attend(q, heads, SCALE, p.out, work, out)
+    torch.cuda.synchronize()
+    assert np.array_equal(cached.view(np.uint32), out.cpu().numpy().view(np.uint32))
+    p.close()
