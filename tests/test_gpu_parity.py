@@ -61,6 +61,28 @@ def test_small_configurations(case):
     p.close()
 
 
+@pytest.mark.parametrize("queries", [1, 2])
+def test_step_that_takes_never_used_slots_and_evicts(queries):
+    """C = 1.5 K with low overlap: the first step fills K slots, the next
+    needs more than the C - K never-used slots left, so one step takes those
+    (evicting nothing) and then evicts through the LRU queue.  The traces
+    must show such a step, and every step stays bit-exact."""
+    K = 1024 // queries
+    wl = W.Workload("fill_then_evict_q%d" % queries, 1, 2, 1, 8000, 8, 3 * K * queries // 2, K,
+                    (0.2,), (1.0,), 4243)
+    p = _pair(wl, queries=queries)
+    mixed = 0
+    for t in range(wl.steps):
+        g, o = p.step(t)
+        p.compare(t, g, o)
+        info = o[2][0]
+        if info["n_evict"] > 0 and info["n_miss"] > info["n_evict"]:
+            mixed += 1
+    p.compare_state()
+    assert mixed >= 1, "no step both filled never-used slots and evicted"
+    p.close()
+
+
 def test_unaligned_score_stride_uses_scalar_loads():
     wl = W.Workload("odd_stride", 2, 2, 2, 9001, 5, 600, 300, (0.5, 0.5), (1.0, 1.0), 99)
     p = _pair(wl, score_stride=wl.hcap + 3)
