@@ -47,13 +47,21 @@ constexpr int kRowsPerPass = 8;
 constexpr int kItemsPerRow = 40;
 constexpr int kGatherThreads = kRowsPerPass * kItemsPerRow;  // 320
 constexpr int kPasses = 1;
-constexpr int kRowsPerRound = kRowsPerPass * kPasses;         // 32
+constexpr int kRowsPerRound = kRowsPerPass * kPasses;         // 8
 // Workgroups reserved for the miss list.  Only about one per kMissRowsPerBlock
-// missing rows is active (at least kMissBlocksMin): few CUs then wait on PCIe
-// while the rest stream HBM, and a cold step still has enough reads in flight.
+// missing rows is active (at least kMissBlocksMin): while the hit rows keep HBM
+// busy, few CUs then wait on PCIe and the rest stream HBM (more miss
+// workgroups slowed such steps, even steps the link bounds: a 78-layer step
+// with 5K-55K missing rows among its 160K took 10% longer with one per 16),
+// and a cold step still has enough reads in flight.  A launch with fewer than
+// kFewHitRows other rows has no such stream to protect, and one workgroup per
+// kMissRowsFewHits missing rows keeps more of them in flight (one layer,
+// ~2,000 missing rows of 2,048: 45 -> 36 us).
 constexpr int kMissBlocks = 256;
 constexpr int kMissBlocksMin = 32;
 constexpr int kMissRowsPerBlock = 64;
+constexpr int kMissRowsFewHits = 16;
+constexpr int kFewHitRows = 16384;
 
 __device__ __forceinline__ uint32_t bf16x2(float lo, float hi) {
   const __bf16 a = (__bf16)lo, b = (__bf16)hi;
@@ -131,7 +139,7 @@ __device__ __forceinline__ int layers_in_group(const DevState& d, int g) {
 
 __global__ __launch_bounds__(kGatherThreads) void k_gather(DevState d,
                                                            uint16_t* __restrict__ out,
-                                                           int miss_rows) {
+                                                           int miss_rows, int few_hits_above) {
   extern __shared__ int32_t pref[];          // [S*G + 1]: miss rows (all layers) before unit u
   __shared__ int32_t wsum[kGatherThreads / 64];
   const int item = threadIdx.x % kItemsPerRow;
@@ -172,7 +180,8 @@ __global__ __launch_bounds__(kGatherThreads) void k_gather(DevState d,
     if (threadIdx.x == 0) pref[0] = 0;
     __syncthreads();
     const int M = pref[U];
-    int active = (M + kMissRowsPerBlock - 1) / kMissRowsPerBlock;
+    const int per = M > few_hits_above ? kMissRowsFewHits : kMissRowsPerBlock;
+    int active = (M + per - 1) / per;
     active = active < kMissBlocksMin ? kMissBlocksMin : (active > kMissBlocks ? kMissBlocks : active);
     if (mb >= active) return;
     for (int base = mb * kRowsPerRound; base < M; base += active * kRowsPerRound) {
@@ -239,8 +248,11 @@ hipError_t launch_gather(const DevState& d, uint16_t* d_out, hipStream_t st) {
   const size_t lds = ((size_t)d.S * d.G + 1) * sizeof(int32_t);
   // without an output buffer only the miss workgroups run (they fill slots)
   const int rows = d_out ? d.S * d.L * d.Q + miss_rows : miss_rows;
+  // more than this many missing rows leaves fewer than kFewHitRows other rows
+  const int64_t rows_total = (int64_t)d.S * d.L * d.Q * d.K;
+  const int few_hits_above = (int)(rows_total - kFewHitRows);
   hipLaunchKernelGGL(k_gather, dim3(gx, rows), dim3(kGatherThreads), lds, st, d, d_out,
-                     miss_rows);
+                     miss_rows, few_hits_above);
   return hipGetLastError();
 }
 
