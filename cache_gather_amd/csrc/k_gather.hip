@@ -31,8 +31,11 @@
 //
 // gfx950 mapping: a row is 40 work items — 32 latent chunks (16 B in, 32 B
 // out) and 8 RoPE chunks (16 B in, 16 B out) — so 320 threads (5 wave64) hold
-// 8 rows with every lane busy, one row item per thread (measured on MI355X:
-// keeping several rows per thread in flight streams slower).  Grid rows
+// 8 rows with every lane busy.  A hit workgroup takes two such passes, both
+// rows' loads in flight before the first store (16 rows per workgroup:
+// measured on MI355X with the caches flushed, 3-4% faster than one row per
+// thread, and 4 rows slower again); a miss workgroup keeps one row per thread
+// in flight (two slowed the PCIe reads).  Grid rows
 // [0, miss_rows) are the miss workgroups, dispatched first; grid row
 // miss_rows + sl holds layer sl's hit rows, so no per-row index division is
 // needed (with Q query rows, grid row miss_rows + sl * Q + q).  HBM-bound:
@@ -46,8 +49,9 @@ namespace hc {
 constexpr int kRowsPerPass = 8;
 constexpr int kItemsPerRow = 40;
 constexpr int kGatherThreads = kRowsPerPass * kItemsPerRow;  // 320
-constexpr int kPasses = 1;
-constexpr int kRowsPerRound = kRowsPerPass * kPasses;         // 8
+constexpr int kHitPasses = 2;                                  // rows per thread, hit workgroups
+constexpr int kRowsPerRound = kRowsPerPass * kHitPasses;       // hit rows per workgroup: 16
+constexpr int kMissRowsPerRound = kRowsPerPass;                // missing rows per workgroup round
 // Workgroups reserved for the miss list.  Only about one per kMissRowsPerBlock
 // missing rows is active (at least kMissBlocksMin): while the hit rows keep HBM
 // busy, few CUs then wait on PCIe and the rest stream HBM (more miss
@@ -76,6 +80,7 @@ __device__ __forceinline__ float i8f(uint32_t w, int k) {
 
 // Where pass p of this thread reads its row, where it writes the output row,
 // and (misses only) which slot it fills.
+template <int kPasses>
 struct RowJob {
   gbyte* src[kPasses];
   uint8_t* dst[kPasses];
@@ -93,7 +98,8 @@ __device__ __forceinline__ float scale_of(const u32x4& blk, int g) {
 // issued before the first store.  Latent lanes read their 16 latent bytes and
 // the row's whole 16-B scale block (one address for all 32 lanes of a row, so
 // it costs one request); RoPE lanes read 16 bytes each.
-__device__ __forceinline__ void run_rows(const RowJob& j, int item) {
+template <int kPasses>
+__device__ __forceinline__ void run_rows(const RowJob<kPasses>& j, int item) {
   u32x4 v[kPasses], sblk[kPasses];
   const int off = item < 32 ? 16 * item : HC_ROPE_OFFSET + 16 * (item - 32);
 #pragma unroll
@@ -146,9 +152,9 @@ __global__ __launch_bounds__(kGatherThreads) void k_gather(DevState d,
   const int lrow = threadIdx.x / kItemsPerRow;
   uint8_t* const out_b = reinterpret_cast<uint8_t*>(out);
   const size_t out_row_bytes = (size_t)kOut * 2;
-  RowJob j;
 
   if ((int)blockIdx.y < miss_rows) {
+    RowJob<1> j;
     const int mb = blockIdx.y * gridDim.x + blockIdx.x;  // miss workgroup number
     // ---- dense miss list: prefix of (misses x layers) over units --------
     const int U = d.S * d.G;
@@ -184,30 +190,25 @@ __global__ __launch_bounds__(kGatherThreads) void k_gather(DevState d,
     int active = (M + per - 1) / per;
     active = active < kMissBlocksMin ? kMissBlocksMin : (active > kMissBlocks ? kMissBlocks : active);
     if (mb >= active) return;
-    for (int base = mb * kRowsPerRound; base < M; base += active * kRowsPerRound) {
-#pragma unroll
-      for (int p = 0; p < kPasses; ++p) {
-        const int q = base + p * kRowsPerPass + lrow;
-        j.dst[p] = nullptr;
-        j.fill[p] = nullptr;
-        if (q >= M) continue;
-        int lo = 0, hi = U;  // largest u with pref[u] <= q
-        while (hi - lo > 1) {
-          const int mid = (lo + hi) >> 1;
-          if (pref[mid] <= q) lo = mid;
-          else hi = mid;
-        }
-        const int u = lo, g = u % d.G, s = u / d.G;
-        const int nl = layers_in_group(d, g);
-        const int r = q - pref[u], m = (pref[u + 1] - pref[u]) / nl;
-        const int lig = r / m, k = r - lig * m;
-        const int64_t sl = (int64_t)s * d.L + g * d.R + lig;
-        const size_t QK = (size_t)d.Q * d.K;
-        const size_t uk = (size_t)u * QK + k;
-        j.src[p] = to_global(d.host[sl] + (size_t)d.miss_pos[uk] * kRow);
-        j.fill[p] = d.hot + ((size_t)sl * d.C + d.victim[uk]) * kSlotStride;
-        j.dst[p] = out ? out_b + ((size_t)sl * QK + d.miss_idx[uk]) * out_row_bytes : nullptr;
+    for (int base = mb * kMissRowsPerRound; base < M; base += active * kMissRowsPerRound) {
+      const int q = base + lrow;
+      if (q >= M) break;   // this thread's later rounds lie further beyond M
+      int lo = 0, hi = U;  // largest u with pref[u] <= q
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (pref[mid] <= q) lo = mid;
+        else hi = mid;
       }
+      const int u = lo, g = u % d.G, s = u / d.G;
+      const int nl = layers_in_group(d, g);
+      const int r = q - pref[u], m = (pref[u + 1] - pref[u]) / nl;
+      const int lig = r / m, k = r - lig * m;
+      const int64_t sl = (int64_t)s * d.L + g * d.R + lig;
+      const size_t QK = (size_t)d.Q * d.K;
+      const size_t uk = (size_t)u * QK + k;
+      j.src[0] = to_global(d.host[sl] + (size_t)d.miss_pos[uk] * kRow);
+      j.fill[0] = d.hot + ((size_t)sl * d.C + d.victim[uk]) * kSlotStride;
+      j.dst[0] = out ? out_b + ((size_t)sl * QK + d.miss_idx[uk]) * out_row_bytes : nullptr;
       run_rows(j, item);
     }
     return;
@@ -221,8 +222,9 @@ __global__ __launch_bounds__(kGatherThreads) void k_gather(DevState d,
   const uint8_t* hot = d.hot + (size_t)sl * d.C * kSlotStride;
   uint8_t* orow = out_b + (size_t)hr * d.K * out_row_bytes;
   const int i0 = blockIdx.x * kRowsPerRound + lrow;
+  RowJob<kHitPasses> j;
 #pragma unroll
-  for (int p = 0; p < kPasses; ++p) {
+  for (int p = 0; p < kHitPasses; ++p) {
     const int i = i0 + p * kRowsPerPass;
     j.dst[p] = nullptr;
     j.fill[p] = nullptr;
