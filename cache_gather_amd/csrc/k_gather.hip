@@ -138,6 +138,16 @@ __device__ __forceinline__ void run_rows(const RowJob<kPasses>& j, int item) {
   }
 }
 
+// n / D for 0 <= n < 2^16 by a multiply: m = ceil(2^32 / D), 0 meaning D = 1.
+// Exact because n * (m * D - 2^32) < 2^16 * D <= 2^32 for D < 2^16.
+__device__ __forceinline__ int div_by(int n, uint32_t m) {
+  return m ? (int)__umulhi((uint32_t)n, m) : n;
+}
+
+__host__ __forceinline__ uint32_t div_magic(uint32_t D) {
+  return D == 1 ? 0u : (uint32_t)(((1ull << 32) + D - 1) / D);
+}
+
 __device__ __forceinline__ int layers_in_group(const DevState& d, int g) {
   const int n = d.L - g * d.R;
   return n < d.R ? n : d.R;
@@ -145,7 +155,8 @@ __device__ __forceinline__ int layers_in_group(const DevState& d, int g) {
 
 __global__ __launch_bounds__(kGatherThreads) void k_gather(DevState d,
                                                            uint16_t* __restrict__ out,
-                                                           int miss_rows, int few_hits_above) {
+                                                           int miss_rows, int few_hits_above,
+                                                           uint32_t m_q, uint32_t m_l, uint32_t m_r) {
   extern __shared__ int32_t pref[];          // [S*G + 1]: miss rows (all layers) before unit u
   __shared__ int32_t wsum[kGatherThreads / 64];
   const int item = threadIdx.x % kItemsPerRow;
@@ -216,9 +227,9 @@ __global__ __launch_bounds__(kGatherThreads) void k_gather(DevState d,
 
   // ---- rows of (layer sl, query q), hr = blockIdx.y - miss_rows = sl * Q + q --
   const int hr = blockIdx.y - miss_rows;
-  const int sl = hr / d.Q, q = hr - sl * d.Q;
-  const int s = sl / d.L, l = sl - s * d.L;           // uniform per workgroup
-  const int32_t* slot = d.sel_slot + ((size_t)(s * d.G + l / d.R) * d.Q + q) * d.K;
+  const int sl = div_by(hr, m_q), q = hr - sl * d.Q;   // uniform per workgroup; hr < 2^16
+  const int s = div_by(sl, m_l), l = sl - s * d.L;
+  const int32_t* slot = d.sel_slot + ((size_t)(s * d.G + div_by(l, m_r)) * d.Q + q) * d.K;
   const uint8_t* hot = d.hot + (size_t)sl * d.C * kSlotStride;
   uint8_t* orow = out_b + (size_t)hr * d.K * out_row_bytes;
   const int i0 = blockIdx.x * kRowsPerRound + lrow;
@@ -253,8 +264,10 @@ hipError_t launch_gather(const DevState& d, uint16_t* d_out, hipStream_t st) {
   // more than this many missing rows leaves fewer than kFewHitRows other rows
   const int64_t rows_total = (int64_t)d.S * d.L * d.Q * d.K;
   const int few_hits_above = (int)(rows_total - kFewHitRows);
+  // grid rows stay below 2^16, as div_by requires: S * L * Q <= 60,000 is checked at creation
   hipLaunchKernelGGL(k_gather, dim3(gx, rows), dim3(kGatherThreads), lds, st, d, d_out,
-                     miss_rows, few_hits_above);
+                     miss_rows, few_hits_above, div_magic((uint32_t)d.Q), div_magic((uint32_t)d.L),
+                     div_magic((uint32_t)d.R));
   return hipGetLastError();
 }
 
