@@ -14,12 +14,7 @@ __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 // Inclusive prefix over the block (thread order); `total` gets the block sum.
 __device__ __forceinline__ int block_incl_scan(int v, int32_t* wtot, int& total) {
   const int lane = lane_id(), w = threadIdx.x >> 6;
-  int x = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    int y = __shfl_up(x, o, 64);
-    if (lane >= o) x += y;
-  }
+  const int x = wave_incl_scan(v);
   if (lane == 63) wtot[w] = x;
   __syncthreads();
   int off = 0, tot = 0;

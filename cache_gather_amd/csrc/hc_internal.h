@@ -100,6 +100,55 @@ __device__ __forceinline__ T gload(gbyte* p) {
   return *reinterpret_cast<const __attribute__((address_space(1))) T*>(p);
 }
 
+// Wave-level steps through DPP lane moves (register to register, no LDS round
+// trip as __shfl's ds_bpermute takes).  DPP controls: quad_perm [1,0,3,2]
+// 0xB1 and [2,3,0,1] 0x4E (partner lane ^1, ^2), row_shr:n 0x110 + n (lane
+// - n within a row of 16), row_mirror 0x140 (lane 15 - l of the row),
+// row_half_mirror 0x141 (lane 7 - l of each half row), row_bcast:15 0x142
+// (lane 15 of each row to the next row), row_bcast:31 0x143 (lane 31 to rows
+// 2 and 3).  Lanes whose move has no source are excluded by the conditions.
+template <int kCtrl>
+__device__ __forceinline__ int dpp_i(int x) {
+  return __builtin_amdgcn_mov_dpp(x, kCtrl, 0xf, 0xf, false);
+}
+template <int kCtrl>
+__device__ __forceinline__ float dpp_f(float x) {
+  return __builtin_bit_cast(float, dpp_i<kCtrl>(__builtin_bit_cast(int, x)));
+}
+
+// Inclusive prefix sum over the 64 lanes of the wave.
+__device__ __forceinline__ int wave_incl_scan(int x) {
+  const int lane = threadIdx.x & 63, r = lane & 15;
+  int t;
+  t = dpp_i<0x111>(x); if (r >= 1) x += t;
+  t = dpp_i<0x112>(x); if (r >= 2) x += t;
+  t = dpp_i<0x114>(x); if (r >= 4) x += t;
+  t = dpp_i<0x118>(x); if (r >= 8) x += t;
+  t = dpp_i<0x142>(x); if (lane & 16) x += t;
+  t = dpp_i<0x143>(x); if (lane >= 32) x += t;
+  return x;
+}
+
+// Sum / maximum over each row of 16 lanes, left in every lane of the row.
+// Each level combines a lane with the lane holding the other half of the
+// partial (^1, ^2, the other quad of the half row, the other half row), the
+// same pairs as a butterfly over lane ^1, ^2, ^4, ^8, so every lane gets the
+// same bits.
+__device__ __forceinline__ float row16_sum(float x) {
+  x += dpp_f<0xB1>(x);
+  x += dpp_f<0x4E>(x);
+  x += dpp_f<0x141>(x);
+  x += dpp_f<0x140>(x);
+  return x;
+}
+__device__ __forceinline__ float row16_max(float x) {
+  x = fmaxf(x, dpp_f<0xB1>(x));
+  x = fmaxf(x, dpp_f<0x4E>(x));
+  x = fmaxf(x, dpp_f<0x141>(x));
+  x = fmaxf(x, dpp_f<0x140>(x));
+  return x;
+}
+
 // IEEE-754 totalOrder of a float as an unsigned integer key.
 __device__ __forceinline__ uint32_t order_key(float f) {
   uint32_t b = __float_as_uint(f);

@@ -222,8 +222,7 @@ __global__ __launch_bounds__(kAttThreads) void k_attend(DevState d, const uint16
         sacc[n][i] = ok ? sacc[n][i] * scale : -INFINITY;
         mx[i] = fmaxf(mx[i], sacc[n][i]);
       }
-#pragma unroll
-      for (int off = 1; off < 16; off <<= 1) mx[i] = fmaxf(mx[i], __shfl_xor(mx[i], off, 64));
+      mx[i] = row16_max(mx[i]);
     }
     float factor[4];
 #pragma unroll
@@ -237,8 +236,7 @@ __global__ __launch_bounds__(kAttThreads) void k_attend(DevState d, const uint16
         sacc[n][i] = pv;
         sum += pv;
       }
-#pragma unroll
-      for (int off = 1; off < 16; off <<= 1) sum += __shfl_xor(sum, off, 64);
+      sum = row16_sum(sum);
       l_run[i] = l_run[i] * factor[i] + sum;
       m_run[i] = m_new;
     }

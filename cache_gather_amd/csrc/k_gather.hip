@@ -175,13 +175,8 @@ __global__ __launch_bounds__(kGatherThreads) void k_gather(DevState d,
       const int c = u < U ? d.cnt[(size_t)u * d.Q * kCntStride + kCntMiss] * layers_in_group(d, u % d.G)
                           : 0;
       // block inclusive scan of c
-      int x = c;
       const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const int y = __shfl_up(x, o, 64);
-        if (lane >= o) x += y;
-      }
+      const int x = wave_incl_scan(c);
       if (lane == 63) wsum[w] = x;
       __syncthreads();
       int off = running, tot = 0;

@@ -71,12 +71,7 @@ __device__ __forceinline__ void load_chunk(const float* src, int n, float (&x)[k
 // Inclusive prefix sum over the 256 threads of the block (thread order).
 __device__ __forceinline__ int block_incl_scan256(int v, int* wtot) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  int x = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    int y = __shfl_up(x, o, 64);
-    if (lane >= o) x += y;
-  }
+  const int x = wave_incl_scan(v);
   if (lane == 63) wtot[w] = x;
   __syncthreads();
   int off = 0;
