@@ -149,6 +149,16 @@ __device__ __forceinline__ float row16_max(float x) {
   return x;
 }
 
+// Maximum over the 64 lanes (all active), returned as a wave-uniform value.
+__device__ __forceinline__ int wave_max(int x) {
+  x = max(x, dpp_i<0xB1>(x));
+  x = max(x, dpp_i<0x4E>(x));
+  x = max(x, dpp_i<0x141>(x));
+  x = max(x, dpp_i<0x140>(x));
+  return max(max(__builtin_amdgcn_readlane(x, 0), __builtin_amdgcn_readlane(x, 16)),
+             max(__builtin_amdgcn_readlane(x, 32), __builtin_amdgcn_readlane(x, 48)));
+}
+
 // IEEE-754 totalOrder of a float as an unsigned integer key.
 __device__ __forceinline__ uint32_t order_key(float f) {
   uint32_t b = __float_as_uint(f);

@@ -161,8 +161,9 @@ __global__ __launch_bounds__(kSelThreads) void k_select(DevState d, StepArgs a,
         if (bu) ou = atomicAdd(&sh.bcast[2], __popcll(bu));
         if (be) oe = atomicAdd(&sh.bcast[3], __popcll(be));
       }
-      ou = __shfl(ou, 0, 64) + __popcll(bu & lt);
-      oe = __shfl(oe, 0, 64) + __popcll(be & lt);
+      // every lane is active here, so the first active lane is lane 0
+      ou = __builtin_amdgcn_readfirstlane(ou) + __popcll(bu & lt);
+      oe = __builtin_amdgcn_readfirstlane(oe) + __popcll(be & lt);
       if (up && ou < K) above_g[ou] = (int32_t)i;
       if (eq && oe < d.hcap) gcand[oe] = make_uint2(key, (uint32_t)i);
     }
@@ -301,7 +302,7 @@ __global__ __launch_bounds__(kSelThreads) void k_select(DevState d, StepArgs a,
       const uint64_t bal = __ballot(win);
       int base = 0;
       if (lane_id() == 0 && bal) base = atomicAdd(&sh.bcast[2], __popcll(bal));
-      base = __shfl(base, 0, 64);
+      base = __builtin_amdgcn_readfirstlane(base);   // lane 0's: every lane is active
       if (win) {
         const int o = n_above + base + __popcll(bal & lt_mask);
         if (o < K) sh.mpos[o] = p;  // exactly K - n_above winners by construction
@@ -313,8 +314,7 @@ __global__ __launch_bounds__(kSelThreads) void k_select(DevState d, StepArgs a,
     win_pass([&](int i) { return sh.u.cand[i]; });
   else
     win_pass([&](int i) { return gcand[i]; });
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) pmax = max(pmax, __shfl_xor(pmax, o, 64));
+  pmax = wave_max(pmax);
   if (lane_id() == 0) atomicMax(&sh.wmax, pmax);
   __syncthreads();
   if (sh.bcast[2] != K - n_above) {
