@@ -109,3 +109,20 @@ def test_null_handles():
     out = ctypes.c_void_p(1)
     assert L.hc_create(ctypes.byref(cfg), None, 0, ctypes.byref(out)) == -1
     assert out.value is None
+
+
+@pytest.mark.parametrize("kw", [
+    dict(n_sessions=1, n_layers=1, layers_per_select=1, cache_slots=262144, top_k=4096,
+         max_positions=300004),
+    dict(n_sessions=1, n_layers=2, layers_per_select=1, cache_slots=8192, top_k=512,
+         max_positions=9005, queries=16),
+    dict(n_sessions=256, n_layers=1, layers_per_select=1, cache_slots=96, top_k=64,
+         max_positions=604),
+    dict(n_sessions=1, n_layers=1, layers_per_select=1, cache_slots=1024, top_k=256,
+         max_positions=4112, ring_rows=65536, copyback_rows=8),
+])
+def test_limit_configurations_are_accepted(kw):
+    """Each of HC_MAX_SLOTS, HC_MAX_TOPK, HC_MAX_QUERIES (with Q * K =
+    HC_MAX_ROUND_ROWS = C), HC_MAX_SESSIONS and HC_MAX_RING_ROWS is accepted
+    (the GPU parity tests run these configurations)."""
+    assert hc.hc_workspace_bytes(hc.make_config(**kw)) > 0

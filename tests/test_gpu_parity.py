@@ -177,3 +177,42 @@ def test_dequant_every_int8_with_every_finite_fp16_scale():
         want = np.stack([oracle.dequant_row(rows[x]) for x in range(t * K, (t + 1) * K)])
         np.testing.assert_array_equal(g["out"][0, 0], want)
     p.close()
+
+
+LIMIT_CASES = [
+    # name, S, L, R, H0, steps, C, K, queries, sigma_b, sigma_n, sigma_draft, must_evict
+    ("max_slots_max_topk", 1, 1, 1, 300000, 4, 262144, 4096, 1, 0.2, 1.0, None, False),
+    # HC_MAX_QUERIES query rows of K = 512 fill HC_MAX_ROUND_ROWS = C; independent-looking
+    # query rows (draft noise 3) make the round's union fill the cache by the fourth step
+    ("max_queries_round_rows", 1, 2, 1, 9000, 6, 8192, 512, 16, 0.2, 1.0, 3.0, True),
+    ("max_sessions", 256, 1, 1, 600, 4, 96, 64, 1, 0.5, 1.0, None, True),
+]
+
+
+@pytest.mark.parametrize("case", LIMIT_CASES, ids=[c[0] for c in LIMIT_CASES])
+def test_configuration_limits(case):
+    """The largest slot count with the largest top-K (HC_MAX_SLOTS,
+    HC_MAX_TOPK), the largest number of query rows filling the largest round
+    with C equal to it (HC_MAX_QUERIES, HC_MAX_ROUND_ROWS), and the largest
+    number of sessions (HC_MAX_SESSIONS): every step bit-exact, then the end
+    state."""
+    name, S, L, R, H0, steps, C, K, Q, sb, sn, draft, must_evict = case
+    wl = W.Workload(name, S, L, R, H0, steps, C, K, (sb,) * S, (sn,) * S, 4244)
+    p = _pair(wl, queries=Q)
+    for t in range(steps):
+        sc = None if draft is None else p.scores.step(t, p.stride, queries=Q, sigma_draft=draft)
+        g, o = p.step(t, scores_np=sc)
+        p.compare(t, g, o)
+    p.compare_state()
+    if must_evict:
+        assert p.evictions > 0, "the case must evict"
+    p.close()
+
+
+def test_largest_recent_ring():
+    """HC_MAX_RING_ROWS ring rows per layer with copyback batches of 8: every
+    appended row stays in the ring, the copybacks still reach host RAM."""
+    from gpu_harness import RingPair
+    p = RingPair(W.TINY.with_(name="max_ring", steps=12), 65536, 8)   # HC_MAX_RING_ROWS
+    p.run()
+    p.close()
