@@ -120,9 +120,14 @@ def test_null_handles():
          max_positions=604),
     dict(n_sessions=1, n_layers=1, layers_per_select=1, cache_slots=1024, top_k=256,
          max_positions=4112, ring_rows=65536, copyback_rows=8),
+    dict(n_sessions=16, n_layers=256, layers_per_select=1, cache_slots=80, top_k=48,
+         max_positions=204),
+    dict(n_sessions=1, n_layers=12000, layers_per_select=4, cache_slots=16, top_k=8,
+         max_positions=44),
 ])
 def test_limit_configurations_are_accepted(kw):
     """Each of HC_MAX_SLOTS, HC_MAX_TOPK, HC_MAX_QUERIES (with Q * K =
-    HC_MAX_ROUND_ROWS = C), HC_MAX_SESSIONS and HC_MAX_RING_ROWS is accepted
-    (the GPU parity tests run these configurations)."""
+    HC_MAX_ROUND_ROWS = C), HC_MAX_SESSIONS, HC_MAX_RING_ROWS and HC_MAX_UNITS
+    is accepted, and so are 12,000 layers of one session (the GPU parity tests
+    run these configurations)."""
     assert hc.hc_workspace_bytes(hc.make_config(**kw)) > 0

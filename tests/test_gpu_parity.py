@@ -186,6 +186,8 @@ LIMIT_CASES = [
     # query rows (draft noise 3) make the round's union fill the cache by the fourth step
     ("max_queries_round_rows", 1, 2, 1, 9000, 6, 8192, 512, 16, 0.2, 1.0, 3.0, True),
     ("max_sessions", 256, 1, 1, 600, 4, 96, 64, 1, 0.5, 1.0, None, True),
+    ("max_units", 16, 256, 1, 200, 4, 80, 48, 1, 0.3, 1.0, None, True),      # HC_MAX_UNITS = S * G
+    ("many_layers", 1, 12000, 4, 40, 4, 16, 8, 1, 0.3, 1.0, None, True),     # 12,000 gather grid rows
 ]
 
 
@@ -193,9 +195,10 @@ LIMIT_CASES = [
 def test_configuration_limits(case):
     """The largest slot count with the largest top-K (HC_MAX_SLOTS,
     HC_MAX_TOPK), the largest number of query rows filling the largest round
-    with C equal to it (HC_MAX_QUERIES, HC_MAX_ROUND_ROWS), and the largest
-    number of sessions (HC_MAX_SESSIONS): every step bit-exact, then the end
-    state."""
+    with C equal to it (HC_MAX_QUERIES, HC_MAX_ROUND_ROWS), the largest
+    number of sessions (HC_MAX_SESSIONS) and of selection units (HC_MAX_UNITS),
+    and 12,000 layers of one session (as many gather grid rows): every step
+    bit-exact, then the end state."""
     name, S, L, R, H0, steps, C, K, Q, sb, sn, draft, must_evict = case
     wl = W.Workload(name, S, L, R, H0, steps, C, K, (sb,) * S, (sn,) * S, 4244)
     p = _pair(wl, queries=Q)
