@@ -109,6 +109,15 @@ def test_attend_ragged_splits_two_head_groups_and_sessions():
     p.close()
 
 
+def test_largest_head_count():
+    """4,096 heads (the largest hc_attend accepts): 64 head groups of one
+    layer, both paths bit for bit, every head against the oracle."""
+    from gpu_harness import Pair
+    p = Pair(W.TINY.with_(name="attend_4096_heads", steps=2))
+    _run(p, 2, 4096)
+    p.close()
+
+
 def test_steps_without_the_bf16_buffer():
     from gpu_harness import Pair
     p = Pair(W.TINY.with_(steps=6))
