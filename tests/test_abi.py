@@ -131,3 +131,23 @@ def test_limit_configurations_are_accepted(kw):
     is accepted, and so are 12,000 layers of one session (the GPU parity tests
     run these configurations)."""
     assert hc.hc_workspace_bytes(hc.make_config(**kw)) > 0
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    """Without libhc.so every call raises: there is no fallback path."""
+    monkeypatch.setattr(hc, "_LIB", None)
+    monkeypatch.setattr(hc, "LIB_PATH", str(tmp_path / "libhc.so"))
+    with pytest.raises(RuntimeError, match="not built"):
+        hc.lib()
+    with pytest.raises(RuntimeError, match="not built"):
+        hc.hc_workspace_bytes(hc.make_config(1, 1, 1, 64, 8, 64))
+
+
+def test_no_gpu_means_no_context():
+    """Creating a context needs a GPU: on a machine without one it raises
+    instead of computing anything on the CPU."""
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    with pytest.raises(Exception):
+        hc.HotCache(1, 1, 1, 64, 8, 64, 0)
