@@ -8,18 +8,25 @@ import subprocess
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB = os.path.join(HERE, "liborc.so")
+# The same source built with AddressSanitizer and UndefinedBehaviorSanitizer,
+# for checking the oracle itself (load it through ORACLE_LIB with the
+# sanitizer runtimes preloaded).
+LIB_SANITIZED = os.path.join(HERE, "liborc_sanitized.so")
 
 
-def build(force: bool = True) -> str:
+def build(force: bool = True, sanitize: bool = False) -> str:
     src = os.path.join(HERE, "oracle.c")
-    if not force and os.path.exists(LIB) and os.path.getmtime(LIB) >= os.path.getmtime(src):
-        return LIB
-    tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = ["gcc", "-std=c11", "-O2", "-fPIC", "-shared", "-Wall", "-Wextra",
+    lib = LIB_SANITIZED if sanitize else LIB
+    if not force and os.path.exists(lib) and os.path.getmtime(lib) >= os.path.getmtime(src):
+        return lib
+    tmp = lib + ".tmp%d" % os.getpid()
+    opt = ["-O1", "-g", "-fno-omit-frame-pointer", "-fsanitize=address,undefined",
+           "-fno-sanitize-recover=undefined"] if sanitize else ["-O2"]
+    cmd = ["gcc", "-std=c11", *opt, "-fPIC", "-shared", "-Wall", "-Wextra",
            "-D_GNU_SOURCE", "-o", tmp, src, "-lm", "-lpthread"]
     subprocess.run(cmd, check=True)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
+    return lib
 
 
 if __name__ == "__main__":
