@@ -155,6 +155,38 @@ def test_no_eviction_while_the_union_fits(seed):
         seen |= new
 
 
+@pytest.mark.parametrize("seed", range(10))
+def test_used_slots_are_a_prefix_and_fill_before_evicting(seed):
+    """No slot ever becomes empty again and an empty slot (last use -1) is
+    older than any used one, lowest slot first: after every step the used
+    slots are exactly [0, fill), and the step that runs out of empty slots
+    takes fill .. C - 1 first (evicting nothing) and evicts only for the
+    misses beyond them.  C is not a multiple of K, so that step is mixed."""
+    rng = np.random.default_rng(300 + seed)
+    k = int(rng.integers(3, 20))
+    C = k + int(rng.integers(1, 3 * k))
+    if C % k == 0:
+        C += 1
+    h = int(rng.integers(4 * C, 8 * C))
+    rows = rows_for(h, seed)
+    c = oracle.Cache(C, h)
+    fill, mixed = 0, 0
+    for t, sel in enumerate(random_stream(rng, h, k, 30, 0.3)):
+        info = c.step(t, sel, rows)
+        m = info["n_miss"]
+        n_new = min(m, C - fill)
+        np.testing.assert_array_equal(info["victim"][:n_new], np.arange(fill, fill + n_new))
+        assert np.all(info["evicted"][:n_new] == -1)
+        assert np.all(info["evicted"][n_new:m] >= 0)
+        assert info["n_evict"] == m - n_new
+        mixed += 0 < n_new < m
+        fill += n_new
+        last = c.last()
+        assert np.all(last[:fill] >= 0) and np.all(last[fill:] == -1)
+    assert fill == C and mixed == 1
+    c.close()
+
+
 def test_capacity_equal_k_holds_exactly_the_current_selection():
     rng = np.random.default_rng(9)
     h, k = 60, 8
