@@ -69,7 +69,8 @@ bool valid_config(const hc_config* c) {
   if (c->replacement > HC_REPLACE_CLOCK) return false;
   const uint64_t layers = (uint64_t)c->n_sessions * c->n_layers;
   if (layers * c->queries > 60000) return false;  // one gather grid row per layer and query
-  const uint64_t G = (c->n_layers + c->layers_per_select - 1) / c->layers_per_select;
+  // in 64 bits: L + R - 1 can pass 2^32
+  const uint64_t G = ((uint64_t)c->n_layers + c->layers_per_select - 1) / c->layers_per_select;
   if ((uint64_t)c->n_sessions * G > (uint64_t)kMaxUnits) return false;
   return true;
 }
@@ -244,7 +245,7 @@ hc_status hc_create(const hc_config* cfg_in, void* dev_workspace, uint64_t ws_by
   c->lo = lo;
   c->ws = static_cast<uint8_t*>(dev_workspace);
   const uint32_t S = cfg->n_sessions, L = cfg->n_layers, R = cfg->layers_per_select;
-  const uint32_t G = (L + R - 1) / R;
+  const uint32_t G = (uint32_t)(((uint64_t)L + R - 1) / R);   // <= HC_MAX_UNITS, checked
   c->last_len.assign(S, 0);
   c->first.assign(S, -1);
   c->end.assign(S, 0);
@@ -314,8 +315,11 @@ hc_status hc_create(const hc_config* cfg_in, void* dev_workspace, uint64_t ws_by
       hipMemcpy(w + lo.host_tab, dev_ptrs.data(), dev_ptrs.size() * sizeof(void*),
                 hipMemcpyHostToDevice) != hipSuccess)
     st = HC_E_HIP;
+  // initialise on the null stream and wait for that work alone (not for every
+  // stream of the device)
   if (st == HC_OK && launch_init(d, nullptr) != hipSuccess) st = HC_E_HIP;
-  if (st == HC_OK && hipDeviceSynchronize() != hipSuccess) st = HC_E_HIP;
+  if (st == HC_OK && hipEventRecord(c->done, nullptr) != hipSuccess) st = HC_E_HIP;
+  if (st == HC_OK && hipEventSynchronize(c->done) != hipSuccess) st = HC_E_HIP;
   if (st != HC_OK) {
     free_host(c);
     if (c->done) (void)hipEventDestroy(c->done);

@@ -39,7 +39,8 @@ uint16_t orc_dequant_elem(int8_t q, uint16_t scale_bits);
 void orc_dequant_row(const uint8_t* row, uint16_t* out);
 
 /* Fills table[q + 128][scale_bits] for all 256 int8 q and all 65,536 scale bit
- * patterns (non-finite scales included; NaN results are 0x7FC0 | sign). */
+ * patterns (non-finite scales included; every NaN result is the canonical
+ * 0x7FC0, whatever the signs of q and the scale). */
 void orc_dequant_table(uint16_t* table);
 
 /* Recent ring of one (session, layer): rows appended by decode steps live

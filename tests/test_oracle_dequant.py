@@ -93,3 +93,8 @@ def test_non_finite_scales():
     assert table[128 + 3, ninf] == 0xFF80
     assert table[128 + 0, inf] == 0x7FC0          # 0 * Inf = NaN (canonical)
     assert table[128 + 1, nan] == 0x7FC0
+    # NaN scales of either sign, times q of either sign, give the one canonical NaN
+    neg_nan = 0xFE00
+    assert table[128 + 1, neg_nan] == 0x7FC0
+    assert table[128 - 1, nan] == 0x7FC0 and table[128 - 1, neg_nan] == 0x7FC0
+    assert table[128 + 0, neg_nan] == 0x7FC0
