@@ -14,6 +14,7 @@
 #include <algorithm>
 #include <cstddef>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <vector>
 
@@ -143,6 +144,34 @@ __global__ void k_init(DevState d, int64_t n_pos, int64_t n_slots) {
   for (int64_t i = i0; i < ref_words; i += stride) d.refbits[i] = 0;
 }
 
+// Scratch of hc_attend_cached_noalloc: the attention's split partials, for
+// callers that cannot allocate.  Each GPU the library runs on holds its own
+// copy for the life of the process.  In host code `scratch` only names the
+// symbol; its device address, per device, comes from hipGetSymbolAddress at
+// context creation and is the only form passed to kernels.
+static __device__ __align__(256) uint8_t scratch[HC_ATTEND_STATIC_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];   // device address of `scratch` per device, once set
+
+// Looks up the current device's address of `scratch` once; false on failure.
+bool init_scratch(int dev) {
+  if (dev < 0 || dev >= kMaxDevices) return false;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (g_scratch_ptr[dev]) return true;
+  void* p = nullptr;
+  if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return false;
+  g_scratch_ptr[dev] = p;
+  return true;
+}
+
+void* scratch_of(int dev) {
+  if (dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  return g_scratch_ptr[dev];
+}
+
 }  // namespace
 
 namespace hc {
@@ -238,6 +267,8 @@ hc_status hc_create(const hc_config* cfg_in, void* dev_workspace, uint64_t ws_by
   if (ws_bytes < lo.total) return HC_E_NOMEM;
   DeviceGuard dg(cfg->device);
   if (!dg.ok) return HC_E_INVAL;
+  // the no-allocation attention's scratch address on this device (once per device)
+  if (!init_scratch(cfg->device)) return HC_E_HIP;
 
   hc_ctx* c = new (std::nothrow) hc_ctx();
   if (!c) return HC_E_NOMEM;
@@ -489,6 +520,17 @@ hc_status hc_attend(hc_ctx* c, void* stream, const uint16_t* d_q, uint32_t heads
 hc_status hc_attend_cached(hc_ctx* c, void* stream, const uint16_t* d_q, uint32_t heads,
                            float scale, void* d_work, uint64_t work_bytes, float* d_out) {
   return attend(c, stream, true, d_q, heads, scale, nullptr, d_work, work_bytes, d_out);
+}
+
+hc_status hc_attend_cached_noalloc(hc_ctx* c, void* stream, const uint16_t* d_q, uint32_t heads,
+                                   float scale, float* d_out) {
+  if (!c) return HC_E_INVAL;
+  if (c->poisoned) return HC_E_STATE;
+  if (heads == 0 || heads % 64 || heads > 4096) return HC_E_INVAL;
+  if (attend_work_bytes(c->dev, (int)heads) > HC_ATTEND_STATIC_BYTES) return HC_E_NOMEM;
+  void* work = scratch_of(c->cfg.device);   // set by hc_create on this device
+  if (!work) return HC_E_STATE;
+  return attend(c, stream, true, d_q, heads, scale, nullptr, work, HC_ATTEND_STATIC_BYTES, d_out);
 }
 
 hc_status hc_export_state(hc_ctx* c, uint32_t session, uint32_t layer, int32_t* slot2pos,

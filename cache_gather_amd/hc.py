@@ -21,6 +21,7 @@ HEADER = os.path.join(ROOT, "include", "hc.h")
 
 ROW_BYTES = 656
 OUT_ELEMS = 576
+ATTEND_STATIC_BYTES = 32 << 20   # HC_ATTEND_STATIC_BYTES
 TRACE_HEADER = 4
 NUM_STAGES = 3
 STAGES = ("topk_scan", "select", "gather")
@@ -97,6 +98,8 @@ def lib():
     L.hc_attend_cached.argtypes = [_vp, _vp, _vp, ctypes.c_uint32, ctypes.c_float, _vp,
                                    ctypes.c_uint64, _vp]
     L.hc_attend_cached.restype = st
+    L.hc_attend_cached_noalloc.argtypes = [_vp, _vp, _vp, ctypes.c_uint32, ctypes.c_float, _vp]
+    L.hc_attend_cached_noalloc.restype = st
     L.hc_export_state.argtypes = [_vp, ctypes.c_uint32, ctypes.c_uint32, _vp, _vp, _vp, _vp]
     L.hc_export_state.restype = st
     L.hc_profile_enable.argtypes = [_vp, ctypes.c_uint32]
@@ -205,6 +208,11 @@ def hc_attend_cached(ctx: int, stream, d_q, heads: int, scale: float, d_work, wo
                                                       _ptr(d_work), work_bytes, _ptr(d_out)))
 
 
+def hc_attend_cached_noalloc(ctx: int, stream, d_q, heads: int, scale: float, d_out) -> None:
+    _check("hc_attend_cached_noalloc", lib().hc_attend_cached_noalloc(ctx, _ptr(stream), _ptr(d_q),
+                                                                      heads, scale, _ptr(d_out)))
+
+
 def hc_export_state(ctx: int, session: int, layer: int, slots: int, max_positions: int,
                     pos2slot=False, hot_rows=False):
     slot2pos = np.empty(slots, np.int32)
@@ -308,6 +316,10 @@ class HotCache:
     def attend_cached(self, q, heads, scale, work, out, stream=None):
         """Attention reading the last step's rows from the slots (no bf16 buffer)."""
         hc_attend_cached(self.ctx, self._stream(stream), q, heads, scale, work, work.numel(), out)
+
+    def attend_cached_noalloc(self, q, heads, scale, out, stream=None):
+        """attend_cached with the library's own scratch (no allocation)."""
+        hc_attend_cached_noalloc(self.ctx, self._stream(stream), q, heads, scale, out)
 
     def export_state(self, s, l, pos2slot=False, hot_rows=False):
         return hc_export_state(self.ctx, s, l, self.C, self.hcap, pos2slot, hot_rows)

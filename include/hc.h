@@ -255,6 +255,21 @@ hc_status hc_attend(hc_ctx* ctx, void* stream, const uint16_t* d_q, uint32_t hea
 hc_status hc_attend_cached(hc_ctx* ctx, void* stream, const uint16_t* d_q, uint32_t heads,
                            float scale, void* d_work, uint64_t work_bytes, float* d_out);
 
+/* The attention of hc_attend_cached for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc): the same kernels and the same result bit for bit, with
+ * the split partials in a scratch array the library holds in device memory
+ * (HC_ATTEND_STATIC_BYTES per GPU, for the life of the process) instead of a
+ * caller-owned d_work.  No allocation of any kind is made.  HC_E_NOMEM if
+ * hc_attend_workspace_bytes(ctx, heads) exceeds HC_ATTEND_STATIC_BYTES (the
+ * 78-layer, 64-head, top-2,048 attention needs 30.9 MiB).  Every call on one
+ * GPU shares that GPU's array: calls that overlap on one GPU (other streams,
+ * other contexts, other threads) race and give wrong results; calls ordered
+ * on one stream do not.  Other arguments and errors as hc_attend_cached. */
+#define HC_ATTEND_STATIC_BYTES (32ull << 20)
+hc_status hc_attend_cached_noalloc(hc_ctx* ctx, void* stream, const uint16_t* d_q,
+                                   uint32_t heads, float scale, float* d_out);
+
 /* Synchronous snapshot for tests: waits for all enqueued steps, then copies
  * the state that layer `layer` of `session` sees into host buffers:
  * slot2pos[C] and last_use[C] (-1 = empty / never used), pos2slot[Hcap] if
