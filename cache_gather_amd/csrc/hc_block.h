@@ -72,7 +72,9 @@ __device__ __forceinline__ void lru_victims(const DevState& d, int u, int32_t t,
   const int C = d.C, QC = d.qcap, tid = threadIdx.x;
   constexpr int kPer = 4;   // queue entries per thread and window (two 16-byte loads)
   int32_t* cnt = d.cnt + (size_t)u * d.Q * kCntStride;
-  const int h = cnt[kCntQHead], e = cnt[kCntQTail], b = cnt[kCntQBuf];
+  // clamped, so that a corrupted counter line still keeps every access in range
+  const int e = min(max(cnt[kCntQTail], 0), QC), h = min(max(cnt[kCntQHead], 0), e);
+  const int b = cnt[kCntQBuf] & 1;
   const int2* q = d.oq + ((size_t)u * 2 + b) * QC;
   const int32_t* last = d.last_use + (size_t)u * C;
   auto pinned = [&](int v) { return (touched[v >> 5] >> (v & 31)) & 1u; };
@@ -88,7 +90,7 @@ __device__ __forceinline__ void lru_victims(const DevState& d, int u, int32_t t,
 
   // never-used slots first, then the first live, untouched entries from the head
   if (tid == 0) *scratch = h - 1;   // queue index of the last victim taken from the queue
-  const int fill = cnt[kCntFill];
+  const int fill = min(max(cnt[kCntFill], 0), C);
   const int n_new = m < C - fill ? m : C - fill;
   for (int k = tid; k < n_new; k += kSelThreads) vic[k] = fill + k;
   int found = n_new;
@@ -124,7 +126,9 @@ __device__ __forceinline__ void lru_victims(const DevState& d, int u, int32_t t,
     }
     found += total;
   }
-  // fewer than m candidates means a corrupted queue: keep every index in range
+  // fewer than m candidates means a corrupted queue: report it, and keep every
+  // index in range
+  if (found < m && tid == 0) report_error(d, kErrLru);
   for (int k = found + tid; k < m; k += kSelThreads) vic[k] = 0;
   __syncthreads();
   const int hn = *scratch + 1;

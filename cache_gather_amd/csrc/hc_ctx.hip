@@ -27,9 +27,17 @@ namespace {
 constexpr uint64_t kAlign = 256;
 
 struct Layout {
-  uint64_t pos2slot, slot2pos, last_use, oq, cnt, above, cand, sel_slot, miss_pos,
-      victim, miss_idx, host_tab, hot, ring, refbits, total;
+  uint64_t pos2slot, slot2pos, last_use, oq, cnt, seg, cand, sel_slot, miss_pos,
+      victim, miss_idx, miss_old, host_tab, hot, ring, refbits, total;
 };
+
+// Score-scan segments per selection unit: enough for the longest history in
+// chunks of 2,048 positions, at most kMaxSegs (longer histories use longer
+// segments).
+uint64_t max_segs_of(uint64_t hcap) {
+  const uint64_t n = (hcap + 2047) / 2048;
+  return n < (uint64_t)kMaxSegs ? n : (uint64_t)kMaxSegs;
+}
 
 // Sizes of hc_config before the recent-ring fields and before `queries` were
 // added; both are accepted (no ring, one query).
@@ -95,12 +103,13 @@ Layout layout_of(const hc_config* c) {
   lo.last_use = take(U * C * 4);
   lo.oq = take(U * 2 * queue_cap(C) * 8);
   lo.cnt = take(SU * kCntStride * 4);
-  lo.above = take(SU * K * 4);
-  lo.cand = take(SU * hcap * 8);
+  lo.seg = take(SU * max_segs_of(hcap) * 8);
+  lo.cand = take(SU * hcap * sizeof(Ent));
   lo.sel_slot = take(SU * K * 4);
   lo.miss_pos = take(SU * K * 4);
   lo.victim = take(SU * K * 4);
   lo.miss_idx = take(SU * K * 4);
+  lo.miss_old = take(SU * K * 4);
   lo.host_tab = take(S * L * 8);
   lo.hot = take(S * L * C * kSlotStride);
   lo.ring = take(S * L * (uint64_t)c->ring_rows * kRow);
@@ -134,7 +143,7 @@ __global__ void k_init(DevState d, int64_t n_pos, int64_t n_slots) {
   for (int64_t i = i0; i < sel_units * d.K; i += stride) d.sel_slot[i] = 0;
   for (int64_t i = i0; i < sel_units * kCntStride; i += stride) {
     const int64_t f = i % kCntStride;
-    d.cnt[i] = f == kCntBin1 ? -1 : 0;   // empty LRU queues, no slot filled
+    d.cnt[i] = f == kCntWinLo || f == kCntWinHi ? -1 : 0;   // no window; empty LRU queues
   }
   // the first step's cut histograms (see launch_cold_cut)
   if (d.hcap >= kColdMinPositions)
@@ -195,6 +204,8 @@ struct hc_ctx {
   std::vector<int64_t> first, end, copied;
   uint64_t* host_count = nullptr;    // pinned [S], written by the device after copybacks
   uint64_t* host_count_dev = nullptr;
+  uint32_t* err = nullptr;           // pinned [kErrKinds]: set by kernels on inconsistent state
+  uint32_t* err_dev = nullptr;
   bool poisoned = false;
   bool enqueued = false;
   hipEvent_t done = nullptr;         // recorded after every step
@@ -211,6 +222,8 @@ void free_host(hc_ctx* c) {
   c->host_rows.clear();
   if (c->host_count) (void)hipHostFree(c->host_count);
   c->host_count = c->host_count_dev = nullptr;
+  if (c->err) (void)hipHostFree(c->err);
+  c->err = c->err_dev = nullptr;
 }
 
 void free_prof(hc_ctx* c) {
@@ -223,6 +236,16 @@ void free_prof(hc_ctx* c) {
 hc_status fail_hip(hc_ctx* c) {
   c->poisoned = true;
   return HC_E_HIP;
+}
+
+// A kernel reported an inconsistent device state (every kernel that has
+// completed has written its report by now): the context is poisoned.
+bool device_error(hc_ctx* c) {
+  const volatile uint32_t* e = c->err;
+  bool any = false;
+  for (int k = 0; k < kErrKinds; ++k) any |= e[k] != 0;
+  if (any) c->poisoned = true;
+  return any;
 }
 
 // Enqueues the copyback of every session with at least `min_pending` appended
@@ -310,6 +333,18 @@ hc_status hc_create(const hc_config* cfg_in, void* dev_workspace, uint64_t ws_by
       c->host_count_dev = static_cast<uint64_t*>(dp);
     }
   }
+  if (st == HC_OK) {
+    void* p = nullptr;
+    if (hipHostMalloc(&p, kErrKinds * sizeof(uint32_t), hipHostMallocMapped) != hipSuccess || !p) {
+      st = HC_E_NOMEM;
+    } else {
+      c->err = static_cast<uint32_t*>(p);
+      std::memset(c->err, 0, kErrKinds * sizeof(uint32_t));
+      void* dp = nullptr;
+      if (hipHostGetDevicePointer(&dp, p, 0) != hipSuccess || !dp) st = HC_E_HIP;
+      c->err_dev = static_cast<uint32_t*>(dp);
+    }
+  }
   if (st == HC_OK && hipEventCreateWithFlags(&c->done, hipEventDisableTiming) != hipSuccess)
     st = HC_E_HIP;
 
@@ -329,12 +364,15 @@ hc_status hc_create(const hc_config* cfg_in, void* dev_workspace, uint64_t ws_by
   d.oq = reinterpret_cast<int2*>(w + lo.oq);
   d.qcap = (int32_t)queue_cap(cfg->cache_slots);
   d.cnt = reinterpret_cast<int32_t*>(w + lo.cnt);
-  d.above = reinterpret_cast<int32_t*>(w + lo.above);
-  d.cand = reinterpret_cast<uint2*>(w + lo.cand);
+  d.seg = reinterpret_cast<int2*>(w + lo.seg);
+  d.max_segs = (int32_t)max_segs_of(cfg->max_positions);
+  d.err = c->err_dev;
+  d.cand = reinterpret_cast<Ent*>(w + lo.cand);
   d.sel_slot = reinterpret_cast<int32_t*>(w + lo.sel_slot);
   d.miss_pos = reinterpret_cast<int32_t*>(w + lo.miss_pos);
   d.victim = reinterpret_cast<int32_t*>(w + lo.victim);
   d.miss_idx = reinterpret_cast<int32_t*>(w + lo.miss_idx);
+  d.miss_old = reinterpret_cast<int32_t*>(w + lo.miss_old);
   d.host = reinterpret_cast<const uint8_t* const*>(w + lo.host_tab);
   d.hot = w + lo.hot;
   d.ring = w + lo.ring;
@@ -370,6 +408,7 @@ hc_status hc_step(hc_ctx* c, void* stream, const float* d_scores, uint64_t score
                   const uint64_t* hist_len, uint16_t* d_out, int32_t* d_sel, int32_t* d_trace) {
   if (!c) return HC_E_INVAL;
   if (c->poisoned) return HC_E_STATE;
+  if (device_error(c)) return HC_E_DEVICE;   // reported by an earlier step that has completed
   if (!d_scores || !hist_len || !d_sel) return HC_E_INVAL;   // d_out may be NULL
   const uint32_t S = c->cfg.n_sessions;
   uint64_t max_len = 0;
@@ -407,10 +446,11 @@ hc_status hc_step(hc_ctx* c, void* stream, const float* d_scores, uint64_t score
     e = launch_cold_cut(c->dev, a, d_scores, score_stride, (int64_t)max_len, st);
   if (e == hipSuccess) e = launch_topk_scan(c->dev, a, d_scores, score_stride, (int64_t)max_len, vec4, st);
   if (e == hipSuccess) e = mark(1);
-  if (e == hipSuccess) e = launch_select(c->dev, a, d_scores, score_stride, d_sel, d_trace, st);
+  if (e == hipSuccess)
+    e = launch_select(c->dev, a, d_scores, score_stride, (int64_t)max_len, d_sel, d_trace, st);
   if (e == hipSuccess && c->dev.Q > 1) e = launch_round(c->dev, a, d_sel, d_trace, st);
   if (e == hipSuccess) e = mark(2);
-  if (e == hipSuccess) e = launch_gather(c->dev, d_out, st);
+  if (e == hipSuccess) e = launch_gather(c->dev, d_out, a.t, st);
   if (e == hipSuccess) e = mark(3);
   if (e == hipSuccess) e = hipEventRecord(c->done, st);
   c->enqueued = true;
@@ -424,6 +464,7 @@ hc_status hc_step(hc_ctx* c, void* stream, const float* d_scores, uint64_t score
 hc_status hc_append(hc_ctx* c, void* stream, const uint8_t* d_rows, const uint64_t* pos) {
   if (!c) return HC_E_INVAL;
   if (c->poisoned) return HC_E_STATE;
+  if (device_error(c)) return HC_E_DEVICE;
   if (!c->cfg.ring_rows || !d_rows || !pos) return HC_E_INVAL;
   if (reinterpret_cast<uintptr_t>(d_rows) % 16) return HC_E_INVAL;
   const uint32_t S = c->cfg.n_sessions;
@@ -472,6 +513,7 @@ hc_status hc_flush(hc_ctx* c, void* stream, uint64_t* host_count) {
   // wait for the copy itself, not for its submission
   if (c->enqueued && hipEventSynchronize(c->done) != hipSuccess) return fail_hip(c);
   if (hipStreamSynchronize(st) != hipSuccess) return fail_hip(c);
+  if (device_error(c)) return HC_E_DEVICE;
   hc_status r = HC_OK;
   for (uint32_t s = 0; s < S; ++s) {
     const uint64_t n = c->host_count ? reinterpret_cast<volatile uint64_t*>(c->host_count)[s] : 0;
@@ -541,6 +583,7 @@ hc_status hc_export_state(hc_ctx* c, uint32_t session, uint32_t layer, int32_t* 
   DeviceGuard dg(c->cfg.device);
   if (!dg.ok) return HC_E_INVAL;
   if (c->enqueued && hipEventSynchronize(c->done) != hipSuccess) return fail_hip(c);
+  if (device_error(c)) return HC_E_DEVICE;
   const DevState& d = c->dev;
   const size_t u = (size_t)session * d.G + layer / d.R;
   const size_t sl = (size_t)session * d.L + layer;
@@ -624,6 +667,7 @@ const char* hc_status_str(hc_status s) {
     case HC_E_HIP: return "HIP error (context poisoned)";
     case HC_E_STATE: return "context poisoned by an earlier HIP error";
     case HC_E_CONSISTENCY: return "host row count differs from the logical row count";
+    case HC_E_DEVICE: return "a kernel found the context's device state inconsistent (context poisoned)";
   }
   return "unknown status";
 }

@@ -15,25 +15,39 @@ constexpr int kOut = HC_OUT_ELEMS;        // 576 bf16 per gathered row
 constexpr int kBin1Bits = 12;             // first radix digit: key bits [20, 32)
 constexpr int kBins1 = 1 << kBin1Bits;    // 4096 histogram bins per unit
 constexpr int kMaxSessions = HC_MAX_SESSIONS;  // session lengths travel as kernel args
-constexpr int64_t kScanSmallMax = 131072;  // histories up to this scan in 2,048-score chunks, longer in 4,096
 constexpr int kMaxUnits = HC_MAX_UNITS;   // S * G: the per-unit miss prefix lives in LDS
+// Score-scan segments per selection unit and step, at most: a segment is one
+// scan workgroup's run of positions, whose candidates it writes in order.
+constexpr int kMaxSegs = 4096;
+// Kinds of inconsistent device state a kernel can report (DevState::err).
+enum { kErrSelect = 0, kErrLru = 1, kErrRound = 2, kErrKinds = 4 };
 
 // Per-selection-unit counters (int32 each): unit su owns cnt[su * kCntStride ..
-// + kCnt).  kCntBin1 is the cut bin of the unit's previous step (-1 before the
-// first); kCntMiss and kCntHand (circular / clock hand) are kept at su = u * Q.
-// kCntAbove and kCntCand form one 8-byte word that every scan workgroup bumps
-// with a single atomic; each unit's counters sit on a 256-byte line of their
-// own, because atomics on neighbouring addresses queue behind each other
-// (measured: 16 units x 257 workgroups took 58 us packed, 20 us spread, 13 us
-// without atomics).
-// kCntQHead / kCntQTail / kCntQBuf: the LRU queue of the unit (at su = u * Q);
-// kCntFill: slots the unit's LRU has filled so far (slots [fill, C) were never
-// used).
+// + kCnt), a 256-byte line of its own.  kCntWinLo / kCntWinHi: the cut window
+// of the unit's next score scan, in units of the key's top 16 bits (-1 before
+// the first step: every key); kCntMiss and kCntHand (circular / clock hand)
+// are kept at su = u * Q.  kCntQHead / kCntQTail / kCntQBuf: the LRU queue of
+// the unit (at su = u * Q); kCntFill: slots the unit's LRU has filled so far
+// (slots [fill, C) were never used).
 enum {
-  kCntAbove = 0, kCntCand = 1, kCntMiss = 2, kCntBin1 = 3, kCntHand = 4,
-  kCntQHead = 5, kCntQTail = 6, kCntQBuf = 7, kCntFill = 8, kCnt = 9
+  kCntMiss = 2, kCntWinLo = 3, kCntHand = 4,
+  kCntQHead = 5, kCntQTail = 6, kCntQBuf = 7, kCntFill = 8, kCntWinHi = 9, kCnt = 10
 };
+// Half-width of the predicted cut window, in top-16-bit key units: the next
+// step's window is the current cut key's 16-bit prefix +- kWinHalf (about
+// +-0.06 around a cut near 2 or 3, several times the cut's movement between
+// decode steps; a cut that leaves it costs a rescan of the scores).
+constexpr int kWinHalf = 8;
 constexpr int kCntStride = 64;
+
+// One entry of a unit's score scan: the totalOrder key of a score, its
+// position, and (one query row) the slot holding that position at the scan,
+// -1 for none or a ring row.  12 bytes: one load brings all three.
+struct Ent {
+  uint32_t key;
+  uint32_t pos;
+  int32_t slot;
+};
 
 // Device view of the caller's workspace.  Unit u = s * G + g; layer index
 // sl = s * L + l.  All arrays are carved from one allocation (see hc_ctx.hip).
@@ -49,14 +63,21 @@ struct DevState {
                        //            last_use[slot] == step
   int32_t qcap;        // entries per queue buffer: 2 C rounded up to a multiple of 4
   int32_t* cnt;        // [U*Q][kCntStride] per selection unit; the round's miss count at su = u*Q
-  int32_t* above;      // [U*Q][K]   positions whose top digit beats the cut bin
-  uint2* cand;         // [U*Q][hcap] (key, position) of scores in the cut bin
+  Ent* cand;           // [U*Q][hcap] entries: the scores above or inside the cut
+                       //            window, segment s of a step at s * seg_len,
+                       //            ascending positions
+  int2* seg;           // [U*Q][max_segs] (entries, of which above the window) per segment
+  int32_t max_segs;    // segments per unit a step may use
+  uint32_t* err;       // [kErrKinds] device-visible pinned host words: nonzero once a
+                       //            kernel found an inconsistent state (kErr*)
   int32_t* sel_slot;   // [U*Q][K]   source of selected row i: slot, C + ring entry,
                        //            -(slot + 1) if it missed and this row fills the slot,
                        //            -(C + 1 + position) for a further row of that miss
   int32_t* miss_pos;   // [U][Q*K]   position of miss k (ascending), k < cnt[u*Q][kCntMiss]
   int32_t* victim;     // [U][Q*K]   slot that miss k fills
   int32_t* miss_idx;   // [U][Q*K]   output row (q * K + i) that miss k fills
+  int32_t* miss_old;   // [U][Q*K]   position victim k held before this step, -1 if empty
+                       //            (one query row: applied to the maps by the gather)
   const uint8_t* const* host;  // [S*L] device-visible pointers of the pinned host rows
   uint8_t* hot;        // [S*L][C][kSlotStride], a row in the first 656 B of its slot
   uint8_t* ring;       // [S*L][ring_rows][kRow] recent ring; position p at p % ring_rows
@@ -165,21 +186,30 @@ __device__ __forceinline__ uint32_t order_key(float f) {
   return b ^ ((uint32_t)((int32_t)b >> 31) | 0x80000000u);
 }
 
-// Cut window of a unit's score scan: the previous step's cut bin +- 1, or every
-// bin when there is none yet (prev < 0).  The scan and the select kernel must
-// agree on it exactly.
-__device__ __forceinline__ void cut_window(int prev, uint32_t& lo, uint32_t& hi) {
-  if (prev < 0) {
+// Cut window of a unit's score scan, [lo, hi] in top-16-bit key units: as
+// stored, or every key when there is none yet (also for values out of range).
+// The scan and the select kernel must agree on it exactly.
+__device__ __forceinline__ void cut_window(int lo16, int hi16, uint32_t& lo, uint32_t& hi) {
+  if (lo16 < 0 || hi16 < lo16 || hi16 > 65535) {
     lo = 0;
-    hi = kBins1 - 1;
+    hi = 65535;
   } else {
-    lo = prev > 0 ? (uint32_t)(prev - 1) : 0u;
-    hi = prev < kBins1 - 1 ? (uint32_t)(prev + 1) : (uint32_t)(kBins1 - 1);
+    lo = (uint32_t)lo16;
+    hi = (uint32_t)hi16;
   }
+}
+
+// Records an inconsistent device state of kind `kind` (kErr*); the host
+// reports it at its next check of the context (HC_E_DEVICE).
+__device__ __forceinline__ void report_error(const DevState& d, int kind) {
+  d.err[kind] = 1u;
 }
 
 // Launchers (each defined next to its kernel).  All return hipGetLastError().
 hipError_t launch_init(const DevState& d, hipStream_t st);
+// Positions per score-scan segment for a step whose longest history is max_len
+// (the scan and the select kernel must use the same).
+int64_t scan_seg_len(int64_t max_len, int max_segs);
 hipError_t launch_topk_scan(const DevState& d, const StepArgs& a, const float* scores,
                             uint64_t stride, int64_t max_len, bool vec4, hipStream_t st);
 // First step only (needs hcap >= kColdMinPositions): sets every selection
@@ -190,11 +220,15 @@ hipError_t launch_cold_cut(const DevState& d, const StepArgs& a, const float* sc
 // Q == 1: the fused per-unit selection + cache kernel.  Q > 1: the top-K part
 // per selection unit, then launch_round per unit.
 hipError_t launch_select(const DevState& d, const StepArgs& a, const float* scores,
-                         uint64_t stride, int32_t* d_sel, int32_t* d_trace, hipStream_t st);
+                         uint64_t stride, int64_t max_len, int32_t* d_sel, int32_t* d_trace,
+                         hipStream_t st);
 hipError_t launch_round(const DevState& d, const StepArgs& a, const int32_t* d_sel,
                         int32_t* d_trace, hipStream_t st);
-// d_out == nullptr: only the missing rows are fetched into their slots.
-hipError_t launch_gather(const DevState& d, uint16_t* d_out, hipStream_t st);
+// d_out == nullptr: only the missing rows are fetched into their slots.  With
+// one query row the launch also carries one bookkeeping workgroup per unit:
+// last-use stamps, the (miss, victim) pairs applied to the slot maps, and the
+// LRU queue's new entries for step t.
+hipError_t launch_gather(const DevState& d, uint16_t* d_out, int32_t t, hipStream_t st);
 hipError_t launch_append(const DevState& d, const AppendArgs& a, const uint8_t* d_rows,
                          hipStream_t st);
 // Attention over the last step's selection: rows from the gathered bf16

@@ -9,8 +9,12 @@
 // in a round is not read by another block of that round, and repeated misses
 // read host RAM.
 //
-// One launch, two kinds of workgroup:
-//   * the first workgroups walk the dense miss list (every layer
+// One launch, three kinds of workgroup:
+//   * with one query row per round, one bookkeeping workgroup per unit, first:
+//     the select kernel only decides, and these write its decisions into the
+//     unit's state (last-use stamps, slot maps, LRU queue) for the next step,
+//     while the rest of the launch streams rows;
+//   * the next workgroups walk the dense miss list (every layer
 //     of every unit): each missing row is read from pinned host RAM over PCIe
 //     (zero-copy), written into its victim slot, and dequantised from the same
 //     registers — so its slot is only ever read in later steps, and all PCIe
@@ -35,13 +39,15 @@
 // rows' loads in flight before the first store (16 rows per workgroup:
 // measured on MI355X with the caches flushed, 3-4% faster than one row per
 // thread, and 4 rows slower again); a miss workgroup keeps one row per thread
-// in flight (two slowed the PCIe reads).  Grid rows
-// [0, miss_rows) are the miss workgroups, dispatched first; grid row
+// in flight (two slowed the PCIe reads).  After the bookkeeping rows, grid
+// rows [0, miss_rows) are the miss workgroups, dispatched first; grid row
 // miss_rows + sl holds layer sl's hit rows, so no per-row index division is
 // needed (with Q query rows, grid row miss_rows + sl * Q + q).  HBM-bound:
 // 656 B read (hit) or written (miss) + 1,152 B written per
 // selected row; PCIe: 656 B per missing row.  bf16 rounding by
 // v_cvt_pk_bf16_f32.
+#include <algorithm>
+
 #include "hc_internal.h"
 
 namespace hc {
@@ -153,20 +159,193 @@ __device__ __forceinline__ int layers_in_group(const DevState& d, int g) {
   return n < d.R ? n : d.R;
 }
 
+// Block-wide sum over the gather workgroup's 320 threads.
+__device__ __forceinline__ int gather_block_sum(int v, int32_t* wsum) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int x = wave_incl_scan(v);
+  if (lane == 63) wsum[w] = x;
+  __syncthreads();
+  int tot = 0;
+#pragma unroll
+  for (int i = 0; i < kGatherThreads / 64; ++i) tot += wsum[i];
+  __syncthreads();
+  return tot;
+}
+
+// Inclusive prefix over the gather workgroup's threads (thread order).
+__device__ __forceinline__ int gather_block_scan(int v, int32_t* wsum, int& total) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int x = wave_incl_scan(v);
+  if (lane == 63) wsum[w] = x;
+  __syncthreads();
+  int off = 0, tot = 0;
+#pragma unroll
+  for (int i = 0; i < kGatherThreads / 64; ++i) {
+    off += i < w ? wsum[i] : 0;
+    tot += wsum[i];
+  }
+  __syncthreads();
+  total = tot;
+  return x + off;
+}
+
+// Bookkeeping of unit u after its select kernel (one query row per round),
+// done beside the gather so that the select kernel's chain ends with its
+// decisions: stamps the step's slots (hits and victims) with last use t,
+// applies the (miss, victim) pairs to pos2slot / slot2pos (the evicted
+// position leaves the map), and, for LRU, appends the step's slots to the
+// unit's queue in slot order, stamped t, after compacting the queue's live
+// entries into its other buffer when the tail would pass the buffer's end.
+// Nothing here is read by this launch's other workgroups; the next step's
+// kernels come after the launch.  `touched` is LDS of ceil(C / 32) words.
+__device__ __forceinline__ void bookkeeping(const DevState& d, int u, int32_t t, uint32_t* touched,
+                            int32_t* wsum) {
+  const int C = d.C, K = d.K, tid = threadIdx.x;
+  const int nwords = (C + 31) >> 5;
+  int32_t* cnt = d.cnt + (size_t)u * kCntStride;
+  const int m = min(max(cnt[kCntMiss], 0), K);
+  int32_t* pos2slot = d.pos2slot + (size_t)u * d.hcap;
+  int32_t* slot2pos = d.slot2pos + (size_t)u * C;
+  int32_t* last_use = d.last_use + (size_t)u * C;
+  const int32_t* g_slot = d.sel_slot + (size_t)u * K;
+  for (int w = tid; w < nwords; w += kGatherThreads) touched[w] = 0;
+  __syncthreads();
+  // hits: stamp; hits and victims: mark
+  for (int i = tid; i < K; i += kGatherThreads) {
+    const int32_t enc = g_slot[i];
+    const int32_t v = enc >= 0 ? (enc < C ? enc : -1) : (enc >= -C ? -enc - 1 : -1);
+    if (v < 0) continue;   // a ring row
+    if (enc >= 0) last_use[v] = t;
+    atomicOr(&touched[v >> 5], 1u << (v & 31));
+  }
+  // (miss, victim) pairs
+  const int32_t* g_miss = d.miss_pos + (size_t)u * K;
+  const int32_t* g_vic = d.victim + (size_t)u * K;
+  const int32_t* g_old = d.miss_old + (size_t)u * K;
+  for (int k = tid; k < m; k += kGatherThreads) {
+    const int32_t v = g_vic[k], p = g_miss[k], old = g_old[k];
+    if (v < 0 || v >= C || p < 0 || p >= d.hcap) continue;
+    if (old >= 0 && old < d.hcap) pos2slot[old] = -1;
+    pos2slot[p] = v;
+    slot2pos[v] = p;
+    last_use[v] = t;
+  }
+  __syncthreads();
+  if (d.policy != HC_REPLACE_LRU) return;
+
+  // ---- the step's slots at the queue's tail -----------------------------------
+  const int QC = d.qcap;
+  const int qe = min(max(cnt[kCntQTail], 0), QC);
+  const int hn = min(max(cnt[kCntQHead], 0), qe);
+  const int qb = cnt[kCntQBuf] & 1;
+  const int2* q = d.oq + ((size_t)u * 2 + qb) * QC;
+  const int g = (nwords + kGatherThreads - 1) / kGatherThreads;   // words per thread
+  int c = 0;
+  for (int i = 0; i < g; ++i) {
+    const int w = tid * g + i;
+    if (w < nwords) c += __popc(touched[w]);
+  }
+  const int n_touched = gather_block_sum(c, wsum);
+  const bool fits = qe + n_touched <= QC;
+  int2* qw = const_cast<int2*>(fits ? q : d.oq + ((size_t)u * 2 + (qb ^ 1)) * QC);
+  int base = qe;
+  if (!fits) {
+    // survivors: the live entries after the last victim that this step did
+    // not use, in order, to the front of the other buffer.  Wave w of a window
+    // owns 64 * kCPer consecutive entries, lane-interleaved so that loads and
+    // stores coalesce; ranks inside the wave come from ballots, and the wave
+    // totals order the waves.
+    constexpr int kCPer = 8;
+    constexpr int kW = kGatherThreads / 64;
+    const int lane = tid & 63, wv = tid >> 6;
+    const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    auto pinned = [&](int v) { return (touched[v >> 5] >> (v & 31)) & 1u; };
+    int kept = 0;
+    for (int j0 = hn; j0 < qe; j0 += kGatherThreads * kCPer) {
+      const int wb = j0 + wv * 64 * kCPer;
+      int2 ent[kCPer];
+#pragma unroll
+      for (int k = 0; k < kCPer; ++k) {
+        const int j = wb + k * 64 + lane;
+        ent[k] = j < qe ? q[j] : make_int2(-1, -1);
+      }
+      bool f[kCPer];
+#pragma unroll
+      for (int k = 0; k < kCPer; ++k) f[k] = ent[k].x >= 0 && ent[k].x < C && !pinned(ent[k].x);
+      int lu[kCPer];
+#pragma unroll
+      for (int k = 0; k < kCPer; ++k) lu[k] = f[k] ? last_use[ent[k].x] : 0;
+      int wave_total = 0;
+#pragma unroll
+      for (int k = 0; k < kCPer; ++k) {
+        f[k] = f[k] && lu[k] == ent[k].y;
+        wave_total += __popcll(__ballot(f[k]));
+      }
+      if (lane == 0) wsum[wv] = wave_total;
+      __syncthreads();
+      int run = kept, total = 0;
+#pragma unroll
+      for (int i = 0; i < kW; ++i) {
+        run += i < wv ? wsum[i] : 0;
+        total += wsum[i];
+      }
+      __syncthreads();
+#pragma unroll
+      for (int k = 0; k < kCPer; ++k) {
+        const uint64_t bal = __ballot(f[k]);
+        if (f[k]) {
+          const int o = run + __popcll(bal & lt_mask);
+          if (o < QC) qw[o] = ent[k];
+        }
+        run += __popcll(bal);
+      }
+      kept += total;
+    }
+    base = kept;
+  }
+  // this thread's words in slot order, after the words of the threads before it
+  int total;
+  int o = base + gather_block_scan(c, wsum, total) - c;
+  for (int i = 0; i < g; ++i) {
+    const int w = tid * g + i;
+    uint32_t bits = w < nwords ? touched[w] : 0u;
+    while (bits) {
+      const int v = w * 32 + __ffs(bits) - 1;
+      bits &= bits - 1;
+      if (o < QC) qw[o] = make_int2(v, t);
+      ++o;
+    }
+  }
+  if (tid == 0) {
+    cnt[kCntQHead] = fits ? hn : 0;
+    cnt[kCntQTail] = base + total < QC ? base + total : QC;
+    cnt[kCntQBuf] = fits ? qb : (qb ^ 1);
+  }
+}
+
 __global__ __launch_bounds__(kGatherThreads) void k_gather(DevState d,
                                                            uint16_t* __restrict__ out,
+                                                           int32_t t, int bk_rows,
                                                            int miss_rows, int few_hits_above,
                                                            uint32_t m_q, uint32_t m_l, uint32_t m_r) {
-  extern __shared__ int32_t pref[];          // [S*G + 1]: miss rows (all layers) before unit u
+  // dynamic LDS: [S*G + 1] miss rows (all layers) before unit u, or the
+  // bookkeeping's touched-slot bitmap
+  extern __shared__ int32_t pref[];
   __shared__ int32_t wsum[kGatherThreads / 64];
   const int item = threadIdx.x % kItemsPerRow;
   const int lrow = threadIdx.x / kItemsPerRow;
   uint8_t* const out_b = reinterpret_cast<uint8_t*>(out);
   const size_t out_row_bytes = (size_t)kOut * 2;
 
-  if ((int)blockIdx.y < miss_rows) {
+  if ((int)blockIdx.y < bk_rows) {
+    const int b = blockIdx.y * gridDim.x + blockIdx.x;
+    if (b < d.S * d.G) bookkeeping(d, b, t, reinterpret_cast<uint32_t*>(pref), wsum);
+    return;
+  }
+  const int row = (int)blockIdx.y - bk_rows;
+  if (row < miss_rows) {
     RowJob<1> j;
-    const int mb = blockIdx.y * gridDim.x + blockIdx.x;  // miss workgroup number
+    const int mb = row * gridDim.x + blockIdx.x;  // miss workgroup number
     // ---- dense miss list: prefix of (misses x layers) over units --------
     const int U = d.S * d.G;
     int running = 0;
@@ -220,8 +399,8 @@ __global__ __launch_bounds__(kGatherThreads) void k_gather(DevState d,
     return;
   }
 
-  // ---- rows of (layer sl, query q), hr = blockIdx.y - miss_rows = sl * Q + q --
-  const int hr = blockIdx.y - miss_rows;
+  // ---- rows of (layer sl, query q), hr = row - miss_rows = sl * Q + q ---------
+  const int hr = row - miss_rows;
   const int sl = div_by(hr, m_q), q = hr - sl * d.Q;   // uniform per workgroup; hr < 2^16
   const int s = div_by(sl, m_l), l = sl - s * d.L;
   const int32_t* slot = d.sel_slot + ((size_t)(s * d.G + div_by(l, m_r)) * d.Q + q) * d.K;
@@ -248,20 +427,25 @@ __global__ __launch_bounds__(kGatherThreads) void k_gather(DevState d,
   run_rows(j, item);
 }
 
-hipError_t launch_gather(const DevState& d, uint16_t* d_out, hipStream_t st) {
-  // grid rows [0, miss_rows): the miss workgroups (dispatched first);
-  // row miss_rows + sl: the hit rows of layer sl
+hipError_t launch_gather(const DevState& d, uint16_t* d_out, int32_t t, hipStream_t st) {
+  // grid rows [0, bk_rows): one bookkeeping workgroup per unit (one query row
+  // per round; k_round does its own), dispatched first; then rows
+  // [0, miss_rows) of the miss workgroups; then row miss_rows + sl: the hit
+  // rows of layer sl
   const int gx = (d.K + kRowsPerRound - 1) / kRowsPerRound;
+  const int units = d.S * d.G;
+  const int bk_rows = d.Q == 1 ? (units + gx - 1) / gx : 0;
   const int miss_rows = (kMissBlocks + gx - 1) / gx;
-  const size_t lds = ((size_t)d.S * d.G + 1) * sizeof(int32_t);
+  const size_t words = bk_rows ? (size_t)(d.C + 31) / 32 : 0;
+  const size_t lds = std::max((size_t)units + 1, words) * sizeof(int32_t);
   // without an output buffer only the miss workgroups run (they fill slots)
-  const int rows = d_out ? d.S * d.L * d.Q + miss_rows : miss_rows;
+  const int rows = bk_rows + (d_out ? d.S * d.L * d.Q + miss_rows : miss_rows);
   // more than this many missing rows leaves fewer than kFewHitRows other rows
   const int64_t rows_total = (int64_t)d.S * d.L * d.Q * d.K;
   const int few_hits_above = (int)(rows_total - kFewHitRows);
   // grid rows stay below 2^16, as div_by requires: S * L * Q <= 60,000 is checked at creation
-  hipLaunchKernelGGL(k_gather, dim3(gx, rows), dim3(kGatherThreads), lds, st, d, d_out,
-                     miss_rows, few_hits_above, div_magic((uint32_t)d.Q), div_magic((uint32_t)d.L),
+  hipLaunchKernelGGL(k_gather, dim3(gx, rows), dim3(kGatherThreads), lds, st, d, d_out, t,
+                     bk_rows, miss_rows, few_hits_above, div_magic((uint32_t)d.Q), div_magic((uint32_t)d.L),
                      div_magic((uint32_t)d.R));
   return hipGetLastError();
 }

@@ -62,10 +62,13 @@ __global__ __launch_bounds__(kSelThreads) void k_round(DevState d, StepArgs a,
   }
   if (tid == 0) sh.n_evict = sh.n_ring = 0;
   if (__syncthreads_or(bad)) {
-    // a query's selection was abandoned (inconsistent scan state): touch
-    // nothing, the gather reads slot 0
+    // a query's selection was abandoned (inconsistent scan state, already
+    // reported): touch nothing, the gather reads slot 0
     for (int e = tid; e < QK; e += kSelThreads) g_slot[e] = 0;
-    if (tid == 0) d.cnt[(size_t)u * Q * kCntStride + kCntMiss] = 0;
+    if (tid == 0) {
+      d.cnt[(size_t)u * Q * kCntStride + kCntMiss] = 0;
+      report_error(d, kErrRound);
+    }
     return;
   }
 

@@ -1,5 +1,6 @@
-// k_select.hip — exact top-K cut, hot-slot lookup, miss compaction and LRU
-// victim selection for one unit (session, selection group) per workgroup.
+// k_select.hip — exact top-K cut, ordering, hot-slot lookup, miss compaction
+// and LRU victim selection for one unit (session, selection group) per
+// workgroup.
 //
 // Method (page "From 1M Total to 15+ × 1M Contexts: GLM-5.3 KV Cache
 // Offloading"): the selection stays on the GPU, which checks its hot slots
@@ -9,72 +10,87 @@
 // step with ties to the lowest slot; the i-th miss (ascending position) takes
 // the i-th victim.
 //
-// Design on gfx950 (1,024 threads = 16 wave64, ~104 KB LDS, one unit each):
-//  1. Radix-select the remaining 20 key bits (2 x 10-bit digits) over the
-//     candidates of the cut bin (kept in LDS when they fit); if more keys
-//     equal the cut key than are needed, radix-select the position cut among
-//     them (lower positions win).
-//  2. Emit the K winners in ascending position order without a sort: count
-//     them into at most 8,192 buckets of 2^s consecutive positions, place
-//     each bucket at its prefix offset, and give each winner its rank inside
-//     its bucket by comparing it with the bucket's other members (rarely more
-//     than a few: 8 positions per bucket at 50K, 128 at a million).
-//  3. Positions the recent ring holds (a suffix of the ascending selection)
-//     are read from the ring and skip the cache.  For the rest, look up
-//     pos2slot; hits get last_use = t and are marked in an LDS bitmap of
-//     touched slots; misses are compacted in ascending order by wave ballot +
-//     mbcnt prefix.
-//  4. LRU without any search: a queue of (slot, step) entries in ascending
-//     (step, slot) order, live while the slot's last use equals the entry's
-//     step.  The victims are the first m live entries the step's hits do not
-//     pin; the step's slots are appended in slot order; the queue is
-//     compacted into its second buffer once every C / K steps or so.
-//  5. Apply the m (miss, victim) pairs to pos2slot / slot2pos / last_use in
-//     parallel (an evicted position is never one of this step's misses).
+// Design on gfx950 (1,024 threads = 16 wave64, one unit each).  The kernel is
+// a chain of dependent steps on one workgroup, and a dependent read of data
+// another XCD's L2 wrote costs about 1.5 us, so the kernel is built around
+// its few unavoidable round trips: every global read is issued as soon as
+// its address is known, the LDS work runs while reads are in flight, and no
+// global store is issued before the last read has been consumed (on this
+// chip the vector memory counter also counts stores, so waiting for a read
+// issued before a store waits for the store too).  Three rounds of reads:
+//  1. the unit's counters and the score scan's segment counts;
+//  2. the entries (keys above or inside the predicted cut window, with their
+//     positions; one segment per scan workgroup, each in ascending position
+//     order): a block scan of the counts places the segments, and each thread
+//     loads a run of up to 8 consecutive entries into registers, so thread
+//     order is position order — and, when the LRU queue may have to supply
+//     victims, its first 4,096 entries from the head;
+//  3. the slot-map entry of every entry's position, and the last use and
+//     position held of every prefetched queue entry.
+// Then, in LDS only: the radix cut over the window entries (the top 22 key
+// bits in one histogram pass, window bin x next 10-bit digit; the entries
+// sharing the cut's 22-bit prefix — usually a handful — rank themselves
+// against each other, which also cuts exact ties by position, lower winning);
+// one pass over the registers for winners, hits and misses, ranked together
+// by one block scan; LRU victims without any search — never-used slots first
+// (slots [fill, C), lowest first), then the first live (last use equal to the
+// entry's stamp), unpinned entries of the queue of (slot, step) entries in
+// ascending (step, slot) order, ranked by one block scan; and each slot the
+// step used gets its place at the queue's tail in slot order from a block
+// scan of per-word popcounts of the touched bitmap.  Finally every store:
+// the selection, the hits' last-use stamps, the queue's new entries, the
+// (miss, victim) pairs applied to pos2slot / slot2pos / last_use (an evicted
+// position is never one of this step's misses), the gather's miss list and
+// the trace.  The queue is compacted into its second buffer once every C / K
+// steps or so.  Inconsistent state (corrupted counters or maps) is reported
+// through the context's error words; every index stays in range.
 #include "hc_block.h"
 
 namespace hc {
 
-constexpr int kCandCache = 8192;               // cut-bin candidates kept in LDS (64 KB)
-constexpr int kOrdBuckets = 8192;              // position buckets of the ordering phase
+constexpr int kRun = 8;                               // entries per thread and round
+constexpr int kRoundEntries = kSelThreads * kRun;     // 8,192 entries per round
+constexpr int kQWin = 4;                              // queue entries per thread, prefetched
+constexpr int kSegPer = kMaxSegs / kSelThreads;       // segment counts per thread
+constexpr int kRankMax = 256;                         // entries of the cut's 22-bit prefix ranked pairwise
 
 struct SelShared {
-  uint32_t hist[kBins1];          // histograms of up to 4,096 bins
-  int32_t sel[HC_MAX_TOPK];     // winners by ascending position, then the slot of each
-  int32_t mpos[HC_MAX_TOPK];    // winners unordered (phase 2), then missing positions
-  union {
-    uint2 cand[kCandCache];       // phase 1: (key, position) of the cut bin
-    struct {
-      uint32_t start[kOrdBuckets];  // winners per bucket, then each bucket's offset
-      int32_t member[HC_MAX_TOPK];  // winners grouped by bucket
-    } ord;                        // phase 2
-    struct {
-      int32_t midx[HC_MAX_TOPK];  // index in sel of miss k
-      int32_t vic[HC_MAX_TOPK];   // victim slot of miss k
-      uint32_t touched[HC_MAX_SLOTS / 32];
-    } lru;                        // phases 3-5
-  } u;
+  uint32_t hist[kBins1];                 // radix histograms; later the victims' evicted positions
+  int32_t segoff[kMaxSegs];              // first entry of each segment
+  uint32_t touched[HC_MAX_SLOTS / 32];   // slots the step's hits use (pinned)
+  int32_t selpos[HC_MAX_TOPK];           // winners' positions, ascending
+  int32_t selslot[HC_MAX_TOPK];          // their sources: slot, C + ring entry, -1 for a miss
+  int32_t mpos[HC_MAX_TOPK];             // missing positions, ascending
+  int32_t midx[HC_MAX_TOPK];             // winner index of miss k
+  int32_t vic[HC_MAX_TOPK];              // victim slot of miss k
+  uint2 near[kRankMax];                  // (key, position) of the entries sharing the cut's prefix
   int32_t wtot[kWaves];
-  int32_t bcast[4];
-  int32_t wmax;
-  int32_t n_ring;                 // selected rows the recent ring holds
+  int32_t wtot2[kWaves];
+  int32_t wdig[kWaves];                  // find_digit's wave totals
+  int32_t bcast[8];
 };
 
-// Digit d (of nb bins, nb = 1024 or 2048) such that the count in bins above d
-// is < r and the count in bins >= d is >= r; *gt = count in bins above d.
-// If `from_top` is false the roles flip: bins below d, ascending.
-__device__ void find_digit(const uint32_t* hist, int nb, int r, bool from_top, SelShared& sh,
+// Digit d (of nb bins, nb a multiple of 1,024 up to 4,096) such that the count
+// in bins above d is < r and the count in bins >= d is >= r; `beyond` = count
+// in bins above d.  If `from_top` is false the roles flip: bins below d,
+// ascending.  Two barriers; its wave totals and answer have LDS words of their
+// own, whose next writes are at least one barrier after every read.
+__device__ __forceinline__ void find_digit(const uint32_t* hist, int nb, int r, bool from_top, SelShared& sh,
                            int& digit, int& beyond) {
-  const int per = nb / kSelThreads;  // 1 or 2 bins per thread
-  if (threadIdx.x == 0) sh.bcast[0] = sh.bcast[1] = 0;  // ordered by the scan's barriers
+  const int per = nb / kSelThreads;
+  const int lane = lane_id(), w = threadIdx.x >> 6;
   int sum = 0;
   for (int i = 0; i < per; ++i) {
     const int b = from_top ? nb - 1 - (per * threadIdx.x + i) : per * threadIdx.x + i;
     sum += (int)hist[b];
   }
-  int total;
-  const int incl = block_incl_scan(sum, sh.wtot, total);
-  const int excl = incl - sum;
+  const int x = wave_incl_scan(sum);
+  if (lane == 63) sh.wdig[w] = x;
+  __syncthreads();
+  int off = 0;
+#pragma unroll
+  for (int i = 0; i < kWaves; ++i) off += i < w ? sh.wdig[i] : 0;
+  const int incl = x + off, excl = incl - sum;
   if (excl < r && r <= incl) {
     int cum = excl;
     for (int i = 0; i < per; ++i) {
@@ -90,7 +106,6 @@ __device__ void find_digit(const uint32_t* hist, int nb, int r, bool from_top, S
   __syncthreads();
   digit = sh.bcast[0];
   beyond = sh.bcast[1];
-  __syncthreads();
 }
 
 __device__ __forceinline__ void clear_hist(SelShared& sh, int nb) {
@@ -98,15 +113,66 @@ __device__ __forceinline__ void clear_hist(SelShared& sh, int nb) {
   __syncthreads();
 }
 
-// Miss count of the step, cleared list counters and the cut bin for the next
-// step's scan.
-__device__ __forceinline__ void reset_scan_state(const DevState& d, int u, int m, int cut_bin) {
-  if (threadIdx.x == 0) {
-    d.cnt[u * kCntStride + kCntAbove] = 0;
-    d.cnt[u * kCntStride + kCntCand] = 0;
-    d.cnt[u * kCntStride + kCntMiss] = m;
-    d.cnt[u * kCntStride + kCntBin1] = cut_bin;  // centre of the next step's cut window
+// Inclusive prefix of v0 over the block (thread order) and the block totals of
+// v0 and v1, with one pair of barriers.
+__device__ __forceinline__ int block_scan_sum(int v0, int v1, SelShared& sh, int& tot0,
+                                              int& tot1) {
+  const int lane = lane_id(), w = threadIdx.x >> 6;
+  const int x0 = wave_incl_scan(v0), x1 = wave_incl_scan(v1);
+  if (lane == 63) {
+    sh.wtot[w] = x0;
+    sh.wtot2[w] = x1;
   }
+  __syncthreads();
+  int off = 0, t0 = 0, t1 = 0;
+#pragma unroll
+  for (int i = 0; i < kWaves; ++i) {
+    off += i < w ? sh.wtot[i] : 0;
+    t0 += sh.wtot[i];
+    t1 += sh.wtot2[i];
+  }
+  __syncthreads();
+  tot0 = t0;
+  tot1 = t1;
+  return x0 + off;
+}
+
+// The K-th key left the predicted window: rebuild the unit's entries from its
+// scores.  A 12-bit histogram of all H keys gives the cut bin bt; every key in
+// a bin >= bt becomes an entry, in position order, at gcand[0 ..).  Returns
+// the entry count; n_above = keys in bins above bt.
+__device__ int rescan(const float* src, int64_t H, int K, Ent* gcand, SelShared& sh,
+                      int& n_above, uint32_t& bt) {
+  const int tid = threadIdx.x;
+  clear_hist(sh, kBins1);
+  for (int64_t i = tid; i < H; i += kSelThreads)
+    atomicAdd(&sh.hist[order_key(src[i]) >> (32 - kBin1Bits)], 1u);
+  __syncthreads();
+  int b, gt;
+  find_digit(sh.hist, kBins1, K, true, sh, b, gt);
+  bt = (uint32_t)b;
+  n_above = gt;
+  int run = 0;
+  for (int64_t base = 0; base < H; base += 4 * kSelThreads) {
+    uint32_t key[4];
+    int c = 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int64_t p = base + 4 * tid + k;
+      key[k] = p < H ? order_key(src[p]) : 0u;
+      c += p < H && (key[k] >> (32 - kBin1Bits)) >= bt;
+    }
+    int total;
+    int o = run + block_incl_scan(c, sh.wtot, total) - c;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int64_t p = base + 4 * tid + k;
+      if (p < H && (key[k] >> (32 - kBin1Bits)) >= bt) gcand[o++] = Ent{key[k], (uint32_t)p, -1};
+    }
+    run += total;
+  }
+  __syncthreads();   // the entries are read back by other threads
+  return run;
 }
 
 // kTopkOnly (multi-query rounds): workgroup u is selection unit (s, g, q) and
@@ -115,364 +181,519 @@ __device__ __forceinline__ void reset_scan_state(const DevState& d, int u, int m
 template <bool kTopkOnly>
 __global__ __launch_bounds__(kSelThreads) void k_select(DevState d, StepArgs a,
                                                         const float* __restrict__ scores,
-                                                        uint64_t stride,
+                                                        uint64_t stride, int64_t seg_len,
                                                         int32_t* __restrict__ d_sel,
                                                         int32_t* __restrict__ d_trace) {
   __shared__ SelShared sh;
+  constexpr bool kCache = !kTopkOnly;
   const int u = blockIdx.x, tid = threadIdx.x;
   const int session = u / (d.G * d.Q);
   const int K = d.K, C = d.C;
   const int32_t t = a.t;
-  int32_t* cnt = d.cnt + u * kCntStride;
-  int32_t* above_g = d.above + (size_t)u * K;
-  uint2* gcand = d.cand + (size_t)u * d.hcap;
-
-  // ---- 0. the cut bin b1: the 12-bit bin holding the K-th key ---------------
-  uint32_t b_lo, b_hi;
-  cut_window(cnt[kCntBin1], b_lo, b_hi);
-  int n_above = cnt[kCntAbove];                      // keys above the window
-  int n_cand = (int)min((int64_t)cnt[kCntCand], d.hcap);
-  if (!(n_above < K && (int64_t)n_above + n_cand >= K)) {
-    // The K-th key left the predicted window: rebuild both lists from the
-    // scores — a 12-bit histogram for b1, then bins above b1 -> above, bin
-    // b1 -> cand — and use the one-bin window [b1, b1].
-    const int64_t H = a.hist_len[session];
-    const float* src = scores + (uint64_t)u * stride;
-    clear_hist(sh, kBins1);
-    for (int64_t i = tid; i < H; i += kSelThreads)
-      atomicAdd(&sh.hist[order_key(src[i]) >> (32 - kBin1Bits)], 1u);
-    __syncthreads();
-    int bt, gt;
-    find_digit(sh.hist, kBins1, K, true, sh, bt, gt);
-    if (tid == 0) sh.bcast[2] = sh.bcast[3] = 0;
-    __syncthreads();
-    const uint64_t lt = (lane_id() == 0) ? 0ull : (~0ull >> (64 - lane_id()));
-    for (int64_t i0 = 0; i0 < H; i0 += kSelThreads) {
-      const int64_t i = i0 + tid;
-      uint32_t key = 0, b = 0;
-      if (i < H) {
-        key = order_key(src[i]);
-        b = key >> (32 - kBin1Bits);
-      }
-      const bool up = i < H && b > (uint32_t)bt, eq = i < H && b == (uint32_t)bt;
-      const uint64_t bu = __ballot(up), be = __ballot(eq);
-      int ou = 0, oe = 0;
-      if (lane_id() == 0) {
-        if (bu) ou = atomicAdd(&sh.bcast[2], __popcll(bu));
-        if (be) oe = atomicAdd(&sh.bcast[3], __popcll(be));
-      }
-      // every lane is active here, so the first active lane is lane 0
-      ou = __builtin_amdgcn_readfirstlane(ou) + __popcll(bu & lt);
-      oe = __builtin_amdgcn_readfirstlane(oe) + __popcll(be & lt);
-      if (up && ou < K) above_g[ou] = (int32_t)i;
-      if (eq && oe < d.hcap) gcand[oe] = make_uint2(key, (uint32_t)i);
-    }
-    __syncthreads();
-    n_above = min(sh.bcast[2], K - 1);   // = gt < K
-    n_cand = (int)min((int64_t)sh.bcast[3], d.hcap);
-    b_lo = b_hi = (uint32_t)bt;
-    __syncthreads();
-  }
-  // Copy the candidates into LDS when they fit, counting them per window bin;
-  // the bin where the count from the top reaches K is b1.
-  const bool cached = n_cand <= kCandCache;
-  // Every pass below visits the candidates through each_cand, with the loop
-  // written once for LDS and once for global memory: through one pointer that
-  // may be either, the compiler emits generic loads that wait for every
-  // outstanding load and LDS operation, one candidate at a time.
-  auto each_cand = [&](auto&& f) {
-    if (cached) {
-#pragma unroll 4
-      for (int i = tid; i < n_cand; i += kSelThreads) f(sh.u.cand[i]);
-    } else {
-      for (int i = tid; i < n_cand; i += kSelThreads) f(gcand[i]);
-    }
-  };
-  clear_hist(sh, kBins1);
-  if (cached) {
-    // all of this thread's global reads in flight together
-    constexpr int kCopy = kCandCache / kSelThreads;   // 8
-    uint2 c[kCopy];
-#pragma unroll
-    for (int r = 0; r < kCopy; ++r) {
-      const int i = r * kSelThreads + tid;
-      c[r] = i < n_cand ? gcand[i] : uint2{0u, 0u};
-    }
-#pragma unroll
-    for (int r = 0; r < kCopy; ++r) {
-      const int i = r * kSelThreads + tid;
-      if (i >= n_cand) continue;
-      sh.u.cand[i] = c[r];
-      atomicAdd(&sh.hist[(c[r].x >> (32 - kBin1Bits)) - b_lo], 1u);
-    }
-  } else {
-    for (int i = tid; i < n_cand; i += kSelThreads)
-      atomicAdd(&sh.hist[(gcand[i].x >> (32 - kBin1Bits)) - b_lo], 1u);
-  }
-  __syncthreads();
-  int rel, beyond;
-  find_digit(sh.hist, kBins1, K - n_above, true, sh, rel, beyond);
-  const uint32_t b1 = b_lo + (uint32_t)rel;
-  int r = K - n_above - beyond;  // winners still to take from bin b1, >= 1
-
-  // ---- 1. exact cut key T and position cut among keys equal to T ----------
-  int d2, d3, skip;
-  clear_hist(sh, 1024);
-  each_cand([&](const uint2 c) {
-    if ((c.x >> 20) == b1) atomicAdd(&sh.hist[(c.x >> 10) & 1023], 1u);
-  });
-  __syncthreads();
-  find_digit(sh.hist, 1024, r, true, sh, d2, skip);
-  r -= skip;
-  clear_hist(sh, 1024);
-  each_cand([&](const uint2 c) {
-    if ((c.x >> 10) == ((b1 << 10) | (uint32_t)d2)) atomicAdd(&sh.hist[c.x & 1023], 1u);
-  });
-  __syncthreads();
-  find_digit(sh.hist, 1024, r, true, sh, d3, skip);
-  r -= skip;
-  const int n_eq = (int)sh.hist[d3];
-  const uint32_t T = (b1 << 20) | ((uint32_t)d2 << 10) | (uint32_t)d3;
-  int32_t pcut = 0x7FFFFFFF;  // take ties at T with position <= pcut
-  if (r < n_eq) {
-    // the r-th smallest position among keys == T: digits of 11, 10, 10 bits
-    int e1, e2, e3, below;
-    __syncthreads();
-    clear_hist(sh, 2048);
-    each_cand([&](const uint2 c) {
-      if (c.x == T) atomicAdd(&sh.hist[c.y >> 20], 1u);
-    });
-    __syncthreads();
-    find_digit(sh.hist, 2048, r, false, sh, e1, below);
-    r -= below;
-    clear_hist(sh, 1024);
-    each_cand([&](const uint2 c) {
-      if (c.x == T && (int)(c.y >> 20) == e1) atomicAdd(&sh.hist[(c.y >> 10) & 1023], 1u);
-    });
-    __syncthreads();
-    find_digit(sh.hist, 1024, r, false, sh, e2, below);
-    r -= below;
-    clear_hist(sh, 1024);
-    const uint32_t hi = ((uint32_t)e1 << 10) | (uint32_t)e2;
-    each_cand([&](const uint2 c) {
-      if (c.x == T && (c.y >> 10) == hi) atomicAdd(&sh.hist[c.y & 1023], 1u);
-    });
-    __syncthreads();
-    find_digit(sh.hist, 1024, r, false, sh, e3, below);
-    pcut = (int32_t)((hi << 10) | (uint32_t)e3);
-  }
-
-  // ---- 2. the K winners, in ascending position order ---------------------
-  if (tid == 0) {
-    sh.bcast[2] = 0;
-    sh.wmax = 0;
-    sh.n_ring = 0;
-  }
-  __syncthreads();
-  int32_t pmax = 0;
-  {
-    // n_above < K: at most 4 per thread, all reads in flight together
-    constexpr int kAbove = HC_MAX_TOPK / kSelThreads;
-    int32_t ap[kAbove];
-#pragma unroll
-    for (int r = 0; r < kAbove; ++r) {
-      const int i = r * kSelThreads + tid;
-      ap[r] = i < n_above ? above_g[i] : 0;
-    }
-#pragma unroll
-    for (int r = 0; r < kAbove; ++r) {
-      const int i = r * kSelThreads + tid;
-      if (i >= n_above) continue;
-      sh.mpos[i] = ap[r];
-      pmax = max(pmax, ap[r]);
-    }
-  }
-  // candidates that win, compacted per wave: one LDS atomic per wave
-  const uint64_t lt_mask = (lane_id() == 0) ? 0ull : (~0ull >> (64 - lane_id()));
-  auto win_pass = [&](auto&& cand_at) {
-    for (int i0 = 0; i0 < n_cand; i0 += kSelThreads) {
-      const int i = i0 + tid;
-      bool win = false;
-      int32_t p = 0;
-      if (i < n_cand) {
-        const uint2 c = cand_at(i);
-        p = (int32_t)c.y;
-        win = c.x > T || (c.x == T && p <= pcut);
-      }
-      const uint64_t bal = __ballot(win);
-      int base = 0;
-      if (lane_id() == 0 && bal) base = atomicAdd(&sh.bcast[2], __popcll(bal));
-      base = __builtin_amdgcn_readfirstlane(base);   // lane 0's: every lane is active
-      if (win) {
-        const int o = n_above + base + __popcll(bal & lt_mask);
-        if (o < K) sh.mpos[o] = p;  // exactly K - n_above winners by construction
-        pmax = max(pmax, p);
-      }
-    }
-  };
-  if (cached)
-    win_pass([&](int i) { return sh.u.cand[i]; });
-  else
-    win_pass([&](int i) { return gcand[i]; });
-  pmax = wave_max(pmax);
-  if (lane_id() == 0) atomicMax(&sh.wmax, pmax);
-  __syncthreads();
-  if (sh.bcast[2] != K - n_above) {
-    // Inconsistent scan state (cannot happen when the histogram was clean):
-    // report an empty selection and touch nothing.
-    for (int i = tid; i < K; i += kSelThreads) {
-      d_sel[(size_t)u * K + i] = -1;
-      d.sel_slot[(size_t)u * K + i] = 0;  // the gather then only reads slot 0
-    }
-    reset_scan_state(d, u, 0, (int)b1);
-    return;
-  }
-  {
-    // buckets of 2^shift positions, at most kOrdBuckets of them
-    const int wmax = sh.wmax;
-    int shift = 0;
-    while ((wmax >> shift) >= kOrdBuckets) ++shift;
-    const int nb = (wmax >> shift) + 1;
-    constexpr int kRounds = HC_MAX_TOPK / kSelThreads;   // winners per thread
-    constexpr int kBPer = kOrdBuckets / kSelThreads;     // buckets per thread
-    for (int b = tid; b < nb; b += kSelThreads) sh.u.ord.start[b] = 0;
-    __syncthreads();
-    int32_t wp[kRounds];
-    int arrival[kRounds];
-#pragma unroll
-    for (int r = 0; r < kRounds; ++r) {
-      const int i = r * kSelThreads + tid;
-      wp[r] = i < K ? sh.mpos[i] : 0;
-      arrival[r] = i < K ? (int)atomicAdd(&sh.u.ord.start[wp[r] >> shift], 1u) : 0;
-    }
-    __syncthreads();
-    int cnt8[kBPer];
-    int sum = 0;
-#pragma unroll
-    for (int j = 0; j < kBPer; ++j) {
-      const int b = tid * kBPer + j;
-      cnt8[j] = b < nb ? (int)sh.u.ord.start[b] : 0;
-      sum += cnt8[j];
-    }
-    int total;
-    int off = block_incl_scan(sum, sh.wtot, total) - sum;
-#pragma unroll
-    for (int j = 0; j < kBPer; ++j) {
-      const int b = tid * kBPer + j;
-      if (b < nb) sh.u.ord.start[b] = (uint32_t)off;
-      off += cnt8[j];
-    }
-    __syncthreads();
-#pragma unroll
-    for (int r = 0; r < kRounds; ++r) {
-      const int i = r * kSelThreads + tid;
-      if (i < K) sh.u.ord.member[sh.u.ord.start[wp[r] >> shift] + arrival[r]] = wp[r];
-    }
-    __syncthreads();
-#pragma unroll
-    for (int r = 0; r < kRounds; ++r) {
-      const int i = r * kSelThreads + tid;
-      if (i >= K) continue;
-      const int b = wp[r] >> shift;
-      const int lo = (int)sh.u.ord.start[b];
-      const int hi = b + 1 < nb ? (int)sh.u.ord.start[b + 1] : K;
-      int rank = 0;
-      for (int q = lo; q < hi; ++q) rank += sh.u.ord.member[q] < wp[r];
-      sh.sel[lo + rank] = wp[r];
-    }
-  }
-  __syncthreads();
-  for (int i = tid; i < K; i += kSelThreads) d_sel[(size_t)u * K + i] = sh.sel[i];
-  if (kTopkOnly) {
-    reset_scan_state(d, u, 0, (int)b1);
-    return;
-  }
-
-  // ---- 3. lookup, hits, ascending miss compaction ------------------------
-  const int nwords = (C + 31) >> 5;
-  for (int w = tid; w < nwords; w += kSelThreads) sh.u.lru.touched[w] = 0;
+  const int64_t H = a.hist_len[session];
+  const uint32_t ring_lo = a.ring_lo[session];
+  int32_t* cnt = d.cnt + (size_t)u * kCntStride;
+  Ent* gcand = d.cand + (size_t)u * d.hcap;
   int32_t* pos2slot = d.pos2slot + (size_t)u * d.hcap;
   int32_t* slot2pos = d.slot2pos + (size_t)u * C;
   int32_t* last_use = d.last_use + (size_t)u * C;
-  constexpr int kLookRounds = HC_MAX_TOPK / kSelThreads;
-  const uint32_t ring_lo = a.ring_lo[session];
-  int32_t lp[kLookRounds], ls[kLookRounds];
-#pragma unroll
-  for (int r = 0; r < kLookRounds; ++r) {   // all map reads in flight together
-    const int i = r * kSelThreads + tid;
-    lp[r] = i < K ? sh.sel[i] : 0;
-    const bool in_ring = i < K && (uint32_t)lp[r] >= ring_lo;
-    ls[r] = i < K && !in_ring ? pos2slot[lp[r]] : 0;
-    // the first ring row of the ascending selection counts the suffix
-    if (in_ring && (i == 0 || (uint32_t)sh.sel[i - 1] < ring_lo)) sh.n_ring = K - i;
+  const bool lru = kCache && d.policy == HC_REPLACE_LRU;
+  const int nwords = (C + 31) >> 5;
+
+  // ==== reads, round 1: counters and segment counts =========================
+  const int win_lo = cnt[kCntWinLo], win_hi = cnt[kCntWinHi];
+  int qh = 0, qe = 0, qb = 0, fill = 0;
+  if (kCache) {
+    qh = cnt[kCntQHead];
+    qe = cnt[kCntQTail];
+    qb = cnt[kCntQBuf] & 1;
+    fill = cnt[kCntFill];
   }
-  __syncthreads();
-  const int n_ring = sh.n_ring;
-  const int first_ring = K - n_ring;
-  int m = 0;
+  const int nseg = (int)((H + seg_len - 1) / seg_len);   // <= max_segs, checked on the host
+  int2 segc[kSegPer];
 #pragma unroll
-  for (int r = 0; r < kLookRounds; ++r) {
-    if (r * kSelThreads >= K) break;
-    const int i = r * kSelThreads + tid;
-    const bool valid = i < K;
-    const bool in_ring = valid && i >= first_ring;
-    const bool miss = valid && !in_ring && ls[r] < 0;
-    if (valid && !in_ring && !miss) {
-      last_use[ls[r]] = t;
-      atomicOr(&sh.u.lru.touched[ls[r] >> 5], 1u << (ls[r] & 31));
+  for (int k = 0; k < kSegPer; ++k) {
+    const int s = tid * kSegPer + k;
+    segc[k] = s < nseg ? d.seg[(size_t)u * d.max_segs + s] : make_int2(0, 0);
+  }
+  for (int b = tid; b < kBins1; b += kSelThreads) sh.hist[b] = 0;
+  if (kCache)
+    for (int w = tid; w < nwords; w += kSelThreads) sh.touched[w] = 0;
+  if (tid == 0) sh.bcast[7] = 0;   // evictions, counted at the stores
+  fill = min(max(fill, 0), C);
+  qe = min(max(qe, 0), d.qcap);
+  qh = min(max(qh, 0), qe);
+  // the queue supplies victims only once fewer than K never-used slots remain
+  const bool q_pf = lru && fill + K > C && qe > qh;
+  const int2* qbuf = d.oq + ((size_t)u * 2 + qb) * d.qcap;
+  const int qj0 = (qh & ~(kQWin - 1)) + tid * kQWin;
+
+  int sc[kSegPer];
+  int se = 0, sa = 0;
+#pragma unroll
+  for (int k = 0; k < kSegPer; ++k) {
+    const int s = tid * kSegPer + k;
+    const int64_t room = H - (int64_t)s * seg_len < seg_len ? H - (int64_t)s * seg_len : seg_len;
+    const int n = s < nseg ? (int)min((int64_t)max(segc[k].x, 0), room) : 0;
+    sc[k] = n;
+    se += n;
+    sa += min(max(segc[k].y, 0), n);
+  }
+  int E, n_above;
+  int o = block_scan_sum(se, sa, sh, E, n_above) - se;
+#pragma unroll
+  for (int k = 0; k < kSegPer; ++k) {
+    const int s = tid * kSegPer + k;
+    if (s < nseg) sh.segoff[s] = o;
+    o += sc[k];
+  }
+  uint32_t b_lo, b_hi;   // the scan's cut window, top-16-bit key units
+  cut_window(win_lo, win_hi, b_lo, b_hi);
+  // Fast path: the K-th key lies inside the predicted window and at most
+  // 8,192 entries lie above or inside it, so every entry fits in registers,
+  // up to 8 per thread.  Otherwise the slow path makes every pass over the
+  // entries in global memory: over the scan's segments if the window holds
+  // the K-th key (ties, flat scores), else over a list rebuilt from the
+  // scores (the cut jumped).
+  const bool window_ok = n_above < K && E >= K;
+  const bool fast = window_ok && E <= kRoundEntries;
+
+  // ==== reads, round 2: the LRU queue's first window, the entries ===========
+  int2 qent[kQWin];
+  {
+    int4 w0 = make_int4(-1, -1, -1, -1), w1 = w0;   // qcap % 4 == 0: both in bounds
+    if (q_pf && qj0 < qe) w0 = *reinterpret_cast<const int4*>(qbuf + qj0);
+    if (q_pf && qj0 + 2 < qe) w1 = *reinterpret_cast<const int4*>(qbuf + qj0 + 2);
+    qent[0] = make_int2(w0.x, w0.y);
+    qent[1] = make_int2(w0.z, w0.w);
+    qent[2] = make_int2(w1.x, w1.y);
+    qent[3] = make_int2(w1.z, w1.w);
+  }
+  // this thread's run of R consecutive entries: thread order is position order
+  uint32_t key[kRun];
+  int32_t pos[kRun];
+  int32_t slot[kRun];   // slot of each entry's position (the scan's lookup), -1: miss or ring
+  int nv = 0;
+  if (fast) {
+    const int R = (E + kSelThreads - 1) / kSelThreads;
+    const int j0 = tid * R;
+    nv = max(0, min(R, E - j0));
+    int lo = 0, hi = nseg;   // the last segment starting at or before j0
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (sh.segoff[mid] <= j0) lo = mid;
+      else hi = mid;
     }
-    // from here on sel[] holds slots: C + ring entry for ring rows, -1 for a
-    // miss (its victim is filled in below)
-    if (valid) sh.sel[i] = in_ring ? d.C + (int32_t)((uint32_t)lp[r] % (uint32_t)d.ring_rows) : ls[r];
-    int total;
-    const int k = m + block_flag_rank(miss, sh.wtot, total);
-    if (miss) {
-      sh.mpos[k] = lp[r];
-      sh.u.lru.midx[k] = i;
+    int sg = lo;
+    int start = sh.segoff[sg];
+    int next = sg + 1 < nseg ? sh.segoff[sg + 1] : 0x7FFFFFFF;
+#pragma unroll
+    for (int k = 0; k < kRun; ++k) {
+      key[k] = 0u;
+      pos[k] = -1;
+      slot[k] = -1;
+      if (k >= nv) continue;
+      const int j = j0 + k;
+      while (j >= next) {   // the run crosses into a later segment
+        ++sg;
+        start = next;
+        next = sg + 1 < nseg ? sh.segoff[sg + 1] : 0x7FFFFFFF;
+      }
+      const Ent e = gcand[(int64_t)sg * seg_len + (j - start)];
+      key[k] = e.key;
+      pos[k] = (int32_t)e.pos;
+      if (kCache) slot[k] = e.slot;
     }
-    m += total;
   }
 
-  // ---- 4. LRU victims: first m live, unpinned entries of the queue -------
-  if (d.policy == HC_REPLACE_LRU)
-    lru_victims(d, u, t, m, K - n_ring, sh.u.lru.touched, sh.u.lru.vic, sh.wtot, &sh.bcast[0]);
-  else
-    hand_victims(d, u, m, d.policy == HC_REPLACE_CLOCK, sh.u.lru.touched, sh.u.lru.vic, sh.wtot,
-                 &sh.bcast[0]);
+  // ==== reads, round 3: the prefetched queue entries' state ==================
+  int qlu[kQWin], qsp[kQWin];
+#pragma unroll
+  for (int k = 0; k < kQWin; ++k) {
+    const int j = qj0 + k;
+    const bool ok = q_pf && j >= qh && j < qe && qent[k].x >= 0 && qent[k].x < C;
+    qlu[k] = ok ? last_use[qent[k].x] : (int)0x80000000;
+    qsp[k] = ok ? slot2pos[qent[k].x] : -1;
+  }
 
-  // ---- 5. apply (miss, victim) pairs --------------------------------------
-  // A miss row is marked in sel_slot as -(slot + 1): the gather then reads it
-  // from host RAM and writes it into that slot itself.
-  if (tid == 0) sh.bcast[3] = 0;
+  // ==== the cut key T and position cut (LDS) =================================
+  // `each` visits every entry once as (key, position): from registers on the
+  // fast path, from global memory on the slow path (entry j of the segments
+  // found by a binary search over their first entries).
+  int nrows = E;   // entries of the slow path
+  int nsegs = nseg;
+  if (!window_ok) {
+    uint32_t bt;
+    nrows = rescan(scores + (uint64_t)u * stride, H, K, gcand, sh, n_above, bt);
+    b_lo = bt << 4;   // the rebuilt list's window: the 12-bit cut bin
+    b_hi = (bt << 4) | 15;
+    nsegs = 1;
+    if (tid == 0) sh.segoff[0] = 0;
+    for (int b = tid; b < kBins1; b += kSelThreads) sh.hist[b] = 0;
+    __syncthreads();
+  }
+  auto entry = [&](int j) {   // slow path: entry j
+    int lo = 0, hi = nsegs;
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (sh.segoff[mid] <= j) lo = mid;
+      else hi = mid;
+    }
+    return gcand[(int64_t)lo * seg_len + (j - sh.segoff[lo])];
+  };
+  auto each = [&](auto&& f) {
+    if (fast) {
+#pragma unroll
+      for (int k = 0; k < kRun; ++k)
+        if (k < nv) f(key[k], pos[k]);
+    } else {
+      for (int j = tid; j < nrows; j += kSelThreads) {
+        const Ent e = entry(j);
+        f(e.key, (int32_t)e.pos);
+      }
+    }
+  };
+  int r = K - n_above;   // winners still to take from the window, >= 1
+  uint32_t lo16 = b_lo, hi16 = b_hi;
+  int beyond;
+  if (hi16 - lo16 + 1 > 64) {
+    // a wide window (a unit's first step without a cut histogram): narrow it
+    // to the 12-bit bin holding the K-th key first
+    const uint32_t lo12 = lo16 >> 4;
+    each([&](uint32_t kk, int32_t) {
+      const uint32_t k16 = kk >> 16;
+      if (k16 >= lo16 && k16 <= hi16) atomicAdd(&sh.hist[(kk >> 20) - lo12], 1u);
+    });
+    __syncthreads();
+    int rel;
+    find_digit(sh.hist, kBins1, r, true, sh, rel, beyond);
+    r -= beyond;
+    const uint32_t b12 = lo12 + (uint32_t)rel;
+    lo16 = max(lo16, b12 << 4);
+    hi16 = min(hi16, (b12 << 4) | 15u);
+    clear_hist(sh, kBins1);
+  }
+  // the top 22 bits: window prefix x the next 6 bits in one histogram of at
+  // most 64 x 64 bins
+  const uint32_t w_lo22 = lo16 << 6, w_hi22 = (hi16 + 1) << 6;
+  each([&](uint32_t kk, int32_t) {
+    const uint32_t p22 = kk >> 10;
+    if (p22 >= w_lo22 && p22 < w_hi22) atomicAdd(&sh.hist[p22 - w_lo22], 1u);
+  });
+  if (tid == 0) sh.bcast[2] = 0;   // entries of the cut prefix listed so far
   __syncthreads();
+  int idx22;
+  find_digit(sh.hist, kBins1, r, true, sh, idx22, beyond);
+  r -= beyond;   // winners to take among the entries of the prefix, >= 1
+  const uint32_t pre22 = w_lo22 + (uint32_t)idx22;
+  const int n22 = (int)sh.hist[idx22];
+  uint32_t T;
+  int32_t pcut = 0x7FFFFFFF;   // take ties at T with position <= pcut
+  if (n22 <= kRankMax) {
+    // the prefix's entries (usually a handful) rank themselves by (key
+    // descending, position ascending): the r-th is the last winner, whose key
+    // and position are the cuts
+    each([&](uint32_t kk, int32_t p) {
+      if ((kk >> 10) == pre22) {
+        const int i = atomicAdd(&sh.bcast[2], 1);
+        if (i < kRankMax) sh.near[i] = make_uint2(kk, (uint32_t)p);
+      }
+    });
+    __syncthreads();
+    const int n = min(sh.bcast[2], kRankMax);
+    for (int i = tid; i < n; i += kSelThreads) {
+      const uint2 me = sh.near[i];
+      int better = 0;
+      for (int j = 0; j < n; ++j) {
+        const uint2 o2 = sh.near[j];
+        better += o2.x > me.x || (o2.x == me.x && o2.y < me.y);
+      }
+      if (better == r - 1) {
+        sh.bcast[3] = (int)me.x;
+        sh.bcast[4] = (int)me.y;
+      }
+    }
+    __syncthreads();
+    T = (uint32_t)sh.bcast[3];
+    pcut = sh.bcast[4];
+  } else {
+    // many entries share the prefix (ties, flat scores): the last 10 key bits
+    // by histogram, then, if the cut falls inside a run of equal keys, the
+    // r-th smallest position among them (digits of 11, 10, 10 bits)
+    clear_hist(sh, 1024);
+    each([&](uint32_t kk, int32_t) {
+      if ((kk >> 10) == pre22) atomicAdd(&sh.hist[kk & 1023], 1u);
+    });
+    __syncthreads();
+    int d3;
+    find_digit(sh.hist, 1024, r, true, sh, d3, beyond);
+    r -= beyond;
+    const int n_eq = (int)sh.hist[d3];
+    T = (pre22 << 10) | (uint32_t)d3;
+    if (r < n_eq) {
+      int e1, e2, e3, below;
+      __syncthreads();
+      clear_hist(sh, 2048);
+      each([&](uint32_t kk, int32_t p) {
+        if (kk == T) atomicAdd(&sh.hist[(uint32_t)p >> 20], 1u);
+      });
+      __syncthreads();
+      find_digit(sh.hist, 2048, r, false, sh, e1, below);
+      r -= below;
+      __syncthreads();
+      clear_hist(sh, 1024);
+      each([&](uint32_t kk, int32_t p) {
+        if (kk == T && (int)((uint32_t)p >> 20) == e1)
+          atomicAdd(&sh.hist[((uint32_t)p >> 10) & 1023], 1u);
+      });
+      __syncthreads();
+      find_digit(sh.hist, 1024, r, false, sh, e2, below);
+      r -= below;
+      __syncthreads();
+      clear_hist(sh, 1024);
+      const uint32_t hi = ((uint32_t)e1 << 10) | (uint32_t)e2;
+      each([&](uint32_t kk, int32_t p) {
+        if (kk == T && ((uint32_t)p >> 10) == hi) atomicAdd(&sh.hist[(uint32_t)p & 1023], 1u);
+      });
+      __syncthreads();
+      find_digit(sh.hist, 1024, r, false, sh, e3, below);
+      pcut = (int32_t)((hi << 10) | (uint32_t)e3);
+    }
+  }
+
+  // the next step's window: this cut's 16-bit prefix +- kWinHalf
+  const int nlo = max((int)(T >> 16) - kWinHalf, 0), nhi = min((int)(T >> 16) + kWinHalf, 65535);
+
+  // ==== winners in position order, hits, misses (LDS) ========================
+  // one block scan ranks winners and misses (two 16-bit fields of one value)
+  // and counts ring rows and corrupt slot-map entries (second value)
+  int nwin = 0, m = 0, n_ring = 0, n_bad = 0;
+  // Records winner wr (miss rank mr) with its source.
+  auto record = [&](int wr, int mr, int32_t p, int32_t sl, bool ring, bool miss) {
+    if (wr >= K) return;
+    sh.selpos[wr] = p;
+    if (!kCache) return;
+    sh.selslot[wr] = ring ? C + (int32_t)((uint32_t)p % (uint32_t)d.ring_rows) : (miss ? -1 : sl);
+    if (miss && mr < K) {
+      sh.mpos[mr] = p;
+      sh.midx[mr] = wr;
+    }
+    if (!ring && !miss) atomicOr(&sh.touched[sl >> 5], 1u << (sl & 31));
+  };
+  if (fast) {
+    int cw = 0, cm = 0, cr = 0, cb = 0;
+    uint32_t fw = 0, fm = 0, fr = 0;   // bit k: entry k wins / misses / is a ring row
+#pragma unroll
+    for (int k = 0; k < kRun; ++k) {
+      const bool win = k < nv && (key[k] > T || (key[k] == T && pos[k] <= pcut));
+      const bool ring = kCache && win && (uint32_t)pos[k] >= ring_lo;
+      const bool corrupt = kCache && win && !ring && slot[k] >= C;   // a corrupt slot map entry
+      const bool miss = kCache && win && !ring && (slot[k] < 0 || corrupt);
+      fw |= (uint32_t)win << k;
+      fm |= (uint32_t)miss << k;
+      fr |= (uint32_t)ring << k;
+      cw += win;
+      cm += miss;
+      cr += ring;
+      cb += corrupt;
+    }
+    // winners <= 8,192, misses and ring rows <= K, corrupt entries <= 8,192:
+    // 16-bit fields, no carry
+    int tot, tot1;
+    const int packed = cw | (cm << 16);
+    const int ex = block_scan_sum(packed, cr | (cb << 16), sh, tot, tot1) - packed;
+    int wr = ex & 0xFFFF, mr = ex >> 16;
+#pragma unroll
+    for (int k = 0; k < kRun; ++k) {
+      if (!((fw >> k) & 1u)) continue;
+      const bool ring = (fr >> k) & 1u, miss = (fm >> k) & 1u;
+      record(wr, mr, pos[k], slot[k], ring, miss);
+      mr += miss;
+      ++wr;
+    }
+    nwin = tot & 0xFFFF;
+    m = tot >> 16;
+    n_ring = tot1 & 0xFFFF;
+    n_bad = tot1 >> 16;
+  } else {
+    // the rebuilt list in position order, 1,024 entries at a time; slots
+    // looked up here
+    for (int j0 = 0; j0 < nrows; j0 += kSelThreads) {
+      const int j = j0 + tid;
+      Ent e{0u, 0u, -1};
+      if (j < nrows) e = entry(j);
+      const int32_t p = (int32_t)e.pos;
+      const bool win = j < nrows && (e.key > T || (e.key == T && p <= pcut));
+      const bool ring = kCache && win && (uint32_t)p >= ring_lo;
+      int32_t sl = -1;
+      if (kCache && win && !ring && p >= 0 && p < H) sl = pos2slot[p];
+      const bool corrupt = kCache && win && !ring && sl >= C;
+      const bool miss = kCache && win && !ring && (sl < 0 || corrupt);
+      int tot, tot1;
+      const int packed = (int)win | ((int)miss << 16);
+      const int ex = block_scan_sum(packed, (int)ring | ((int)corrupt << 16), sh, tot, tot1) - packed;
+      if (win) record(nwin + (ex & 0xFFFF), m + (ex >> 16), p, sl, ring, miss);
+      nwin += tot & 0xFFFF;
+      m += tot >> 16;
+      n_ring += tot1 & 0xFFFF;
+      n_bad += tot1 >> 16;
+    }
+  }
+  if (n_bad || nwin != K || m > K) {
+    // inconsistent scan state or slot map: report it and touch nothing more;
+    // the selection stays in range (the gather reads slot 0)
+    if (tid == 0) report_error(d, kErrSelect);
+    for (int i = tid; i < K; i += kSelThreads) {
+      d_sel[(size_t)u * K + i] = -1;
+      if (kCache) d.sel_slot[(size_t)u * K + i] = 0;
+    }
+    if (tid == 0) {
+      if (kCache) cnt[kCntMiss] = 0;
+      cnt[kCntWinLo] = cnt[kCntWinHi] = -1;   // the next step considers every key
+    }
+    return;
+  }
+  __syncthreads();   // the recorded winners are read by other threads below
+  if (kTopkOnly) {
+    for (int i = tid; i < K; i += kSelThreads) d_sel[(size_t)u * K + i] = sh.selpos[i];
+    if (tid == 0) {
+      cnt[kCntWinLo] = nlo;
+      cnt[kCntWinHi] = nhi;
+    }
+    return;
+  }
+
+  // ==== victims (LDS; further queue reads only when the window falls short) ==
+  int32_t* vold = reinterpret_cast<int32_t*>(sh.hist);   // position each victim held
+  int32_t* vic = sh.vic;
+  int n_new = 0;
+  if (lru) {
+    // never-used slots first, then the first live, unpinned queue entries
+    n_new = min(m, C - fill);
+    for (int k = tid; k < n_new; k += kSelThreads) {
+      vic[k] = fill + k;
+      vold[k] = -1;
+    }
+    const int need = m - n_new;
+    if (tid == 0) sh.bcast[6] = qh - 1;   // queue index of the last victim
+    if (need > 0) {
+      // the prefetched window: entries [qh & ~3, + 4,096)
+      auto pinned = [&](int v) { return (sh.touched[v >> 5] >> (v & 31)) & 1u; };
+      bool f[kQWin];
+      int c = 0;
+#pragma unroll
+      for (int k = 0; k < kQWin; ++k) {
+        const int j = qj0 + k;
+        f[k] = q_pf && j >= qh && j < qe && qent[k].x >= 0 && qent[k].x < C &&
+               !pinned(qent[k].x) && qlu[k] == qent[k].y;
+        c += f[k];
+      }
+      int total, dummy;
+      int k0 = block_scan_sum(c, 0, sh, total, dummy) - c;
+#pragma unroll
+      for (int k = 0; k < kQWin; ++k) {
+        if (!f[k]) continue;
+        if (k0 < need) {
+          vic[n_new + k0] = qent[k].x;
+          vold[n_new + k0] = qsp[k];
+          if (k0 == need - 1) sh.bcast[6] = qj0 + k;
+        }
+        ++k0;
+      }
+      int found = total;
+      // further windows (rare: the 4,096 entries from the head hold fewer live
+      // ones than the step needs)
+      for (int jw = (qh & ~(kQWin - 1)) + kSelThreads * kQWin; found < need && jw < qe;
+           jw += kSelThreads * kQWin) {
+        const int jb = jw + tid * kQWin;
+        int2 ent[kQWin];
+        {
+          int4 w0 = make_int4(-1, -1, -1, -1), w1 = w0;
+          if (jb < qe) w0 = *reinterpret_cast<const int4*>(qbuf + jb);
+          if (jb + 2 < qe) w1 = *reinterpret_cast<const int4*>(qbuf + jb + 2);
+          ent[0] = make_int2(w0.x, w0.y);
+          ent[1] = make_int2(w0.z, w0.w);
+          ent[2] = make_int2(w1.x, w1.y);
+          ent[3] = make_int2(w1.z, w1.w);
+        }
+        bool g[kQWin];
+        int lu[kQWin], sp[kQWin];
+#pragma unroll
+        for (int k = 0; k < kQWin; ++k) {
+          g[k] = jb + k < qe && ent[k].x >= 0 && ent[k].x < C && !pinned(ent[k].x);
+          lu[k] = g[k] ? last_use[ent[k].x] : 0;
+          sp[k] = g[k] ? slot2pos[ent[k].x] : -1;
+        }
+        int cc = 0;
+#pragma unroll
+        for (int k = 0; k < kQWin; ++k) {
+          g[k] = g[k] && lu[k] == ent[k].y;
+          cc += g[k];
+        }
+        int tot2;
+        int q0 = found + block_scan_sum(cc, 0, sh, tot2, dummy) - cc;
+#pragma unroll
+        for (int k = 0; k < kQWin; ++k) {
+          if (!g[k]) continue;
+          if (q0 < need) {
+            vic[n_new + q0] = ent[k].x;
+            vold[n_new + q0] = sp[k];
+            if (q0 == need - 1) sh.bcast[6] = jb + k;
+          }
+          ++q0;
+        }
+        found += tot2;
+      }
+      if (found < need) {
+        // a corrupted queue: report it; keep every index in range
+        if (tid == 0) report_error(d, kErrLru);
+        for (int k = n_new + found + tid; k < m; k += kSelThreads) {
+          vic[k] = 0;
+          vold[k] = -1;
+        }
+      }
+    }
+  } else {
+    hand_victims(d, u, m, d.policy == HC_REPLACE_CLOCK, sh.touched, vic, sh.wtot, &sh.bcast[6]);
+    for (int k = tid; k < m; k += kSelThreads) vold[k] = slot2pos[vic[k]];
+  }
+  __syncthreads();
+
+  // ==== stores ================================================================
+  // The selection, each selected row's source for the gather (a miss row is
+  // marked -(slot + 1): the gather reads it from host RAM and writes it into
+  // that slot itself), the dense miss list with each victim's previous
+  // position, and the trace.  The gather's bookkeeping workgroup of the unit
+  // stamps the step's slots, applies the (miss, victim) pairs to the slot maps
+  // and appends the step's slots to the LRU queue.
   int32_t* tr = d_trace ? d_trace + (size_t)u * HC_TRACE_INTS(K) : nullptr;
-  int32_t* g_miss = d.miss_pos + (size_t)u * K;   // the gather's dense miss list
+  int32_t* g_miss = d.miss_pos + (size_t)u * K;
   int32_t* g_vic = d.victim + (size_t)u * K;
   int32_t* g_midx = d.miss_idx + (size_t)u * K;
+  int32_t* g_old = d.miss_old + (size_t)u * K;
+  int n_evict = 0;
   for (int k = tid; k < m; k += kSelThreads) {
-    const int32_t v = sh.u.lru.vic[k], p = sh.mpos[k];
-    const int32_t old = slot2pos[v];
-    if (old >= 0) {
-      pos2slot[old] = -1;
-      atomicAdd(&sh.bcast[3], 1);
-    }
-    pos2slot[p] = v;
-    slot2pos[v] = p;
-    last_use[v] = t;
-    sh.sel[sh.u.lru.midx[k]] = -(v + 1);
+    const int32_t v = vic[k], p = sh.mpos[k];
+    int32_t old = vold[k];
+    if (old < 0 || old >= d.hcap) old = -1;
+    n_evict += old >= 0;
+    sh.selslot[sh.midx[k]] = -(v + 1);
     g_miss[k] = p;
     g_vic[k] = v;
-    g_midx[k] = sh.u.lru.midx[k];
+    g_midx[k] = sh.midx[k];
+    g_old[k] = old;
     if (tr) {
       tr[HC_TRACE_HEADER + K + k] = p;
       tr[HC_TRACE_HEADER + 2 * K + k] = v;
       tr[HC_TRACE_HEADER + 3 * K + k] = old;
     }
   }
+  if (n_evict) atomicAdd(&sh.bcast[7], n_evict);
   __syncthreads();
   int32_t* g_slot = d.sel_slot + (size_t)u * K;
   for (int i = tid; i < K; i += kSelThreads) {
-    const int32_t enc = sh.sel[i];
+    d_sel[(size_t)u * K + i] = sh.selpos[i];
+    const int32_t enc = sh.selslot[i];
     g_slot[i] = enc;
     if (tr) {
       tr[HC_TRACE_HEADER + i] = enc < 0 ? -enc - 1 : enc;
@@ -483,24 +704,33 @@ __global__ __launch_bounds__(kSelThreads) void k_select(DevState d, StepArgs a,
       }
     }
   }
-  if (tr && tid == 0) {
-    tr[0] = K - m - n_ring;
-    tr[1] = m;
-    tr[2] = sh.bcast[3];
-    tr[3] = n_ring;
+  if (tid == 0) {
+    if (tr) {
+      tr[0] = K - m - n_ring;
+      tr[1] = m;
+      tr[2] = sh.bcast[7];
+      tr[3] = n_ring;
+    }
+    if (lru) {
+      cnt[kCntQHead] = sh.bcast[6] + 1;   // past the last victim; the gather appends at the tail
+      cnt[kCntFill] = fill + n_new;
+    }
+    cnt[kCntMiss] = m;
+    cnt[kCntWinLo] = nlo;   // the next step's cut window
+    cnt[kCntWinHi] = nhi;
   }
-
-  reset_scan_state(d, u, m, (int)b1);
 }
 
 hipError_t launch_select(const DevState& d, const StepArgs& a, const float* scores,
-                         uint64_t stride, int32_t* d_sel, int32_t* d_trace, hipStream_t st) {
+                         uint64_t stride, int64_t max_len, int32_t* d_sel, int32_t* d_trace,
+                         hipStream_t st) {
+  const int64_t seg_len = scan_seg_len(max_len, d.max_segs);
   if (d.Q == 1)
     hipLaunchKernelGGL(k_select<false>, dim3(d.S * d.G), dim3(kSelThreads), 0, st, d, a, scores,
-                       stride, d_sel, d_trace);
+                       stride, seg_len, d_sel, d_trace);
   else
     hipLaunchKernelGGL(k_select<true>, dim3(d.S * d.G * d.Q), dim3(kSelThreads), 0, st, d, a,
-                       scores, stride, d_sel, d_trace);
+                       scores, stride, seg_len, d_sel, d_trace);
   return hipGetLastError();
 }
 

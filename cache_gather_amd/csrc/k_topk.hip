@@ -9,63 +9,92 @@
 // digit is the top 12 bits (4,096 bins).
 //
 // k_topk_scan reads every score once and classifies it against a cut window
-// [b_lo, b_hi] of 12-bit bins predicted from the previous step's cut bin (one
-// bin either side; the whole key range on a unit's first step): keys above the
-// window go to `above` (only counted once `above` holds K), keys inside it go
-// to `cand` with their key.  k_select then knows how many keys lie above the
-// window and can count the window's bins from the candidates, which decides
-// whether the K-th key fell inside the window.  If it did, the lists are exact
-// (everything above the cut bin is selected; only the cut bin's candidates
-// need the remaining 20 bits); if not, k_select rescans the scores itself.
-// Scores change little between decode steps (the history is the same apart
-// from one appended position), so the window almost always holds and a step
-// reads the history once.
+// [b_lo, b_hi] of top-16-bit key prefixes predicted from the previous step's
+// cut key (its prefix +- 8; the whole key range on a unit's first step, or
+// the bin of a first-step histogram one bin either side): keys above the
+// window and keys inside it are the unit's entries, kept with their key.  Each
+// workgroup owns one segment of consecutive positions and writes the
+// segment's entries in ascending position order to a region of its own
+// (cand[su][segment * seg_len ...]) and its counts to seg[su][segment]
+// (entries, how many of them lie above the window): no atomics and no
+// ordering work is left for k_select, which reads the counts, knows how many
+// keys lie above the window, and whether the K-th key fell inside it.  If it
+// did, the entries are exact (everything above the cut bin is selected; only
+// the cut bin's entries need the remaining 20 bits), and concatenated in
+// segment order they are already in position order; if not, k_select rescans
+// the scores itself.  Scores change little between decode steps (the history
+// is the same apart from one appended position), so the window almost always
+// holds and a step reads the history once.
+//
+// With one query row per round the scan also looks up each entry's slot, so
+// that the select kernel reads it beside the entry instead of making about
+// 3,000 dependent random reads from one workgroup (a workgroup serves about
+// one cache line of a random gather per clock).
 //
 // A context's first step has no previous cut bin.  Rather than classify every
-// key as a candidate (which leaves one k_select workgroup to rank the whole
+// key as an entry (which leaves one k_select workgroup to rank the whole
 // history: 1.4 ms at a million positions), k_cold_hist counts the keys of
 // every 12-bit bin over many workgroups and k_cold_cut places the window on
-// the bin holding the K-th key, so the first step's lists are as small as any
-// other step's.
+// the bin holding the K-th key, so the first step's lists are small too.
 //
-// Grid = (chunks of 2,048 or 4,096 positions) x (selection units: one per query row of
-// each session and group), 256 threads; HBM-bound streaming read of 4 B per
-// position.
+// Grid = (segments) x (selection units: one per query row of each session and
+// group), 256 threads; a segment is `tiles` chunks of 2,048 positions (one
+// chunk unless the history has more than kMaxSegs chunks); a streaming read of
+// 4 B per position, plus one slot-map read per entry.
 #include "hc_internal.h"
 
 namespace hc {
 
 constexpr int kScanThreads = 256;
+constexpr int kScanChunk = 2048;   // positions per scan pass of a workgroup
 
-// Loads this thread's scores of the chunk: element j of the thread is position
-// base + pos[j]; positions >= n are invalid.
-template <bool VEC, int kPerThread>
-__device__ __forceinline__ void load_chunk(const float* src, int n, float (&x)[kPerThread],
-                                           int (&pos)[kPerThread]) {
+// Loads this thread's scores of a chunk: four consecutive positions per group,
+// group j of thread tid at chunk positions 4 * (tid + 256 j) + [0, 4), so that
+// the order (j, thread, element) is the position order.  Invalid positions
+// (>= n) read as 0 and are masked by the caller.
+template <bool VEC, int kGroups>
+__device__ __forceinline__ void load_chunk(const float* src, int n, float (&x)[4 * kGroups]) {
   const int tid = threadIdx.x;
-  if (VEC) {
-    // float4 j of this thread covers chunk positions 4 * (tid + 256 j) + [0, 4).
-    const float4* s4 = reinterpret_cast<const float4*>(src);
 #pragma unroll
-    for (int j = 0; j < kPerThread / 4; ++j) {
-      const int q = tid + kScanThreads * j;
+  for (int j = 0; j < kGroups; ++j) {
+    const int q = tid + kScanThreads * j;
+    if (VEC) {
       float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (4 * q < n) v = s4[q];
+      if (4 * q < n) v = reinterpret_cast<const float4*>(src)[q];
       x[4 * j + 0] = v.x;
       x[4 * j + 1] = v.y;
       x[4 * j + 2] = v.z;
       x[4 * j + 3] = v.w;
+    } else {
 #pragma unroll
-      for (int c = 0; c < 4; ++c) pos[4 * j + c] = 4 * q + c;
-    }
-  } else {
-#pragma unroll
-    for (int j = 0; j < kPerThread; ++j) {
-      const int q = tid + kScanThreads * j;
-      x[j] = q < n ? src[q] : 0.f;
-      pos[j] = q;
+      for (int c = 0; c < 4; ++c) x[4 * j + c] = 4 * q + c < n ? src[4 * q + c] : 0.f;
     }
   }
+}
+
+// Inclusive prefix sums over the 256 threads of the block (thread order) of
+// three values at once, with their block totals.
+__device__ __forceinline__ void block_incl_scan256x3(int (&v)[3], int (&tot)[3], int (*wtot)[4]) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  int x[3];
+#pragma unroll
+  for (int f = 0; f < 3; ++f) {
+    x[f] = wave_incl_scan(v[f]);
+    if (lane == 63) wtot[f][w] = x[f];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int f = 0; f < 3; ++f) {
+    int off = 0, t = 0;
+#pragma unroll
+    for (int i = 0; i < kScanThreads / 64; ++i) {
+      off += i < w ? wtot[f][i] : 0;
+      t += wtot[f][i];
+    }
+    v[f] = x[f] + off;
+    tot[f] = t;
+  }
+  __syncthreads();
 }
 
 // Inclusive prefix sum over the 256 threads of the block (thread order).
@@ -80,72 +109,89 @@ __device__ __forceinline__ int block_incl_scan256(int v, int* wtot) {
   return x + off;
 }
 
-// CHUNK scores per workgroup (2,048 or 4,096), CHUNK / 256 per thread.
+// CHUNK scores per pass (2,048: two groups of four per thread; 4,096 would be
+// four); `tiles` chunks per workgroup (its segment).
 template <bool VEC, int CHUNK>
 __global__ __launch_bounds__(kScanThreads) void k_topk_scan(DevState d, StepArgs a,
                                                             const float* __restrict__ scores,
-                                                            uint64_t stride) {
-  __shared__ int wtot[kScanThreads / 64];
-  __shared__ int off_above, off_cand;
-  const int u = blockIdx.y;  // selection unit (s, g, q)
-  const int64_t H = a.hist_len[u / (d.G * d.Q)];
-  constexpr int kPerThread = CHUNK / kScanThreads;
-  const int64_t base = (int64_t)blockIdx.x * CHUNK;
-  if (base >= H) return;
-  const int n = (int)(H - base < CHUNK ? H - base : CHUNK);
+                                                            uint64_t stride, int tiles) {
+  constexpr int kGroups = CHUNK / (4 * kScanThreads);   // 2 or 4
+  static_assert(kGroups == 2 || kGroups == 4, "chunk of 2,048 or 4,096");
+  __shared__ int wtot[3][kScanThreads / 64];
+  const int su = blockIdx.y;  // selection unit (s, g, q)
+  const int64_t H = a.hist_len[su / (d.G * d.Q)];
+  const int64_t seg_len = (int64_t)CHUNK * tiles;
+  const int64_t seg0 = (int64_t)blockIdx.x * seg_len;
+  if (seg0 >= H) return;
   const int tid = threadIdx.x;
 
-  // predicted cut window from the previous step's cut bin (-1: none yet)
+  // predicted cut window, in top-16-bit key units (none yet: every key)
   uint32_t b_lo, b_hi;
-  cut_window(d.cnt[u * kCntStride + kCntBin1], b_lo, b_hi);
-
-  float x[kPerThread];
-  int pos[kPerThread];
-  load_chunk<VEC, kPerThread>(scores + (uint64_t)u * stride + base, n, x, pos);
-  uint32_t key[kPerThread];
-  int na = 0, nc = 0;
+  cut_window(d.cnt[su * kCntStride + kCntWinLo], d.cnt[su * kCntStride + kCntWinHi], b_lo, b_hi);
+  Ent* out = d.cand + (size_t)su * d.hcap + seg0;
+  // one query row: each entry's slot, looked up here by the many scan
+  // workgroups rather than one per unit later (the step's slot map is that of
+  // the previous step until its select kernel has run)
+  const bool lookup = d.Q == 1;
+  const int32_t* pos2slot = d.pos2slot + (size_t)su * d.hcap;
+  const uint32_t ring_lo = a.ring_lo[su / (d.G * d.Q)];
+  int run = 0, n_above = 0;   // entries of the segment so far, of which above the window
+  for (int tile = 0; tile < tiles; ++tile) {
+    const int64_t base = seg0 + (int64_t)tile * CHUNK;
+    if (base >= H) break;
+    const int n = (int)(H - base < CHUNK ? H - base : CHUNK);
+    float x[4 * kGroups];
+    load_chunk<VEC, kGroups>(scores + (uint64_t)su * stride + base, n, x);
+    uint32_t key[4 * kGroups];
+    uint32_t ent = 0;   // bit 4j + c: element c of group j is an entry
+    int cj[4] = {0, 0, 0, 0}, na = 0;
 #pragma unroll
-  for (int j = 0; j < kPerThread; ++j) {
-    key[j] = order_key(x[j]);
-    const uint32_t b = key[j] >> (32 - kBin1Bits);
-    const bool ok = pos[j] < n;
-    na += ok && b > b_hi;
-    nc += ok && b >= b_lo && b <= b_hi;
-  }
-  // both counts fit 16 bits (at most 4,096 per block): scan them packed
-  const int packed = (na << 16) | nc;
-  const int pincl = block_incl_scan256(packed, wtot);
-  if (tid == kScanThreads - 1) {
-    // one atomic reserves both lists: above count in the low word, candidate
-    // count in the high word (neither total exceeds 2^31, so no carry)
-    static_assert(kCntCand == kCntAbove + 1 && kCntAbove % 2 == 0, "counter pair");
-    const uint64_t add = ((uint64_t)(pincl & 0xFFFF) << 32) | (uint32_t)(pincl >> 16);
-    const uint64_t old = atomicAdd(
-        reinterpret_cast<unsigned long long*>(&d.cnt[u * kCntStride + kCntAbove]),
-        (unsigned long long)add);
-    off_above = (int)(uint32_t)old;
-    off_cand = (int)(old >> 32);
-  }
-  __syncthreads();
-  int ia = off_above + ((pincl - packed) >> 16);
-  int ic = off_cand + ((pincl - packed) & 0xFFFF);
-  int32_t* above = d.above + (size_t)u * d.K;
-  uint2* cand = d.cand + (size_t)u * d.hcap;
+    for (int j = 0; j < kGroups; ++j)
 #pragma unroll
-  for (int j = 0; j < kPerThread; ++j) {
-    if (pos[j] >= n) continue;
-    const uint32_t b = key[j] >> (32 - kBin1Bits);
-    const int32_t p = (int32_t)(base + pos[j]);
-    // a wrong prediction can overfill `above`; k_select then rescans, and the
-    // guards keep the lists in bounds meanwhile
-    if (b > b_hi) {
-      if (ia < d.K) above[ia] = p;
-      ++ia;
-    } else if (b >= b_lo) {
-      if (ic < d.hcap) cand[ic] = make_uint2(key[j], (uint32_t)p);
-      ++ic;
+      for (int c = 0; c < 4; ++c) {
+        const int e = 4 * j + c;
+        key[e] = order_key(x[e]);
+        const uint32_t b = key[e] >> 16;
+        const bool ok = 4 * (tid + kScanThreads * j) + c < n;
+        const bool up = ok && b > b_hi, in = ok && b >= b_lo && b <= b_hi;
+        ent |= (uint32_t)(up || in) << e;
+        cj[j] += up || in;
+        na += up;
+      }
+    // the entries' slots, requested now so that the block scan below runs
+    // while they are in flight
+    int32_t sl[4 * kGroups];
+#pragma unroll
+    for (int e = 0; e < 4 * kGroups; ++e) {
+      const int64_t p = base + 4 * (tid + kScanThreads * (e >> 2)) + (e & 3);
+      sl[e] = lookup && ((ent >> e) & 1u) && (uint64_t)p < (uint64_t)ring_lo ? pos2slot[p] : -1;
     }
+    // group totals are at most 1,024 per chunk: two groups per packed word
+    int v[3] = {cj[0] | (cj[1] << 16), cj[2] | (cj[3] << 16), na};
+    const int own[3] = {v[0], v[1], v[2]};
+    int tot[3];
+    block_incl_scan256x3(v, tot, wtot);
+    const int gtot[4] = {tot[0] & 0xFFFF, tot[0] >> 16, tot[1] & 0xFFFF, tot[1] >> 16};
+    const int gexc[4] = {(v[0] - own[0]) & 0xFFFF, (v[0] - own[0]) >> 16,
+                         (v[1] - own[1]) & 0xFFFF, (v[1] - own[1]) >> 16};
+    int gbase = run;
+#pragma unroll
+    for (int j = 0; j < kGroups; ++j) {
+      int o = gbase + gexc[j];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const int e = 4 * j + c;
+        if ((ent >> e) & 1u) {
+          const int64_t p = base + 4 * (tid + kScanThreads * j) + c;
+          out[o++] = Ent{key[e], (uint32_t)p, sl[e]};
+        }
+      }
+      gbase += gtot[j];
+    }
+    run = gbase;
+    n_above += tot[2];
   }
+  if (tid == 0) d.seg[(size_t)su * d.max_segs + blockIdx.x] = make_int2(run, n_above);
 }
 
 constexpr int kColdChunk = 16384;   // positions per workgroup of the cold histogram
@@ -205,8 +251,12 @@ __global__ __launch_bounds__(kScanThreads) void k_cold_cut(DevState d) {
   if (cum < d.K && incl >= d.K) {
 #pragma unroll
     for (int j = 0; j < kPer; ++j) {
-      if (cum < d.K && cum + c[j] >= d.K)
-        d.cnt[u * kCntStride + kCntBin1] = kBins1 - 1 - (tid * kPer + j);
+      if (cum < d.K && cum + c[j] >= d.K) {
+        // the bin holding the K-th key, one bin either side, in 16-bit units
+        const int b = kBins1 - 1 - (tid * kPer + j);
+        d.cnt[u * kCntStride + kCntWinLo] = b > 0 ? (b - 1) << 4 : 0;
+        d.cnt[u * kCntStride + kCntWinHi] = b < kBins1 - 1 ? ((b + 2) << 4) - 1 : 65535;
+      }
       cum += c[j];
     }
   }
@@ -223,23 +273,27 @@ hipError_t launch_cold_cut(const DevState& d, const StepArgs& a, const float* sc
   return hipGetLastError();
 }
 
+// Segment length of a step whose longest history is max_len: one chunk of
+// 2,048 positions, or several once there would be more segments than
+// max_segs.
+int64_t scan_seg_len(int64_t max_len, int max_segs) {
+  const int64_t chunks = (max_len + kScanChunk - 1) / kScanChunk;
+  const int64_t tiles = (chunks + max_segs - 1) / max_segs;
+  return kScanChunk * (tiles < 1 ? 1 : tiles);
+}
+
 hipError_t launch_topk_scan(const DevState& d, const StepArgs& a, const float* scores,
                             uint64_t stride, int64_t max_len, bool vec4, hipStream_t st) {
-  // Short histories: more, smaller workgroups (the scan is latency-bound);
-  // long ones: fewer, because every workgroup bumps its unit's list counters
-  // (measured: 2,048-score chunks 4.95 vs 6.2 us at 50K positions x 20 units,
-  // but 39 vs 25 us at 1M positions x 16 units).
-  const bool small = max_len <= kScanSmallMax;
-  const int chunk = small ? 2048 : 4096;
-  dim3 grid((unsigned)((max_len + chunk - 1) / chunk), d.S * d.G * d.Q);
-  if (vec4 && small)
-    hipLaunchKernelGGL((k_topk_scan<true, 2048>), grid, dim3(kScanThreads), 0, st, d, a, scores, stride);
-  else if (vec4)
-    hipLaunchKernelGGL((k_topk_scan<true, 4096>), grid, dim3(kScanThreads), 0, st, d, a, scores, stride);
-  else if (small)
-    hipLaunchKernelGGL((k_topk_scan<false, 2048>), grid, dim3(kScanThreads), 0, st, d, a, scores, stride);
+  // 2,048 positions per workgroup: the scan is latency-bound, so more, smaller
+  // workgroups (more of them resident per CU) finish sooner (the 16 x 1M scan:
+  // 24.6 us against 28.5 us in 4,096-position workgroups)
+  const int64_t seg_len = scan_seg_len(max_len, d.max_segs);
+  const int tiles = (int)(seg_len / kScanChunk);
+  dim3 grid((unsigned)((max_len + seg_len - 1) / seg_len), d.S * d.G * d.Q);
+  if (vec4)
+    hipLaunchKernelGGL((k_topk_scan<true, kScanChunk>), grid, dim3(kScanThreads), 0, st, d, a, scores, stride, tiles);
   else
-    hipLaunchKernelGGL((k_topk_scan<false, 4096>), grid, dim3(kScanThreads), 0, st, d, a, scores, stride);
+    hipLaunchKernelGGL((k_topk_scan<false, kScanChunk>), grid, dim3(kScanThreads), 0, st, d, a, scores, stride, tiles);
   return hipGetLastError();
 }
 

@@ -26,7 +26,7 @@ TRACE_HEADER = 4
 NUM_STAGES = 3
 STAGES = ("topk_scan", "select", "gather")
 STATUS = {0: "HC_OK", -1: "HC_E_INVAL", -2: "HC_E_NOMEM", -3: "HC_E_HIP", -4: "HC_E_STATE",
-          -5: "HC_E_CONSISTENCY"}
+          -5: "HC_E_CONSISTENCY", -6: "HC_E_DEVICE"}
 NO_APPEND = (1 << 64) - 1
 
 

@@ -132,8 +132,14 @@ typedef enum {
   HC_E_NOMEM = -2,  /* workspace too small or host allocation failed        */
   HC_E_HIP   = -3,  /* a HIP call failed; the context is now poisoned       */
   HC_E_STATE = -4,  /* the context is poisoned; only hc_destroy is allowed  */
-  HC_E_CONSISTENCY = -5  /* hc_flush: a host row count differs from the
+  HC_E_CONSISTENCY = -5, /* hc_flush: a host row count differs from the
                             logical row count                               */
+  HC_E_DEVICE = -6       /* a kernel found the context's device state
+                            inconsistent (corrupted workspace: counters, slot
+                            maps or LRU queue); the context is now poisoned.
+                            Reported by the first check after the kernel has
+                            completed: hc_step and hc_append at their call,
+                            hc_flush and hc_export_state after their wait    */
 } hc_status;
 
 typedef struct hc_config {
