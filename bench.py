@@ -67,15 +67,11 @@ def traffic_from_profile(kernel_file, workload):
     return float(b.group(1))
 
 
-def run_cpu_baseline(wl, rows, n_steps, threads=0):
-    """The oracle as it stands, on the first n_steps of the workload; the rate
-    is taken over steps 1..n_steps-1 (step 0 is the cold fill).  threads = 0:
-    one per selection group, at most 16 (the machine's CPU share)."""
+def time_oracle(wl, rows, n_steps, threads):
+    """Seconds per step of the oracle on the first n_steps of the workload."""
     import numpy as np
     import oracle
     from cache_gather_amd import workload as W
-    if threads <= 0:
-        threads = max(1, min(16, os.cpu_count() or 1, wl.n_units))
     model = oracle.Model(wl.n_sessions, wl.n_layers, wl.layers_per_select, wl.top_k,
                          wl.cache_slots, wl.hcap, rows)
     sc = W.Scores(wl)
@@ -86,11 +82,23 @@ def run_cpu_baseline(wl, rows, n_steps, threads=0):
         model.step(t, list(s), wl.hist_len(t).astype(np.int64), gather=True, info=False,
                    nthreads=threads)
         times.append(time.perf_counter() - t0)
-        log("cpu baseline: step %d took %.2f s" % (t, times[-1]))
+        log("cpu baseline (%d thread%s): step %d took %.2f s" % (
+            threads, "" if threads == 1 else "s", t, times[-1]))
     model.close()
+    return times
+
+
+def run_cpu_baseline(wl, rows, n_steps, threads=0, single_steps=3):
+    """The oracle as it stands, on the first n_steps of the workload with
+    `threads` threads (0: one per selection group, at most 16, the machine's CPU
+    share), and on the first single_steps steps with one thread; each rate is
+    taken over the steps after step 0 (the cold fill)."""
+    if threads <= 0:
+        threads = max(1, min(16, os.cpu_count() or 1, wl.n_units))
     rows_per_step = wl.n_sessions * wl.n_layers * wl.top_k
+    times = time_oracle(wl, rows, n_steps, threads)
     warm = times[1:] if len(times) > 1 else times
-    return {
+    res = {
         "value": rows_per_step * len(warm) / sum(warm),
         "unit": "rows/s",
         "cores": threads,
@@ -98,7 +106,17 @@ def run_cpu_baseline(wl, rows, n_steps, threads=0):
         "sample": "first %d decode steps of %s on %d threads (at most one per selection "
                   "group); rate over steps 1-%d, cold step 0 took %.2f s" % (
                       n_steps, wl.name, threads, n_steps - 1, times[0]),
+        "nproc": os.cpu_count(),
+        "cpu_model": cpu_model(),
     }
+    if single_steps > 1 and threads != 1:
+        t1 = time_oracle(wl, rows, single_steps, 1)
+        res["single_thread"] = {
+            "value": rows_per_step * (len(t1) - 1) / sum(t1[1:]),
+            "unit": "rows/s", "cores": 1,
+            "sample": "first %d decode steps on one thread; rate over steps 1-%d, cold step 0 "
+                      "took %.2f s" % (single_steps, single_steps - 1, t1[0])}
+    return res
 
 
 def cpu_model():
@@ -215,6 +233,8 @@ def main():
     ap.add_argument("--cpu-threads", type=int, default=0,
                     help="threads of the CPU oracle baseline (0: one per selection group, "
                          "at most 16)")
+    ap.add_argument("--cpu-single-steps", type=int, default=3,
+                    help="steps of the one-thread oracle leg of the CPU baseline (0: none)")
     ap.add_argument("--cpu-only", action="store_true",
                     help="time only the CPU oracle baseline on --workload (first --cpu-steps "
                          "steps, --cpu-threads threads); no GPU work")
@@ -254,7 +274,7 @@ def main():
         t0 = time.time()
         rows = W.fill_all_rows(wl)
         log("host rows generated in %.1fs" % (time.time() - t0))
-        res = run_cpu_baseline(wl, rows, args.cpu_steps, args.cpu_threads)
+        res = run_cpu_baseline(wl, rows, args.cpu_steps, args.cpu_threads, args.cpu_single_steps)
         print(json.dumps({"metric": "oracle rows/s (CPU)", "workload": wl.name,
                           "cpu_baseline": res, "ms_per_step": round(
                               wl.n_sessions * wl.n_layers * wl.top_k / res["value"] * 1e3, 2),
@@ -319,9 +339,11 @@ def main():
 
     def run_pass(kernel_events, variant=None):
         """A fresh context over the same inputs: cold step, warmup, then the
-        timed steps.  With kernel_events, HIP events bracket every kernel of the
-        timed steps on the step's stream (they add a few us per kernel, so the
-        pass that produces `value` runs without them)."""
+        timed steps.  With kernel_events, each stage of the timed steps carries
+        a pair of HIP events attached to its first and last dispatch (the
+        kernels' own begin and end), and every step writes its trace (a
+        debugging output of the ABI, from which the miss counts come); the pass
+        that produces `value` has neither."""
         cache = hc.HotCache(S, L, wl.layers_per_select, wl.cache_slots, K, wl.hcap, 0,
                             ring_rows=args.ring,
                             copyback_rows=args.copyback_rows if args.ring else 0, queries=Q)
@@ -334,7 +356,8 @@ def main():
                 else:
                     np.copyto(h, rows[s][l])
         out, sel, _ = cache.alloc_outputs()
-        trace = torch.empty((total, U, hc.trace_ints(Q * K)), dtype=torch.int32, device=dev)
+        trace = (torch.empty((total, U, hc.trace_ints(Q * K)), dtype=torch.int32, device=dev)
+                 if kernel_events else None)
         append_ev = ([(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                       for _ in range(total)] if args.ring and kernel_events else None)
 
@@ -342,12 +365,13 @@ def main():
             work, att_out = cache.attention_buffers(att["heads"])
 
         def step(t):
+            tr = trace[t] if trace is not None else None
             if variant == "fused":
-                cache.step(d_scores[t], stride, wl.hist_len(t), None, sel, trace[t])
+                cache.step(d_scores[t], stride, wl.hist_len(t), None, sel, tr)
                 cache.attend_cached(att["q"][t], att["heads"], att["scale"], work, att_out)
                 return
             if variant == "buffer":
-                cache.step(d_scores[t], stride, wl.hist_len(t), out, sel, trace[t])
+                cache.step(d_scores[t], stride, wl.hist_len(t), out, sel, tr)
                 cache.attend(att["q"][t], att["heads"], att["scale"], out, work, att_out)
                 return
             if args.ring:
@@ -357,7 +381,7 @@ def main():
                 cache.append(d_new[t], [first + t] * S)
                 if timed_append:
                     append_ev[t][1].record()
-            cache.step(d_scores[t], stride, wl.hist_len(t), out, sel, trace[t])
+            cache.step(d_scores[t], stride, wl.hist_len(t), out, sel, tr)
 
         # cold step (every row misses), then the rest of the warmup
         hc.hc_profile_enable(cache.ctx, 1)
@@ -378,7 +402,8 @@ def main():
         torch.cuda.synchronize()
         elapsed = time.perf_counter() - t0
         res = {"elapsed": elapsed, "cold_ms": cold_ms, "cold_stage_ms": cold_stage_ms,
-               "trace": trace.cpu().numpy()}
+               "trace": trace.cpu().numpy() if trace is not None else None,
+               "last_out": out, "last_sel": sel}
         if args.ring:
             f0 = time.perf_counter()
             status, counts = cache.flush()
@@ -395,7 +420,7 @@ def main():
             res["gather_us"] = per_step[:, list(hc.STAGES).index("gather")] * 1e3
             res["elapsed_with_events"] = elapsed
         cache.close()
-        del out, sel, trace
+        del trace
         return res
 
     if att:
@@ -422,15 +447,18 @@ def main():
     cold_ms, cold_stage_ms = timed["cold_ms"], timed["cold_stage_ms"]
     stage_avg = kernels_pass["stage_avg"]
     step_kernel_us = kernels_pass["step_kernel_us"]
-    if not np.array_equal(timed["trace"], kernels_pass["trace"]):
+    # both passes ran the same steps on fresh contexts: same last selection and output
+    if not (torch.equal(timed["last_sel"], kernels_pass["last_sel"])
+            and torch.equal(timed["last_out"], kernels_pass["last_out"])):
         raise SystemExit("the two passes disagree")
+    del timed["last_out"], kernels_pass["last_out"]
 
     ms_per_step = elapsed * 1e3 / args.steps
     rows_per_step = S * L * Q * K       # every query row's K rows of every layer
     value = rows_per_step / (ms_per_step / 1e3)
 
     # misses per step from the trace (n_miss of each unit x layers of its group)
-    tr = timed["trace"]
+    tr = kernels_pass["trace"]
     layers_of_group = np.array([min(wl.layers_per_select, L - g * wl.layers_per_select)
                                 for g in range(wl.n_groups)] * S)
     miss_rows = (tr[:, :, 1] * layers_of_group[None, :]).sum(axis=1)   # per step
@@ -504,6 +532,8 @@ def main():
         "gather_regimes": regimes,
         "stage_us": {k: round(v * 1e3, 2) for k, v in stage_avg.items()},
         "kernel_sum_us": round(sum(stage_avg.values()) * 1e3, 2),
+        "kernel_timing": "HIP events attached to each stage's first and last kernel dispatch "
+                         "(hipExtLaunchKernel) in a second pass over the same steps",
         "ms_per_step_with_kernel_events": round(
             kernels_pass["elapsed_with_events"] * 1e3 / args.steps, 5),
         "gather_hbm_gbs": roofline("gather")["achieved"],
@@ -557,7 +587,8 @@ def main():
         log("cpu baseline: timed only for the single-query step without a ring")
     elif not args.no_cpu_baseline:
         log("cpu baseline: oracle on the first %d steps ..." % args.cpu_steps)
-        result["cpu_baseline"] = run_cpu_baseline(wl, rows, args.cpu_steps, args.cpu_threads)
+        result["cpu_baseline"] = run_cpu_baseline(wl, rows, args.cpu_steps, args.cpu_threads,
+                                                  args.cpu_single_steps)
     print(json.dumps(result), flush=True)
 
 

@@ -12,6 +12,7 @@
 // page "Making KV offload correct", sections "A grouped allocation is a
 // transaction" and "Response completion is not copy completion").
 #include <algorithm>
+#include <atomic>
 #include <cstddef>
 #include <cstring>
 #include <mutex>
@@ -19,6 +20,9 @@
 #include <vector>
 
 #include "hc_internal.h"
+#ifdef HC_TEST_HOOKS
+#include "hc_test.h"
+#endif
 
 using namespace hc;
 
@@ -125,6 +129,9 @@ struct DeviceGuard {
   explicit DeviceGuard(int dev) {
     if (hipGetDevice(&prev) != hipSuccess) prev = -1;
     ok = hipSetDevice(dev) == hipSuccess;
+    // the launchers read hipGetLastError(): leave no error of this call (or of
+    // the caller's earlier HIP calls) behind for them to take as their own
+    (void)hipGetLastError();
   }
   ~DeviceGuard() {
     if (prev >= 0) (void)hipSetDevice(prev);
@@ -208,22 +215,62 @@ struct hc_ctx {
   uint32_t* err_dev = nullptr;
   bool poisoned = false;
   bool enqueued = false;
-  hipEvent_t done = nullptr;         // recorded after every step
-  // profiling: HC_NUM_STAGES + 1 events per step, bracketing the kernels
+  bool appended_since_step = false;  // an hc_append after the last hc_step
+  hipStream_t last_stream = nullptr; // stream of the last enqueued work
+  hipEvent_t done = nullptr;         // recorded after all enqueued work
+#ifdef HC_TEST_HOOKS
+  bool test_fail_launch = false;     // the next hc_step fails before its first launch
+  bool test_poison = false;          // sentinel over victim slots before each gather
+#endif
+  // profiling: a (start, stop) event pair per stage and step, attached to the
+  // stage's first and last kernel dispatch
   std::vector<hipEvent_t> prof;
   uint32_t prof_cap = 0, prof_used = 0;
 };
 
 namespace {
 
+// Pinned host memory the library holds (all contexts), for the tests of
+// all-or-nothing creation.
+std::atomic<uint64_t> g_pinned_bytes{0};
+#ifdef HC_TEST_HOOKS
+std::atomic<int64_t> g_fail_pinned{-1};   // pinned allocations to grant before one fails
+#endif
+
+// Mapped pinned host memory of `bytes`, or nullptr.
+void* pinned_alloc(uint64_t bytes) {
+#ifdef HC_TEST_HOOKS
+  if (g_fail_pinned.load() >= 0 && g_fail_pinned.fetch_sub(1) == 0) return nullptr;
+#endif
+  void* p = nullptr;
+  if (hipHostMalloc(&p, bytes, hipHostMallocMapped) != hipSuccess || !p) return nullptr;
+  g_pinned_bytes += bytes;
+  return p;
+}
+
+void pinned_free(void* p, uint64_t bytes) {
+  if (!p) return;
+  (void)hipHostFree(p);
+  g_pinned_bytes -= bytes;
+}
+
 void free_host(hc_ctx* c) {
-  for (uint8_t* p : c->host_rows)
-    if (p) (void)hipHostFree(p);
+  const uint64_t row_bytes = c->cfg.max_positions * (uint64_t)kRow;
+  for (uint8_t* p : c->host_rows) pinned_free(p, row_bytes);
   c->host_rows.clear();
-  if (c->host_count) (void)hipHostFree(c->host_count);
+  pinned_free(c->host_count, c->cfg.n_sessions * sizeof(uint64_t));
   c->host_count = c->host_count_dev = nullptr;
-  if (c->err) (void)hipHostFree(c->err);
+  pinned_free(c->err, kErrKinds * sizeof(uint32_t));
   c->err = c->err_dev = nullptr;
+}
+
+// Orders work enqueued on `st` after everything the context enqueued on
+// another stream before (entry points may be called on different streams).
+hipError_t order_after_last(hc_ctx* c, hipStream_t st) {
+  hipError_t e = hipSuccess;
+  if (c->enqueued && st != c->last_stream) e = hipStreamWaitEvent(st, c->done, 0);
+  c->last_stream = st;
+  return e;
 }
 
 void free_prof(hc_ctx* c) {
@@ -311,8 +358,8 @@ hc_status hc_create(const hc_config* cfg_in, void* dev_workspace, uint64_t ws_by
   c->host_rows.assign(S * (size_t)L, nullptr);
   hc_status st = HC_OK;
   for (size_t i = 0; i < c->host_rows.size() && st == HC_OK; ++i) {
-    void* p = nullptr;
-    if (hipHostMalloc(&p, row_bytes, hipHostMallocMapped) != hipSuccess || !p) {
+    void* p = pinned_alloc(row_bytes);
+    if (!p) {
       st = HC_E_NOMEM;
       break;
     }
@@ -322,8 +369,8 @@ hc_status hc_create(const hc_config* cfg_in, void* dev_workspace, uint64_t ws_by
     dev_ptrs[i] = static_cast<const uint8_t*>(dp);
   }
   if (st == HC_OK && cfg->ring_rows) {
-    void* p = nullptr;
-    if (hipHostMalloc(&p, S * sizeof(uint64_t), hipHostMallocMapped) != hipSuccess || !p) {
+    void* p = pinned_alloc(S * sizeof(uint64_t));
+    if (!p) {
       st = HC_E_NOMEM;
     } else {
       c->host_count = static_cast<uint64_t*>(p);
@@ -334,8 +381,8 @@ hc_status hc_create(const hc_config* cfg_in, void* dev_workspace, uint64_t ws_by
     }
   }
   if (st == HC_OK) {
-    void* p = nullptr;
-    if (hipHostMalloc(&p, kErrKinds * sizeof(uint32_t), hipHostMallocMapped) != hipSuccess || !p) {
+    void* p = pinned_alloc(kErrKinds * sizeof(uint32_t));
+    if (!p) {
       st = HC_E_NOMEM;
     } else {
       c->err = static_cast<uint32_t*>(p);
@@ -438,26 +485,46 @@ hc_status hc_step(hc_ctx* c, void* stream, const float* d_scores, uint64_t score
       (reinterpret_cast<uintptr_t>(d_scores) % 16 == 0) && (score_stride % 4 == 0);
 
   const bool prof = c->prof_used < c->prof_cap;
-  hipEvent_t* ev = prof ? &c->prof[(size_t)c->prof_used * (HC_NUM_STAGES + 1)] : nullptr;
-  auto mark = [&](int i) { return prof ? hipEventRecord(ev[i], st) : hipSuccess; };
+  StageEv ev[HC_NUM_STAGES];
+  if (prof)
+    for (int i = 0; i < HC_NUM_STAGES; ++i) {
+      ev[i].start = c->prof[((size_t)c->prof_used * HC_NUM_STAGES + i) * 2];
+      ev[i].stop = c->prof[((size_t)c->prof_used * HC_NUM_STAGES + i) * 2 + 1];
+    }
+  const StageEv ev_scan = ev[HC_STAGE_TOPK_SCAN], ev_sel = ev[HC_STAGE_SELECT];
+  DevState d = c->dev;
 
-  hipError_t e = mark(0);
-  if (e == hipSuccess && c->t == 0 && c->dev.hcap >= kColdMinPositions)
-    e = launch_cold_cut(c->dev, a, d_scores, score_stride, (int64_t)max_len, st);
-  if (e == hipSuccess) e = launch_topk_scan(c->dev, a, d_scores, score_stride, (int64_t)max_len, vec4, st);
-  if (e == hipSuccess) e = mark(1);
+  hipError_t e = order_after_last(c, st);
+#ifdef HC_TEST_HOOKS
+  if (c->test_fail_launch && e == hipSuccess) e = hipErrorLaunchFailure;   // as if a launch failed
+  c->test_fail_launch = false;
+#endif
+  const bool cold = c->t == 0 && d.hcap >= kColdMinPositions;
+  if (cold && e == hipSuccess)
+    e = launch_cold_cut(d, a, d_scores, score_stride, (int64_t)max_len, st,
+                        StageEv{ev_scan.start, nullptr});
   if (e == hipSuccess)
-    e = launch_select(c->dev, a, d_scores, score_stride, (int64_t)max_len, d_sel, d_trace, st);
-  if (e == hipSuccess && c->dev.Q > 1) e = launch_round(c->dev, a, d_sel, d_trace, st);
-  if (e == hipSuccess) e = mark(2);
-  if (e == hipSuccess) e = launch_gather(c->dev, d_out, a.t, st);
-  if (e == hipSuccess) e = mark(3);
+    e = launch_topk_scan(d, a, d_scores, score_stride, (int64_t)max_len, vec4, st,
+                         StageEv{cold ? nullptr : ev_scan.start, ev_scan.stop});
+  if (e == hipSuccess)
+    e = launch_select(d, a, d_scores, score_stride, (int64_t)max_len, d_sel, d_trace, st,
+                      StageEv{ev_sel.start, d.Q > 1 ? nullptr : ev_sel.stop});
+  if (e == hipSuccess && d.Q > 1)
+    e = launch_round(d, a, d_sel, d_trace, st, StageEv{nullptr, ev_sel.stop});
+#ifdef HC_TEST_HOOKS
+  if (e == hipSuccess && c->test_poison) e = launch_poison(d, st);
+#endif
+  if (e == hipSuccess) e = launch_gather(d, d_out, a.t, st, ev[HC_STAGE_GATHER]);
   if (e == hipSuccess) e = hipEventRecord(c->done, st);
   c->enqueued = true;
+#ifdef HC_TEST_HOOKS
+  c->dev.test_force = 0;   // a forced report concerns one step
+#endif
   if (e != hipSuccess) return fail_hip(c);
   if (prof) ++c->prof_used;
   for (uint32_t s = 0; s < S; ++s) c->last_len[s] = hist_len[s];
   ++c->t;
+  c->appended_since_step = false;
   return HC_OK;
 }
 
@@ -482,8 +549,10 @@ hc_status hc_append(hc_ctx* c, void* stream, const uint8_t* d_rows, const uint64
   hipStream_t st = static_cast<hipStream_t>(stream);
   // the entry being overwritten left the ring copyback_rows <= ring_rows
   // appends ago, so its copyback is already enqueued ahead of this launch
-  hipError_t e = launch_append(c->dev, a, d_rows, st);
+  hipError_t e = order_after_last(c, st);
+  if (e == hipSuccess) e = launch_append(c->dev, a, d_rows, st);
   c->enqueued = true;
+  c->appended_since_step = true;
   if (e == hipSuccess) {
     for (uint32_t s = 0; s < S; ++s) {
       if (pos[s] == HC_NO_APPEND) continue;
@@ -505,7 +574,8 @@ hc_status hc_flush(hc_ctx* c, void* stream, uint64_t* host_count) {
   hipStream_t st = static_cast<hipStream_t>(stream);
   const uint32_t S = c->cfg.n_sessions;
   if (c->cfg.ring_rows) {
-    hipError_t e = copy_back(c, st, 1);
+    hipError_t e = order_after_last(c, st);
+    if (e == hipSuccess) e = copy_back(c, st, 1);
     if (e == hipSuccess) e = hipEventRecord(c->done, st);
     c->enqueued = true;
     if (e != hipSuccess) return fail_hip(c);
@@ -543,10 +613,15 @@ hc_status attend(hc_ctx* c, void* stream, bool from_slots, const uint16_t* d_q, 
     return HC_E_INVAL;
   if (work_bytes < attend_work_bytes(c->dev, (int)heads)) return HC_E_NOMEM;
   if (c->t == 0) return HC_E_INVAL;   // no step has selected rows yet
+  // an append since the last step may have overwritten a ring entry that step
+  // selected: the ring no longer holds the step's rows
+  if (from_slots && c->cfg.ring_rows && c->appended_since_step) return HC_E_INVAL;
   DeviceGuard dg(c->cfg.device);
   if (!dg.ok) return HC_E_INVAL;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  hipError_t e = launch_attend(c->dev, from_slots, d_q, (int)heads, scale, d_rows, d_work, d_out, st);
+  hipError_t e = order_after_last(c, st);
+  if (e == hipSuccess)
+    e = launch_attend(c->dev, from_slots, d_q, (int)heads, scale, d_rows, d_work, d_out, st);
   if (e == hipSuccess) e = hipEventRecord(c->done, st);
   c->enqueued = true;
   return e == hipSuccess ? HC_OK : fail_hip(c);
@@ -607,7 +682,7 @@ hc_status hc_profile_enable(hc_ctx* c, uint32_t max_steps) {
   if (c->enqueued && hipEventSynchronize(c->done) != hipSuccess) return fail_hip(c);
   free_prof(c);
   if (max_steps == 0) return HC_OK;
-  c->prof.assign((size_t)max_steps * (HC_NUM_STAGES + 1), nullptr);
+  c->prof.assign((size_t)max_steps * HC_NUM_STAGES * 2, nullptr);
   for (hipEvent_t& e : c->prof) {
     if (hipEventCreate(&e) != hipSuccess) {
       free_prof(c);
@@ -626,11 +701,11 @@ hc_status hc_profile_read(hc_ctx* c, double* stage_ms, double* per_step, uint64_
   if (!dg.ok) return HC_E_INVAL;
   for (int i = 0; i < HC_NUM_STAGES; ++i) stage_ms[i] = 0.0;
   for (uint32_t k = 0; k < c->prof_used; ++k) {
-    hipEvent_t* ev = &c->prof[(size_t)k * (HC_NUM_STAGES + 1)];
-    if (hipEventSynchronize(ev[HC_NUM_STAGES]) != hipSuccess) return fail_hip(c);
+    hipEvent_t* ev = &c->prof[(size_t)k * HC_NUM_STAGES * 2];
+    if (hipEventSynchronize(ev[HC_NUM_STAGES * 2 - 1]) != hipSuccess) return fail_hip(c);
     for (int i = 0; i < HC_NUM_STAGES; ++i) {
       float ms = 0.f;
-      if (hipEventElapsedTime(&ms, ev[i], ev[i + 1]) != hipSuccess) return fail_hip(c);
+      if (hipEventElapsedTime(&ms, ev[2 * i], ev[2 * i + 1]) != hipSuccess) return fail_hip(c);
       stage_ms[i] += ms;
       if (per_step && k < per_step_cap) per_step[(size_t)k * HC_NUM_STAGES + i] = ms;
     }
@@ -658,6 +733,50 @@ hc_status hc_destroy(hc_ctx* c) {
   delete c;
   return st;
 }
+
+#ifdef HC_TEST_HOOKS
+hc_status hc_test_hook(hc_ctx* c, int kind, int64_t arg, uint64_t* out) {
+  switch (kind) {
+    case HC_TEST_FAIL_LAUNCH:
+      if (!c) return HC_E_INVAL;
+      c->test_fail_launch = true;
+      return HC_OK;
+    case HC_TEST_FORCE_SELECT:
+      if (!c) return HC_E_INVAL;
+      c->dev.test_force = 1;
+      return HC_OK;
+    case HC_TEST_CORRUPT_LRU: {
+      if (!c) return HC_E_INVAL;
+      DeviceGuard dg(c->cfg.device);
+      if (c->enqueued && hipEventSynchronize(c->done) != hipSuccess) return fail_hip(c);
+      // every slot claimed used, an empty queue: the next step that misses
+      // finds no victim
+      const size_t U = (size_t)c->dev.S * c->dev.G;
+      for (size_t u = 0; u < U; ++u) {
+        int32_t* line = c->dev.cnt + u * c->dev.Q * kCntStride;
+        const int32_t zero = 0, full = c->dev.C;
+        if (hipMemcpy(line + kCntQHead, &zero, 4, hipMemcpyHostToDevice) != hipSuccess ||
+            hipMemcpy(line + kCntQTail, &zero, 4, hipMemcpyHostToDevice) != hipSuccess ||
+            hipMemcpy(line + kCntFill, &full, 4, hipMemcpyHostToDevice) != hipSuccess)
+          return fail_hip(c);
+      }
+      return HC_OK;
+    }
+    case HC_TEST_POISON_VICTIMS:
+      if (!c) return HC_E_INVAL;
+      c->test_poison = arg != 0;
+      return HC_OK;
+    case HC_TEST_FAIL_PINNED:
+      g_fail_pinned = arg;
+      return HC_OK;
+    case HC_TEST_PINNED_BYTES:
+      if (!out) return HC_E_INVAL;
+      *out = g_pinned_bytes.load();
+      return HC_OK;
+  }
+  return HC_E_INVAL;
+}
+#endif
 
 const char* hc_status_str(hc_status s) {
   switch (s) {

@@ -2,6 +2,7 @@
 // gfx950 kernels of the hot-cache decode step.  Not part of the public ABI.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -84,6 +85,9 @@ struct DevState {
   int32_t ring_rows;   // 0: no ring
   int32_t policy;      // HC_REPLACE_LRU, HC_REPLACE_CIRCULAR or HC_REPLACE_CLOCK
   uint32_t* refbits;   // [U][ceil(C / 32)] clock reference bits
+#ifdef HC_TEST_HOOKS
+  int32_t test_force;  // test build only: the select kernels report an inconsistent state
+#endif
 };
 
 struct StepArgs {
@@ -205,30 +209,44 @@ __device__ __forceinline__ void report_error(const DevState& d, int kind) {
   d.err[kind] = 1u;
 }
 
+// Timing of a stage's kernels: `start` is attached to the stage's first
+// dispatch and `stop` to its last (hipExtLaunchKernel records them when the
+// kernel itself begins and ends, so no separate event sits between kernels);
+// null events: an ordinary launch.
+struct StageEv {
+  hipEvent_t start = nullptr, stop = nullptr;
+};
+
 // Launchers (each defined next to its kernel).  All return hipGetLastError().
 hipError_t launch_init(const DevState& d, hipStream_t st);
 // Positions per score-scan segment for a step whose longest history is max_len
 // (the scan and the select kernel must use the same).
 int64_t scan_seg_len(int64_t max_len, int max_segs);
 hipError_t launch_topk_scan(const DevState& d, const StepArgs& a, const float* scores,
-                            uint64_t stride, int64_t max_len, bool vec4, hipStream_t st);
+                            uint64_t stride, int64_t max_len, bool vec4, hipStream_t st,
+                            StageEv ev = {});
 // First step only (needs hcap >= kColdMinPositions): sets every selection
 // unit's cut bin from a histogram of its scores.
 constexpr int64_t kColdMinPositions = 2048;   // the histogram borrows 16 KB of `cand`
 hipError_t launch_cold_cut(const DevState& d, const StepArgs& a, const float* scores,
-                           uint64_t stride, int64_t max_len, hipStream_t st);
+                           uint64_t stride, int64_t max_len, hipStream_t st, StageEv ev = {});
 // Q == 1: the fused per-unit selection + cache kernel.  Q > 1: the top-K part
 // per selection unit, then launch_round per unit.
 hipError_t launch_select(const DevState& d, const StepArgs& a, const float* scores,
                          uint64_t stride, int64_t max_len, int32_t* d_sel, int32_t* d_trace,
-                         hipStream_t st);
+                         hipStream_t st, StageEv ev = {});
 hipError_t launch_round(const DevState& d, const StepArgs& a, const int32_t* d_sel,
-                        int32_t* d_trace, hipStream_t st);
+                        int32_t* d_trace, hipStream_t st, StageEv ev = {});
 // d_out == nullptr: only the missing rows are fetched into their slots.  With
 // one query row the launch also carries one bookkeeping workgroup per unit:
 // last-use stamps, the (miss, victim) pairs applied to the slot maps, and the
 // LRU queue's new entries for step t.
-hipError_t launch_gather(const DevState& d, uint16_t* d_out, int32_t t, hipStream_t st);
+hipError_t launch_gather(const DevState& d, uint16_t* d_out, int32_t t, hipStream_t st,
+                         StageEv ev = {});
+#ifdef HC_TEST_HOOKS
+// Test build: a sentinel over every victim slot before the gather fills it.
+hipError_t launch_poison(const DevState& d, hipStream_t st);
+#endif
 hipError_t launch_append(const DevState& d, const AppendArgs& a, const uint8_t* d_rows,
                          hipStream_t st);
 // Attention over the last step's selection: rows from the gathered bf16

@@ -10,11 +10,7 @@
 // read host RAM.
 //
 // One launch, three kinds of workgroup:
-//   * with one query row per round, one bookkeeping workgroup per unit, first:
-//     the select kernel only decides, and these write its decisions into the
-//     unit's state (last-use stamps, slot maps, LRU queue) for the next step,
-//     while the rest of the launch streams rows;
-//   * the next workgroups walk the dense miss list (every layer
+//   * the first workgroups walk the dense miss list (every layer
 //     of every unit): each missing row is read from pinned host RAM over PCIe
 //     (zero-copy), written into its victim slot, and dequantised from the same
 //     registers — so its slot is only ever read in later steps, and all PCIe
@@ -24,7 +20,11 @@
 //     skipped; the miss workgroups write them).  In a multi-query round a
 //     position several queries missed is filled by its first query's row; the
 //     other queries' rows of it read host RAM directly (the page's rule for
-//     duplicate misses), never the slot being filled.
+//     duplicate misses), never the slot being filled;
+//   * between them, with one query row per round, one bookkeeping workgroup
+//     per unit: the select kernel only decides, and these write its decisions
+//     into the unit's state (last-use stamps, slot maps, LRU queue) for the
+//     next step while the rest of the launch streams rows.
 // The PCIe transfer of the few missing rows thus overlaps the HBM stream of
 // the many hits.
 //
@@ -39,10 +39,10 @@
 // rows' loads in flight before the first store (16 rows per workgroup:
 // measured on MI355X with the caches flushed, 3-4% faster than one row per
 // thread, and 4 rows slower again); a miss workgroup keeps one row per thread
-// in flight (two slowed the PCIe reads).  After the bookkeeping rows, grid
-// rows [0, miss_rows) are the miss workgroups, dispatched first; grid row
-// miss_rows + sl holds layer sl's hit rows, so no per-row index division is
-// needed (with Q query rows, grid row miss_rows + sl * Q + q).  HBM-bound:
+// in flight (two slowed the PCIe reads).  Grid rows [0, miss_rows) are the
+// miss workgroups, dispatched first; after the bookkeeping rows, grid row
+// miss_rows + bk_rows + sl holds layer sl's hit rows, so no per-row index
+// division is needed (with Q query rows, layer sl's query q).  HBM-bound:
 // 656 B read (hit) or written (miss) + 1,152 B written per
 // selected row; PCIe: 656 B per missing row.  bf16 rounding by
 // v_cvt_pk_bf16_f32.
@@ -337,12 +337,12 @@ __global__ __launch_bounds__(kGatherThreads) void k_gather(DevState d,
   uint8_t* const out_b = reinterpret_cast<uint8_t*>(out);
   const size_t out_row_bytes = (size_t)kOut * 2;
 
-  if ((int)blockIdx.y < bk_rows) {
-    const int b = blockIdx.y * gridDim.x + blockIdx.x;
+  if ((int)blockIdx.y >= miss_rows && (int)blockIdx.y < miss_rows + bk_rows) {
+    const int b = (blockIdx.y - miss_rows) * gridDim.x + blockIdx.x;
     if (b < d.S * d.G) bookkeeping(d, b, t, reinterpret_cast<uint32_t*>(pref), wsum);
     return;
   }
-  const int row = (int)blockIdx.y - bk_rows;
+  const int row = (int)blockIdx.y < miss_rows ? (int)blockIdx.y : (int)blockIdx.y - bk_rows;
   if (row < miss_rows) {
     RowJob<1> j;
     const int mb = row * gridDim.x + blockIdx.x;  // miss workgroup number
@@ -427,11 +427,38 @@ __global__ __launch_bounds__(kGatherThreads) void k_gather(DevState d,
   run_rows(j, item);
 }
 
-hipError_t launch_gather(const DevState& d, uint16_t* d_out, int32_t t, hipStream_t st) {
-  // grid rows [0, bk_rows): one bookkeeping workgroup per unit (one query row
-  // per round; k_round does its own), dispatched first; then rows
-  // [0, miss_rows) of the miss workgroups; then row miss_rows + sl: the hit
-  // rows of layer sl
+#ifdef HC_TEST_HOOKS
+// Test build: writes a sentinel over every victim slot of every layer before
+// the gather fills it, so that a read of a slot being filled in the same
+// launch (a read before the fill) would carry the sentinel into the output.
+__global__ __launch_bounds__(64) void k_poison(DevState d) {
+  const int QK = d.Q * d.K;
+  const int64_t n = (int64_t)d.S * d.G * QK * d.R;
+  for (int64_t i = blockIdx.x; i < n; i += gridDim.x) {
+    const int u = (int)(i / ((int64_t)QK * d.R));
+    const int r = (int)(i - (int64_t)u * QK * d.R);
+    const int k = r / d.R, lig = r - k * d.R;
+    const int g = u % d.G, s = u / d.G;
+    if (k >= d.cnt[(size_t)u * d.Q * kCntStride + kCntMiss] || lig >= layers_in_group(d, g)) continue;
+    const int v = d.victim[(size_t)u * QK + k];
+    if (v < 0 || v >= d.C) continue;
+    uint8_t* slot = d.hot + ((size_t)(s * d.L + g * d.R + lig) * d.C + v) * kSlotStride;
+    for (int j = threadIdx.x; j < kRow; j += blockDim.x) slot[j] = 0xA5;
+  }
+}
+
+hipError_t launch_poison(const DevState& d, hipStream_t st) {
+  hipLaunchKernelGGL(k_poison, dim3(4096), dim3(64), 0, st, d);
+  return hipGetLastError();
+}
+#endif
+
+hipError_t launch_gather(const DevState& d, uint16_t* d_out, int32_t t, hipStream_t st,
+                         StageEv ev) {
+  // grid rows [0, miss_rows): the miss workgroups, dispatched first (their
+  // PCIe reads have the longest latency); then bk_rows rows holding one
+  // bookkeeping workgroup per unit (one query row per round; k_round does its
+  // own); then row miss_rows + bk_rows + sl: the hit rows of layer sl
   const int gx = (d.K + kRowsPerRound - 1) / kRowsPerRound;
   const int units = d.S * d.G;
   const int bk_rows = d.Q == 1 ? (units + gx - 1) / gx : 0;
@@ -444,9 +471,9 @@ hipError_t launch_gather(const DevState& d, uint16_t* d_out, int32_t t, hipStrea
   const int64_t rows_total = (int64_t)d.S * d.L * d.Q * d.K;
   const int few_hits_above = (int)(rows_total - kFewHitRows);
   // grid rows stay below 2^16, as div_by requires: S * L * Q <= 60,000 is checked at creation
-  hipLaunchKernelGGL(k_gather, dim3(gx, rows), dim3(kGatherThreads), lds, st, d, d_out, t,
-                     bk_rows, miss_rows, few_hits_above, div_magic((uint32_t)d.Q), div_magic((uint32_t)d.L),
-                     div_magic((uint32_t)d.R));
+  hipExtLaunchKernelGGL(k_gather, dim3(gx, rows), dim3(kGatherThreads), (uint32_t)lds, st, ev.start,
+                        ev.stop, 0, d, d_out, t, bk_rows, miss_rows, few_hits_above,
+                        div_magic((uint32_t)d.Q), div_magic((uint32_t)d.L), div_magic((uint32_t)d.R));
   return hipGetLastError();
 }
 

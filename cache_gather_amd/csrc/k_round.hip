@@ -274,8 +274,9 @@ __global__ __launch_bounds__(kSelThreads) void k_round(DevState d, StepArgs a,
 }
 
 hipError_t launch_round(const DevState& d, const StepArgs& a, const int32_t* d_sel,
-                        int32_t* d_trace, hipStream_t st) {
-  hipLaunchKernelGGL(k_round, dim3(d.S * d.G), dim3(kSelThreads), 0, st, d, a, d_sel, d_trace);
+                        int32_t* d_trace, hipStream_t st, StageEv ev) {
+  hipExtLaunchKernelGGL(k_round, dim3(d.S * d.G), dim3(kSelThreads), 0, st, ev.start, ev.stop, 0, d,
+                        a, d_sel, d_trace);
   return hipGetLastError();
 }
 

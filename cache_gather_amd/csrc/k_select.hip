@@ -269,6 +269,10 @@ __global__ __launch_bounds__(kSelThreads) void k_select(DevState d, StepArgs a,
     qent[2] = make_int2(w1.x, w1.y);
     qent[3] = make_int2(w1.z, w1.w);
   }
+  // every thread reads segment offsets other threads wrote above (the fast
+  // path's run placement, the slow path's entry lookup); the queue reads
+  // issued just before stay in flight across the barrier
+  __syncthreads();
   // this thread's run of R consecutive entries: thread order is position order
   uint32_t key[kRun];
   int32_t pos[kRun];
@@ -539,6 +543,9 @@ __global__ __launch_bounds__(kSelThreads) void k_select(DevState d, StepArgs a,
       n_bad += tot1 >> 16;
     }
   }
+#ifdef HC_TEST_HOOKS
+  if (d.test_force) n_bad = 1;
+#endif
   if (n_bad || nwin != K || m > K) {
     // inconsistent scan state or slot map: report it and touch nothing more;
     // the selection stays in range (the gather reads slot 0)
@@ -723,14 +730,14 @@ __global__ __launch_bounds__(kSelThreads) void k_select(DevState d, StepArgs a,
 
 hipError_t launch_select(const DevState& d, const StepArgs& a, const float* scores,
                          uint64_t stride, int64_t max_len, int32_t* d_sel, int32_t* d_trace,
-                         hipStream_t st) {
+                         hipStream_t st, StageEv ev) {
   const int64_t seg_len = scan_seg_len(max_len, d.max_segs);
   if (d.Q == 1)
-    hipLaunchKernelGGL(k_select<false>, dim3(d.S * d.G), dim3(kSelThreads), 0, st, d, a, scores,
-                       stride, seg_len, d_sel, d_trace);
+    hipExtLaunchKernelGGL(k_select<false>, dim3(d.S * d.G), dim3(kSelThreads), 0, st, ev.start,
+                          ev.stop, 0, d, a, scores, stride, seg_len, d_sel, d_trace);
   else
-    hipLaunchKernelGGL(k_select<true>, dim3(d.S * d.G * d.Q), dim3(kSelThreads), 0, st, d, a,
-                       scores, stride, seg_len, d_sel, d_trace);
+    hipExtLaunchKernelGGL(k_select<true>, dim3(d.S * d.G * d.Q), dim3(kSelThreads), 0, st,
+                          ev.start, ev.stop, 0, d, a, scores, stride, seg_len, d_sel, d_trace);
   return hipGetLastError();
 }
 

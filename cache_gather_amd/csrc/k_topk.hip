@@ -263,13 +263,14 @@ __global__ __launch_bounds__(kScanThreads) void k_cold_cut(DevState d) {
 }
 
 hipError_t launch_cold_cut(const DevState& d, const StepArgs& a, const float* scores,
-                           uint64_t stride, int64_t max_len, hipStream_t st) {
+                           uint64_t stride, int64_t max_len, hipStream_t st, StageEv ev) {
   const int units = d.S * d.G * d.Q;
   dim3 grid((unsigned)((max_len + kColdChunk - 1) / kColdChunk), units);
-  hipLaunchKernelGGL(k_cold_hist, grid, dim3(kScanThreads), 0, st, d, a, scores, stride);
+  hipExtLaunchKernelGGL(k_cold_hist, grid, dim3(kScanThreads), 0, st, ev.start, nullptr, 0, d, a,
+                        scores, stride);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_cold_cut, dim3(units), dim3(kScanThreads), 0, st, d);
+  hipExtLaunchKernelGGL(k_cold_cut, dim3(units), dim3(kScanThreads), 0, st, nullptr, ev.stop, 0, d);
   return hipGetLastError();
 }
 
@@ -283,7 +284,8 @@ int64_t scan_seg_len(int64_t max_len, int max_segs) {
 }
 
 hipError_t launch_topk_scan(const DevState& d, const StepArgs& a, const float* scores,
-                            uint64_t stride, int64_t max_len, bool vec4, hipStream_t st) {
+                            uint64_t stride, int64_t max_len, bool vec4, hipStream_t st,
+                            StageEv ev) {
   // 2,048 positions per workgroup: the scan is latency-bound, so more, smaller
   // workgroups (more of them resident per CU) finish sooner (the 16 x 1M scan:
   // 24.6 us against 28.5 us in 4,096-position workgroups)
@@ -291,9 +293,11 @@ hipError_t launch_topk_scan(const DevState& d, const StepArgs& a, const float* s
   const int tiles = (int)(seg_len / kScanChunk);
   dim3 grid((unsigned)((max_len + seg_len - 1) / seg_len), d.S * d.G * d.Q);
   if (vec4)
-    hipLaunchKernelGGL((k_topk_scan<true, kScanChunk>), grid, dim3(kScanThreads), 0, st, d, a, scores, stride, tiles);
+    hipExtLaunchKernelGGL((k_topk_scan<true, kScanChunk>), grid, dim3(kScanThreads), 0, st, ev.start,
+                          ev.stop, 0, d, a, scores, stride, tiles);
   else
-    hipLaunchKernelGGL((k_topk_scan<false, kScanChunk>), grid, dim3(kScanThreads), 0, st, d, a, scores, stride, tiles);
+    hipExtLaunchKernelGGL((k_topk_scan<false, kScanChunk>), grid, dim3(kScanThreads), 0, st, ev.start,
+                          ev.stop, 0, d, a, scores, stride, tiles);
   return hipGetLastError();
 }
 

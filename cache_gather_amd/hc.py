@@ -64,18 +64,54 @@ def make_config(n_sessions, n_layers, layers_per_select, cache_slots, top_k, max
 
 
 _LIB = None
+_TEST_LIB = None
 _vp = ctypes.c_void_p
+TEST_LIB_PATH = os.path.join(HERE, "libhc_test.so")
 
 
 def lib():
     """The loaded libhc.so; raises if it was not built."""
     global _LIB
-    if _LIB is not None:
-        return _LIB
+    if _LIB is None:
+        _LIB = _load(LIB_PATH)
+    return _LIB
+
+
+def test_lib():
+    """The test build libhc_test.so (the same entry points plus hc_test_hook,
+    include/hc_test.h), loaded beside libhc.so; for the tests of failure paths."""
+    global _TEST_LIB
+    if _TEST_LIB is None:
+        L = _load(TEST_LIB_PATH)
+        L.hc_test_hook.argtypes = [_vp, ctypes.c_int, ctypes.c_int64, ctypes.POINTER(ctypes.c_uint64)]
+        L.hc_test_hook.restype = ctypes.c_int
+        _TEST_LIB = L
+    return _TEST_LIB
+
+
+class using:
+    """with using(test_lib()): every hc_* call of this module goes to that
+    library (contexts are not shared between libraries)."""
+
+    def __init__(self, L):
+        self.L = L
+
+    def __enter__(self):
+        global _LIB
+        lib()
+        self.prev, _LIB = _LIB, self.L
+        return self.L
+
+    def __exit__(self, *exc):
+        global _LIB
+        _LIB = self.prev
+
+
+def _load(path):
     import torch  # noqa: F401  (its HIP runtime must be the one in the process)
-    if not os.path.exists(LIB_PATH):
-        raise RuntimeError("libhc.so is not built (%s); run __graft_entry__.build()" % LIB_PATH)
-    L = ctypes.CDLL(LIB_PATH)
+    if not os.path.exists(path):
+        raise RuntimeError("%s is not built; run __graft_entry__.build()" % path)
+    L = ctypes.CDLL(path)
     st = ctypes.c_int
     L.hc_workspace_bytes.argtypes = [ctypes.POINTER(hc_config), ctypes.POINTER(ctypes.c_uint64)]
     L.hc_workspace_bytes.restype = st
@@ -113,7 +149,6 @@ def lib():
     L.hc_destroy.restype = st
     L.hc_status_str.argtypes = [ctypes.c_int]
     L.hc_status_str.restype = ctypes.c_char_p
-    _LIB = L
     return L
 
 
@@ -246,6 +281,17 @@ def hc_steps_done(ctx: int) -> int:
     return n.value
 
 
+def hc_test_hook(ctx, kind: int, arg: int = 0) -> int:
+    """The test build's hook (include/hc_test.h); returns its output value."""
+    out = ctypes.c_uint64()
+    _check("hc_test_hook", test_lib().hc_test_hook(ctx, kind, arg, ctypes.byref(out)))
+    return out.value
+
+
+(TEST_FAIL_LAUNCH, TEST_FORCE_SELECT, TEST_CORRUPT_LRU, TEST_FAIL_PINNED, TEST_PINNED_BYTES,
+ TEST_POISON_VICTIMS) = 1, 2, 3, 4, 5, 6
+
+
 def hc_destroy(ctx: int) -> None:
     _check("hc_destroy", lib().hc_destroy(ctx))
 
@@ -274,6 +320,8 @@ class HotCache:
         self.G = -(-n_layers // layers_per_select)
         self.C, self.K, self.hcap = cache_slots, top_k, max_positions
         self.device = torch.device("cuda", device)
+        self.ctx = 0
+        self._L = lib()   # the library the context belongs to (see `using`)
         self.ws_bytes = hc_workspace_bytes(self.cfg)
         self.workspace = torch.empty(self.ws_bytes, dtype=torch.uint8, device=self.device)
         assert self.workspace.data_ptr() % 256 == 0
@@ -339,7 +387,8 @@ class HotCache:
 
     def close(self):
         if self.ctx:
-            hc_destroy(self.ctx)
+            with using(self._L):
+                hc_destroy(self.ctx)
             self.ctx = 0
 
     def __del__(self):

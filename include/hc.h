@@ -279,13 +279,16 @@ hc_status hc_attend_cached_noalloc(hc_ctx* ctx, void* stream, const uint16_t* d_
 /* Synchronous snapshot for tests: waits for all enqueued steps, then copies
  * the state that layer `layer` of `session` sees into host buffers:
  * slot2pos[C] and last_use[C] (-1 = empty / never used), pos2slot[Hcap] if
- * non-NULL, and the layer's hot rows [C][656] if hot_rows is non-NULL. */
+ * non-NULL, and the layer's hot rows [C][656] if hot_rows is non-NULL (the
+ * bytes of an empty slot are whatever the workspace held: unspecified). */
 hc_status hc_export_state(hc_ctx* ctx, uint32_t session, uint32_t layer,
                           int32_t* slot2pos, int32_t* last_use,
                           int32_t* pos2slot, uint8_t* hot_rows);
 
-/* Per-stage kernel timing with HIP events recorded around each launch on the
- * step's stream.  hc_profile_enable(ctx, n) arms timing for the next n steps
+/* Per-stage kernel timing: a pair of HIP events per stage, attached to the
+ * stage's first and last kernel dispatch on the step's stream, so that they
+ * record the kernels' own begin and end (no event is enqueued between
+ * kernels).  hc_profile_enable(ctx, n) arms timing for the next n steps
  * (n = 0 disarms; any earlier timing is dropped).  hc_profile_read waits for
  * the timed steps and returns the summed milliseconds per stage
  * (stage_ms[HC_NUM_STAGES]), the number of timed steps, and, if per_step is

@@ -28,3 +28,16 @@ def test_cpu_only_baseline_line():
     assert cb["kind"] == "oracle" and cb["unit"] == "rows/s" and cb["cores"] == 1
     assert cb["value"] > 0 and "tiny_4k" in cb["sample"]
     assert line["workload"] == "tiny_4k" and line["ms_per_step"] > 0
+
+
+def test_cpu_baseline_states_the_host_and_a_single_thread_rate():
+    """The baseline names the host it ran on (core count, CPU model) and also
+    times the oracle on one thread."""
+    r = _bench("--cpu-only", "--workload", "tiny_4k", "--cpu-steps", "3", "--cpu-threads", "2",
+               "--cpu-single-steps", "2")
+    assert r.returncode == 0, r.stderr
+    cb = json.loads(r.stdout.strip().splitlines()[-1])["cpu_baseline"]
+    assert cb["cores"] == 2 and cb["nproc"] == os.cpu_count()
+    assert "cpu_model" in cb
+    st = cb["single_thread"]
+    assert st["cores"] == 1 and st["value"] > 0 and st["unit"] == "rows/s"
