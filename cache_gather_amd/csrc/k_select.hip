@@ -14,42 +14,41 @@
 // a chain of dependent steps on one workgroup, and a dependent read of data
 // another XCD's L2 wrote costs about 1.5 us, so the kernel is built around
 // its few unavoidable round trips: every global read is issued as soon as
-// its address is known, the LDS work runs while reads are in flight, and no
-// global store is issued before the last read has been consumed (on this
-// chip the vector memory counter also counts stores, so waiting for a read
-// issued before a store waits for the store too).  Three rounds of reads:
-//  1. the unit's counters and the score scan's segment counts;
-//  2. the entries (keys above or inside the predicted cut window, with their
-//     positions; one segment per scan workgroup, each in ascending position
-//     order): a block scan of the counts places the segments, and each thread
-//     loads a run of up to 8 consecutive entries into registers, so thread
-//     order is position order — and, when the LRU queue may have to supply
-//     victims, its first 4,096 entries from the head;
-//  3. the slot-map entry of every entry's position, and the last use and
-//     position held of every prefetched queue entry.
+// its address is known, without a branch between the loads of one round (a
+// load behind a branch was issued only after the previous one returned), the
+// LDS work runs while reads are in flight, and no global store is issued
+// before the last read has been consumed (on this chip the vector memory
+// counter also counts stores, so waiting for a read issued before a store
+// waits for the store too).  Reads:
+//  1. one round trip for the unit's counter line, each thread's segment count
+//     and its 8 entry slots: the score scan wrote one segment of entries per
+//     scan workgroup (keys above or inside the predicted cut window, their
+//     positions and the slots holding them, in ascending position order),
+//     and segment s belongs to 1,024 / nseg consecutive threads, so thread
+//     order is position order (a segment with more entries than its threads
+//     hold takes a second round for every segment count, and the entries
+//     from global memory);
+//  2. when the LRU queue may have to supply victims, its first 4,096 entries
+//     from the head, and 3. the last use and position held of each.
 // Then, in LDS only: the radix cut over the window entries (the top 22 key
-// bits in one histogram pass, window bin x next 10-bit digit; the entries
-// sharing the cut's 22-bit prefix — usually a handful — rank themselves
-// against each other, which also cuts exact ties by position, lower winning);
-// one pass over the registers for winners, hits and misses, ranked together
-// by one block scan; LRU victims without any search — never-used slots first
-// (slots [fill, C), lowest first), then the first live (last use equal to the
-// entry's stamp), unpinned entries of the queue of (slot, step) entries in
-// ascending (step, slot) order, ranked by one block scan; and each slot the
-// step used gets its place at the queue's tail in slot order from a block
-// scan of per-word popcounts of the touched bitmap.  Finally every store:
-// the selection, the hits' last-use stamps, the queue's new entries, the
-// (miss, victim) pairs applied to pos2slot / slot2pos / last_use (an evicted
-// position is never one of this step's misses), the gather's miss list and
-// the trace.  The queue is compacted into its second buffer once every C / K
-// steps or so.  Inconsistent state (corrupted counters or maps) is reported
-// through the context's error words; every index stays in range.
+// bits in one histogram, window bin x next 6 bits, built before the block
+// totals are known; the entries sharing the cut's 22-bit prefix — usually a
+// handful — rank themselves against each other, which also cuts exact ties
+// by position, lower winning); one pass over the registers for winners, hits
+// and misses, ranked together by one block scan; LRU victims without any
+// search — never-used slots first (slots [fill, C), lowest first), then the
+// first live (last use equal to the entry's stamp), unpinned entries of the
+// queue of (slot, step) entries in ascending (step, slot) order, ranked by
+// one block scan.  Finally every store: the selection, each selected row's
+// source for the gather, the miss list with each victim's previous position,
+// the trace and the counters.  The last-use stamps, the slot-map updates and
+// the queue's new entries are left to the unit's bookkeeping workgroup in
+// the gather launch.  Inconsistent state (corrupted counters or maps) is
+// reported through the context's error words; every index stays in range.
 #include "hc_block.h"
 
 namespace hc {
 
-constexpr int kRun = 8;                               // entries per thread and round
-constexpr int kRoundEntries = kSelThreads * kRun;     // 8,192 entries per round
 constexpr int kQWin = 4;                              // queue entries per thread, prefetched
 constexpr int kSegPer = kMaxSegs / kSelThreads;       // segment counts per thread
 constexpr int kRankMax = 256;                         // entries of the cut's 22-bit prefix ranked pairwise
@@ -178,7 +177,10 @@ __device__ int rescan(const float* src, int64_t H, int K, Ent* gcand, SelShared&
 // kTopkOnly (multi-query rounds): workgroup u is selection unit (s, g, q) and
 // stops after writing its selection; k_round then runs steps 3-5 on the union
 // of the group's selections.  Otherwise (one query) u is the unit (s, g).
-template <bool kTopkOnly>
+// kRun: entries a thread holds in registers (4 for top-K up to 3,072, else
+// 8): the per-entry code is unrolled, and on this kernel every instruction is
+// fetched cold, so the smaller variant runs measurably faster.
+template <bool kTopkOnly, int kRun>
 __global__ __launch_bounds__(kSelThreads) void k_select(DevState d, StepArgs a,
                                                         const float* __restrict__ scores,
                                                         uint64_t stride, int64_t seg_len,
@@ -186,8 +188,10 @@ __global__ __launch_bounds__(kSelThreads) void k_select(DevState d, StepArgs a,
                                                         int32_t* __restrict__ d_trace) {
   __shared__ SelShared sh;
   constexpr bool kCache = !kTopkOnly;
-  const int u = blockIdx.x, tid = threadIdx.x;
-  const int session = u / (d.G * d.Q);
+  constexpr int kRoundEntries = kSelThreads * kRun;   // entries in registers at most
+  // grid (G Q, S): the session is the grid row, so no division is needed
+  const int session = blockIdx.y;
+  const int u = blockIdx.y * gridDim.x + blockIdx.x, tid = threadIdx.x;
   const int K = d.K, C = d.C;
   const int32_t t = a.t;
   const int64_t H = a.hist_len[session];
@@ -200,26 +204,64 @@ __global__ __launch_bounds__(kSelThreads) void k_select(DevState d, StepArgs a,
   const bool lru = kCache && d.policy == HC_REPLACE_LRU;
   const int nwords = (C + 31) >> 5;
 
-  // ==== reads, round 1: counters and segment counts =========================
-  const int win_lo = cnt[kCntWinLo], win_hi = cnt[kCntWinHi];
-  int qh = 0, qe = 0, qb = 0, fill = 0;
-  if (kCache) {
-    qh = cnt[kCntQHead];
-    qe = cnt[kCntQTail];
-    qb = cnt[kCntQBuf] & 1;
-    fill = cnt[kCntFill];
-  }
-  const int nseg = (int)((H + seg_len - 1) / seg_len);   // <= max_segs, checked on the host
-  int2 segc[kSegPer];
+  // ==== reads, round 1: counters, segment counts, entries ===================
+  // With few segments (each gets at least 64 entry slots), segment s of the
+  // scan's entries is held by spt = 1,024 / nseg consecutive threads, thread
+  // c of them taking entry slots [kRun c, kRun (c + 1)) of it, so every
+  // address is known at the start: the counter line, the thread's segment
+  // count and its entry slots are read in one round trip, with clamped
+  // in-range indices and no branch (slots past the segment's count are
+  // ignored); thread order is position order.  With many segments, or when
+  // a segment holds more entries than its threads, every segment count is
+  // read and a second round gives each thread a run of consecutive entries.
+  // lane i holds counter word i mod 16: a vector load (a scalar load of the
+  // line would make the wait for the kernel's argument loads wait for it)
+  static_assert(kCnt <= 16, "counters read from lanes 0-15");
+  const int cword = cnt[tid & 15];
+  // positions, segment lengths and entry indices are below 2^31: 32-bit math
+  const uint32_t H32 = (uint32_t)H, len32 = (uint32_t)seg_len;
+  const int nseg = (int)((H32 + len32 - 1) / len32);   // 1 .. max_segs, checked on the host
+  const int spt = nseg <= kSelThreads ? kSelThreads / nseg : 0;
+  const bool spec = spt * kRun >= 64;
+  const int my_seg = spec ? min(tid / spt, nseg - 1) : 0;
+  const bool has_seg = spec && tid < spt * nseg;
+  const int c_lo = has_seg ? (tid - my_seg * spt) * kRun : 0;   // first entry slot of the thread
+  const uint32_t s_base = (uint32_t)my_seg * len32;
+  const uint32_t s_slots = min(len32, (uint32_t)d.hcap - s_base);   // >= 1: s_base < H <= hcap
+  int2 segv = make_int2(0, 0);
+  Ent ent[kRun];
+  int2 segc[kSegPer];   // every segment count (kSegPer per thread), when read
+  if (spec) {
+    segv = d.seg[(size_t)u * d.max_segs + my_seg];
 #pragma unroll
-  for (int k = 0; k < kSegPer; ++k) {
-    const int s = tid * kSegPer + k;
-    segc[k] = s < nseg ? d.seg[(size_t)u * d.max_segs + s] : make_int2(0, 0);
+    for (int k = 0; k < kRun; ++k) ent[k] = gcand[s_base + min((uint32_t)(c_lo + k), s_slots - 1)];
+  } else {
+#pragma unroll
+    for (int k = 0; k < kSegPer; ++k)
+      segc[k] = d.seg[(size_t)u * d.max_segs + min(tid * kSegPer + k, nseg - 1)];
+#pragma unroll
+    for (int k = 0; k < kRun; ++k) ent[k] = Ent{0u, 0u, -1};
   }
+
   for (int b = tid; b < kBins1; b += kSelThreads) sh.hist[b] = 0;
   if (kCache)
     for (int w = tid; w < nwords; w += kSelThreads) sh.touched[w] = 0;
-  if (tid == 0) sh.bcast[7] = 0;   // evictions, counted at the stores
+  if (tid == 0) {
+    sh.bcast[2] = 0;   // entries of the cut prefix listed so far
+    sh.bcast[5] = 0;   // a segment holds more entries than its threads
+    sh.bcast[7] = 0;   // evictions, counted at the stores
+  }
+  __syncthreads();   // the round-1 reads stay in flight across it
+
+  const int win_lo = __builtin_amdgcn_readlane(cword, kCntWinLo);
+  const int win_hi = __builtin_amdgcn_readlane(cword, kCntWinHi);
+  int qh = 0, qe = 0, qb = 0, fill = 0;
+  if (kCache) {
+    qh = __builtin_amdgcn_readlane(cword, kCntQHead);
+    qe = __builtin_amdgcn_readlane(cword, kCntQTail);
+    qb = __builtin_amdgcn_readlane(cword, kCntQBuf) & 1;
+    fill = __builtin_amdgcn_readlane(cword, kCntFill);
+  }
   fill = min(max(fill, 0), C);
   qe = min(max(qe, 0), d.qcap);
   qh = min(max(qh, 0), qe);
@@ -228,37 +270,8 @@ __global__ __launch_bounds__(kSelThreads) void k_select(DevState d, StepArgs a,
   const int2* qbuf = d.oq + ((size_t)u * 2 + qb) * d.qcap;
   const int qj0 = (qh & ~(kQWin - 1)) + tid * kQWin;
 
-  int sc[kSegPer];
-  int se = 0, sa = 0;
-#pragma unroll
-  for (int k = 0; k < kSegPer; ++k) {
-    const int s = tid * kSegPer + k;
-    const int64_t room = H - (int64_t)s * seg_len < seg_len ? H - (int64_t)s * seg_len : seg_len;
-    const int n = s < nseg ? (int)min((int64_t)max(segc[k].x, 0), room) : 0;
-    sc[k] = n;
-    se += n;
-    sa += min(max(segc[k].y, 0), n);
-  }
-  int E, n_above;
-  int o = block_scan_sum(se, sa, sh, E, n_above) - se;
-#pragma unroll
-  for (int k = 0; k < kSegPer; ++k) {
-    const int s = tid * kSegPer + k;
-    if (s < nseg) sh.segoff[s] = o;
-    o += sc[k];
-  }
-  uint32_t b_lo, b_hi;   // the scan's cut window, top-16-bit key units
-  cut_window(win_lo, win_hi, b_lo, b_hi);
-  // Fast path: the K-th key lies inside the predicted window and at most
-  // 8,192 entries lie above or inside it, so every entry fits in registers,
-  // up to 8 per thread.  Otherwise the slow path makes every pass over the
-  // entries in global memory: over the scan's segments if the window holds
-  // the K-th key (ties, flat scores), else over a list rebuilt from the
-  // scores (the cut jumped).
-  const bool window_ok = n_above < K && E >= K;
-  const bool fast = window_ok && E <= kRoundEntries;
-
-  // ==== reads, round 2: the LRU queue's first window, the entries ===========
+  // ==== reads, round 2: the LRU queue's first window (when it may supply
+  // victims); consumed after the cut ==========================================
   int2 qent[kQWin];
   {
     int4 w0 = make_int4(-1, -1, -1, -1), w1 = w0;   // qcap % 4 == 0: both in bounds
@@ -269,17 +282,100 @@ __global__ __launch_bounds__(kSelThreads) void k_select(DevState d, StepArgs a,
     qent[2] = make_int2(w1.x, w1.y);
     qent[3] = make_int2(w1.z, w1.w);
   }
-  // every thread reads segment offsets other threads wrote above (the fast
-  // path's run placement, the slow path's entry lookup); the queue reads
-  // issued just before stay in flight across the barrier
-  __syncthreads();
-  // this thread's run of R consecutive entries: thread order is position order
+
+  uint32_t b_lo, b_hi;   // the scan's cut window, top-16-bit key units
+  cut_window(win_lo, win_hi, b_lo, b_hi);
+  const int s_room = has_seg ? (int)min(len32, H32 - s_base) : 0;
+  const int n_s = has_seg ? min(max(segv.x, 0), s_room) : 0;
+  int nv = max(0, min(kRun, n_s - c_lo));   // this thread's entries
   uint32_t key[kRun];
   int32_t pos[kRun];
   int32_t slot[kRun];   // slot of each entry's position (the scan's lookup), -1: miss or ring
-  int nv = 0;
-  if (fast) {
-    const int R = (E + kSelThreads - 1) / kSelThreads;
+#pragma unroll
+  for (int k = 0; k < kRun; ++k) {
+    key[k] = ent[k].key;
+    pos[k] = (int32_t)ent[k].pos;
+    slot[k] = kCache ? ent[k].slot : -1;
+  }
+  // The fast path's first histogram, built before the totals are known: the
+  // window's 22-bit prefixes (window prefix x the next 6 bits, at most 64 x 64
+  // bins), or for a wide window (a unit's first step without a cut histogram)
+  // its 12-bit bins, which narrow it first.
+  const bool wide0 = b_hi - b_lo + 1 > 64;
+  int E = 0, n_above = 0;
+  bool layout_ok = false;
+  if (spec) {
+#pragma unroll
+    for (int k = 0; k < kRun; ++k) {
+      if (k >= nv) continue;
+      const uint32_t kk = key[k];
+      if (wide0) {
+        const uint32_t k16 = kk >> 16;
+        if (k16 >= b_lo && k16 <= b_hi) atomicAdd(&sh.hist[(kk >> 20) - (b_lo >> 4)], 1u);
+      } else {
+        const uint32_t p22 = kk >> 10;
+        if (p22 >= (b_lo << 6) && p22 < ((b_hi + 1) << 6)) atomicAdd(&sh.hist[p22 - (b_lo << 6)], 1u);
+      }
+    }
+    // block totals: entries and entries above the window (one lane per segment)
+    const bool lead = has_seg && c_lo == 0;
+    if (lead && n_s > spt * kRun) sh.bcast[5] = 1;
+    const int ev = wave_incl_scan(lead ? n_s : 0);
+    const int av = wave_incl_scan(lead ? min(max(segv.y, 0), n_s) : 0);
+    if (lane_id() == 63) {
+      sh.wtot[tid >> 6] = ev;
+      sh.wtot2[tid >> 6] = av;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < kWaves; ++i) {
+      E += sh.wtot[i];
+      n_above += sh.wtot2[i];
+    }
+    layout_ok = sh.bcast[5] == 0;
+  }
+  if (!layout_ok) {
+    // every segment count (a second read round after the speculative one),
+    // their offsets and totals
+    if (spec) {
+#pragma unroll
+      for (int k = 0; k < kSegPer; ++k)
+        segc[k] = d.seg[(size_t)u * d.max_segs + min(tid * kSegPer + k, nseg - 1)];
+    }
+    int sc[kSegPer];
+    int se = 0, sa = 0;
+#pragma unroll
+    for (int k = 0; k < kSegPer; ++k) {
+      const int sg = tid * kSegPer + k;
+      const int room = sg < nseg ? (int)min(len32, H32 - (uint32_t)sg * len32) : 0;
+      const int n = min(max(segc[k].x, 0), room);
+      sc[k] = n;
+      se += n;
+      sa += min(max(segc[k].y, 0), n);
+    }
+    if (spec) __syncthreads();   // the wave totals above are read before the scan rewrites them
+    int o = block_scan_sum(se, sa, sh, E, n_above) - se;
+#pragma unroll
+    for (int k = 0; k < kSegPer; ++k) {
+      const int sg = tid * kSegPer + k;
+      if (sg < nseg) sh.segoff[sg] = o;
+      o += sc[k];
+    }
+    __syncthreads();   // every thread reads the segment offsets
+  }
+  // Fast path: the K-th key lies inside the predicted window and the entries
+  // are in registers — already, if every segment fit its threads' slots, or
+  // else after a second round that gives each thread a run of consecutive
+  // entries (at most kRoundEntries in all).  Otherwise the slow path makes
+  // every pass over the entries in global memory: over the scan's segments
+  // if the window holds the K-th key (ties, flat scores), else over a list
+  // rebuilt from the scores (the cut jumped).
+  const bool window_ok = n_above < K && E >= K;
+  const bool hist0 = layout_ok && window_ok;   // the first histogram holds every entry
+  bool fast = hist0;
+  if (!layout_ok && window_ok && E <= kRoundEntries) {
+    fast = true;
+    const int R = (E + kSelThreads - 1) / kSelThreads;   // <= kRun
     const int j0 = tid * R;
     nv = max(0, min(R, E - j0));
     int lo = 0, hi = nseg;   // the last segment starting at or before j0
@@ -293,9 +389,6 @@ __global__ __launch_bounds__(kSelThreads) void k_select(DevState d, StepArgs a,
     int next = sg + 1 < nseg ? sh.segoff[sg + 1] : 0x7FFFFFFF;
 #pragma unroll
     for (int k = 0; k < kRun; ++k) {
-      key[k] = 0u;
-      pos[k] = -1;
-      slot[k] = -1;
       if (k >= nv) continue;
       const int j = j0 + k;
       while (j >= next) {   // the run crosses into a later segment
@@ -303,21 +396,11 @@ __global__ __launch_bounds__(kSelThreads) void k_select(DevState d, StepArgs a,
         start = next;
         next = sg + 1 < nseg ? sh.segoff[sg + 1] : 0x7FFFFFFF;
       }
-      const Ent e = gcand[(int64_t)sg * seg_len + (j - start)];
+      const Ent e = gcand[(uint32_t)sg * len32 + (uint32_t)(j - start)];
       key[k] = e.key;
       pos[k] = (int32_t)e.pos;
       if (kCache) slot[k] = e.slot;
     }
-  }
-
-  // ==== reads, round 3: the prefetched queue entries' state ==================
-  int qlu[kQWin], qsp[kQWin];
-#pragma unroll
-  for (int k = 0; k < kQWin; ++k) {
-    const int j = qj0 + k;
-    const bool ok = q_pf && j >= qh && j < qe && qent[k].x >= 0 && qent[k].x < C;
-    qlu[k] = ok ? last_use[qent[k].x] : (int)0x80000000;
-    qsp[k] = ok ? slot2pos[qent[k].x] : -1;
   }
 
   // ==== the cut key T and position cut (LDS) =================================
@@ -335,6 +418,8 @@ __global__ __launch_bounds__(kSelThreads) void k_select(DevState d, StepArgs a,
     if (tid == 0) sh.segoff[0] = 0;
     for (int b = tid; b < kBins1; b += kSelThreads) sh.hist[b] = 0;
     __syncthreads();
+  } else if (!hist0) {
+    clear_hist(sh, kBins1);   // the first histogram held the first slots of each segment only
   }
   auto entry = [&](int j) {   // slow path: entry j
     int lo = 0, hi = nsegs;
@@ -361,14 +446,15 @@ __global__ __launch_bounds__(kSelThreads) void k_select(DevState d, StepArgs a,
   uint32_t lo16 = b_lo, hi16 = b_hi;
   int beyond;
   if (hi16 - lo16 + 1 > 64) {
-    // a wide window (a unit's first step without a cut histogram): narrow it
-    // to the 12-bit bin holding the K-th key first
+    // a wide window: narrow it to the 12-bit bin holding the K-th key first
     const uint32_t lo12 = lo16 >> 4;
-    each([&](uint32_t kk, int32_t) {
-      const uint32_t k16 = kk >> 16;
-      if (k16 >= lo16 && k16 <= hi16) atomicAdd(&sh.hist[(kk >> 20) - lo12], 1u);
-    });
-    __syncthreads();
+    if (!hist0) {
+      each([&](uint32_t kk, int32_t) {
+        const uint32_t k16 = kk >> 16;
+        if (k16 >= lo16 && k16 <= hi16) atomicAdd(&sh.hist[(kk >> 20) - lo12], 1u);
+      });
+      __syncthreads();
+    }
     int rel;
     find_digit(sh.hist, kBins1, r, true, sh, rel, beyond);
     r -= beyond;
@@ -378,14 +464,16 @@ __global__ __launch_bounds__(kSelThreads) void k_select(DevState d, StepArgs a,
     clear_hist(sh, kBins1);
   }
   // the top 22 bits: window prefix x the next 6 bits in one histogram of at
-  // most 64 x 64 bins
+  // most 64 x 64 bins (the fast path's, for a window that was not wide, is
+  // already complete)
   const uint32_t w_lo22 = lo16 << 6, w_hi22 = (hi16 + 1) << 6;
-  each([&](uint32_t kk, int32_t) {
-    const uint32_t p22 = kk >> 10;
-    if (p22 >= w_lo22 && p22 < w_hi22) atomicAdd(&sh.hist[p22 - w_lo22], 1u);
-  });
-  if (tid == 0) sh.bcast[2] = 0;   // entries of the cut prefix listed so far
-  __syncthreads();
+  if (!hist0 || wide0) {
+    each([&](uint32_t kk, int32_t) {
+      const uint32_t p22 = kk >> 10;
+      if (p22 >= w_lo22 && p22 < w_hi22) atomicAdd(&sh.hist[p22 - w_lo22], 1u);
+    });
+    __syncthreads();
+  }
   int idx22;
   find_digit(sh.hist, kBins1, r, true, sh, idx22, beyond);
   r -= beyond;   // winners to take among the entries of the prefix, >= 1
@@ -468,25 +556,53 @@ __global__ __launch_bounds__(kSelThreads) void k_select(DevState d, StepArgs a,
   // the next step's window: this cut's 16-bit prefix +- kWinHalf
   const int nlo = max((int)(T >> 16) - kWinHalf, 0), nhi = min((int)(T >> 16) + kWinHalf, 65535);
 
+  // ==== reads, round 3: the prefetched queue entries' state (consumed by the
+  // victims) ==================================================================
+  int qlu[kQWin], qsp[kQWin];
+#pragma unroll
+  for (int k = 0; k < kQWin; ++k) {
+    qlu[k] = (int)0x80000000;
+    qsp[k] = -1;
+  }
+  if (q_pf) {
+#pragma unroll
+    for (int k = 0; k < kQWin; ++k) {
+      const int j = qj0 + k;
+      if (j >= qh && j < qe && qent[k].x >= 0 && qent[k].x < C) {
+        qlu[k] = last_use[qent[k].x];
+        qsp[k] = slot2pos[qent[k].x];
+      }
+    }
+  }
+
   // ==== winners in position order, hits, misses (LDS) ========================
   // one block scan ranks winners and misses (two 16-bit fields of one value)
   // and counts ring rows and corrupt slot-map entries (second value)
   int nwin = 0, m = 0, n_ring = 0, n_bad = 0;
+  // The ring holds positions [ring_lo, ring_lo + ring_rows), position p in
+  // entry p mod ring_rows: entry ring_base + (p - ring_lo), wrapped once.
+  const uint32_t rrows = d.ring_rows > 0 ? (uint32_t)d.ring_rows : 1u;
+  const uint32_t ring_base = kCache && ring_lo != kNoRing ? ring_lo % rrows : 0u;
+  auto ring_entry = [&](int32_t p) {
+    uint32_t re = ring_base + ((uint32_t)p - ring_lo);
+    re = re >= rrows ? re - rrows : re;
+    return (int32_t)min(re, rrows - 1);   // in range whatever the inputs
+  };
   // Records winner wr (miss rank mr) with its source.
   auto record = [&](int wr, int mr, int32_t p, int32_t sl, bool ring, bool miss) {
     if (wr >= K) return;
     sh.selpos[wr] = p;
     if (!kCache) return;
-    sh.selslot[wr] = ring ? C + (int32_t)((uint32_t)p % (uint32_t)d.ring_rows) : (miss ? -1 : sl);
+    sh.selslot[wr] = ring ? C + ring_entry(p) : (miss ? -1 : sl);
     if (miss && mr < K) {
       sh.mpos[mr] = p;
       sh.midx[mr] = wr;
     }
-    if (!ring && !miss) atomicOr(&sh.touched[sl >> 5], 1u << (sl & 31));
   };
+  uint32_t fw = 0, fm = 0, fr = 0;   // fast path, bit k: entry k wins / misses / is a ring row
+  int ex = 0;                        // fast path: winners (low 16 bits) and misses before this thread
   if (fast) {
     int cw = 0, cm = 0, cr = 0, cb = 0;
-    uint32_t fw = 0, fm = 0, fr = 0;   // bit k: entry k wins / misses / is a ring row
 #pragma unroll
     for (int k = 0; k < kRun; ++k) {
       const bool win = k < nv && (key[k] > T || (key[k] == T && pos[k] <= pcut));
@@ -505,16 +621,7 @@ __global__ __launch_bounds__(kSelThreads) void k_select(DevState d, StepArgs a,
     // 16-bit fields, no carry
     int tot, tot1;
     const int packed = cw | (cm << 16);
-    const int ex = block_scan_sum(packed, cr | (cb << 16), sh, tot, tot1) - packed;
-    int wr = ex & 0xFFFF, mr = ex >> 16;
-#pragma unroll
-    for (int k = 0; k < kRun; ++k) {
-      if (!((fw >> k) & 1u)) continue;
-      const bool ring = (fr >> k) & 1u, miss = (fm >> k) & 1u;
-      record(wr, mr, pos[k], slot[k], ring, miss);
-      mr += miss;
-      ++wr;
-    }
+    ex = block_scan_sum(packed, cr | (cb << 16), sh, tot, tot1) - packed;
     nwin = tot & 0xFFFF;
     m = tot >> 16;
     n_ring = tot1 & 0xFFFF;
@@ -560,6 +667,78 @@ __global__ __launch_bounds__(kSelThreads) void k_select(DevState d, StepArgs a,
     }
     return;
   }
+  // Direct stores: a top-K-only step, or a fast-path step whose victims are
+  // all never-used slots (miss k takes slot fill + k: nothing to search,
+  // nothing evicted), stores each thread's winners from its registers.
+  if (fast && (kTopkOnly || (lru && m <= C - fill))) {
+    int32_t* tr = kCache && d_trace ? d_trace + (size_t)u * HC_TRACE_INTS(K) : nullptr;
+    int32_t* g_slot = d.sel_slot + (size_t)u * K;
+    int32_t* g_miss = d.miss_pos + (size_t)u * K;
+    int32_t* g_vic = d.victim + (size_t)u * K;
+    int32_t* g_midx = d.miss_idx + (size_t)u * K;
+    int32_t* g_old = d.miss_old + (size_t)u * K;
+    int wr = ex & 0xFFFF, mr = ex >> 16;
+#pragma unroll
+    for (int k = 0; k < kRun; ++k) {
+      if (!((fw >> k) & 1u)) continue;
+      const int32_t p = pos[k];
+      d_sel[(size_t)u * K + wr] = p;
+      if (kCache) {
+        int32_t enc = slot[k];
+        if ((fr >> k) & 1u) enc = C + ring_entry(p);
+        if ((fm >> k) & 1u) {
+          const int32_t v = fill + mr;
+          enc = -(v + 1);
+          g_miss[mr] = p;
+          g_vic[mr] = v;
+          g_midx[mr] = wr;
+          g_old[mr] = -1;
+          if (tr) {
+            tr[HC_TRACE_HEADER + K + mr] = p;
+            tr[HC_TRACE_HEADER + 2 * K + mr] = v;
+            tr[HC_TRACE_HEADER + 3 * K + mr] = -1;
+          }
+          ++mr;
+        }
+        g_slot[wr] = enc;
+        if (tr) {
+          tr[HC_TRACE_HEADER + wr] = enc < 0 ? -enc - 1 : enc;
+          if (wr >= m) {
+            tr[HC_TRACE_HEADER + K + wr] = -1;
+            tr[HC_TRACE_HEADER + 2 * K + wr] = -1;
+            tr[HC_TRACE_HEADER + 3 * K + wr] = -1;
+          }
+        }
+      }
+      ++wr;
+    }
+    if (tid == 0) {
+      if (kCache) {
+        if (tr) {
+          tr[0] = K - m - n_ring;
+          tr[1] = m;
+          tr[2] = 0;
+          tr[3] = n_ring;
+        }
+        cnt[kCntFill] = fill + m;
+        cnt[kCntMiss] = m;
+      }
+      cnt[kCntWinLo] = nlo;   // the next step's cut window
+      cnt[kCntWinHi] = nhi;
+    }
+    return;
+  }
+  if (fast) {
+    int wr = ex & 0xFFFF, mr = ex >> 16;
+#pragma unroll
+    for (int k = 0; k < kRun; ++k) {
+      if (!((fw >> k) & 1u)) continue;
+      const bool ring = (fr >> k) & 1u, miss = (fm >> k) & 1u;
+      record(wr, mr, pos[k], slot[k], ring, miss);
+      mr += miss;
+      ++wr;
+    }
+  }
   __syncthreads();   // the recorded winners are read by other threads below
   if (kTopkOnly) {
     for (int i = tid; i < K; i += kSelThreads) d_sel[(size_t)u * K + i] = sh.selpos[i];
@@ -571,6 +750,16 @@ __global__ __launch_bounds__(kSelThreads) void k_select(DevState d, StepArgs a,
   }
 
   // ==== victims (LDS; further queue reads only when the window falls short) ==
+  // The slots this step's hits use are pinned: a bitmap of them, built only
+  // when the queue or a hand supplies victims (never-used slots cannot be
+  // pinned).
+  if (!lru || m > C - fill) {
+    for (int i = tid; i < K; i += kSelThreads) {
+      const int32_t e = sh.selslot[i];   // a hit's slot, C + ring entry, or -1
+      if (e >= 0 && e < C) atomicOr(&sh.touched[e >> 5], 1u << (e & 31));
+    }
+    __syncthreads();
+  }
   int32_t* vold = reinterpret_cast<int32_t*>(sh.hist);   // position each victim held
   int32_t* vic = sh.vic;
   int n_new = 0;
@@ -732,12 +921,22 @@ hipError_t launch_select(const DevState& d, const StepArgs& a, const float* scor
                          uint64_t stride, int64_t max_len, int32_t* d_sel, int32_t* d_trace,
                          hipStream_t st, StageEv ev) {
   const int64_t seg_len = scan_seg_len(max_len, d.max_segs);
-  if (d.Q == 1)
-    hipExtLaunchKernelGGL(k_select<false>, dim3(d.S * d.G), dim3(kSelThreads), 0, st, ev.start,
-                          ev.stop, 0, d, a, scores, stride, seg_len, d_sel, d_trace);
-  else
-    hipExtLaunchKernelGGL(k_select<true>, dim3(d.S * d.G * d.Q), dim3(kSelThreads), 0, st,
-                          ev.start, ev.stop, 0, d, a, scores, stride, seg_len, d_sel, d_trace);
+  // 4 entries per thread hold up to 4,096 entries: top-K plus the window's
+  // other keys for K up to 3,072 in practice (a larger count takes the slow
+  // path, exact as well)
+  const bool small = d.K <= 3072;
+  // grid (units per session, sessions)
+  auto go = [&](auto kern) {
+    hipExtLaunchKernelGGL(kern, dim3(d.G * d.Q, d.S), dim3(kSelThreads), 0, st, ev.start, ev.stop,
+                          0, d, a, scores, stride, seg_len, d_sel, d_trace);
+  };
+  if (d.Q == 1) {
+    if (small) go(k_select<false, 4>);
+    else go(k_select<false, 8>);
+  } else {
+    if (small) go(k_select<true, 4>);
+    else go(k_select<true, 8>);
+  }
   return hipGetLastError();
 }
 
