@@ -144,16 +144,6 @@ __device__ __forceinline__ void run_rows(const RowJob<kPasses>& j, int item) {
   }
 }
 
-// n / D for 0 <= n < 2^16 by a multiply: m = ceil(2^32 / D), 0 meaning D = 1.
-// Exact because n * (m * D - 2^32) < 2^16 * D <= 2^32 for D < 2^16.
-__device__ __forceinline__ int div_by(int n, uint32_t m) {
-  return m ? (int)__umulhi((uint32_t)n, m) : n;
-}
-
-__host__ __forceinline__ uint32_t div_magic(uint32_t D) {
-  return D == 1 ? 0u : (uint32_t)(((1ull << 32) + D - 1) / D);
-}
-
 __device__ __forceinline__ int layers_in_group(const DevState& d, int g) {
   const int n = d.L - g * d.R;
   return n < d.R ? n : d.R;

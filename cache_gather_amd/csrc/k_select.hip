@@ -474,6 +474,26 @@ __global__ __launch_bounds__(kSelThreads) void k_select(DevState d, StepArgs a,
     });
     __syncthreads();
   }
+  // ==== reads, round 3: the prefetched queue entries' state (consumed by the
+  // victims), issued once the queue window has arrived, so the reads overlap
+  // the cut ==================================================================
+  int qlu[kQWin], qsp[kQWin];
+#pragma unroll
+  for (int k = 0; k < kQWin; ++k) {
+    qlu[k] = (int)0x80000000;
+    qsp[k] = -1;
+  }
+  if (q_pf) {
+#pragma unroll
+    for (int k = 0; k < kQWin; ++k) {
+      const int j = qj0 + k;
+      if (j >= qh && j < qe && qent[k].x >= 0 && qent[k].x < C) {
+        qlu[k] = last_use[qent[k].x];
+        qsp[k] = slot2pos[qent[k].x];
+      }
+    }
+  }
+
   int idx22;
   find_digit(sh.hist, kBins1, r, true, sh, idx22, beyond);
   r -= beyond;   // winners to take among the entries of the prefix, >= 1
@@ -555,25 +575,6 @@ __global__ __launch_bounds__(kSelThreads) void k_select(DevState d, StepArgs a,
 
   // the next step's window: this cut's 16-bit prefix +- kWinHalf
   const int nlo = max((int)(T >> 16) - kWinHalf, 0), nhi = min((int)(T >> 16) + kWinHalf, 65535);
-
-  // ==== reads, round 3: the prefetched queue entries' state (consumed by the
-  // victims) ==================================================================
-  int qlu[kQWin], qsp[kQWin];
-#pragma unroll
-  for (int k = 0; k < kQWin; ++k) {
-    qlu[k] = (int)0x80000000;
-    qsp[k] = -1;
-  }
-  if (q_pf) {
-#pragma unroll
-    for (int k = 0; k < kQWin; ++k) {
-      const int j = qj0 + k;
-      if (j >= qh && j < qe && qent[k].x >= 0 && qent[k].x < C) {
-        qlu[k] = last_use[qent[k].x];
-        qsp[k] = slot2pos[qent[k].x];
-      }
-    }
-  }
 
   // ==== winners in position order, hits, misses (LDS) ========================
   // one block scan ranks winners and misses (two 16-bit fields of one value)

@@ -111,37 +111,51 @@ __device__ __forceinline__ int block_incl_scan256(int v, int* wtot) {
 
 // CHUNK scores per pass (2,048: two groups of four per thread; 4,096 would be
 // four); `tiles` chunks per workgroup (its segment).
+// The workgroup is latency-bound: its first tile's scores are requested
+// before anything else is known — their addresses need only the grid
+// position, the score pointer and the stride (the loads are bounded by the
+// row's stride, as the caller's array is [units][stride], and masked by the
+// history length afterwards) — and the unit's counter line comes in the same
+// round as a vector load (lane i holds word i mod 16).  m_gq = div_magic(G Q)
+// gives the session without a division.
 template <bool VEC, int CHUNK>
 __global__ __launch_bounds__(kScanThreads) void k_topk_scan(DevState d, StepArgs a,
                                                             const float* __restrict__ scores,
-                                                            uint64_t stride, int tiles) {
+                                                            uint64_t stride, int tiles,
+                                                            uint32_t m_gq) {
   constexpr int kGroups = CHUNK / (4 * kScanThreads);   // 2 or 4
   static_assert(kGroups == 2 || kGroups == 4, "chunk of 2,048 or 4,096");
   __shared__ int wtot[3][kScanThreads / 64];
   const int su = blockIdx.y;  // selection unit (s, g, q)
-  const int64_t H = a.hist_len[su / (d.G * d.Q)];
-  const int64_t seg_len = (int64_t)CHUNK * tiles;
-  const int64_t seg0 = (int64_t)blockIdx.x * seg_len;
-  if (seg0 >= H) return;
   const int tid = threadIdx.x;
+  const int64_t seg_len = (int64_t)CHUNK * tiles;
+  const int64_t seg0 = (int64_t)blockIdx.x * seg_len;   // < max history <= stride
+  const float* row = scores + (uint64_t)su * stride;
+  float x[4 * kGroups];
+  load_chunk<VEC, kGroups>(row + seg0, (int)min((int64_t)CHUNK, (int64_t)stride - seg0), x);
+  static_assert(kCnt <= 16, "counters read from lanes 0-15");
+  const int cword = d.cnt[(size_t)su * kCntStride + (tid & 15)];
+  const int session = div_by(su, m_gq);
+  const int64_t H = a.hist_len[session];
+  if (seg0 >= H) return;
 
   // predicted cut window, in top-16-bit key units (none yet: every key)
   uint32_t b_lo, b_hi;
-  cut_window(d.cnt[su * kCntStride + kCntWinLo], d.cnt[su * kCntStride + kCntWinHi], b_lo, b_hi);
+  cut_window(__builtin_amdgcn_readlane(cword, kCntWinLo), __builtin_amdgcn_readlane(cword, kCntWinHi),
+             b_lo, b_hi);
   Ent* out = d.cand + (size_t)su * d.hcap + seg0;
   // one query row: each entry's slot, looked up here by the many scan
   // workgroups rather than one per unit later (the step's slot map is that of
   // the previous step until its select kernel has run)
   const bool lookup = d.Q == 1;
   const int32_t* pos2slot = d.pos2slot + (size_t)su * d.hcap;
-  const uint32_t ring_lo = a.ring_lo[su / (d.G * d.Q)];
+  const uint32_t ring_lo = a.ring_lo[session];
   int run = 0, n_above = 0;   // entries of the segment so far, of which above the window
   for (int tile = 0; tile < tiles; ++tile) {
     const int64_t base = seg0 + (int64_t)tile * CHUNK;
     if (base >= H) break;
     const int n = (int)(H - base < CHUNK ? H - base : CHUNK);
-    float x[4 * kGroups];
-    load_chunk<VEC, kGroups>(scores + (uint64_t)su * stride + base, n, x);
+    if (tile > 0) load_chunk<VEC, kGroups>(row + base, n, x);
     uint32_t key[4 * kGroups];
     uint32_t ent = 0;   // bit 4j + c: element c of group j is an entry
     int cj[4] = {0, 0, 0, 0}, na = 0;
@@ -292,12 +306,13 @@ hipError_t launch_topk_scan(const DevState& d, const StepArgs& a, const float* s
   const int64_t seg_len = scan_seg_len(max_len, d.max_segs);
   const int tiles = (int)(seg_len / kScanChunk);
   dim3 grid((unsigned)((max_len + seg_len - 1) / seg_len), d.S * d.G * d.Q);
+  const uint32_t m_gq = div_magic((uint32_t)(d.G * d.Q));
   if (vec4)
     hipExtLaunchKernelGGL((k_topk_scan<true, kScanChunk>), grid, dim3(kScanThreads), 0, st, ev.start,
-                          ev.stop, 0, d, a, scores, stride, tiles);
+                          ev.stop, 0, d, a, scores, stride, tiles, m_gq);
   else
     hipExtLaunchKernelGGL((k_topk_scan<false, kScanChunk>), grid, dim3(kScanThreads), 0, st, ev.start,
-                          ev.stop, 0, d, a, scores, stride, tiles);
+                          ev.stop, 0, d, a, scores, stride, tiles, m_gq);
   return hipGetLastError();
 }
 
