@@ -531,7 +531,9 @@ __global__ __launch_bounds__(kSelThreads) void k_select(DevState d, StepArgs a,
   } else {
     // many entries share the prefix (ties, flat scores): the last 10 key bits
     // by histogram, then, if the cut falls inside a run of equal keys, the
-    // r-th smallest position among them (digits of 11, 10, 10 bits)
+    // r-th smallest position among them (digits of 11, 10, 10 bits).  Every
+    // thread has read n22 from the histogram before it is cleared.
+    __syncthreads();
     clear_hist(sh, 1024);
     each([&](uint32_t kk, int32_t) {
       if ((kk >> 10) == pre22) atomicAdd(&sh.hist[kk & 1023], 1u);
