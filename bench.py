@@ -14,11 +14,12 @@ nearly lossless result").  Inputs are seeded synthetic data
 One step = one hc_step call = the whole path: top-K scan and cut, lookup, LRU,
 host->HBM miss fetch, gather + dequant.  W warmup steps (the first is the cold
 step that fills the caches) are followed by exactly K timed steps.  The steps
-run twice, each time on a fresh context over the same inputs: the first pass
-has nothing but the steps inside its timed region and gives `value` and
-`ms_per_step`; the second brackets every kernel of the same timed steps with
-HIP events (a few microseconds each) and gives the per-kernel times behind
-`stage_us` and `roofline`.
+run three times, each time on a fresh context over the same inputs: the first
+pass has nothing but the steps inside its timed region and gives `value` and
+`ms_per_step`; the second attaches HIP events to each stage's first and last
+kernel dispatch and gives the per-kernel times behind `stage_us` and
+`roofline`; the third, untimed, writes the trace, from which the miss counts
+and the gather's own counts of the rows it moved come.
 
 Prints one JSON line on stdout.  `roofline` is for the kernel that takes the
 most time per step; `cpu_baseline` times the CPU oracle on a short prefix of
@@ -337,13 +338,15 @@ def main():
             d_q[t].copy_(torch.from_numpy(W.queries(wl, t, args.attend, Q).view(np.int16)))
         att = {"heads": args.attend, "scale": 1.0 / math.sqrt(576.0), "q": d_q}
 
-    def run_pass(kernel_events, variant=None):
+    def run_pass(kernel_events, variant=None, with_trace=False):
         """A fresh context over the same inputs: cold step, warmup, then the
         timed steps.  With kernel_events, each stage of the timed steps carries
         a pair of HIP events attached to its first and last dispatch (the
-        kernels' own begin and end), and every step writes its trace (a
-        debugging output of the ABI, from which the miss counts come); the pass
-        that produces `value` has neither."""
+        kernels' own begin and end).  With with_trace, every step writes its
+        trace (a debugging output of the ABI, from which the miss counts and
+        the gather's own movement counts come; the counting adds atomics to
+        the gather, so no timed pass writes one).  The pass that produces
+        `value` has neither."""
         cache = hc.HotCache(S, L, wl.layers_per_select, wl.cache_slots, K, wl.hcap, 0,
                             ring_rows=args.ring,
                             copyback_rows=args.copyback_rows if args.ring else 0, queries=Q)
@@ -357,7 +360,7 @@ def main():
                     np.copyto(h, rows[s][l])
         out, sel, _ = cache.alloc_outputs()
         trace = (torch.empty((total, U, hc.trace_ints(Q * K)), dtype=torch.int32, device=dev)
-                 if kernel_events else None)
+                 if with_trace else None)
         append_ev = ([(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                       for _ in range(total)] if args.ring and kernel_events else None)
 
@@ -443,27 +446,32 @@ def main():
         return
     timed = run_pass(False)
     kernels_pass = run_pass(True)
+    trace_pass = run_pass(False, with_trace=True)
     elapsed = timed["elapsed"]
     cold_ms, cold_stage_ms = timed["cold_ms"], timed["cold_stage_ms"]
     stage_avg = kernels_pass["stage_avg"]
     step_kernel_us = kernels_pass["step_kernel_us"]
-    # both passes ran the same steps on fresh contexts: same last selection and output
-    if not (torch.equal(timed["last_sel"], kernels_pass["last_sel"])
-            and torch.equal(timed["last_out"], kernels_pass["last_out"])):
-        raise SystemExit("the two passes disagree")
-    del timed["last_out"], kernels_pass["last_out"]
+    # the passes ran the same steps on fresh contexts: same last selection and output
+    for other in (kernels_pass, trace_pass):
+        if not (torch.equal(timed["last_sel"], other["last_sel"])
+                and torch.equal(timed["last_out"], other["last_out"])):
+            raise SystemExit("the passes disagree")
+    del timed["last_out"], kernels_pass["last_out"], trace_pass["last_out"]
 
     ms_per_step = elapsed * 1e3 / args.steps
     rows_per_step = S * L * Q * K       # every query row's K rows of every layer
     value = rows_per_step / (ms_per_step / 1e3)
 
     # misses per step from the trace (n_miss of each unit x layers of its group)
-    tr = kernels_pass["trace"]
+    tr = trace_pass["trace"]
     layers_of_group = np.array([min(wl.layers_per_select, L - g * wl.layers_per_select)
                                 for g in range(wl.n_groups)] * S)
     miss_rows = (tr[:, :, 1] * layers_of_group[None, :]).sum(axis=1)   # per step
     timed_miss_rows = miss_rows[args.warmup:]
     fetch_bytes = float(timed_miss_rows.mean()) * ROW
+    # the rows as the gather's own lanes counted them while moving them (trace
+    # fields 4-7: read from host RAM, read from HBM, slot fills, output rows)
+    moved = tr[args.warmup:, :, 4:8].sum(axis=1).astype(np.float64).mean(axis=0)
     gather_bytes = float(rows_per_step) * (ROW + OUT_ROW)
     hist_len_mean = float(np.mean([wl.hist0 + t for t in range(args.warmup, total)]))
     scan_bytes = U * hist_len_mean * 4   # one fp32 read per position per pass
@@ -539,6 +547,10 @@ def main():
         "gather_hbm_gbs": roofline("gather")["achieved"],
         "fetch_pcie_gbs": roofline("fetch")["achieved"],
         "miss_rows_per_step": round(float(timed_miss_rows.mean()), 1),
+        "moved_per_step_counted": {"host_read_bytes": round(moved[0] * ROW, 1),
+                                   "hbm_read_rows": round(moved[1], 1),
+                                   "slot_fill_rows": round(moved[2], 1),
+                                   "output_rows": round(moved[3], 1)},
         "step_kernel_us": {"median": round(float(np.median(step_kernel_us)), 2),
                            "p99": round(float(np.percentile(step_kernel_us, 99)), 2),
                            "max": round(float(step_kernel_us.max()), 2),

@@ -514,7 +514,7 @@ hc_status hc_step(hc_ctx* c, void* stream, const float* d_scores, uint64_t score
 #ifdef HC_TEST_HOOKS
   if (e == hipSuccess && c->test_poison) e = launch_poison(d, st);
 #endif
-  if (e == hipSuccess) e = launch_gather(d, d_out, a.t, st, ev[HC_STAGE_GATHER]);
+  if (e == hipSuccess) e = launch_gather(d, d_out, a.t, d_trace, st, ev[HC_STAGE_GATHER]);
   if (e == hipSuccess) e = hipEventRecord(c->done, st);
   c->enqueued = true;
 #ifdef HC_TEST_HOOKS

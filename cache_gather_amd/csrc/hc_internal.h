@@ -250,9 +250,11 @@ hipError_t launch_round(const DevState& d, const StepArgs& a, const int32_t* d_s
 // d_out == nullptr: only the missing rows are fetched into their slots.  With
 // one query row the launch also carries one bookkeeping workgroup per unit:
 // last-use stamps, the (miss, victim) pairs applied to the slot maps, and the
-// LRU queue's new entries for step t.
-hipError_t launch_gather(const DevState& d, uint16_t* d_out, int32_t t, hipStream_t st,
-                         StageEv ev = {});
+// LRU queue's new entries for step t.  d_trace (or nullptr): the step's trace,
+// whose movement counts (rows read from host RAM and from HBM, slot fills,
+// output rows) the gather adds after the select has zeroed them.
+hipError_t launch_gather(const DevState& d, uint16_t* d_out, int32_t t, int32_t* d_trace,
+                         hipStream_t st, StageEv ev = {});
 #ifdef HC_TEST_HOOKS
 // Test build: a sentinel over every victim slot before the gather fills it.
 hipError_t launch_poison(const DevState& d, hipStream_t st);

@@ -317,7 +317,8 @@ __global__ __launch_bounds__(kGatherThreads) void k_gather(DevState d,
                                                            uint16_t* __restrict__ out,
                                                            int32_t t, int bk_rows,
                                                            int miss_rows, int few_hits_above,
-                                                           uint32_t m_q, uint32_t m_l, uint32_t m_r) {
+                                                           uint32_t m_q, uint32_t m_l, uint32_t m_r,
+                                                           int32_t* __restrict__ trace) {
   // dynamic LDS: [S*G + 1] miss rows (all layers) before unit u, or the
   // bookkeeping's touched-slot bitmap
   extern __shared__ int32_t pref[];
@@ -385,6 +386,12 @@ __global__ __launch_bounds__(kGatherThreads) void k_gather(DevState d,
       j.fill[0] = d.hot + ((size_t)sl * d.C + d.victim[uk]) * kSlotStride;
       j.dst[0] = out ? out_b + ((size_t)sl * QK + d.miss_idx[uk]) * out_row_bytes : nullptr;
       run_rows(j, item);
+      if (trace && item == 0) {   // the unit's movement counts (a trace was requested)
+        int32_t* tu = trace + (size_t)u * HC_TRACE_INTS(QK);
+        atomicAdd(&tu[4], 1);     // read from host RAM
+        atomicAdd(&tu[6], 1);     // written into its victim slot
+        if (out) atomicAdd(&tu[7], 1);
+      }
     }
     return;
   }
@@ -398,6 +405,7 @@ __global__ __launch_bounds__(kGatherThreads) void k_gather(DevState d,
   uint8_t* orow = out_b + (size_t)hr * d.K * out_row_bytes;
   const int i0 = blockIdx.x * kRowsPerRound + lrow;
   RowJob<kHitPasses> j;
+  int n_host = 0, n_hbm = 0;   // this thread's rows by source (item 0 of each row counts)
 #pragma unroll
   for (int p = 0; p < kHitPasses; ++p) {
     const int i = i0 + p * kRowsPerPass;
@@ -413,8 +421,27 @@ __global__ __launch_bounds__(kGatherThreads) void k_gather(DevState d,
     else                                   // another query's row of a miss: host RAM
       j.src[p] = to_global(d.host[sl] + (size_t)(-(int64_t)enc - d.C - 1) * kRow);
     j.dst[p] = orow + (size_t)i * out_row_bytes;
+    n_host += enc < -d.C;
+    n_hbm += enc >= 0;
   }
   run_rows(j, item);
+  if (trace) {
+    // the unit's movement counts (a trace was requested): this workgroup's
+    // rows by source, one atomic add per count
+    if (threadIdx.x == 0) wsum[0] = wsum[1] = 0;
+    __syncthreads();
+    if (item == 0) {
+      if (n_host) atomicAdd(&wsum[0], n_host);
+      if (n_hbm) atomicAdd(&wsum[1], n_hbm);
+    }
+    __syncthreads();
+    if (threadIdx.x == 0 && wsum[0] + wsum[1] > 0) {
+      int32_t* tu = trace + (size_t)(s * d.G + div_by(l, m_r)) * HC_TRACE_INTS(d.Q * d.K);
+      if (wsum[0]) atomicAdd(&tu[4], wsum[0]);
+      if (wsum[1]) atomicAdd(&tu[5], wsum[1]);
+      atomicAdd(&tu[7], wsum[0] + wsum[1]);
+    }
+  }
 }
 
 #ifdef HC_TEST_HOOKS
@@ -443,8 +470,8 @@ hipError_t launch_poison(const DevState& d, hipStream_t st) {
 }
 #endif
 
-hipError_t launch_gather(const DevState& d, uint16_t* d_out, int32_t t, hipStream_t st,
-                         StageEv ev) {
+hipError_t launch_gather(const DevState& d, uint16_t* d_out, int32_t t, int32_t* d_trace,
+                         hipStream_t st, StageEv ev) {
   // grid rows [0, miss_rows): the miss workgroups, dispatched first (their
   // PCIe reads have the longest latency); then bk_rows rows holding one
   // bookkeeping workgroup per unit (one query row per round; k_round does its
@@ -463,7 +490,8 @@ hipError_t launch_gather(const DevState& d, uint16_t* d_out, int32_t t, hipStrea
   // grid rows stay below 2^16, as div_by requires: S * L * Q <= 60,000 is checked at creation
   hipExtLaunchKernelGGL(k_gather, dim3(gx, rows), dim3(kGatherThreads), (uint32_t)lds, st, ev.start,
                         ev.stop, 0, d, d_out, t, bk_rows, miss_rows, few_hits_above,
-                        div_magic((uint32_t)d.Q), div_magic((uint32_t)d.L), div_magic((uint32_t)d.R));
+                        div_magic((uint32_t)d.Q), div_magic((uint32_t)d.L), div_magic((uint32_t)d.R),
+                        d_trace);
   return hipGetLastError();
 }
 

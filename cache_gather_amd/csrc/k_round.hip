@@ -268,6 +268,7 @@ __global__ __launch_bounds__(kSelThreads) void k_round(DevState d, StepArgs a,
       tr[1] = m;
       tr[2] = sh.n_evict;
       tr[3] = n_ring;
+      tr[4] = tr[5] = tr[6] = tr[7] = 0;   // the gather's movement counts
     }
   }
   if (tid == 0) d.cnt[(size_t)u * Q * kCntStride + kCntMiss] = m;

@@ -722,6 +722,7 @@ __global__ __launch_bounds__(kSelThreads) void k_select(DevState d, StepArgs a,
           tr[1] = m;
           tr[2] = 0;
           tr[3] = n_ring;
+          tr[4] = tr[5] = tr[6] = tr[7] = 0;   // the gather's movement counts
         }
         cnt[kCntFill] = fill + m;
         cnt[kCntMiss] = m;
@@ -909,6 +910,7 @@ __global__ __launch_bounds__(kSelThreads) void k_select(DevState d, StepArgs a,
       tr[1] = m;
       tr[2] = sh.bcast[7];
       tr[3] = n_ring;
+      tr[4] = tr[5] = tr[6] = tr[7] = 0;   // the gather's movement counts
     }
     if (lru) {
       cnt[kCntQHead] = sh.bcast[6] + 1;   // past the last victim; the gather appends at the tail

@@ -22,7 +22,7 @@ HEADER = os.path.join(ROOT, "include", "hc.h")
 ROW_BYTES = 656
 OUT_ELEMS = 576
 ATTEND_STATIC_BYTES = 32 << 20   # HC_ATTEND_STATIC_BYTES
-TRACE_HEADER = 4
+TRACE_HEADER = 8
 NUM_STAGES = 3
 STAGES = ("topk_scan", "select", "gather")
 STATUS = {0: "HC_OK", -1: "HC_E_INVAL", -2: "HC_E_NOMEM", -3: "HC_E_HIP", -4: "HC_E_STATE",

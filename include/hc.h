@@ -109,13 +109,23 @@ extern "C" {
  * in ascending position order, below written with K meaning Q * K).  Layout:
  *   [0] n_hit   [1] n_miss   [2] n_evict (victims whose slot held a position)
  *   [3] n_ring  (selected rows read from the recent ring)
- *   [4 + 0K .. 4 + 1K)  slot of union entry j after the step (ascending
+ *   [4] rows the gather read from pinned host RAM over PCIe (656 B each),
+ *       counted by the lanes that read them: each missing row of each layer
+ *       of the group, and with several query rows each further query row of
+ *       a missing position
+ *   [5] rows the gather read from HBM (hot slots or the recent ring)
+ *   [6] slot fills written (missing rows x layers)
+ *   [7] output rows written (Q * K x layers; 0 without an output buffer)
+ *   [8 + 0K .. 8 + 1K)  slot of union entry j after the step (ascending
  *                       position); C + p % ring_rows for a row read from the
  *                       ring; -1 past the N entries
- *   [4 + 1K .. 4 + 2K)  miss_pos: missing positions, ascending; -1 past n_miss
- *   [4 + 2K .. 4 + 3K)  victim slot paired with miss i; -1 past n_miss
- *   [4 + 3K .. 4 + 4K)  position evicted from that slot, -1 if it was empty   */
-#define HC_TRACE_HEADER  4
+ *   [8 + 1K .. 8 + 2K)  miss_pos: missing positions, ascending; -1 past n_miss
+ *   [8 + 2K .. 8 + 3K)  victim slot paired with miss i; -1 past n_miss
+ *   [8 + 3K .. 8 + 4K)  position evicted from that slot, -1 if it was empty
+ * The counts [4]-[7] make the data movement itself observable (page "Making
+ * KV offload correct", section "What I tested and what each check could
+ * show"); requesting a trace costs a few atomic adds per workgroup. */
+#define HC_TRACE_HEADER  8
 #define HC_TRACE_INTS(k) (HC_TRACE_HEADER + 4 * (k))
 
 /* Kernel stages timed by hc_profile_read, in launch order. */

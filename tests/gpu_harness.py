@@ -94,6 +94,21 @@ class Pair:
                 assert tr[0] == info["n_hit"] and tr[1] == info["n_miss"], msg
                 assert tr[2] == info["n_evict"] and tr[3] == info["n_ring"], msg
                 self.evictions += int(info["n_evict"])
+                # the data movement the gather's lanes counted: each missing row
+                # read from host RAM once per layer and written into its slot;
+                # further query rows of a missing position read host RAM again;
+                # every other selected row comes from HBM (slot or ring)
+                nl = min(wl.layers_per_select, wl.n_layers - gi * wl.layers_per_select)
+                n_miss = int(info["n_miss"])
+                dup = 0
+                if self.Q > 1:
+                    sel_u = np.asarray(g["sel"]).reshape(wl.n_units, K)[u]
+                    dup = int(np.isin(sel_u, np.asarray(info["miss_pos"][:n_miss])).sum()) - n_miss
+                gathered = not self.fill_only
+                assert tr[4] == (n_miss + (dup if gathered else 0)) * nl, msg + " host rows"
+                assert tr[5] == ((K - n_miss - dup) * nl if gathered else 0), msg + " HBM rows"
+                assert tr[6] == n_miss * nl, msg + " slot fills"
+                assert tr[7] == (K * nl if gathered else 0), msg + " output rows"
                 base = hc.TRACE_HEADER
                 np.testing.assert_array_equal(tr[base:base + K], info["slot"], err_msg=msg)
                 np.testing.assert_array_equal(tr[base + K:base + 2 * K], info["miss_pos"],

@@ -143,10 +143,14 @@ def test_full_length_properties(name):
             tr = g_tr[s]
             n_hit, n_miss = int(tr[0]), int(tr[1])
             assert n_hit + n_miss == K
-            slots = tr[4:4 + K]
-            miss = tr[4 + K:4 + K + n_miss]
-            vic = tr[4 + 2 * K:4 + 2 * K + n_miss]
-            ev = tr[4 + 3 * K:4 + 3 * K + n_miss]
+            # the gather's own counts: one host read and one slot fill per
+            # missing row, every other row from HBM, K output rows (one layer)
+            assert (tr[4], tr[5], tr[6], tr[7]) == (n_miss, n_hit, n_miss, K)
+            b = hc.TRACE_HEADER
+            slots = tr[b:b + K]
+            miss = tr[b + K:b + K + n_miss]
+            vic = tr[b + 2 * K:b + 2 * K + n_miss]
+            ev = tr[b + 3 * K:b + 3 * K + n_miss]
             # misses: ascending, exactly the selected positions not resident before
             was = np.array([p in resident[s] for p in sv])
             np.testing.assert_array_equal(miss, sv[~was])
