@@ -180,10 +180,16 @@ typedef struct hc_config {
 typedef struct hc_ctx hc_ctx;
 
 /* Exact device-workspace size in bytes for cfg (slot maps, LRU order, score
- * scan scratch, and the S*L*C hot rows).  HC_E_INVAL for an invalid cfg. */
+ * scan entries, and the S*L*C hot rows).  HC_E_INVAL for an invalid cfg.
+ * Exact sizes rather than pooled over-reservation follow page "From 1M Total
+ * to 15+ x 1M Contexts: GLM-5.3 KV Cache Offloading", section "Ten sessions
+ * exposed a physical-allocation problem" (memory is sized to what a context
+ * actually needs). */
 hc_status hc_workspace_bytes(const hc_config* cfg, uint64_t* bytes);
 
-/* Creates a context on cfg->device.  dev_workspace: caller-owned device memory
+/* Creates a context on cfg->device (page "Making KV offload correct", section
+ * "A grouped allocation is a transaction": the context's allocations succeed
+ * or fail together).  dev_workspace: caller-owned device memory
  * of at least hc_workspace_bytes bytes, 256-B aligned, that the caller keeps
  * alive and untouched until hc_destroy returns.  The library allocates the
  * pinned host row store itself: S*L buffers of Hcap*656 B (hipHostMalloc,
@@ -312,7 +318,10 @@ hc_status hc_profile_read(hc_ctx* ctx, double* stage_ms, double* per_step,
 hc_status hc_steps_done(const hc_ctx* ctx, uint64_t* n);
 
 /* Waits for every step the context enqueued, then frees the pinned host store
- * and the context.  The caller's workspace is not freed.  NULL-safe. */
+ * and the context (page "Making KV offload correct", section "Response
+ * completion is not copy completion": memory a queued copy still uses is not
+ * released before that copy has finished).  The caller's workspace is not
+ * freed.  NULL-safe. */
 hc_status hc_destroy(hc_ctx* ctx);
 
 const char* hc_status_str(hc_status s);
