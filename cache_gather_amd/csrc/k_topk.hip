@@ -52,22 +52,28 @@ constexpr int kScanChunk = 2048;   // positions per scan pass of a workgroup
 // group j of thread tid at chunk positions 4 * (tid + 256 j) + [0, 4), so that
 // the order (j, thread, element) is the position order.  Invalid positions
 // (>= n) read as 0 and are masked by the caller.
+// The loads are non-temporal: a step reads its scores once, and a normal load
+// would allocate them in the 256 MB Infinity Cache, displacing what the
+// step's later kernels read again (the hot slots the gather reads, the maps
+// and queues of the select kernel).
 template <bool VEC, int kGroups>
 __device__ __forceinline__ void load_chunk(const float* src, int n, float (&x)[4 * kGroups]) {
+  typedef float f32x4 __attribute__((ext_vector_type(4)));
   const int tid = threadIdx.x;
 #pragma unroll
   for (int j = 0; j < kGroups; ++j) {
     const int q = tid + kScanThreads * j;
     if (VEC) {
-      float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (4 * q < n) v = reinterpret_cast<const float4*>(src)[q];
+      f32x4 v = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (4 * q < n) v = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(src) + q);
       x[4 * j + 0] = v.x;
       x[4 * j + 1] = v.y;
       x[4 * j + 2] = v.z;
       x[4 * j + 3] = v.w;
     } else {
 #pragma unroll
-      for (int c = 0; c < 4; ++c) x[4 * j + c] = 4 * q + c < n ? src[4 * q + c] : 0.f;
+      for (int c = 0; c < 4; ++c)
+        x[4 * j + c] = 4 * q + c < n ? __builtin_nontemporal_load(src + 4 * q + c) : 0.f;
     }
   }
 }
@@ -117,12 +123,13 @@ __device__ __forceinline__ int block_incl_scan256(int v, int* wtot) {
 // row's stride, as the caller's array is [units][stride], and masked by the
 // history length afterwards) — and the unit's counter line comes in the same
 // round as a vector load (lane i holds word i mod 16).  m_gq = div_magic(G Q)
-// gives the session without a division.
+// gives the session without a division.  The compiler is held to eight waves
+// per SIMD (it spills scalar registers to vector lanes to stay within 96), so
+// that 2,048 workgroups are resident at once rather than 1,792.
 template <bool VEC, int CHUNK>
-__global__ __launch_bounds__(kScanThreads) void k_topk_scan(DevState d, StepArgs a,
-                                                            const float* __restrict__ scores,
-                                                            uint64_t stride, int tiles,
-                                                            uint32_t m_gq) {
+__global__ __launch_bounds__(kScanThreads) __attribute__((amdgpu_waves_per_eu(8, 8)))
+void k_topk_scan(DevState d, StepArgs a, const float* __restrict__ scores, uint64_t stride,
+                 int tiles, uint32_t m_gq) {
   constexpr int kGroups = CHUNK / (4 * kScanThreads);   // 2 or 4
   static_assert(kGroups == 2 || kGroups == 4, "chunk of 2,048 or 4,096");
   __shared__ int wtot[3][kScanThreads / 64];

@@ -142,6 +142,31 @@ def test_cut_jumping_between_steps_rescans_exactly():
     _run_custom_scores(wl, mk)
 
 
+@pytest.mark.parametrize("queries", [1, 2])
+def test_many_units_with_flat_and_ordinary_scores(queries):
+    """Sixteen sessions of 264,000 positions: 2,064 scan workgroups per query
+    row, more than the chip holds in one resident round.  The even sessions'
+    scores are flat, so every key lies inside the cut window and the select
+    kernel ranks the whole history as entries; the odd sessions' are
+    ordinary.  Every step stays bit-exact."""
+    S = 16
+    wl = W.Workload("many_units_q%d" % queries, S, 1, 1, 264000, 3, 512, 256, (1.0,) * S,
+                    (1.0,) * S, 17)
+    p = _pair(wl, queries=queries)
+    for t in range(wl.steps):
+        h = wl.hist0 + t
+        sc = np.zeros((wl.n_units * queries, p.stride), np.float32)
+        for uq in range(wl.n_units * queries):
+            if (uq // queries) % 2 == 0:
+                sc[uq, :h] = 0.5
+            else:
+                sc[uq, :h] = np.random.default_rng((t, uq, 3)).standard_normal(h)
+        g, o = p.step(t, scores_np=sc)
+        p.compare(t, g, o)
+    p.compare_state()
+    p.close()
+
+
 def test_dequant_every_int8_with_every_finite_fp16_scale():
     """Rows covering all 256 int8 values against all 63,488 finite fp16 scales,
     gathered 2,048 rows per step through hc_step."""
