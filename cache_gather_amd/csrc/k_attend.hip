@@ -151,10 +151,13 @@ __global__ __launch_bounds__(kAttThreads) void k_attend(DevState d, const uint16
     const int r0 = r_begin + j * kSub;
     const bool vr = r0 + rr < r_end;
     if (SRC == kFromBuffer) {
+      // non-temporal: the buffer is read once, and normal loads would allocate
+      // it in the Infinity Cache over the hot slots the next step reads again
       const uint16_t* base = rows_buf + ((size_t)slq * K + r0 + rr) * HC_OUT_ELEMS + 8 * cc;
 #pragma unroll
       for (int k = 0; k <= kLat; ++k)
-        bv[k] = vr ? *reinterpret_cast<const u32x4*>(base + 64 * k) : u32x4{0u, 0u, 0u, 0u};
+        bv[k] = vr ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(base + 64 * k))
+                   : u32x4{0u, 0u, 0u, 0u};
     } else {
       gbyte* src = to_global(vr ? sh.src[j * kSub + rr] : nullptr);
 #pragma unroll
