@@ -245,7 +245,7 @@ __device__ __forceinline__ void bookkeeping(const DevState& d, int u, int32_t t,
     // owns 64 * kCPer consecutive entries, lane-interleaved so that loads and
     // stores coalesce; ranks inside the wave come from ballots, and the wave
     // totals order the waves.
-    constexpr int kCPer = 8;
+    constexpr int kCPer = 12;   // 3,840 entries per window (at 16 the kernel needs 79 VGPRs)
     constexpr int kW = kGatherThreads / 64;
     const int lane = tid & 63, wv = tid >> 6;
     const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
