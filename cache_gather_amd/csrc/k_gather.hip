@@ -200,13 +200,26 @@ __device__ __forceinline__ void bookkeeping(const DevState& d, int u, int32_t t,
   const int32_t* g_slot = d.sel_slot + (size_t)u * K;
   for (int w = tid; w < nwords; w += kGatherThreads) touched[w] = 0;
   __syncthreads();
-  // hits: stamp; hits and victims: mark
-  for (int i = tid; i < K; i += kGatherThreads) {
-    const int32_t enc = g_slot[i];
-    const int32_t v = enc >= 0 ? (enc < C ? enc : -1) : (enc >= -C ? -enc - 1 : -1);
-    if (v < 0) continue;   // a ring row
-    if (enc >= 0) last_use[v] = t;
-    atomicOr(&touched[v >> 5], 1u << (v & 31));
+  // hits: stamp; hits and victims: mark.  Eight sources per thread are loaded
+  // before any is used (a store between two loads keeps the compiler from
+  // issuing the second before the first returns: seven dependent round
+  // trips for K = 2,048 otherwise, which a compaction would wait for).
+  constexpr int kSPer = 8;
+  for (int i0 = 0; i0 < K; i0 += kGatherThreads * kSPer) {
+    int32_t enc[kSPer];
+#pragma unroll
+    for (int k = 0; k < kSPer; ++k) {
+      const int i = i0 + k * kGatherThreads + tid;
+      enc[k] = i < K ? g_slot[i] : INT32_MIN;   // INT32_MIN: no slot
+    }
+#pragma unroll
+    for (int k = 0; k < kSPer; ++k) {
+      const int32_t e = enc[k];
+      const int32_t v = e >= 0 ? (e < C ? e : -1) : (e >= -C ? -e - 1 : -1);
+      if (v < 0) continue;   // a ring row, a host row, or past K
+      if (e >= 0) last_use[v] = t;
+      atomicOr(&touched[v >> 5], 1u << (v & 31));
+    }
   }
   // (miss, victim) pairs
   const int32_t* g_miss = d.miss_pos + (size_t)u * K;
