@@ -154,6 +154,63 @@ def copy_ceiling(torch, dev):
     return round(2 * n / (ms * 1e-3) / 1e9, 1)
 
 
+def memory_ceilings(torch, dev):
+    """Reference rates of the chip's memory paths, measured with torch's own
+    kernels only (so that they rest on nothing of this package): the plain
+    device copy; a 64 MiB copy after 1 GiB of reads and after 1 GiB of
+    ordinary stores, whose dirty lines its reads must evict from the 256 MB
+    Infinity Cache; a gather of 159,744 random 704-B rows out
+    of a 1.8 GB array (the slot reads of the 78-layer step, without the
+    dequantisation: read and write 704 B per row); and a contiguous 256 MiB
+    copy from pinned host memory.  Medians of 7, kernel time by events."""
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+
+    def timed(prep, fn, reps=7):
+        ts = []
+        for _ in range(reps):
+            prep()
+            ev[0].record()
+            fn()
+            ev[1].record()
+            torch.cuda.synchronize()
+            ts.append(ev[0].elapsed_time(ev[1]) * 1e3)
+        return sorted(ts)[reps // 2]
+
+    out = {"copy_256mib_gbs": copy_ceiling(torch, dev)}
+    flush = torch.ones(1 << 30, dtype=torch.uint8, device=dev)
+    acc = torch.zeros((), dtype=torch.int64, device=dev)
+    src = torch.ones(64 << 20, dtype=torch.uint8, device=dev)
+    dst64 = torch.empty_like(src)
+
+    def after_reads():
+        acc.add_(flush.view(torch.int64).sum())
+
+    def after_stores():
+        flush.fill_(1)
+
+    def copy64():
+        dst64.copy_(src)
+    us_r = timed(after_reads, copy64)
+    us_w = timed(after_stores, copy64)
+    out["copy_64mib_after_reads_us"] = round(us_r, 2)
+    out["copy_64mib_after_stores_us"] = round(us_w, 2)
+    out["copy_64mib_after_reads_gbs"] = round(2 * (64 << 20) / us_r / 1e3, 1)
+    del src, dst64
+    rows = torch.ones((78 * 32768, 704), dtype=torch.uint8, device=dev)
+    g = torch.Generator(device="cpu").manual_seed(7)
+    idx = torch.randint(0, rows.shape[0], (78 * 2048,), generator=g).to(dev)
+    dst = torch.empty((idx.numel(), 704), dtype=torch.uint8, device=dev)
+    us_g = timed(after_reads, lambda: torch.index_select(rows, 0, idx, out=dst))
+    out["row_gather_704b_us"] = round(us_g, 2)
+    out["row_gather_704b_gbs"] = round(2 * 704 * idx.numel() / us_g / 1e3, 1)
+    del rows, dst, flush
+    host = torch.ones(256 << 20, dtype=torch.uint8).pin_memory()
+    dev_buf = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
+    us_h = timed(lambda: None, lambda: dev_buf.copy_(host, non_blocking=True), reps=5)
+    out["host_to_device_256mib_gbs"] = round((256 << 20) / us_h / 1e3, 1)
+    return out
+
+
 def replacement_probe(hc, W, np, torch, reps=10):
     """The page's probe (section "GPU cache management has hazards too"): a
     full hot cache of 32,768 slots whose reference bits are all set, then one
@@ -251,6 +308,10 @@ def main():
                     help="time the page's replacement probe instead: a full 32,768-slot hot "
                          "cache with every reference bit set, then one 2,048-row step with 1%% "
                          "misses, for LRU, circular and clock replacement")
+    ap.add_argument("--ceilings", action="store_true",
+                    help="print reference rates of the memory paths (device copy, a 64 MiB copy "
+                         "after reads / after stores, random 704-B row gather, pinned host to "
+                         "device copy), measured with torch's kernels only, and exit")
     ap.add_argument("--attend", type=int, default=0, metavar="HEADS",
                     help="follow every step with MLA decode attention of HEADS heads over the "
                          "selected rows, once through the bf16 buffer and once fused (the step "
@@ -289,6 +350,10 @@ def main():
 
     if args.replacement_probe:
         print(json.dumps(replacement_probe(hc, W, np, torch)), flush=True)
+        return
+    if args.ceilings:
+        print(json.dumps({"metric": "memory ceilings", "ceilings": memory_ceilings(torch, "cuda:0")}),
+              flush=True)
         return
 
     base = W.ALL[args.workload]
