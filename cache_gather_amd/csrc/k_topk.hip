@@ -124,8 +124,9 @@ __device__ __forceinline__ int block_incl_scan256(int v, int* wtot) {
 // history length afterwards) — and the unit's counter line comes in the same
 // round as a vector load (lane i holds word i mod 16).  m_gq = div_magic(G Q)
 // gives the session without a division.  The compiler is held to eight waves
-// per SIMD (it spills scalar registers to vector lanes to stay within 96), so
-// that 2,048 workgroups are resident at once rather than 1,792.
+// per SIMD (it keeps fewer scalar registers, spilling some to vector lanes):
+// without the bound the kernel's scalar registers allowed seven, so 1,792
+// workgroups were resident at once instead of 2,048.
 template <bool VEC, int CHUNK>
 __global__ __launch_bounds__(kScanThreads) __attribute__((amdgpu_waves_per_eu(8, 8)))
 void k_topk_scan(DevState d, StepArgs a, const float* __restrict__ scores, uint64_t stride,
