@@ -237,6 +237,17 @@ def test_configuration_limits(case):
     p.close()
 
 
+def test_history_beyond_4096_scan_segments():
+    """8,400,000 positions: more than 4,096 chunks of 2,048, so the scan gives
+    each workgroup two chunks (a segment of 4,096 positions, 2,051 segments)
+    and the select kernel reads the longer segments.  One session and layer,
+    small K and C; every step bit-exact, then the end state."""
+    wl = W.Workload("long_8m", 1, 1, 1, 8400000, 3, 4096, 1024, (1.0,), (1.0,), 4245)
+    p = _pair(wl)
+    p.run()
+    p.close()
+
+
 def test_largest_recent_ring():
     """HC_MAX_RING_ROWS ring rows per layer with copyback batches of 8: every
     appended row stays in the ring, the copybacks still reach host RAM."""
