@@ -31,7 +31,7 @@ namespace {
 constexpr uint64_t kAlign = 256;
 
 struct Layout {
-  uint64_t pos2slot, slot2pos, last_use, oq, cnt, seg, cand, sel_slot, miss_pos,
+  uint64_t pos2slot, slot2pos, last_use, oq, qlive, cnt, seg, cand, sel_slot, miss_pos,
       victim, miss_idx, miss_old, host_tab, hot, ring, refbits, total;
 };
 
@@ -89,6 +89,8 @@ bool valid_config(const hc_config* c) {
 }
 
 uint64_t queue_cap(uint64_t C) { return (2 * C + 3) / 4 * 4; }
+// Words of a unit's live-entry bitmap: a bit per queue entry, in 64-bit groups.
+uint64_t qlive_words(uint64_t C) { return (queue_cap(C) + 63) / 64 * 2; }
 
 Layout layout_of(const hc_config* c) {
   const uint64_t S = c->n_sessions, L = c->n_layers;
@@ -106,6 +108,7 @@ Layout layout_of(const hc_config* c) {
   lo.slot2pos = take(U * C * 4);
   lo.last_use = take(U * C * 4);
   lo.oq = take(U * 2 * queue_cap(C) * 8);
+  lo.qlive = take(U * qlive_words(C) * 4);
   lo.cnt = take(SU * kCntStride * 4);
   lo.seg = take(SU * max_segs_of(hcap) * 8);
   lo.cand = take(SU * hcap * sizeof(Ent));
@@ -150,7 +153,8 @@ __global__ void k_init(DevState d, int64_t n_pos, int64_t n_slots) {
   for (int64_t i = i0; i < sel_units * d.K; i += stride) d.sel_slot[i] = 0;
   for (int64_t i = i0; i < sel_units * kCntStride; i += stride) {
     const int64_t f = i % kCntStride;
-    d.cnt[i] = f == kCntWinLo || f == kCntWinHi ? -1 : 0;   // no window; empty LRU queues
+    // no window, no compaction prepared; empty LRU queues
+    d.cnt[i] = f == kCntWinLo || f == kCntWinHi || f == kCntCntStep ? -1 : 0;
   }
   // the first step's cut histograms (see launch_cold_cut)
   if (d.hcap >= kColdMinPositions)
@@ -410,6 +414,8 @@ hc_status hc_create(const hc_config* cfg_in, void* dev_workspace, uint64_t ws_by
   d.last_use = reinterpret_cast<int32_t*>(w + lo.last_use);
   d.oq = reinterpret_cast<int2*>(w + lo.oq);
   d.qcap = (int32_t)queue_cap(cfg->cache_slots);
+  d.qlive = reinterpret_cast<uint32_t*>(w + lo.qlive);
+  d.qlive_words = (int32_t)qlive_words(cfg->cache_slots);
   d.cnt = reinterpret_cast<int32_t*>(w + lo.cnt);
   d.seg = reinterpret_cast<int2*>(w + lo.seg);
   d.max_segs = (int32_t)max_segs_of(cfg->max_positions);

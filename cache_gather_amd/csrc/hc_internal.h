@@ -29,17 +29,31 @@ enum { kErrSelect = 0, kErrLru = 1, kErrRound = 2, kErrKinds = 4 };
 // the first step: every key); kCntMiss and kCntHand (circular / clock hand)
 // are kept at su = u * Q.  kCntQHead / kCntQTail / kCntQBuf: the LRU queue of
 // the unit (at su = u * Q); kCntFill: slots the unit's LRU has filled so far
-// (slots [fill, C) were never used).
+// (slots [fill, C) were never used).  kCntCntStep: the step whose select
+// launch marked the LRU queue's live entries for a compaction (-1: none),
+// carried out by that step's gather launch; kCntCntTail, kCntCntBuf: the
+// queue's tail and buffer then (one query row; see kBkSlices).
 enum {
   kCntMiss = 2, kCntWinLo = 3, kCntHand = 4,
-  kCntQHead = 5, kCntQTail = 6, kCntQBuf = 7, kCntFill = 8, kCntWinHi = 9, kCnt = 10
+  kCntQHead = 5, kCntQTail = 6, kCntQBuf = 7, kCntFill = 8, kCntWinHi = 9, kCnt = 10,
+  kCntCntStep = 16, kCntCntTail = 17, kCntCntBuf = 18
 };
+// LRU queue compaction (one query row): when a step's slots might not fit
+// after the tail, kCountWGs extra workgroups per unit of the select launch
+// mark the queue's live entries in a bitmap, and kBkSlices workgroups per
+// unit of the gather launch each write the survivors of one slice of the
+// queue to their final places, found by counting the bitmap's bits before the
+// slice, without waiting for one another.  Ranges are whole multiples of 64
+// entries, so that each owns whole words of the bitmap.
+constexpr int kCountWGs = 4;
+constexpr int kBkSlices = 16;
 // Half-width of the predicted cut window, in top-16-bit key units: the next
 // step's window is the current cut key's 16-bit prefix +- kWinHalf (about
 // +-0.06 around a cut near 2 or 3, several times the cut's movement between
 // decode steps; a cut that leaves it costs a rescan of the scores).
 constexpr int kWinHalf = 8;
 constexpr int kCntStride = 64;
+static_assert(kCntCntBuf < kCntStride, "the compaction's words fit the counter line");
 
 // One entry of a unit's score scan: the totalOrder key of a score, its
 // position, and (one query row) the slot holding that position at the scan,
@@ -63,6 +77,9 @@ struct DevState {
                        //            over the used slots; an entry is live while
                        //            last_use[slot] == step
   int32_t qcap;        // entries per queue buffer: 2 C rounded up to a multiple of 4
+  uint32_t* qlive;     // [U][qlive_words] LRU, one query row: bit j, entry j of the queue
+                       //            live when the select launch marked it for a compaction
+  int32_t qlive_words; // words per unit: 2 ceil(qcap / 64)
   int32_t* cnt;        // [U*Q][kCntStride] per selection unit; the round's miss count at su = u*Q
   Ent* cand;           // [U*Q][hcap] entries: the scores above or inside the cut
                        //            window, segment s of a step at s * seg_len,

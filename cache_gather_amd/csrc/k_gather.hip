@@ -184,15 +184,27 @@ __device__ __forceinline__ int gather_block_scan(int v, int32_t* wsum, int& tota
 // decisions: stamps the step's slots (hits and victims) with last use t,
 // applies the (miss, victim) pairs to pos2slot / slot2pos (the evicted
 // position leaves the map), and, for LRU, appends the step's slots to the
-// unit's queue in slot order, stamped t, after compacting the queue's live
-// entries into its other buffer when the tail would pass the buffer's end.
-// Nothing here is read by this launch's other workgroups; the next step's
-// kernels come after the launch.  `touched` is LDS of ceil(C / 32) words.
-__device__ __forceinline__ void bookkeeping(const DevState& d, int u, int32_t t, uint32_t* touched,
-                            int32_t* wsum) {
+// unit's queue in slot order, stamped t.  Workgroup p of kBkSlices per unit;
+// p = 0 stamps, maps and appends.  When this step's select launch marked the
+// queue for a compaction (its slots might not fit after the tail), every slice
+// p writes the survivors of its part of the queue — marked live then, and not
+// used by this step — in order, to the other buffer at the place that the
+// marks before the slice give, and fills the rest of its marked places with
+// dead entries (-1, -1: entries this step used, which the queue's readers
+// skip); p = 0 then appends after all of them.  Everything a slice reads to
+// place its survivors was written by the select launch, so the slices never
+// wait for one another.  Otherwise the queue
+// is compacted, if it must be, by p = 0 alone.  Nothing else here is read by
+// this launch's other workgroups; the next step's kernels come after the
+// launch.  `touched` is LDS of ceil(C / 32) words.
+__device__ __forceinline__ void bookkeeping(const DevState& d, int u, int p, int32_t t,
+                                            uint32_t* touched, int32_t* wsum) {
   const int C = d.C, K = d.K, tid = threadIdx.x;
   const int nwords = (C + 31) >> 5;
   int32_t* cnt = d.cnt + (size_t)u * kCntStride;
+  const bool lru = d.policy == HC_REPLACE_LRU;
+  const bool counted = lru && cnt[kCntCntStep] == t;   // a compaction prepared for this step
+  if (p > 0 && !counted) return;
   const int m = min(max(cnt[kCntMiss], 0), K);
   int32_t* pos2slot = d.pos2slot + (size_t)u * d.hcap;
   int32_t* slot2pos = d.slot2pos + (size_t)u * C;
@@ -200,10 +212,9 @@ __device__ __forceinline__ void bookkeeping(const DevState& d, int u, int32_t t,
   const int32_t* g_slot = d.sel_slot + (size_t)u * K;
   for (int w = tid; w < nwords; w += kGatherThreads) touched[w] = 0;
   __syncthreads();
-  // hits: stamp; hits and victims: mark.  Eight sources per thread are loaded
-  // before any is used (a store between two loads keeps the compiler from
-  // issuing the second before the first returns: seven dependent round
-  // trips for K = 2,048 otherwise, which a compaction would wait for).
+  // hits: stamp (slice 0); hits and victims: mark.  Eight sources per thread
+  // are loaded before any is used (a store between two loads keeps the
+  // compiler from issuing the second before the first returns).
   constexpr int kSPer = 8;
   for (int i0 = 0; i0 < K; i0 += kGatherThreads * kSPer) {
     int32_t enc[kSPer];
@@ -217,80 +228,93 @@ __device__ __forceinline__ void bookkeeping(const DevState& d, int u, int32_t t,
       const int32_t e = enc[k];
       const int32_t v = e >= 0 ? (e < C ? e : -1) : (e >= -C ? -e - 1 : -1);
       if (v < 0) continue;   // a ring row, a host row, or past K
-      if (e >= 0) last_use[v] = t;
+      if (e >= 0 && p == 0) last_use[v] = t;
       atomicOr(&touched[v >> 5], 1u << (v & 31));
     }
   }
-  // (miss, victim) pairs
-  const int32_t* g_miss = d.miss_pos + (size_t)u * K;
-  const int32_t* g_vic = d.victim + (size_t)u * K;
-  const int32_t* g_old = d.miss_old + (size_t)u * K;
-  for (int k = tid; k < m; k += kGatherThreads) {
-    const int32_t v = g_vic[k], p = g_miss[k], old = g_old[k];
-    if (v < 0 || v >= C || p < 0 || p >= d.hcap) continue;
-    if (old >= 0 && old < d.hcap) pos2slot[old] = -1;
-    pos2slot[p] = v;
-    slot2pos[v] = p;
-    last_use[v] = t;
+  if (p == 0) {
+    // (miss, victim) pairs
+    const int32_t* g_miss = d.miss_pos + (size_t)u * K;
+    const int32_t* g_vic = d.victim + (size_t)u * K;
+    const int32_t* g_old = d.miss_old + (size_t)u * K;
+    for (int k = tid; k < m; k += kGatherThreads) {
+      const int32_t v = g_vic[k], pp = g_miss[k], old = g_old[k];
+      if (v < 0 || v >= C || pp < 0 || pp >= d.hcap) continue;
+      if (old >= 0 && old < d.hcap) pos2slot[old] = -1;
+      pos2slot[pp] = v;
+      slot2pos[v] = pp;
+      last_use[v] = t;
+    }
   }
   __syncthreads();
-  if (d.policy != HC_REPLACE_LRU) return;
+  if (!lru) return;
 
-  // ---- the step's slots at the queue's tail -----------------------------------
   const int QC = d.qcap;
-  const int qe = min(max(cnt[kCntQTail], 0), QC);
-  const int hn = min(max(cnt[kCntQHead], 0), qe);
-  const int qb = cnt[kCntQBuf] & 1;
-  const int2* q = d.oq + ((size_t)u * 2 + qb) * QC;
+  constexpr int kW = kGatherThreads / 64;
+  const int lane = tid & 63, wv = tid >> 6;
+  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  auto pinned = [&](int v) { return (touched[v >> 5] >> (v & 31)) & 1u; };
+  // the step's slots: this thread's bitmap words, in slot order
   const int g = (nwords + kGatherThreads - 1) / kGatherThreads;   // words per thread
   int c = 0;
   for (int i = 0; i < g; ++i) {
     const int w = tid * g + i;
     if (w < nwords) c += __popc(touched[w]);
   }
-  const int n_touched = gather_block_sum(c, wsum);
-  const bool fits = qe + n_touched <= QC;
-  int2* qw = const_cast<int2*>(fits ? q : d.oq + ((size_t)u * 2 + (qb ^ 1)) * QC);
-  int base = qe;
-  if (!fits) {
-    // survivors: the live entries after the last victim that this step did
-    // not use, in order, to the front of the other buffer.  Wave w of a window
-    // owns 64 * kCPer consecutive entries, lane-interleaved so that loads and
-    // stores coalesce; ranks inside the wave come from ballots, and the wave
-    // totals order the waves.
-    constexpr int kCPer = 12;   // 3,840 entries per window (at 16 the kernel needs 79 VGPRs)
-    constexpr int kW = kGatherThreads / 64;
-    const int lane = tid & 63, wv = tid >> 6;
-    const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-    auto pinned = [&](int v) { return (touched[v >> 5] >> (v & 31)) & 1u; };
+  int2* qw;          // the buffer that receives the step's slots
+  int base, head, buf;
+  if (counted) {
+    // the queue as the select launch marked it (none of these words changes
+    // in this launch): entries [0, qe) of buffer qb; slice p starts at a
+    // multiple of 64 entries, so it owns whole words of the marks
+    const int qe = min(max(cnt[kCntCntTail], 0), QC);
+    const int qb = cnt[kCntCntBuf] & 1;
+    const int len = ((qe + kBkSlices - 1) / kBkSlices + 63) / 64 * 64;
+    const int lo = min(qe, p * len), hi = min(qe, lo + len);
+    const uint32_t* live = d.qlive + (size_t)u * d.qlive_words;
+    // the marks before the slice (its first place), in it, and in all
+    const int lo_w = lo >> 5, hi_w = lo < hi ? (hi + 31) >> 5 : lo_w, all_w = (qe + 31) >> 5;
+    int b0 = 0, b1 = 0, b2 = 0;
+    for (int w = tid; w < all_w; w += kGatherThreads) {
+      const int n = __popc(live[w]);
+      b0 += w < lo_w ? n : 0;
+      b1 += w >= lo_w && w < hi_w ? n : 0;
+      b2 += n;
+    }
+    const int off = gather_block_sum(b0, wsum);
+    const int mine = gather_block_sum(b1, wsum);
+    const int total = gather_block_sum(b2, wsum);
+    const int2* q = d.oq + ((size_t)u * 2 + qb) * QC;
+    int2* dst = d.oq + ((size_t)u * 2 + (qb ^ 1)) * QC + off;
+    // wave w of a window owns 64 * kCPer consecutive entries, lane-interleaved;
+    // ranks inside the wave come from ballots, the wave totals order the waves
+    constexpr int kCPer = 8;
     int kept = 0;
-    for (int j0 = hn; j0 < qe; j0 += kGatherThreads * kCPer) {
+    for (int j0 = lo; j0 < hi; j0 += kGatherThreads * kCPer) {
       const int wb = j0 + wv * 64 * kCPer;
       int2 ent[kCPer];
+      uint32_t lw[kCPer];
 #pragma unroll
       for (int k = 0; k < kCPer; ++k) {
         const int j = wb + k * 64 + lane;
-        ent[k] = j < qe ? q[j] : make_int2(-1, -1);
+        ent[k] = j < hi ? q[j] : make_int2(-1, -1);
+        lw[k] = j < hi ? live[j >> 5] : 0u;
       }
       bool f[kCPer];
-#pragma unroll
-      for (int k = 0; k < kCPer; ++k) f[k] = ent[k].x >= 0 && ent[k].x < C && !pinned(ent[k].x);
-      int lu[kCPer];
-#pragma unroll
-      for (int k = 0; k < kCPer; ++k) lu[k] = f[k] ? last_use[ent[k].x] : 0;
       int wave_total = 0;
 #pragma unroll
       for (int k = 0; k < kCPer; ++k) {
-        f[k] = f[k] && lu[k] == ent[k].y;
+        const int j = wb + k * 64 + lane;
+        f[k] = ((lw[k] >> (j & 31)) & 1u) && ent[k].x >= 0 && ent[k].x < C && !pinned(ent[k].x);
         wave_total += __popcll(__ballot(f[k]));
       }
       if (lane == 0) wsum[wv] = wave_total;
       __syncthreads();
-      int run = kept, total = 0;
+      int run = kept, wtotal = 0;
 #pragma unroll
       for (int i = 0; i < kW; ++i) {
         run += i < wv ? wsum[i] : 0;
-        total += wsum[i];
+        wtotal += wsum[i];
       }
       __syncthreads();
 #pragma unroll
@@ -298,17 +322,83 @@ __device__ __forceinline__ void bookkeeping(const DevState& d, int u, int32_t t,
         const uint64_t bal = __ballot(f[k]);
         if (f[k]) {
           const int o = run + __popcll(bal & lt_mask);
-          if (o < QC) qw[o] = ent[k];
+          if (o < mine) dst[o] = ent[k];
         }
         run += __popcll(bal);
       }
-      kept += total;
+      kept += wtotal;
     }
-    base = kept;
+    for (int i = min(kept, mine) + tid; i < mine; i += kGatherThreads) dst[i] = make_int2(-1, -1);
+    if (p != 0) return;
+    qw = d.oq + ((size_t)u * 2 + (qb ^ 1)) * QC;
+    base = total;
+    head = 0;
+    buf = qb ^ 1;
+  } else {
+    const int qe = min(max(cnt[kCntQTail], 0), QC);
+    const int hn = min(max(cnt[kCntQHead], 0), qe);
+    const int qb = cnt[kCntQBuf] & 1;
+    int2* q = d.oq + ((size_t)u * 2 + qb) * QC;
+    const bool fits = qe + gather_block_sum(c, wsum) <= QC;
+    qw = fits ? q : d.oq + ((size_t)u * 2 + (qb ^ 1)) * QC;
+    base = qe;
+    head = hn;
+    buf = qb;
+    if (!fits) {
+      // (not reached when the scan launch prepared the compaction) survivors:
+      // the live entries after the head that this step did not use, in
+      // order, to the front of the other buffer, by this workgroup alone
+      constexpr int kCPer = 8;
+      int kept = 0;
+      for (int j0 = hn; j0 < qe; j0 += kGatherThreads * kCPer) {
+        const int wb = j0 + wv * 64 * kCPer;
+        int2 ent[kCPer];
+#pragma unroll
+        for (int k = 0; k < kCPer; ++k) {
+          const int j = wb + k * 64 + lane;
+          ent[k] = j < qe ? q[j] : make_int2(-1, -1);
+        }
+        bool f[kCPer];
+#pragma unroll
+        for (int k = 0; k < kCPer; ++k) f[k] = ent[k].x >= 0 && ent[k].x < C && !pinned(ent[k].x);
+        int lu[kCPer];
+#pragma unroll
+        for (int k = 0; k < kCPer; ++k) lu[k] = f[k] ? last_use[ent[k].x] : 0;
+        int wave_total = 0;
+#pragma unroll
+        for (int k = 0; k < kCPer; ++k) {
+          f[k] = f[k] && lu[k] == ent[k].y;
+          wave_total += __popcll(__ballot(f[k]));
+        }
+        if (lane == 0) wsum[wv] = wave_total;
+        __syncthreads();
+        int run = kept, total = 0;
+#pragma unroll
+        for (int i = 0; i < kW; ++i) {
+          run += i < wv ? wsum[i] : 0;
+          total += wsum[i];
+        }
+        __syncthreads();
+#pragma unroll
+        for (int k = 0; k < kCPer; ++k) {
+          const uint64_t bal = __ballot(f[k]);
+          if (f[k]) {
+            const int o = run + __popcll(bal & lt_mask);
+            if (o < QC) qw[o] = ent[k];
+          }
+          run += __popcll(bal);
+        }
+        kept += total;
+      }
+      base = kept;
+      head = 0;
+      buf = qb ^ 1;
+    }
   }
-  // this thread's words in slot order, after the words of the threads before it
-  int total;
-  int o = base + gather_block_scan(c, wsum, total) - c;
+  // the step's slots at base, this thread's words after the words of the
+  // threads before it
+  int n_touched;
+  int o = base + gather_block_scan(c, wsum, n_touched) - c;
   for (int i = 0; i < g; ++i) {
     const int w = tid * g + i;
     uint32_t bits = w < nwords ? touched[w] : 0u;
@@ -320,13 +410,13 @@ __device__ __forceinline__ void bookkeeping(const DevState& d, int u, int32_t t,
     }
   }
   if (tid == 0) {
-    cnt[kCntQHead] = fits ? hn : 0;
-    cnt[kCntQTail] = base + total < QC ? base + total : QC;
-    cnt[kCntQBuf] = fits ? qb : (qb ^ 1);
+    cnt[kCntQHead] = head;
+    cnt[kCntQTail] = base + n_touched < QC ? base + n_touched : QC;
+    cnt[kCntQBuf] = buf;
   }
 }
 
-__global__ __launch_bounds__(kGatherThreads) void k_gather(DevState d,
+__global__ __launch_bounds__(kGatherThreads) __attribute__((amdgpu_waves_per_eu(8, 8))) void k_gather(DevState d,
                                                            uint16_t* __restrict__ out,
                                                            int32_t t, int bk_rows,
                                                            int miss_rows, int few_hits_above,
@@ -342,8 +432,9 @@ __global__ __launch_bounds__(kGatherThreads) void k_gather(DevState d,
   const size_t out_row_bytes = (size_t)kOut * 2;
 
   if ((int)blockIdx.y >= miss_rows && (int)blockIdx.y < miss_rows + bk_rows) {
-    const int b = (blockIdx.y - miss_rows) * gridDim.x + blockIdx.x;
-    if (b < d.S * d.G) bookkeeping(d, b, t, reinterpret_cast<uint32_t*>(pref), wsum);
+    // slice-major: every unit's slice 0 (which stamps, maps and appends) first
+    const int b = (blockIdx.y - miss_rows) * gridDim.x + blockIdx.x, U = d.S * d.G;
+    if (b < U * kBkSlices) bookkeeping(d, b % U, b / U, t, reinterpret_cast<uint32_t*>(pref), wsum);
     return;
   }
   const int row = (int)blockIdx.y < miss_rows ? (int)blockIdx.y : (int)blockIdx.y - bk_rows;
@@ -486,12 +577,13 @@ hipError_t launch_poison(const DevState& d, hipStream_t st) {
 hipError_t launch_gather(const DevState& d, uint16_t* d_out, int32_t t, int32_t* d_trace,
                          hipStream_t st, StageEv ev) {
   // grid rows [0, miss_rows): the miss workgroups, dispatched first (their
-  // PCIe reads have the longest latency); then bk_rows rows holding one
-  // bookkeeping workgroup per unit (one query row per round; k_round does its
-  // own); then row miss_rows + bk_rows + sl: the hit rows of layer sl
+  // PCIe reads have the longest latency); then bk_rows rows holding
+  // kBkSlices bookkeeping workgroups per unit (one query row per round;
+  // k_round does its own); then row miss_rows + bk_rows + sl: the hit rows of
+  // layer sl
   const int gx = (d.K + kRowsPerRound - 1) / kRowsPerRound;
   const int units = d.S * d.G;
-  const int bk_rows = d.Q == 1 ? (units + gx - 1) / gx : 0;
+  const int bk_rows = d.Q == 1 ? (units * kBkSlices + gx - 1) / gx : 0;
   const int miss_rows = (kMissBlocks + gx - 1) / gx;
   const size_t words = bk_rows ? (size_t)(d.C + 31) / 32 : 0;
   const size_t lds = std::max((size_t)units + 1, words) * sizeof(int32_t);

@@ -180,6 +180,56 @@ __device__ int rescan(const float* src, int64_t H, int K, Ent* gcand, SelShared&
 // kRun: entries a thread holds in registers (4 for top-K up to 3,072, else
 // 8): the per-entry code is unrolled, and on this kernel every instruction is
 // fetched cold, so the smaller variant runs measurably faster.
+// Workgroup c of kCountWGs marking unit u's LRU queue for a compaction (one
+// query row), beside the select workgroups, when the step's slots might not
+// fit after the tail: bit j of the unit's bitmap is set when entry j of
+// [0, tail) is live (its slot's last use is the entry's step — every earlier
+// step's stamps are in place, and this step's are the gather's).  The range
+// starts at 0 rather than at the head, which the select workgroups move
+// meanwhile: entries before any head value are dead or this step's victims,
+// which the compaction drops as used by this step.  Workgroup 0 records the
+// tail, the buffer and the step.  The queue itself is only read.
+__device__ void queue_count(const DevState& d, int u, int c, int32_t t) {
+  int32_t* cnt = d.cnt + (size_t)u * kCntStride;
+  const int QC = d.qcap, C = d.C, tid = threadIdx.x;
+  const int qe = min(max(cnt[kCntQTail], 0), QC);
+  if (qe + d.K <= QC) return;   // the step's slots surely fit: nothing to prepare
+  const int qb = cnt[kCntQBuf] & 1;
+  const int len = ((qe + kCountWGs - 1) / kCountWGs + 63) / 64 * 64;
+  const int lo = min(qe, c * len), hi = min(qe, lo + len);
+  const int2* q = d.oq + ((size_t)u * 2 + qb) * QC;
+  const int32_t* last_use = d.last_use + (size_t)u * C;
+  uint32_t* bits = d.qlive + (size_t)u * d.qlive_words;
+  const int lane = lane_id(), wv = tid >> 6;
+  constexpr int kPer = 8;
+  for (int j0 = lo; j0 < hi; j0 += kSelThreads * kPer) {
+    int2 e[kPer];
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+      const int j = j0 + k * kSelThreads + wv * 64 + lane;
+      e[k] = j < hi ? q[j] : make_int2(-1, -1);
+    }
+    int lu[kPer];
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) lu[k] = e[k].x >= 0 && e[k].x < C ? last_use[e[k].x] : -1;
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+      // 64 consecutive entries per wave, starting at a multiple of 64
+      const int jb = j0 + k * kSelThreads + wv * 64;
+      const uint64_t live = __ballot(e[k].x >= 0 && e[k].x < C && e[k].y >= 0 && lu[k] == e[k].y);
+      if (lane == 0 && jb < hi) {
+        bits[jb >> 5] = (uint32_t)live;
+        bits[(jb >> 5) + 1] = (uint32_t)(live >> 32);
+      }
+    }
+  }
+  if (c == 0 && tid == 0) {
+    cnt[kCntCntTail] = qe;
+    cnt[kCntCntBuf] = qb;
+    cnt[kCntCntStep] = t;
+  }
+}
+
 template <bool kTopkOnly, int kRun>
 __global__ __launch_bounds__(kSelThreads) void k_select(DevState d, StepArgs a,
                                                         const float* __restrict__ scores,
@@ -189,9 +239,14 @@ __global__ __launch_bounds__(kSelThreads) void k_select(DevState d, StepArgs a,
   __shared__ SelShared sh;
   constexpr bool kCache = !kTopkOnly;
   constexpr int kRoundEntries = kSelThreads * kRun;   // entries in registers at most
-  // grid (G Q, S): the session is the grid row, so no division is needed
+  // grid (G Q, S): the session is the grid row, so no division is needed;
+  // grid layers z >= 1 (one query row, LRU): the queue-marking workgroups
   const int session = blockIdx.y;
   const int u = blockIdx.y * gridDim.x + blockIdx.x, tid = threadIdx.x;
+  if (blockIdx.z > 0) {
+    queue_count(d, u, (int)blockIdx.z - 1, a.t);
+    return;
+  }
   const int K = d.K, C = d.C;
   const int32_t t = a.t;
   const int64_t H = a.hist_len[session];
@@ -931,9 +986,12 @@ hipError_t launch_select(const DevState& d, const StepArgs& a, const float* scor
   // path, exact as well)
   const bool small = d.K <= 3072;
   // grid (units per session, sessions)
+  // with one query row and LRU, kCountWGs more workgroups per unit (grid
+  // layers 1 ..) mark the queue's live entries when a compaction is due
+  const unsigned layers = d.Q == 1 && d.policy == HC_REPLACE_LRU ? 1 + kCountWGs : 1;
   auto go = [&](auto kern) {
-    hipExtLaunchKernelGGL(kern, dim3(d.G * d.Q, d.S), dim3(kSelThreads), 0, st, ev.start, ev.stop,
-                          0, d, a, scores, stride, seg_len, d_sel, d_trace);
+    hipExtLaunchKernelGGL(kern, dim3(d.G * d.Q, d.S, layers), dim3(kSelThreads), 0, st, ev.start,
+                          ev.stop, 0, d, a, scores, stride, seg_len, d_sel, d_trace);
   };
   if (d.Q == 1) {
     if (small) go(k_select<false, 4>);
