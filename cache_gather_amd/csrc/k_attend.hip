@@ -25,12 +25,27 @@
 // v_mfma_f32_16x16x32_bf16: its half of Q.K^T in 9 k-steps x 4 row tiles; the
 // pair adds its two partial scores through LDS (fp32 addition commutes, so
 // both waves hold the same sums); online softmax in fp32 (each lane holds 4
-// heads of one row per tile); P rounded to bf16 through LDS; P.V in 2 k-steps
-// x 16 dim tiles, its B operand read from the row-major rows with the gfx950
-// transposing LDS load (ds_read_b64_tr_b16: within each 16-lane group, lane j
-// receives value j % 4 of what lane 4k + j / 4 addressed, so four lanes
-// addressing four consecutive rows give every lane four consecutive rows of
-// one column).  Each split writes (max, sum, unnormalised output) per head; a
+// heads of one row per tile), in base-2 units: both waves of a pair take the
+// maximum over all 64 rows, and each computes the weights of its own 32 rows
+// (half 0 rows 0-31, half 1 rows 32-63) and keeps their running sum per lane;
+// P rounded to bf16 through LDS; P.V in 2 k-steps x 16 dim tiles, its B
+// operand read from the row-major rows with the gfx950 transposing LDS load
+// (ds_read_b64_tr_b16: within each 16-lane group, lane j receives value j % 4
+// of what lane 4k + j / 4 addressed, so four lanes addressing four
+// consecutive rows give every lane four consecutive rows of one column).
+// LDS bank layout (64 banks of 4 bytes; measured with the LDS bank-conflict
+// counter): rows are 1,184 B apart, at which the Q.K^T operand reads (16 rows,
+// one 16-byte column) are conflict-free, where the 1,168-B stride served them
+// in two passes.  A transposing load serves 32 lanes per pass, which must
+// touch eight rows in distinct 32-byte bank blocks; at this stride rows with
+// distinct residues mod 8 do.  So the k slots of a 32-row k-step are not in
+// row order: slots 8g..8g+7 of lane group g hold rows 4g..4g+3 and
+// 16+4g..16+4g+3 (the summation order of P.V is free, and P is stored in the
+// same slot order).  The reference maximum of a head is raised only when a
+// sub-chunk's maximum exceeds it by more than kLazy (weights at most
+// 2^kLazy, far inside the bf16 and fp32 range), so after the first sub-chunk
+// the 64 accumulators of a wave are seldom rescaled.  Each split writes
+// (reference maximum, the two halves' sums, unnormalised output) per head; a
 // second kernel merges the splits.
 #include "hc_internal.h"
 
@@ -46,18 +61,20 @@ constexpr int kHeadsPerGroup = 64;                // 4 tiles of 16
 constexpr int kMaxSplitRows = 1024;              // rows per workgroup, at most
 constexpr int kResident = 256;                    // workgroups the chip runs at once (1 per CU)
 constexpr int kSub = 64;                          // rows per LDS sub-chunk
-constexpr int kRowLd = HC_OUT_ELEMS + 8;          // 584 bf16: padded row-major row
+constexpr int kRowLd = HC_OUT_ELEMS + 16;         // 592 bf16 = 1,184 B: padded row-major row
 constexpr int kPLd = kSub + 8;
-constexpr int kPartStride = 516;                  // floats per (head) partial: 512 + m + l + pad
+constexpr int kPartStride = 516;                  // floats per (head) partial: 512 + m + l0 + l1 + pad
 static_assert(kPartStride % 4 == 0, "partials stay 16-byte aligned");
 constexpr int kHalfK = HC_OUT_ELEMS / 32 / 2;     // 9 Q.K^T k-steps per half
 constexpr int kDimTiles = 512 / 2 / 16;           // 16 P.V dim tiles per half
+constexpr float kLazy = 8.f;                      // base-2 headroom of the reference maximum
+constexpr float kLog2e = 1.4426950408889634f;
 
 enum { kFromBuffer = 0, kFromSlots = 1 };
 
 struct AttShared {
-  alignas(16) __bf16 rows[kSub * kRowLd];         // 74,752 B
-  alignas(16) float sx[8 * 4 * 4 * 64];           // 32,768 B: partial scores [wave][n][i][lane]
+  alignas(16) __bf16 rows[kSub * kRowLd];         // 75,776 B
+  alignas(16) f32x4 sx[8 * 4 * 64];               // 32,768 B: partial scores [wave][n][lane]
   alignas(16) __bf16 p[4 * 16 * kPLd];            //  9,216 B: weights [head tile][head][row]
   const uint8_t* src[kMaxSplitRows];              //  8,192 B: slot source of each row
 };
@@ -124,12 +141,15 @@ __global__ __launch_bounds__(kAttThreads) void k_attend(DevState d, const uint16
   f32x4 o[kDimTiles];
 #pragma unroll
   for (int n = 0; n < kDimTiles; ++n) o[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // per head i of this lane: the reference maximum (base 2, scaled), and the
+  // running sum of this lane's weights (its row of each of the wave's own tiles)
   float m_run[4], l_run[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     m_run[i] = -INFINITY;
     l_run[i] = 0.f;
   }
+  const float scale2 = scale * kLog2e;
 
   // staging: thread tid handles row rr = tid / 8 of a sub-chunk and chunks
   // cc, cc + 8, ..., cc + 64 of 8 values (cc = tid % 8): 8 latent chunks, chunk
@@ -202,17 +222,15 @@ __global__ __launch_bounds__(kAttThreads) void k_attend(DevState d, const uint16
       }
     }
     // ---- the pair's two halves added through LDS ----------------------------
-    float* mine = sh.sx + wave * 1024;
 #pragma unroll
-    for (int n = 0; n < 4; ++n)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) mine[n * 256 + i * 64 + lane] = sacc[n][i];
+    for (int n = 0; n < 4; ++n) sh.sx[(wave * 4 + n) * 64 + lane] = sacc[n];
     __syncthreads();
-    const float* other = sh.sx + (wave ^ 4) * 1024;
 #pragma unroll
-    for (int n = 0; n < 4; ++n)
+    for (int n = 0; n < 4; ++n) {
+      const f32x4 other = sh.sx[((wave ^ 4) * 4 + n) * 64 + lane];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) sacc[n][i] += other[n * 256 + i * 64 + lane];
+      for (int i = 0; i < 4; ++i) sacc[n][i] += other[i];
+    }
 
     // ---- online softmax: lane holds heads 4*(lane/16)+i of row 16n + lane%16
     float mx[4];
@@ -222,39 +240,44 @@ __global__ __launch_bounds__(kAttThreads) void k_attend(DevState d, const uint16
 #pragma unroll
       for (int n = 0; n < 4; ++n) {
         const bool ok = 16 * n + (lane & 15) < nvalid;
-        sacc[n][i] = ok ? sacc[n][i] * scale : -INFINITY;
+        sacc[n][i] = ok ? sacc[n][i] * scale2 : -INFINITY;
         mx[i] = fmaxf(mx[i], sacc[n][i]);
       }
       mx[i] = row16_max(mx[i]);
     }
-    float factor[4];
+    // both waves of the pair hold the same maxima, so they take this branch
+    // together and keep the same reference maxima
+    bool grow = false;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float m_new = fmaxf(m_run[i], mx[i]);
-      factor[i] = m_run[i] == -INFINITY ? 0.f : __expf(m_run[i] - m_new);
-      float sum = 0.f;
+    for (int i = 0; i < 4; ++i) grow |= mx[i] > m_run[i] + kLazy;
+    if (__ballot(grow) != 0) {
+      float factor[4];
 #pragma unroll
-      for (int n = 0; n < 4; ++n) {
-        const float pv = sacc[n][i] == -INFINITY ? 0.f : __expf(sacc[n][i] - m_new);
-        sacc[n][i] = pv;
-        sum += pv;
+      for (int i = 0; i < 4; ++i) {
+        const float m_new = fmaxf(m_run[i], mx[i]);
+        factor[i] = m_run[i] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run[i] - m_new);
+        l_run[i] *= factor[i];
+        m_run[i] = m_new;
       }
-      sum = row16_sum(sum);
-      l_run[i] = l_run[i] * factor[i] + sum;
-      m_run[i] = m_new;
+#pragma unroll
+      for (int n = 0; n < kDimTiles; ++n)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) o[n][i] *= factor[i];
     }
-#pragma unroll
-    for (int n = 0; n < kDimTiles; ++n)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) o[n][i] *= factor[i];
-    // P (bf16) of the head tile to LDS as [head][row], written by half 0
+    // P (bf16) of this wave's own 32 rows to LDS as [head][k slot]: row r of
+    // a 32-row k-step sits in slot 8 * ((r % 16) / 4) + r % 4 + 4 * (r / 16)
     __bf16* pw = sh.p + ht * 16 * kPLd;
-    if (half == 0) {
+    const int kslot = 8 * ((lane & 15) >> 2) + (lane & 3);
 #pragma unroll
-      for (int n = 0; n < 4; ++n)
+    for (int nn = 0; nn < 2; ++nn) {
+      const f32x4 z = half ? sacc[2 + nn] : sacc[nn];
+      const int n = 2 * half + nn;
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          pw[(4 * (lane >> 4) + i) * kPLd + 16 * n + (lane & 15)] = (__bf16)sacc[n][i];
+      for (int i = 0; i < 4; ++i) {
+        const float pv = __builtin_amdgcn_exp2f(z[i] - m_run[i]);   // 0 for a masked row
+        l_run[i] += pv;
+        pw[(4 * (lane >> 4) + i) * kPLd + 32 * (n >> 1) + 4 * (n & 1) + kslot] = (__bf16)pv;
+      }
     }
     __syncthreads();
     // ---- O[:, this half] += P V -------------------------------------------
@@ -262,11 +285,11 @@ __global__ __launch_bounds__(kAttThreads) void k_attend(DevState d, const uint16
 #pragma unroll
     for (int ks = 0; ks < kSub / 32; ++ks) {
       const bf16x8 a = *reinterpret_cast<const bf16x8*>(&pw[gl * kPLd + 32 * ks + 8 * grp]);
-      const __bf16* vb = &sh.rows[(32 * ks + 8 * grp + (gl >> 2)) * kRowLd + 256 * half + 4 * (gl & 3)];
+      const __bf16* vb = &sh.rows[(32 * ks + 4 * grp + (gl >> 2)) * kRowLd + 256 * half + 4 * (gl & 3)];
 #pragma unroll
       for (int n = 0; n < kDimTiles; ++n) {
         const i16x4 lo = lds_tr4(vb + 16 * n);
-        const i16x4 hi = lds_tr4(vb + 4 * kRowLd + 16 * n);
+        const i16x4 hi = lds_tr4(vb + 16 * kRowLd + 16 * n);
         const i16x8 v8 = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
         o[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8, v8), o[n],
                                                       0, 0, 0);
@@ -274,24 +297,26 @@ __global__ __launch_bounds__(kAttThreads) void k_attend(DevState d, const uint16
     }
   }
 
-  // ---- this split's partial: unnormalised output, max, sum per head --------
+  // ---- this split's partial: unnormalised output, reference maximum, and
+  // the sums of the two halves' rows per head
   const int nsplit = gridDim.x;
   float* base = part + (((size_t)slq * gridDim.y + hg) * nsplit + split) * kHeadsPerGroup * kPartStride;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int h = ht * 16 + 4 * (lane >> 4) + i;
     float* ph = base + (size_t)h * kPartStride;
+    const float lsum = row16_sum(l_run[i]);
 #pragma unroll
     for (int n = 0; n < kDimTiles; ++n) ph[256 * half + 16 * n + (lane & 15)] = o[n][i];
-    if (half == 0 && (lane & 15) == 0) {
-      ph[512] = m_run[i];
-      ph[513] = l_run[i];
+    if ((lane & 15) == 0) {
+      if (half == 0) ph[512] = m_run[i];
+      ph[513 + half] = lsum;
     }
   }
 }
 
-// Merges the splits of four heads of one slq: out = sum_c e^(m_c - M) O_c /
-// sum_c e^(m_c - M) l_c.  128 threads per head, four output values each
+// Merges the splits of four heads of one slq: out = sum_c 2^(m_c - M) O_c /
+// sum_c 2^(m_c - M) (l0_c + l1_c), maxima in base-2 units.  128 threads per head, four output values each
 // (16-byte loads and stores; a partial's 516-float stride keeps them aligned).
 constexpr int kMergeHeads = 4;
 __global__ __launch_bounds__(512) void k_attend_merge(const float* __restrict__ part, int heads,
@@ -309,8 +334,8 @@ __global__ __launch_bounds__(512) void k_attend_merge(const float* __restrict__ 
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
   for (int c = 0; c < nsplit; ++c) {
     const float mc = base[c * cstride + 512];
-    const float w = mc == -INFINITY ? 0.f : __expf(mc - M);
-    L += w * base[c * cstride + 513];
+    const float w = mc == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mc - M);
+    L += w * (base[c * cstride + 513] + base[c * cstride + 514]);
     const float4 o = *reinterpret_cast<const float4*>(base + c * cstride + dd);
     acc.x += w * o.x;
     acc.y += w * o.y;
