@@ -43,7 +43,7 @@ def _val(bits):
     return (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
 
 
-def check_attention(p, t, o_out, heads, layers=None, oracle_units=None):
+def check_attention(p, t, o_out, heads, layers=None, oracle_units=None, scale=SCALE):
     """Runs both attention paths after step t; o_out: the oracle's gathered
     rows of that step ([S, L, K, 576] or [S, L, Q, K, 576])."""
     import torch
@@ -54,10 +54,10 @@ def check_attention(p, t, o_out, heads, layers=None, oracle_units=None):
     work, out = p.hc.attention_buffers(heads)
     cached = None
     if not p.fill_only:
-        p.hc.attend(d_q, heads, SCALE, p.out, work, out)
+        p.hc.attend(d_q, heads, scale, p.out, work, out)
         torch.cuda.synchronize()
         buf = out.cpu().numpy().copy()
-    p.hc.attend_cached(d_q, heads, SCALE, work, out)
+    p.hc.attend_cached(d_q, heads, scale, work, out)
     torch.cuda.synchronize()
     cached = out.cpu().numpy()
     if not p.fill_only:
@@ -71,7 +71,7 @@ def check_attention(p, t, o_out, heads, layers=None, oracle_units=None):
     for s in range(wl.n_sessions):
         for l in layers:
             for qi in range(Q):
-                ref = oracle.attend(qq[s, l, qi], oo[s, l, qi], SCALE)
+                ref = oracle.attend(qq[s, l, qi], oo[s, l, qi], scale)
                 vmax = np.abs(_val(oo[s, l, qi][:, :512])).max(axis=0)
                 err = np.abs(gg[s, l, qi].astype(np.float64) - ref)
                 bound = 4e-3 * vmax[None, :] + 1e-6
@@ -106,6 +106,27 @@ def test_attend_ragged_splits_two_head_groups_and_sessions():
                       sigma_noise=(1.0, 1.0))
     p = Pair(wl)
     _run(p, 3, 128)
+    p.close()
+
+
+def test_scales_that_move_the_maximum_and_negative_scales():
+    """The kernel keeps a reference maximum per head and raises it only when a
+    64-row sub-chunk exceeds it by more than 2^8.  32 layers of top-2,048 give
+    eight splits of 256 rows, four sub-chunks each.  At scale 1.0 this data's
+    scores spread over hundreds of powers of two, so later sub-chunks often
+    raise the maximum too; scale 1e-6 gives nearly equal weights, and a
+    negative scale the softmax of negated scores.  Both paths bit for bit on
+    every layer, three layers against the oracle."""
+    from gpu_harness import Pair, say
+    wl = W.TINY.with_(name="attend_scales", n_layers=32, layers_per_select=4, top_k=2048,
+                      cache_slots=4096, steps=2)
+    p = Pair(wl)
+    for t in range(2):
+        g, o = p.step(t)
+        p.compare(t, g, o)
+    for scale in (1.0, 1e-6, -SCALE):
+        worst = check_attention(p, 1, o[1], 64, layers=[0, 13, 31], scale=scale)
+        say("scale %g: attention within %.2e of max|v| (bound 4e-3)" % (scale, worst))
     p.close()
 
 
