@@ -67,6 +67,9 @@ constexpr int kPartStride = 516;                  // floats per (head) partial: 
 static_assert(kPartStride % 4 == 0, "partials stay 16-byte aligned");
 constexpr int kHalfK = HC_OUT_ELEMS / 32 / 2;     // 9 Q.K^T k-steps per half
 constexpr int kDimTiles = 512 / 2 / 16;           // 16 P.V dim tiles per half
+// instruction classes of __builtin_amdgcn_sched_group_barrier
+constexpr int kSchedMfma = 0x008;
+constexpr int kSchedDsRead = 0x100;
 constexpr float kLazy = 8.f;                      // base-2 headroom of the reference maximum
 constexpr float kLog2e = 1.4426950408889634f;
 
@@ -221,6 +224,15 @@ __global__ __launch_bounds__(kAttThreads) void k_attend(DevState d, const uint16
         sacc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[ks], b, sacc[n], 0, 0, 0);
       }
     }
+    // schedule: six operand reads ahead of the matrix instructions, then one
+    // read per matrix instruction, so the LDS latency is not waited out 18 times
+    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 6, 0);
+#pragma unroll
+    for (int k = 0; k < 4 * kHalfK - 6; ++k) {
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(kSchedMfma, 6, 0);
     // ---- the pair's two halves added through LDS ----------------------------
 #pragma unroll
     for (int n = 0; n < 4; ++n) sh.sx[(wave * 4 + n) * 64 + lane] = sacc[n];
@@ -295,6 +307,15 @@ __global__ __launch_bounds__(kAttThreads) void k_attend(DevState d, const uint16
                                                       0, 0, 0);
       }
     }
+    // schedule: the P fragment and four tiles' operands read ahead, then two
+    // reads per matrix instruction
+    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 10, 0);
+#pragma unroll
+    for (int k = 0; k < kSub / 32 * kDimTiles - 4; ++k) {
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(kSchedMfma, 4, 0);
   }
 
   // ---- this split's partial: unnormalised output, reference maximum, and
