@@ -70,6 +70,7 @@ constexpr int kDimTiles = 512 / 2 / 16;           // 16 P.V dim tiles per half
 // instruction classes of __builtin_amdgcn_sched_group_barrier
 constexpr int kSchedMfma = 0x008;
 constexpr int kSchedDsRead = 0x100;
+constexpr int kSchedVmemRead = 0x020;
 constexpr float kLazy = 8.f;                      // base-2 headroom of the reference maximum
 constexpr float kLog2e = 1.4426950408889634f;
 
@@ -158,7 +159,7 @@ __global__ __launch_bounds__(kAttThreads) void k_attend(DevState d, const uint16
   // cc, cc + 8, ..., cc + 64 of 8 values (cc = tid % 8): 8 latent chunks, chunk
   // k in scale group k, and one RoPE chunk.  Eight consecutive lanes cover 128
   // contiguous bytes of a row.  Software pipeline: the raw loads of sub-chunk
-  // j + 1 are issued before the matrix work of sub-chunk j.
+  // j + 1 are issued during the matrix work of sub-chunk j.
   const int nsub = (r_end - r_begin + kSub - 1) / kSub;
   constexpr int kLat = 8;
   const int rr = tid >> 3, cc = tid & 7;
@@ -170,27 +171,27 @@ __global__ __launch_bounds__(kAttThreads) void k_attend(DevState d, const uint16
   u32x4 bv[kLat + 1];                              // buffer source: 9 chunks of 16 B
   uint2 q8[kLat];                                  // slot source: 8 latent chunks of 8 B
   u32x4 rope, scb;                                 // slot source: RoPE chunk, scale block
+  // Branch-free, so the loads can be interleaved with the matrix work: a row
+  // past the split reads the split's last row instead, and staging stores
+  // zeros for it.
   auto fetch = [&](int j) {
-    const int r0 = r_begin + j * kSub;
-    const bool vr = r0 + rr < r_end;
+    const int r = min(r_begin + j * kSub + rr, r_end - 1);
     if (SRC == kFromBuffer) {
       // non-temporal: the buffer is read once, and normal loads would allocate
       // it in the Infinity Cache over the hot slots the next step reads again
-      const uint16_t* base = rows_buf + ((size_t)slq * K + r0 + rr) * HC_OUT_ELEMS + 8 * cc;
+      const uint16_t* base = rows_buf + ((size_t)slq * K + r) * HC_OUT_ELEMS + 8 * cc;
 #pragma unroll
       for (int k = 0; k <= kLat; ++k)
-        bv[k] = vr ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(base + 64 * k))
-                   : u32x4{0u, 0u, 0u, 0u};
+        bv[k] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(base + 64 * k));
     } else {
-      gbyte* src = to_global(vr ? sh.src[j * kSub + rr] : nullptr);
+      gbyte* src = to_global(sh.src[r - r_begin]);
 #pragma unroll
-      for (int k = 0; k < kLat; ++k)
-      {
-        const u32x2 w = vr ? gload<u32x2>(src + 8 * (cc + 8 * k)) : u32x2{0u, 0u};
+      for (int k = 0; k < kLat; ++k) {
+        const u32x2 w = gload<u32x2>(src + 8 * (cc + 8 * k));
         q8[k] = uint2{w.x, w.y};
       }
-      rope = vr ? gload<u32x4>(src + HC_ROPE_OFFSET + 16 * cc) : u32x4{0u, 0u, 0u, 0u};
-      scb = vr ? gload<u32x4>(src + HC_SCALE_OFFSET) : u32x4{0u, 0u, 0u, 0u};
+      rope = gload<u32x4>(src + HC_ROPE_OFFSET + 16 * cc);
+      scb = gload<u32x4>(src + HC_SCALE_OFFSET);
     }
   };
   auto chunk = [&](int k) -> u32x4 {
@@ -204,11 +205,21 @@ __global__ __launch_bounds__(kAttThreads) void k_attend(DevState d, const uint16
   for (int j = 0; j < nsub; ++j) {
     const int nvalid = min(kSub, r_end - (r_begin + j * kSub));
     __syncthreads();   // the previous sub-chunk's matrix work is done with LDS
+    if (nvalid == kSub) {
 #pragma unroll
-    for (int k = 0; k <= kLat; ++k)
-      *reinterpret_cast<u32x4*>(&sh.rows[rr * kRowLd + 8 * (cc + 8 * k)]) = chunk(k);
+      for (int k = 0; k <= kLat; ++k)
+        *reinterpret_cast<u32x4*>(&sh.rows[rr * kRowLd + 8 * (cc + 8 * k)]) = chunk(k);
+    } else {   // the split's ragged last sub-chunk
+      const bool vr = rr < nvalid;
+#pragma unroll
+      for (int k = 0; k <= kLat; ++k)
+        *reinterpret_cast<u32x4*>(&sh.rows[rr * kRowLd + 8 * (cc + 8 * k)]) =
+            vr ? chunk(k) : u32x4{0u, 0u, 0u, 0u};
+    }
     __syncthreads();
-    if (j + 1 < nsub) fetch(j + 1);   // in flight during this sub-chunk's matrix work
+    // the next sub-chunk's loads, in flight during this one's matrix work (the
+    // last sub-chunk requests itself again rather than branch)
+    fetch(min(j + 1, nsub - 1));
 
     // ---- this wave's half of S = Q K^T: 16 heads x 64 rows ----------------
     f32x4 sacc[4];
@@ -226,11 +237,14 @@ __global__ __launch_bounds__(kAttThreads) void k_attend(DevState d, const uint16
     }
     // schedule: six operand reads ahead of the matrix instructions, then one
     // read per matrix instruction, so the LDS latency is not waited out 18 times
+    // The next sub-chunk's global loads go one per matrix instruction: issued
+    // in a burst they held the address unit ahead of the operand reads.
     __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 6, 0);
 #pragma unroll
     for (int k = 0; k < 4 * kHalfK - 6; ++k) {
       __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
       __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+      if (k < kLat + 2) __builtin_amdgcn_sched_group_barrier(kSchedVmemRead, 1, 0);
     }
     __builtin_amdgcn_sched_group_barrier(kSchedMfma, 6, 0);
     // ---- the pair's two halves added through LDS ----------------------------
