@@ -222,6 +222,8 @@ __global__ __launch_bounds__(kAttThreads) void k_attend(DevState d, const uint16
     fetch(min(j + 1, nsub - 1));
 
     // ---- this wave's half of S = Q K^T: 16 heads x 64 rows ----------------
+    // slot t holds row tile t ^ (2 * half): the wave's own two tiles (those
+    // it exponentiates) come first
     f32x4 sacc[4];
 #pragma unroll
     for (int n = 0; n < 4; ++n) sacc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -231,7 +233,7 @@ __global__ __launch_bounds__(kAttThreads) void k_attend(DevState d, const uint16
 #pragma unroll
       for (int n = 0; n < 4; ++n) {
         const bf16x8 b = *reinterpret_cast<const bf16x8*>(
-            &sh.rows[(16 * n + (lane & 15)) * kRowLd + 32 * kk + 8 * (lane >> 4)]);
+            &sh.rows[(16 * (n ^ (2 * half)) + (lane & 15)) * kRowLd + 32 * kk + 8 * (lane >> 4)]);
         sacc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[ks], b, sacc[n], 0, 0, 0);
       }
     }
@@ -249,38 +251,40 @@ __global__ __launch_bounds__(kAttThreads) void k_attend(DevState d, const uint16
     __builtin_amdgcn_sched_group_barrier(kSchedMfma, 6, 0);
     // ---- the pair's two halves added through LDS ----------------------------
 #pragma unroll
-    for (int n = 0; n < 4; ++n) sh.sx[(wave * 4 + n) * 64 + lane] = sacc[n];
+    for (int n = 0; n < 4; ++n) sh.sx[(wave * 4 + (n ^ (2 * half))) * 64 + lane] = sacc[n];
     __syncthreads();
 #pragma unroll
     for (int n = 0; n < 4; ++n) {
-      const f32x4 other = sh.sx[((wave ^ 4) * 4 + n) * 64 + lane];
+      const f32x4 other = sh.sx[((wave ^ 4) * 4 + (n ^ (2 * half))) * 64 + lane];
 #pragma unroll
       for (int i = 0; i < 4; ++i) sacc[n][i] += other[i];
     }
 
-    // ---- online softmax: lane holds heads 4*(lane/16)+i of row 16n + lane%16
+    // ---- online softmax: in slot n a lane holds heads 4*(lane/16)+i of row
+    // 16 * (n ^ (2 * half)) + lane%16
+    // A head's maximum over the 64 rows is needed only when it exceeds the
+    // reference by more than kLazy, and some lane's own maximum then does too:
+    // the 16-lane reduction runs only in that (rare) branch.
     float mx[4];
+    bool grow = false;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       mx[i] = -INFINITY;
 #pragma unroll
       for (int n = 0; n < 4; ++n) {
-        const bool ok = 16 * n + (lane & 15) < nvalid;
+        const bool ok = 16 * (n ^ (2 * half)) + (lane & 15) < nvalid;
         sacc[n][i] = ok ? sacc[n][i] * scale2 : -INFINITY;
         mx[i] = fmaxf(mx[i], sacc[n][i]);
       }
-      mx[i] = row16_max(mx[i]);
+      grow |= mx[i] > m_run[i] + kLazy;
     }
-    // both waves of the pair hold the same maxima, so they take this branch
+    // both waves of the pair hold the same scores, so they take this branch
     // together and keep the same reference maxima
-    bool grow = false;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) grow |= mx[i] > m_run[i] + kLazy;
     if (__ballot(grow) != 0) {
       float factor[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float m_new = fmaxf(m_run[i], mx[i]);
+        const float m_new = fmaxf(m_run[i], row16_max(mx[i]));
         factor[i] = m_run[i] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run[i] - m_new);
         l_run[i] *= factor[i];
         m_run[i] = m_new;
@@ -296,7 +300,7 @@ __global__ __launch_bounds__(kAttThreads) void k_attend(DevState d, const uint16
     const int kslot = 8 * ((lane & 15) >> 2) + (lane & 3);
 #pragma unroll
     for (int nn = 0; nn < 2; ++nn) {
-      const f32x4 z = half ? sacc[2 + nn] : sacc[nn];
+      const f32x4 z = sacc[nn];
       const int n = 2 * half + nn;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
