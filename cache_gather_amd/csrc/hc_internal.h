@@ -130,6 +130,15 @@ struct CopybackArgs {
 // 16-byte vector usable with the nontemporal load/store builtins.
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+
+// Two floats rounded to bf16 (nearest, ties to even), lo in the low half, as
+// one packed conversion: converting them one at a time made the compiler pack
+// each with a dummy and merge the halves with two more instructions.
+__device__ __forceinline__ uint32_t bf16x2_rne(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2v));
+}
 
 // Global-memory views of row pointers (hot slots, ring, pinned host rows
 // mapped for the device).  Loads through them compile to global loads; through

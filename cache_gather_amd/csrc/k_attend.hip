@@ -83,12 +83,6 @@ struct AttShared {
   const uint8_t* src[kMaxSplitRows];              //  8,192 B: slot source of each row
 };
 
-__device__ __forceinline__ uint32_t bf16x2_rne(float lo, float hi) {
-  const __bf16 a = (__bf16)lo, b = (__bf16)hi;
-  return (uint32_t)__builtin_bit_cast(uint16_t, a) |
-         ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
-}
-
 __device__ __forceinline__ float i8f(uint32_t w, int k) {
   return (float)((int32_t)(w << (24 - 8 * k)) >> 24);
 }

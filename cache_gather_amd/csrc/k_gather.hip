@@ -73,12 +73,6 @@ constexpr int kMissRowsPerBlock = 64;
 constexpr int kMissRowsFewHits = 16;
 constexpr int kFewHitRows = 16384;
 
-__device__ __forceinline__ uint32_t bf16x2(float lo, float hi) {
-  const __bf16 a = (__bf16)lo, b = (__bf16)hi;
-  return (uint32_t)__builtin_bit_cast(uint16_t, a) |
-         ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
-}
-
 // Sign-extended int8 number k (0..3) of w, as float.
 __device__ __forceinline__ float i8f(uint32_t w, int k) {
   return (float)((int32_t)(w << (24 - 8 * k)) >> 24);
@@ -126,14 +120,14 @@ __device__ __forceinline__ void run_rows(const RowJob<kPasses>& j, int item) {
       const float sc = scale_of(sblk[p], item >> 2);
       const u32x4 q = v[p];
       u32x4 a, b;
-      a.x = bf16x2(i8f(q.x, 0) * sc, i8f(q.x, 1) * sc);
-      a.y = bf16x2(i8f(q.x, 2) * sc, i8f(q.x, 3) * sc);
-      a.z = bf16x2(i8f(q.y, 0) * sc, i8f(q.y, 1) * sc);
-      a.w = bf16x2(i8f(q.y, 2) * sc, i8f(q.y, 3) * sc);
-      b.x = bf16x2(i8f(q.z, 0) * sc, i8f(q.z, 1) * sc);
-      b.y = bf16x2(i8f(q.z, 2) * sc, i8f(q.z, 3) * sc);
-      b.z = bf16x2(i8f(q.w, 0) * sc, i8f(q.w, 1) * sc);
-      b.w = bf16x2(i8f(q.w, 2) * sc, i8f(q.w, 3) * sc);
+      a.x = bf16x2_rne(i8f(q.x, 0) * sc, i8f(q.x, 1) * sc);
+      a.y = bf16x2_rne(i8f(q.x, 2) * sc, i8f(q.x, 3) * sc);
+      a.z = bf16x2_rne(i8f(q.y, 0) * sc, i8f(q.y, 1) * sc);
+      a.w = bf16x2_rne(i8f(q.y, 2) * sc, i8f(q.y, 3) * sc);
+      b.x = bf16x2_rne(i8f(q.z, 0) * sc, i8f(q.z, 1) * sc);
+      b.y = bf16x2_rne(i8f(q.z, 2) * sc, i8f(q.z, 3) * sc);
+      b.z = bf16x2_rne(i8f(q.w, 0) * sc, i8f(q.w, 1) * sc);
+      b.w = bf16x2_rne(i8f(q.w, 2) * sc, i8f(q.w, 3) * sc);
       u32x4* o = reinterpret_cast<u32x4*>(j.dst[p] + 32 * item);
       __builtin_nontemporal_store(a, o);
       __builtin_nontemporal_store(b, o + 1);
