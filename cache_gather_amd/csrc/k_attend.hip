@@ -351,7 +351,10 @@ __global__ __launch_bounds__(kAttThreads) void k_attend(DevState d, const uint16
 // Merges the splits of four heads of one slq: out = sum_c 2^(m_c - M) O_c /
 // sum_c 2^(m_c - M) (l0_c + l1_c), maxima in base-2 units.  128 threads per head, four output values each
 // (16-byte loads and stores; a partial's 516-float stride keeps them aligned).
+// NS > 0: exactly NS splits, whose loads all go out in one round; NS = 0: any
+// number, maxima first.  Both add the splits in the same order.
 constexpr int kMergeHeads = 4;
+template <int NS>
 __global__ __launch_bounds__(512) void k_attend_merge(const float* __restrict__ part, int heads,
                                                       int nsplit, float* __restrict__ out) {
   const int h = blockIdx.x * kMergeHeads + (threadIdx.x >> 7), slq = blockIdx.y;
@@ -362,18 +365,34 @@ __global__ __launch_bounds__(512) void k_attend_merge(const float* __restrict__ 
                       (size_t)hh * kPartStride;
   const size_t cstride = (size_t)kHeadsPerGroup * kPartStride;
   float M = -INFINITY;
-  for (int c = 0; c < nsplit; ++c) M = fmaxf(M, base[c * cstride + 512]);
   float L = 0.f;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int c = 0; c < nsplit; ++c) {
-    const float mc = base[c * cstride + 512];
+  auto add = [&](float mc, float lc, const float4& o) {
     const float w = mc == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mc - M);
-    L += w * (base[c * cstride + 513] + base[c * cstride + 514]);
-    const float4 o = *reinterpret_cast<const float4*>(base + c * cstride + dd);
+    L += w * lc;
     acc.x += w * o.x;
     acc.y += w * o.y;
     acc.z += w * o.z;
     acc.w += w * o.w;
+  };
+  if (NS > 0) {
+    float mc[NS > 0 ? NS : 1], lc[NS > 0 ? NS : 1];
+    float4 oc[NS > 0 ? NS : 1];
+#pragma unroll
+    for (int c = 0; c < NS; ++c) {
+      mc[c] = base[c * cstride + 512];
+      lc[c] = base[c * cstride + 513] + base[c * cstride + 514];
+      oc[c] = *reinterpret_cast<const float4*>(base + c * cstride + dd);
+    }
+#pragma unroll
+    for (int c = 0; c < NS; ++c) M = fmaxf(M, mc[c]);
+#pragma unroll
+    for (int c = 0; c < NS; ++c) add(mc[c], lc[c], oc[c]);
+  } else {
+    for (int c = 0; c < nsplit; ++c) M = fmaxf(M, base[c * cstride + 512]);
+    for (int c = 0; c < nsplit; ++c)
+      add(base[c * cstride + 512], base[c * cstride + 513] + base[c * cstride + 514],
+          *reinterpret_cast<const float4*>(base + c * cstride + dd));
   }
   *reinterpret_cast<float4*>(out + ((size_t)slq * heads + h) * 512 + dd) =
       make_float4(acc.x / L, acc.y / L, acc.z / L, acc.w / L);
@@ -426,8 +445,15 @@ hipError_t launch_attend(const DevState& d, bool from_slots, const uint16_t* q, 
                        sp.rows, rows, part);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_attend_merge, dim3(heads / kMergeHeads, d.S * d.L * d.Q), dim3(512), 0, st,
-                     part, heads, sp.nsplit, out);
+  const dim3 mgrid(heads / kMergeHeads, d.S * d.L * d.Q);
+  switch (sp.nsplit) {
+    case 1: hipLaunchKernelGGL(k_attend_merge<1>, mgrid, dim3(512), 0, st, part, heads, 1, out); break;
+    case 2: hipLaunchKernelGGL(k_attend_merge<2>, mgrid, dim3(512), 0, st, part, heads, 2, out); break;
+    case 3: hipLaunchKernelGGL(k_attend_merge<3>, mgrid, dim3(512), 0, st, part, heads, 3, out); break;
+    case 4: hipLaunchKernelGGL(k_attend_merge<4>, mgrid, dim3(512), 0, st, part, heads, 4, out); break;
+    default:
+      hipLaunchKernelGGL(k_attend_merge<0>, mgrid, dim3(512), 0, st, part, heads, sp.nsplit, out);
+  }
   return hipGetLastError();
 }
 
