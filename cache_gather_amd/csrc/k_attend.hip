@@ -25,9 +25,11 @@
 // v_mfma_f32_16x16x32_bf16: its half of Q.K^T in 9 k-steps x 4 row tiles; the
 // pair adds its two partial scores through LDS (fp32 addition commutes, so
 // both waves hold the same sums); online softmax in fp32 (each lane holds 4
-// heads of one row per tile), in base-2 units: both waves of a pair take the
-// maximum over all 64 rows, and each computes the weights of its own 32 rows
-// (half 0 rows 0-31, half 1 rows 32-63) and keeps their running sum per lane;
+// heads of one row per tile), in base-2 units: both waves of a pair test all
+// 64 rows against each head's reference maximum (reducing over the 16 lanes
+// of a head only when it must rise), and each computes the weights of its own
+// 32 rows (half 0 rows 0-31, half 1 rows 32-63) and keeps their running sum
+// per lane;
 // P rounded to bf16 through LDS; P.V in 2 k-steps x 16 dim tiles, its B
 // operand read from the row-major rows with the gfx950 transposing LDS load
 // (ds_read_b64_tr_b16: within each 16-lane group, lane j receives value j % 4
