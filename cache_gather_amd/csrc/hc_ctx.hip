@@ -221,7 +221,9 @@ struct hc_ctx {
   bool enqueued = false;
   bool appended_since_step = false;  // an hc_append after the last hc_step
   hipStream_t last_stream = nullptr; // stream of the last enqueued work
-  hipEvent_t done = nullptr;         // recorded after all enqueued work
+  hipEvent_t done = nullptr;         // recorded after all enqueued work; device-scope only
+  hipEvent_t host_done = nullptr;    // system-scope: the host's waits (host_wait)
+  hipStream_t sync_stream = nullptr; // private, non-blocking: where host_done is recorded
 #ifdef HC_TEST_HOOKS
   bool test_fail_launch = false;     // the next hc_step fails before its first launch
   bool test_poison = false;          // sentinel over victim slots before each gather
@@ -275,6 +277,26 @@ hipError_t order_after_last(hc_ctx* c, hipStream_t st) {
   if (c->enqueued && st != c->last_stream) e = hipStreamWaitEvent(st, c->done, 0);
   c->last_stream = st;
   return e;
+}
+
+// Waits on the host until everything the context enqueued has completed, its
+// writes to device memory visible to the host.  `done`, recorded after every
+// call to order the context's streams, has no system-scope fence (with one,
+// each record cost about 2 us of device time per step), so the system-scope
+// event is recorded here, on a private stream that waits for `done` first.
+hipError_t host_wait(hc_ctx* c) {
+  hipError_t e = hipStreamWaitEvent(c->sync_stream, c->done, 0);
+  if (e == hipSuccess) e = hipEventRecord(c->host_done, c->sync_stream);
+  if (e == hipSuccess) e = hipEventSynchronize(c->host_done);
+  return e;
+}
+
+void destroy_sync(hc_ctx* c) {
+  if (c->done) (void)hipEventDestroy(c->done);
+  if (c->host_done) (void)hipEventDestroy(c->host_done);
+  if (c->sync_stream) (void)hipStreamDestroy(c->sync_stream);
+  c->done = c->host_done = nullptr;
+  c->sync_stream = nullptr;
 }
 
 void free_prof(hc_ctx* c) {
@@ -396,7 +418,13 @@ hc_status hc_create(const hc_config* cfg_in, void* dev_workspace, uint64_t ws_by
       c->err_dev = static_cast<uint32_t*>(dp);
     }
   }
-  if (st == HC_OK && hipEventCreateWithFlags(&c->done, hipEventDisableTiming) != hipSuccess)
+  if (st == HC_OK &&
+      hipEventCreateWithFlags(&c->done, hipEventDisableTiming | hipEventDisableSystemFence) !=
+          hipSuccess)
+    st = HC_E_HIP;
+  if (st == HC_OK && hipEventCreateWithFlags(&c->host_done, hipEventDisableTiming) != hipSuccess)
+    st = HC_E_HIP;
+  if (st == HC_OK && hipStreamCreateWithFlags(&c->sync_stream, hipStreamNonBlocking) != hipSuccess)
     st = HC_E_HIP;
 
   DevState& d = c->dev;
@@ -440,11 +468,11 @@ hc_status hc_create(const hc_config* cfg_in, void* dev_workspace, uint64_t ws_by
   // initialise on the null stream and wait for that work alone (not for every
   // stream of the device)
   if (st == HC_OK && launch_init(d, nullptr) != hipSuccess) st = HC_E_HIP;
-  if (st == HC_OK && hipEventRecord(c->done, nullptr) != hipSuccess) st = HC_E_HIP;
-  if (st == HC_OK && hipEventSynchronize(c->done) != hipSuccess) st = HC_E_HIP;
+  if (st == HC_OK && hipEventRecord(c->host_done, nullptr) != hipSuccess) st = HC_E_HIP;
+  if (st == HC_OK && hipEventSynchronize(c->host_done) != hipSuccess) st = HC_E_HIP;
   if (st != HC_OK) {
     free_host(c);
-    if (c->done) (void)hipEventDestroy(c->done);
+    destroy_sync(c);
     delete c;
     return st;
   }
@@ -587,7 +615,7 @@ hc_status hc_flush(hc_ctx* c, void* stream, uint64_t* host_count) {
     if (e != hipSuccess) return fail_hip(c);
   }
   // wait for the copy itself, not for its submission
-  if (c->enqueued && hipEventSynchronize(c->done) != hipSuccess) return fail_hip(c);
+  if (c->enqueued && host_wait(c) != hipSuccess) return fail_hip(c);
   if (hipStreamSynchronize(st) != hipSuccess) return fail_hip(c);
   if (device_error(c)) return HC_E_DEVICE;
   hc_status r = HC_OK;
@@ -663,7 +691,7 @@ hc_status hc_export_state(hc_ctx* c, uint32_t session, uint32_t layer, int32_t* 
   if (session >= c->cfg.n_sessions || layer >= c->cfg.n_layers) return HC_E_INVAL;
   DeviceGuard dg(c->cfg.device);
   if (!dg.ok) return HC_E_INVAL;
-  if (c->enqueued && hipEventSynchronize(c->done) != hipSuccess) return fail_hip(c);
+  if (c->enqueued && host_wait(c) != hipSuccess) return fail_hip(c);
   if (device_error(c)) return HC_E_DEVICE;
   const DevState& d = c->dev;
   const size_t u = (size_t)session * d.G + layer / d.R;
@@ -685,7 +713,7 @@ hc_status hc_profile_enable(hc_ctx* c, uint32_t max_steps) {
   if (c->poisoned) return HC_E_STATE;
   DeviceGuard dg(c->cfg.device);
   if (!dg.ok) return HC_E_INVAL;
-  if (c->enqueued && hipEventSynchronize(c->done) != hipSuccess) return fail_hip(c);
+  if (c->enqueued && host_wait(c) != hipSuccess) return fail_hip(c);
   free_prof(c);
   if (max_steps == 0) return HC_OK;
   c->prof.assign((size_t)max_steps * HC_NUM_STAGES * 2, nullptr);
@@ -731,9 +759,9 @@ hc_status hc_destroy(hc_ctx* c) {
   hc_status st = HC_OK;
   {
     DeviceGuard dg(c->cfg.device);
-    if (c->enqueued && c->done && hipEventSynchronize(c->done) != hipSuccess) st = HC_E_HIP;
+    if (c->enqueued && c->done && host_wait(c) != hipSuccess) st = HC_E_HIP;
     free_prof(c);
-    if (c->done) (void)hipEventDestroy(c->done);
+    destroy_sync(c);
     free_host(c);
   }
   delete c;
@@ -754,7 +782,7 @@ hc_status hc_test_hook(hc_ctx* c, int kind, int64_t arg, uint64_t* out) {
     case HC_TEST_CORRUPT_LRU: {
       if (!c) return HC_E_INVAL;
       DeviceGuard dg(c->cfg.device);
-      if (c->enqueued && hipEventSynchronize(c->done) != hipSuccess) return fail_hip(c);
+      if (c->enqueued && host_wait(c) != hipSuccess) return fail_hip(c);
       // every slot claimed used, an empty queue: the next step that misses
       // finds no victim
       const size_t U = (size_t)c->dev.S * c->dev.G;
